@@ -1,0 +1,309 @@
+"""CPU oracle for the fine-grained blockwise FP8 path (TEST INFRASTRUCTURE).
+
+Only the tests, ``__graft_entry__.smoke()`` and the bench's ``cpu_baseline``
+leg may import this package.  It wraps ``fgb_oracle.c`` (plain C, fp64 unless
+an operation is defined in fp32) through ctypes with numpy arrays, and shares
+no code with the HIP library.  Each wrapper's docstring names the C function;
+the C source cites the page section each one follows.
+"""
+import ctypes as C
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = _build.LIB
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+            _build.build()
+        L = C.CDLL(path)
+        p = C.c_void_p
+        i64 = C.c_int64
+        i32 = C.c_int
+        L.orc_e4m3_decode.restype = C.c_double
+        L.orc_e4m3_decode.argtypes = [C.c_uint8]
+        L.orc_e4m3_encode.restype = C.c_uint8
+        L.orc_e4m3_encode.argtypes = [C.c_double]
+        L.orc_scale_exp.restype = C.c_int
+        L.orc_scale_exp.argtypes = [C.c_double, C.c_int]
+        L.orc_e4m3_encode_f32.argtypes = [p, i64, p]
+        L.orc_e4m3_decode_all.argtypes = [p]
+        L.orc_scale_exp_f32.argtypes = [p, i64, i32, p]
+        L.orc_quant_rowwise.argtypes = [p, i32, i64, i64, i64, i32, i32, p, i64, p, i64]
+        L.orc_quant_blockwise.argtypes = [p, i32, i64, i64, i64, p, i64, p, i64]
+        L.orc_dequant.argtypes = [p, p, i32, i64, i64, p]
+        L.orc_direct_transpose.argtypes = [p, p, i64, i64, p, p]
+        L.orc_block_transpose.argtypes = [p, p, i64, i64, p, p]
+        L.orc_block_gemm.argtypes = [p, p, i32, p, p, i32, p, i64, i64, i64, i64, i64, i64, p]
+        L.orc_block_gemm_sampled.argtypes = [p, p, i32, p, p, i32, p, i64, i64, i64, i64, i64,
+                                             p, p, i64, p]
+        L.orc_grouped_gemm_sampled.argtypes = [p, p, p, p, p, i32, i64, i64, p, p, i64, p]
+        L.orc_permute_pad.restype = C.c_int64
+        L.orc_permute_pad.argtypes = [p, p, p, i64, i32, i32, i64, i32, p, p, p, p, i64]
+        L.orc_unpermute_unpad.argtypes = [p, p, p, i64, i32, i64, p]
+        L.orc_expf.restype = C.c_float
+        L.orc_expf.argtypes = [C.c_float]
+        L.orc_expf_bulk.argtypes = [p, i64, p]
+        L.orc_swiglu_quant.argtypes = [p, i64, i64, i64, p, i32, p, p]
+        L.orc_mx2_quant.argtypes = [p, i64, i64, i64, p, p, p]
+        L.orc_mx2_dequant.argtypes = [p, p, p, i64, i64, i64, p]
+        L.orc_snr_db.restype = C.c_double
+        L.orc_snr_db.argtypes = [p, p, i64]
+        L.orc_bf16_to_f32.argtypes = [p, i64, p]
+        _lib = L
+    return _lib
+
+
+F32, BF16 = 0, 1
+ROW1x128, ROW1x32, BLOCK128 = 0, 1, 2
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a)
+    assert a.dtype == dtype, (a.dtype, dtype)
+    return a
+
+
+def _xdtype(x):
+    if x.dtype == np.float32:
+        return F32
+    if x.dtype == np.uint16:  # bf16 bit patterns
+        return BF16
+    raise TypeError("oracle inputs are float32 or bf16 bit patterns (uint16)")
+
+
+# ---- formats -------------------------------------------------------------
+def e4m3_decode_table():
+    """orc_e4m3_decode over all 256 codes (fp64; NaN for 0x7F/0xFF)."""
+    out = np.empty(256, np.float64)
+    lib().orc_e4m3_decode_all(_p(out))
+    return out
+
+
+def e4m3_encode(x):
+    """orc_e4m3_encode applied to float32 values."""
+    x = _c(x, np.float32)
+    q = np.empty(x.shape, np.uint8)
+    lib().orc_e4m3_encode_f32(_p(x), x.size, _p(q))
+    return q
+
+
+def scale_exp(amax, emin=-22):
+    """orc_scale_exp applied to float32 amax values."""
+    a = _c(amax, np.float32)
+    e = np.empty(a.shape, np.int32)
+    lib().orc_scale_exp_f32(_p(a), a.size, emin, _p(e))
+    return e
+
+
+def expf(x):
+    """orc_expf (the SwiGLU exponential) applied elementwise."""
+    x = _c(x, np.float32)
+    y = np.empty_like(x)
+    lib().orc_expf_bulk(_p(x), x.size, _p(y))
+    return y
+
+
+def bf16_to_f32(h):
+    h = _c(h, np.uint16)
+    out = np.empty(h.shape, np.float32)
+    lib().orc_bf16_to_f32(_p(h), h.size, _p(out))
+    return out
+
+
+# ---- quantization --------------------------------------------------------
+def quant_rowwise(x, group=128):
+    """orc_quant_rowwise: x [rows, cols] fp32 or bf16 bits -> (q, s)."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    emin = -22 if group == 128 else -127
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty((rows, cols // group), np.uint8)
+    lib().orc_quant_rowwise(_p(x), _xdtype(x), rows, cols, cols, group, emin, _p(q), cols,
+                            _p(s), cols // group)
+    return q, s
+
+
+def quant_blockwise(w):
+    """orc_quant_blockwise: w [rows, cols] -> (q, s[ceil(rows/128), cols/128])."""
+    w = np.ascontiguousarray(w)
+    rows, cols = w.shape
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty(((rows + 127) // 128, cols // 128), np.uint8)
+    lib().orc_quant_blockwise(_p(w), _xdtype(w), rows, cols, cols, _p(q), cols, _p(s),
+                              cols // 128)
+    return q, s
+
+
+def dequant(q, s, gran):
+    """orc_dequant -> fp64 [rows, cols]."""
+    q = _c(q, np.uint8)
+    s = _c(s, np.uint8)
+    out = np.empty(q.shape, np.float64)
+    lib().orc_dequant(_p(q), _p(s), gran, q.shape[0], q.shape[1], _p(out))
+    return out
+
+
+def direct_transpose(q, s):
+    """orc_direct_transpose: row-wise (q[T,C], s[T,C/128]) -> (qt[C,T], st[C,T/128])."""
+    q = _c(q, np.uint8)
+    s = _c(s, np.uint8)
+    T, Cc = q.shape
+    qt = np.empty((Cc, T), np.uint8)
+    st = np.empty((Cc, T // 128), np.uint8)
+    lib().orc_direct_transpose(_p(q), _p(s), T, Cc, _p(qt), _p(st))
+    return qt, st
+
+
+def block_transpose(q, s):
+    """orc_block_transpose: (W[rows,cols], s[rows/128, cols/128]) -> transposed pair."""
+    q = _c(q, np.uint8)
+    s = _c(s, np.uint8)
+    rows, cols = q.shape
+    qt = np.empty((cols, rows), np.uint8)
+    st = np.empty((cols // 128, rows // 128), np.uint8)
+    lib().orc_block_transpose(_p(q), _p(s), rows, cols, _p(qt), _p(st))
+    return qt, st
+
+
+# ---- GEMMs ---------------------------------------------------------------
+def block_gemm(a, sa, a_gran, b, sb, b_gran, b_l1=None, g1=0):
+    """orc_block_gemm: D[M,N] = A[M,K] * B[N,K]^T with block scales, fp64."""
+    a = _c(a, np.uint8)
+    b = _c(b, np.uint8)
+    sa = _c(sa, np.uint8)
+    sb = _c(sb, np.uint8)
+    if b_l1 is not None:
+        b_l1 = _c(b_l1, np.float32)
+    M, K = a.shape
+    N = b.shape[0]
+    d = np.empty((M, N), np.float64)
+    lib().orc_block_gemm(_p(a), _p(sa), a_gran, _p(b), _p(sb), b_gran, _p(b_l1), g1, M, N, K,
+                         K, K, _p(d))
+    return d
+
+
+def block_gemm_sampled(a, sa, a_gran, b, sb, b_gran, mi, ni, b_l1=None, g1=0):
+    """orc_block_gemm_sampled: the same result at coordinates (mi[i], ni[i])."""
+    a = _c(a, np.uint8)
+    b = _c(b, np.uint8)
+    sa = _c(sa, np.uint8)
+    sb = _c(sb, np.uint8)
+    if b_l1 is not None:
+        b_l1 = _c(b_l1, np.float32)
+    mi = _c(np.asarray(mi, np.int64), np.int64)
+    ni = _c(np.asarray(ni, np.int64), np.int64)
+    K = a.shape[1]
+    N = b.shape[0]
+    out = np.empty(mi.shape, np.float64)
+    lib().orc_block_gemm_sampled(_p(a), _p(sa), a_gran, _p(b), _p(sb), b_gran, _p(b_l1), g1, N,
+                                 K, K, K, _p(mi), _p(ni), mi.size, _p(out))
+    return out
+
+
+def grouped_gemm_sampled(a, sa, b, sb, off, mi, ni):
+    """orc_grouped_gemm_sampled: M-grouped contiguous GEMM at (mi, ni); NaN outside segments."""
+    a = _c(a, np.uint8)
+    sa = _c(sa, np.uint8)
+    b = _c(b, np.uint8)
+    sb = _c(sb, np.uint8)
+    off = _c(np.asarray(off, np.int32), np.int32)
+    G, N, K = b.shape
+    mi = _c(np.asarray(mi, np.int64), np.int64)
+    ni = _c(np.asarray(ni, np.int64), np.int64)
+    out = np.empty(mi.shape, np.float64)
+    lib().orc_grouped_gemm_sampled(_p(a), _p(sa), _p(b), _p(sb), _p(off), G, N, K, _p(mi),
+                                   _p(ni), mi.size, _p(out))
+    return out
+
+
+# ---- MoE data movement ---------------------------------------------------
+def permute_pad(xq, xs, topk_idx, G, pad_multiple=16, M_cap=None):
+    """orc_permute_pad -> (out_q, out_s, row_map, offsets, rows_used)."""
+    xq = _c(xq, np.uint8)
+    xs = _c(xs, np.uint8)
+    topk_idx = _c(np.asarray(topk_idx, np.int32), np.int32)
+    T, H = xq.shape
+    topk = topk_idx.shape[1]
+    if M_cap is None:
+        M_cap = T * topk + (pad_multiple - 1) * G
+    out_q = np.full((M_cap, H), 0xCD, np.uint8)
+    out_s = np.full((M_cap, H // 128), 0xCD, np.uint8)
+    row_map = np.empty((T, topk), np.int32)
+    off = np.empty(G + 1, np.int32)
+    used = lib().orc_permute_pad(_p(xq), _p(xs), _p(topk_idx), T, topk, G, H, pad_multiple,
+                                 _p(out_q), _p(out_s), _p(row_map), _p(off), M_cap)
+    if used < 0:
+        raise ValueError("M_cap too small")
+    return out_q, out_s, row_map, off, int(used)
+
+
+def unpermute_unpad(y, row_map, probs=None):
+    """orc_unpermute_unpad: y bf16 bits [M, H] -> out bf16 bits [T, H]."""
+    y = _c(y, np.uint16)
+    row_map = _c(np.asarray(row_map, np.int32), np.int32)
+    if probs is not None:
+        probs = _c(probs, np.float32)
+    T, topk = row_map.shape
+    H = y.shape[1]
+    out = np.empty((T, H), np.uint16)
+    lib().orc_unpermute_unpad(_p(y), _p(row_map), _p(probs), T, topk, H, _p(out))
+    return out
+
+
+def swiglu_quant(h, off=None):
+    """orc_swiglu_quant: h bf16 bits [M, 2F] (gate|up) -> (q [M,F], s [M,F/128]).
+
+    Rows at or past off[G] (when off is given) are left as zeros here."""
+    h = _c(h, np.uint16)
+    M, F2 = h.shape
+    F = F2 // 2
+    q = np.zeros((M, F), np.uint8)
+    s = np.zeros((M, F // 128), np.uint8)
+    G = 0
+    if off is not None:
+        off = _c(np.asarray(off, np.int32), np.int32)
+        G = off.size - 1
+    lib().orc_swiglu_quant(_p(h), M, F, F2, _p(off), G, _p(q), _p(s))
+    return q, s
+
+
+# ---- MOSS two-level ------------------------------------------------------
+def mx2_quant(x, g1=10240):
+    """orc_mx2_quant: x bf16 bits [R, C] -> (q, s2 [R, C/32], s1 [R, ceil(C/g1)])."""
+    x = _c(x, np.uint16)
+    R, Cc = x.shape
+    ng = (Cc + g1 - 1) // g1
+    q = np.empty((R, Cc), np.uint8)
+    s2 = np.empty((R, Cc // 32), np.uint8)
+    s1 = np.empty((R, ng), np.float32)
+    lib().orc_mx2_quant(_p(x), R, Cc, g1, _p(q), _p(s2), _p(s1))
+    return q, s2, s1
+
+
+def mx2_dequant(q, s2, s1, g1=10240):
+    """orc_mx2_dequant -> float32 [R, C]."""
+    q = _c(q, np.uint8)
+    s2 = _c(s2, np.uint8)
+    s1 = _c(s1, np.float32)
+    R, Cc = q.shape
+    out = np.empty((R, Cc), np.float32)
+    lib().orc_mx2_dequant(_p(q), _p(s2), _p(s1), R, Cc, g1, _p(out))
+    return out
+
+
+def snr_db(x, xhat):
+    """orc_snr_db: 10 log10(sum x^2 / sum (x - xhat)^2) in fp64."""
+    x = _c(x, np.float32)
+    xhat = _c(xhat, np.float32)
+    return lib().orc_snr_db(_p(x), _p(xhat), x.size)
