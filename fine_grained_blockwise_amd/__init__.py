@@ -1,0 +1,286 @@
+"""fine_grained_blockwise_amd -- fine-grained blockwise FP8 for AMD MI355X (gfx950).
+
+A thin Python binding over libfgb.so (include/fgb.h).  Every function here
+only marshals arguments: it checks shapes, allocates outputs with
+``torch.empty`` on the input's device and calls the C entry point of the same
+name on torch's current HIP stream.  All arithmetic runs in the HIP kernels.
+
+There is no fallback: if libfgb.so is missing, importing this package raises.
+"""
+import ctypes as C
+import os
+
+import torch
+
+__all__ = [
+    "lib", "symbols", "FgbError",
+    "fp8_quant_rowwise", "fp8_quant_blockwise", "fp8_dequant", "fgb_e4m3_encode",
+    "fp8_direct_transpose", "fp8_block_gemm", "fp8_grouped_gemm", "permute_pad",
+    "permute_pad_workspace_size", "unpermute_unpad", "swiglu_quant", "mx2_quant", "mx2_dequant",
+    "F32", "BF16", "ROW1x128", "ROW1x32", "BLOCK128",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfgb.so")
+
+F32, BF16 = 0, 1
+ROW1x128, ROW1x32, BLOCK128 = 0, 1, 2
+
+SYMBOLS = [
+    "fgb_last_error", "fgb_version", "fp8_quant_rowwise", "fp8_quant_blockwise", "fp8_dequant",
+    "fgb_e4m3_encode", "fp8_direct_transpose", "fp8_block_gemm", "fp8_grouped_gemm",
+    "permute_pad", "permute_pad_workspace_size", "unpermute_unpad", "swiglu_quant", "mx2_quant",
+    "mx2_dequant",
+]
+
+
+class FgbError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__(f"{fn} failed with status {code}: {msg}")
+        self.code = code
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libfgb.so not found at {LIB_PATH}; build it with "
+                      "`python -c 'import __graft_entry__ as g; g.build()'`")
+
+_lib = C.CDLL(LIB_PATH)
+_p, _i64, _i32, _sz = C.c_void_p, C.c_int64, C.c_int, C.c_size_t
+_SIG = {
+    "fgb_last_error": (C.c_char_p, []),
+    "fgb_version": (C.c_char_p, []),
+    "fp8_quant_rowwise": (_i32, [_p, _i32, _i64, _i64, _i64, _i32, _p, _i64, _p, _i64, _p]),
+    "fp8_quant_blockwise": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p]),
+    "fp8_dequant": (_i32, [_p, _p, _i32, _i64, _i64, _p, _i32, _p]),
+    "fgb_e4m3_encode": (_i32, [_p, _i64, _p, _p]),
+    "fp8_direct_transpose": (_i32, [_p, _p, _i32, _i64, _i64, _p, _p, _p]),
+    "fp8_block_gemm": (_i32, [_p, _p, _i32, _p, _p, _i32, _p, _i64, _i64, _i64, _i64, _i64, _i64,
+                              _p, _i32, _i64, _i32, _p, _sz, _p]),
+    "fp8_grouped_gemm": (_i32, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, _i32, _p]),
+    "permute_pad": (_i32, [_p, _p, _p, _i64, _i32, _i32, _i64, _i32, _p, _p, _p, _p, _i64, _p,
+                           _sz, _p]),
+    "permute_pad_workspace_size": (_sz, [_i64, _i32, _i32]),
+    "unpermute_unpad": (_i32, [_p, _p, _p, _i64, _i32, _i64, _p, _p]),
+    "swiglu_quant": (_i32, [_p, _i64, _i64, _i64, _p, _i32, _p, _p, _p]),
+    "mx2_quant": (_i32, [_p, _i64, _i64, _i64, _p, _p, _p, _p]),
+    "mx2_dequant": (_i32, [_p, _p, _p, _i64, _i64, _i64, _p, _p]),
+}
+for _name, (_res, _args) in _SIG.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+def lib():
+    """The loaded ctypes library (C ABI of include/fgb.h)."""
+    return _lib
+
+
+def symbols():
+    return list(SYMBOLS)
+
+
+def _call(name, *args):
+    rc = getattr(_lib, name)(*args)
+    if rc != 0:
+        raise FgbError(name, rc, _lib.fgb_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return C.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"expected float32 or bfloat16, got {t.dtype}")
+
+
+def _check_dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on the same GPU")
+    return dev
+
+
+def _row_ld(t):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    return t.stride(0)
+
+
+# ---------------------------------------------------------------------------
+def fp8_quant_rowwise(x, group=128, q=None, s=None):
+    """1 x group quantization of x [rows, cols] (fp32/bf16) -> (q uint8, s uint8 [rows, cols/group])."""
+    _check_dev(x, q, s)
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((rows, cols // group), dtype=torch.uint8, device=x.device)
+    _call("fp8_quant_rowwise", _ptr(x), _dtype_code(x), rows, cols, _row_ld(x), group, _ptr(q),
+          _row_ld(q), _ptr(s), _row_ld(s), _stream(x))
+    return q, s
+
+
+def fp8_quant_blockwise(w, q=None, s=None):
+    """128 x 128 quantization of w [rows, cols] -> (q, s [ceil(rows/128), cols/128])."""
+    _check_dev(w, q, s)
+    rows, cols = w.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=w.device)
+    if s is None:
+        s = torch.empty(((rows + 127) // 128, cols // 128), dtype=torch.uint8, device=w.device)
+    _call("fp8_quant_blockwise", _ptr(w), _dtype_code(w), rows, cols, _row_ld(w), _ptr(q),
+          _row_ld(q), _ptr(s), _row_ld(s), _stream(w))
+    return q, s
+
+
+def fp8_dequant(q, s, gran, out_dtype=torch.float32):
+    """decode(q) * 2^(s-127) -> out [rows, cols] (fp32 or bf16); q, s dense."""
+    _check_dev(q, s)
+    rows, cols = q.shape
+    out = torch.empty((rows, cols), dtype=out_dtype, device=q.device)
+    _call("fp8_dequant", _ptr(q.contiguous()), _ptr(s.contiguous()), gran, rows, cols, _ptr(out),
+          _dtype_code(out), _stream(q))
+    return out
+
+
+def fgb_e4m3_encode(x):
+    """Device E4M3 encoding of a float32 tensor (nearest even, saturating)."""
+    _check_dev(x)
+    x = x.contiguous()
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _call("fgb_e4m3_encode", _ptr(x), x.numel(), _ptr(q), _stream(x))
+    return q
+
+
+def fp8_direct_transpose(q, s, s_gran=ROW1x128):
+    """Scaling-aware transpose: (q [T, C], s) -> (qt [C, T], st)."""
+    _check_dev(q, s)
+    T, Cc = q.shape
+    qt = torch.empty((Cc, T), dtype=torch.uint8, device=q.device)
+    if s_gran == ROW1x128:
+        st = torch.empty((Cc, T // 128), dtype=torch.uint8, device=q.device)
+    else:
+        st = torch.empty((Cc // 128, T // 128), dtype=torch.uint8, device=q.device)
+    _call("fp8_direct_transpose", _ptr(q.contiguous()), _ptr(s.contiguous()), s_gran, T, Cc,
+          _ptr(qt), _ptr(st), _stream(q))
+    return qt, st
+
+
+def fp8_block_gemm(a, sa, a_gran, b, sb, b_gran, b_l1=None, g1=0, out_dtype=torch.bfloat16,
+                   d=None, accumulate=False):
+    """D = A * B^T with blockwise scales (A [M,K], B [N,K] codes) -> D [M, N]."""
+    _check_dev(a, sa, b, sb, b_l1, d)
+    M, K = a.shape
+    N = b.shape[0]
+    if d is None:
+        d = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _call("fp8_block_gemm", _ptr(a), _ptr(sa.contiguous()), a_gran, _ptr(b), _ptr(sb.contiguous()),
+          b_gran, _ptr(b_l1), g1, M, N, K, _row_ld(a), _row_ld(b), _ptr(d), _dtype_code(d),
+          _row_ld(d), int(bool(accumulate)), None, 0, _stream(a))
+    return d
+
+
+def fp8_grouped_gemm(a, sa, b, sb, group_offsets, out_dtype=torch.bfloat16, d=None):
+    """M-grouped contiguous GEMM: a [M_cap, K], b [G, N, K], offsets [G+1] (device) -> d [M_cap, N]."""
+    _check_dev(a, sa, b, sb, group_offsets, d)
+    M_cap, K = a.shape
+    G, N, _ = b.shape
+    if d is None:
+        d = torch.empty((M_cap, N), dtype=out_dtype, device=a.device)
+    _call("fp8_grouped_gemm", _ptr(a.contiguous()), _ptr(sa.contiguous()), _ptr(b.contiguous()),
+          _ptr(sb.contiguous()), _ptr(group_offsets), G, M_cap, N, K, _ptr(d), _dtype_code(d),
+          _stream(a))
+    return d
+
+
+def permute_pad_workspace_size(T, topk, G):
+    return int(_lib.permute_pad_workspace_size(T, topk, G))
+
+
+def permute_pad(xq, xs, topk_idx, G, pad_multiple=16, M_cap=None, workspace=None, out=None):
+    """Fused permute + pad -> (out_q [M_cap, H], out_s, row_map [T, topk], group_offsets [G+1])."""
+    _check_dev(xq, xs, topk_idx)
+    T, H = xq.shape
+    topk = topk_idx.shape[1]
+    if M_cap is None:
+        M_cap = T * topk + (pad_multiple - 1) * G
+    dev = xq.device
+    if out is None:
+        out_q = torch.empty((M_cap, H), dtype=torch.uint8, device=dev)
+        out_s = torch.empty((M_cap, H // 128), dtype=torch.uint8, device=dev)
+        row_map = torch.empty((T, topk), dtype=torch.int32, device=dev)
+        offs = torch.empty((G + 1,), dtype=torch.int32, device=dev)
+    else:
+        out_q, out_s, row_map, offs = out
+    ws_need = permute_pad_workspace_size(T, topk, G)
+    if workspace is None:
+        workspace = torch.empty((max(ws_need, 1),), dtype=torch.uint8, device=dev)
+    _call("permute_pad", _ptr(xq.contiguous()), _ptr(xs.contiguous()), _ptr(topk_idx.contiguous()),
+          T, topk, G, H, pad_multiple, _ptr(out_q), _ptr(out_s), _ptr(row_map), _ptr(offs), M_cap,
+          _ptr(workspace), workspace.numel(), _stream(xq))
+    return out_q, out_s, row_map, offs
+
+
+def unpermute_unpad(y, row_map, probs=None, out=None):
+    """out [T, H] bf16 = sum over slots of probs * y[row_map] (fmaf fold, RNE to bf16)."""
+    _check_dev(y, row_map, probs)
+    T, topk = row_map.shape
+    H = y.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    _call("unpermute_unpad", _ptr(y.contiguous()), _ptr(row_map.contiguous()),
+          _ptr(None if probs is None else probs.contiguous()), T, topk, H, _ptr(out), _stream(y))
+    return out
+
+
+def swiglu_quant(h, group_offsets=None, q=None, s=None):
+    """SwiGLU of h [M, 2F] (gate|up, bf16) + 1x128 quant -> (q [M, F], s [M, F/128])."""
+    _check_dev(h, group_offsets, q, s)
+    M, F2 = h.shape
+    F = F2 // 2
+    if q is None:
+        q = torch.empty((M, F), dtype=torch.uint8, device=h.device)
+    if s is None:
+        s = torch.empty((M, F // 128), dtype=torch.uint8, device=h.device)
+    G = 0 if group_offsets is None else group_offsets.numel() - 1
+    _call("swiglu_quant", _ptr(h), M, F, _row_ld(h), _ptr(group_offsets), G, _ptr(q), _ptr(s),
+          _stream(h))
+    return q, s
+
+
+def mx2_quant(x, g1=10240):
+    """MOSS two-level quantization of x [R, C] bf16 -> (q, s2 [R, C/32], s1 fp32 [R, ceil(C/g1)])."""
+    _check_dev(x)
+    R, Cc = x.shape
+    ng = (Cc + g1 - 1) // g1
+    q = torch.empty((R, Cc), dtype=torch.uint8, device=x.device)
+    s2 = torch.empty((R, Cc // 32), dtype=torch.uint8, device=x.device)
+    s1 = torch.empty((R, ng), dtype=torch.float32, device=x.device)
+    _call("mx2_quant", _ptr(x.contiguous()), R, Cc, g1, _ptr(q), _ptr(s2), _ptr(s1), _stream(x))
+    return q, s2, s1
+
+
+def mx2_dequant(q, s2, s1, g1=10240):
+    """x_hat = (decode(q) * 2^(s2-127)) * s1 -> fp32 [R, C]."""
+    _check_dev(q, s2, s1)
+    R, Cc = q.shape
+    out = torch.empty((R, Cc), dtype=torch.float32, device=q.device)
+    _call("mx2_dequant", _ptr(q.contiguous()), _ptr(s2.contiguous()), _ptr(s1.contiguous()), R, Cc,
+          g1, _ptr(out), _stream(q))
+    return out

@@ -1,0 +1,475 @@
+// moe.hip -- MoE expert data movement on row-wise FP8, and fused SwiGLU + quant.
+//
+// awesome-system-papers, "FP8-Flow-MoE: A Casting-Free FP8 Recipe without
+// Double Quantization Error", "Core method": fused permute + 16-aligned padding,
+// fused unpermute + unpadding, and SwiGLU fused with quantization so the
+// activation boundary emits FP8 directly; assumption 2: the expert linears'
+// outputs stay BF16 (the fc1 output feeding the activation, the fc2 output
+// feeding the combine).
+//
+// permute_pad runs in four launches, none of which needs a host sync:
+//   count   per chunk of tokens, a histogram of expert ids (LDS integer atomics)
+//   scan    per expert: total, padded segment size, segment start, and the
+//           start of each chunk's run inside the segment
+//   rowmap  per chunk, the rank of every (token, slot) among the chunk's slots
+//           of the same expert, in (token, slot) order -> row_map
+//   copy    one wave per token: the 16-byte chunks of the code row and the
+//           scale row are read once and written to each destination; extra
+//           waves fill the padding rows (code 0, scale byte 127).
+#include "fgb_internal.h"
+
+namespace fgb {
+
+constexpr int PP_CHUNK = 256; // tokens per histogram chunk
+
+struct PPWorkspace {
+    int32_t *cnt;    // [nchunks][G] slots per chunk per expert
+    int32_t *base;   // [nchunks][G] first destination row of the chunk's run
+    int32_t *total;  // [G] slots per expert
+};
+
+static size_t pp_nchunks(int64_t T) { return (size_t)((T + PP_CHUNK - 1) / PP_CHUNK); }
+
+static PPWorkspace pp_carve(void *ws, int64_t T, int G)
+{
+    size_t nc = pp_nchunks(T);
+    PPWorkspace w;
+    w.cnt = (int32_t *)ws;
+    w.base = w.cnt + nc * G;
+    w.total = w.base + nc * G;
+    return w;
+}
+
+__global__ __launch_bounds__(256) void pp_count_kernel(const int32_t *__restrict__ idx, int64_t T,
+                                                       int topk, int G, int32_t *__restrict__ cnt)
+{
+    extern __shared__ int32_t hist[];
+    for (int e = threadIdx.x; e < G; e += blockDim.x)
+        hist[e] = 0;
+    __syncthreads();
+    int64_t t0 = (int64_t)blockIdx.x * PP_CHUNK;
+    int64_t t1 = min(t0 + PP_CHUNK, T);
+    for (int64_t i = t0 * topk + threadIdx.x; i < t1 * topk; i += blockDim.x) {
+        int e = idx[i];
+        if (e >= 0 && e < G)
+            atomicAdd(&hist[e], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < G; e += blockDim.x)
+        cnt[(int64_t)blockIdx.x * G + e] = hist[e];
+}
+
+__global__ __launch_bounds__(256) void pp_scan_kernel(const int32_t *__restrict__ cnt, int nchunks,
+                                                      int G, int pad, int32_t *__restrict__ base,
+                                                      int32_t *__restrict__ total,
+                                                      int32_t *__restrict__ offs)
+{
+    extern __shared__ int32_t sh[]; // [G] padded sizes, then [G+1] offsets
+    int32_t *padded = sh, *off = sh + G;
+    for (int e = threadIdx.x; e < G; e += blockDim.x) {
+        int32_t s = 0;
+        for (int c = 0; c < nchunks; c++)
+            s += cnt[(int64_t)c * G + e];
+        total[e] = s;
+        padded[e] = (s + pad - 1) / pad * pad;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int32_t acc = 0;
+        for (int e = 0; e < G; e++) {
+            off[e] = acc;
+            acc += padded[e];
+        }
+        off[G] = acc;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e <= G; e += blockDim.x)
+        offs[e] = off[e];
+    for (int e = threadIdx.x; e < G; e += blockDim.x) {
+        int32_t run = off[e];
+        for (int c = 0; c < nchunks; c++) {
+            base[(int64_t)c * G + e] = run;
+            run += cnt[(int64_t)c * G + e];
+        }
+    }
+}
+
+// Ranks inside a chunk: slots are taken 256 at a time in (token, slot) order;
+// a slot's rank = running count of its expert + slots of the same expert in
+// earlier waves of this pass + same-expert lanes below it in its wave.
+__global__ __launch_bounds__(256) void pp_rowmap_kernel(const int32_t *__restrict__ idx, int64_t T,
+                                                        int topk, int G,
+                                                        const int32_t *__restrict__ base,
+                                                        int32_t *__restrict__ row_map)
+{
+    extern __shared__ int32_t sm[]; // running[G], wcnt[4][G]
+    int32_t *running = sm, *wcnt = sm + G;
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    for (int e = threadIdx.x; e < G; e += blockDim.x)
+        running[e] = base[(int64_t)blockIdx.x * G + e];
+    int nbits = 0;
+    while ((1 << nbits) < G + 1)
+        nbits++;
+    int64_t s0 = (int64_t)blockIdx.x * PP_CHUNK * topk;
+    int64_t s1 = min((int64_t)(blockIdx.x + 1) * PP_CHUNK, T) * topk;
+    for (int64_t p = s0; p < s1; p += 256) {
+        for (int e = threadIdx.x; e < 4 * G; e += blockDim.x)
+            wcnt[e] = 0;
+        __syncthreads();
+        int64_t i = p + threadIdx.x;
+        int e = i < s1 ? idx[i] : -1;
+        int key = (e >= 0 && e < G) ? e : G; // G = dropped / out of range
+        uint64_t peers = __ballot(i < s1);
+        for (int b = 0; b < nbits; b++) {
+            uint64_t m = __ballot((key >> b) & 1);
+            peers &= ((key >> b) & 1) ? m : ~m;
+        }
+        uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+        int rank_w = __popcll(peers & below);
+        bool leader = (peers & below) == 0;
+        if (i < s1 && key < G && leader)
+            wcnt[wave * G + key] = __popcll(peers);
+        __syncthreads();
+        if (i < s1) {
+            if (key < G) {
+                int r = running[key] + rank_w;
+                for (int w = 0; w < wave; w++)
+                    r += wcnt[w * G + key];
+                row_map[i] = r;
+            } else {
+                row_map[i] = -1;
+            }
+        }
+        __syncthreads();
+        for (int ee = threadIdx.x; ee < G; ee += blockDim.x)
+            running[ee] += wcnt[ee] + wcnt[G + ee] + wcnt[2 * G + ee] + wcnt[3 * G + ee];
+        __syncthreads();
+    }
+}
+
+// One wave per token (blocks [0, tok_blocks)), then one wave per potential
+// padding row (pad-1 per expert).
+__global__ __launch_bounds__(256) void pp_copy_kernel(const uint8_t *__restrict__ xq,
+                                                      const uint8_t *__restrict__ xs,
+                                                      const int32_t *__restrict__ row_map,
+                                                      int64_t T, int topk, int G, int64_t H,
+                                                      int pad, const int32_t *__restrict__ total,
+                                                      const int32_t *__restrict__ offs,
+                                                      uint8_t *__restrict__ out_q,
+                                                      uint8_t *__restrict__ out_s, int64_t tok_blocks,
+                                                      int64_t M_cap)
+{
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int64_t H16 = H / 16, H128 = H / 128;
+    if ((int64_t)blockIdx.x < tok_blocks) {
+        int64_t t = (int64_t)blockIdx.x * 4 + wave;
+        if (t >= T)
+            return;
+        int32_t my_row = lane < topk ? row_map[t * topk + lane] : -1;
+        my_row = my_row < M_cap ? my_row : -1; // defensive: never write past the buffer
+        const uint8_t *src = xq + t * H;
+        for (int64_t c0 = 0; c0 < H16; c0 += 64 * 8) {
+            uint4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                int64_t c = c0 + u * 64 + lane;
+                v[u] = c < H16 ? *reinterpret_cast<const uint4 *>(src + c * 16) : make_uint4(0, 0, 0, 0);
+            }
+            for (int k = 0; k < topk; k++) {
+                int32_t r = __shfl(my_row, k);
+                if (r < 0)
+                    continue;
+                uint8_t *dst = out_q + (int64_t)r * H;
+#pragma unroll
+                for (int u = 0; u < 8; u++) {
+                    int64_t c = c0 + u * 64 + lane;
+                    if (c < H16)
+                        *reinterpret_cast<uint4 *>(dst + c * 16) = v[u];
+                }
+            }
+        }
+        for (int64_t c0 = 0; c0 < H128; c0 += 64) {
+            int64_t c = c0 + lane;
+            uint8_t sv = c < H128 ? xs[t * H128 + c] : 0;
+            for (int k = 0; k < topk; k++) {
+                int32_t r = __shfl(my_row, k);
+                if (r >= 0 && c < H128)
+                    out_s[(int64_t)r * H128 + c] = sv;
+            }
+        }
+    } else {
+        int64_t pidx = ((int64_t)blockIdx.x - tok_blocks) * 4 + wave;
+        if (pad <= 1 || pidx >= (int64_t)(pad - 1) * G)
+            return;
+        int e = (int)(pidx / (pad - 1)), j = (int)(pidx % (pad - 1));
+        int64_t r = (int64_t)offs[e] + total[e] + j;
+        if (r >= offs[e + 1])
+            return;
+        uint8_t *dst = out_q + r * H;
+        for (int64_t c = lane; c < H16; c += 64)
+            *reinterpret_cast<uint4 *>(dst + c * 16) = make_uint4(0, 0, 0, 0);
+        for (int64_t c = lane; c < H128; c += 64)
+            out_s[r * H128 + c] = 127;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// unpermute + unpad: one wave per token; each lane owns 16-byte chunks (8 bf16)
+// of the output row; the topk source rows are gathered 8 at a time with all
+// their loads in flight, then folded in slot order with fused multiply-adds.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void unpermute_kernel(const uint16_t *__restrict__ y,
+                                                        const int32_t *__restrict__ row_map,
+                                                        const float *__restrict__ probs, int64_t T,
+                                                        int topk, int64_t H,
+                                                        uint16_t *__restrict__ out)
+{
+    const int lane = lane_id();
+    const int64_t H8 = H / 8;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    for (int64_t t = wave; t < T; t += nwaves) {
+        int32_t my_row = lane < topk ? row_map[t * topk + lane] : -1;
+        float my_w = lane < topk ? (probs ? probs[t * topk + lane] : 1.0f) : 0.0f;
+        for (int64_t c0 = 0; c0 < H8; c0 += 64 * 2) {
+            float acc[2][8];
+#pragma unroll
+            for (int u = 0; u < 2; u++)
+#pragma unroll
+                for (int x = 0; x < 8; x++)
+                    acc[u][x] = 0.0f;
+            for (int k0 = 0; k0 < topk; k0 += 8) {
+                uint4 v[8][2];
+                int32_t rr[8];
+                float ww[8];
+#pragma unroll
+                for (int kk = 0; kk < 8; kk++) {
+                    int k = k0 + kk;
+                    rr[kk] = __shfl(my_row, k < topk ? k : 63);
+                    ww[kk] = __shfl(my_w, k < topk ? k : 63);
+                    if (k >= topk)
+                        rr[kk] = -1;
+#pragma unroll
+                    for (int u = 0; u < 2; u++) {
+                        int64_t c = c0 + u * 64 + lane;
+                        v[kk][u] = (rr[kk] >= 0 && c < H8)
+                                       ? *reinterpret_cast<const uint4 *>(y + (int64_t)rr[kk] * H + c * 8)
+                                       : make_uint4(0, 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int kk = 0; kk < 8; kk++) {
+                    if (rr[kk] < 0)
+                        continue;
+#pragma unroll
+                    for (int u = 0; u < 2; u++) {
+                        uint32_t w4[4] = {v[kk][u].x, v[kk][u].y, v[kk][u].z, v[kk][u].w};
+#pragma unroll
+                        for (int x = 0; x < 4; x++) {
+                            acc[u][2 * x] = __builtin_fmaf(ww[kk], bf16lo(w4[x]), acc[u][2 * x]);
+                            acc[u][2 * x + 1] = __builtin_fmaf(ww[kk], bf16hi(w4[x]), acc[u][2 * x + 1]);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 2; u++) {
+                int64_t c = c0 + u * 64 + lane;
+                if (c < H8) {
+                    uint4 o;
+                    o.x = bf16_rne(acc[u][0]) | (bf16_rne(acc[u][1]) << 16);
+                    o.y = bf16_rne(acc[u][2]) | (bf16_rne(acc[u][3]) << 16);
+                    o.z = bf16_rne(acc[u][4]) | (bf16_rne(acc[u][5]) << 16);
+                    o.w = bf16_rne(acc[u][6]) | (bf16_rne(acc[u][7]) << 16);
+                    *reinterpret_cast<uint4 *>(out + t * H + c * 8) = o;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// SwiGLU + 1x128 quant.
+// The exponential is the library's own fp32 function: Cody-Waite reduction
+// x = n*ln2 + r with ln2 split in two (Cody & Waite 1980), the degree-7 Taylor
+// polynomial of e^r (coefficients 1/j! rounded to fp32) in Horner form with
+// fused multiply-adds, and scaling by 2^n in two exact power-of-two steps.
+// Every step rounds once in fp32, so the result is reproducible bit for bit.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float fgb_expf(float x)
+{
+    float n = __builtin_rintf(x * 0x1.715476p+0f);
+    float r = __builtin_fmaf(-n, 0x1.62e4p-1f, x);
+    r = __builtin_fmaf(-n, 0x1.7f7d1cp-20f, r);
+    float p = 0x1.a01a02p-13f;
+    p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);
+    p = __builtin_fmaf(p, r, 0x1.111112p-7f);
+    p = __builtin_fmaf(p, r, 0x1.555556p-5f);
+    p = __builtin_fmaf(p, r, 0x1.555556p-3f);
+    p = __builtin_fmaf(p, r, 0x1p-1f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    int ni = (int)n;
+    int n1 = ni / 2, n2 = ni - n1;
+    float res = (p * pow2f(n1)) * pow2f(n2);
+    res = x > 0x1.62e43p+6f ? __builtin_inff() : res;
+    res = x < -0x1.9fe36ap+6f ? 0.0f : res;
+    return res;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u)
+{
+    float e = fgb_expf(-g);
+    float s = g / (1.0f + e);
+    return s * u;
+}
+
+// One wave per row; lane owns 8 gate and the matching 8 up values (16-byte
+// loads); 16 lanes form one 128-element output group.
+__global__ __launch_bounds__(256) void swiglu_quant_kernel(const uint8_t *__restrict__ h, int64_t M,
+                                                           int64_t F, int64_t ldh_bytes,
+                                                           const int32_t *__restrict__ offs, int G,
+                                                           uint8_t *__restrict__ q,
+                                                           uint8_t *__restrict__ s)
+{
+    const int lane = lane_id();
+    const int64_t rows = offs ? (int64_t)offs[G] : M;
+    const int64_t F8 = F / 8;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    for (int64_t r = wave; r < rows && r < M; r += nwaves) {
+        const uint8_t *hr = h + r * ldh_bytes;
+        for (int64_t c0 = 0; c0 < F8; c0 += 64 * 2) {
+            uint4 gv[2], uv[2];
+#pragma unroll
+            for (int u = 0; u < 2; u++) {
+                int64_t c = c0 + u * 64 + lane;
+                gv[u] = c < F8 ? *reinterpret_cast<const uint4 *>(hr + c * 16) : make_uint4(0, 0, 0, 0);
+                uv[u] = c < F8 ? *reinterpret_cast<const uint4 *>(hr + F * 2 + c * 16) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < 2; u++) {
+                int64_t c = c0 + u * 64 + lane;
+                uint32_t gw[4] = {gv[u].x, gv[u].y, gv[u].z, gv[u].w};
+                uint32_t uw[4] = {uv[u].x, uv[u].y, uv[u].z, uv[u].w};
+                float a[8];
+                uint32_t m = 0;
+#pragma unroll
+                for (int x = 0; x < 4; x++) {
+                    a[2 * x] = silu_mul(bf16lo(gw[x]), bf16lo(uw[x]));
+                    a[2 * x + 1] = silu_mul(bf16hi(gw[x]), bf16hi(uw[x]));
+                    m = max(m, __float_as_uint(a[2 * x]) & 0x7FFFFFFFu);
+                    m = max(m, __float_as_uint(a[2 * x + 1]) & 0x7FFFFFFFu);
+                }
+                m = group_max_u32<16>(m);
+                int e = scale_exp_from_bits(m, -22);
+                float sc = pow2f(-e);
+                if (c < F8) {
+                    uint2 o;
+                    o.x = cvt4_e4m3(a[0] * sc, a[1] * sc, a[2] * sc, a[3] * sc);
+                    o.y = cvt4_e4m3(a[4] * sc, a[5] * sc, a[6] * sc, a[7] * sc);
+                    *reinterpret_cast<uint2 *>(q + r * F + c * 8) = o;
+                    if ((lane & 15) == 0)
+                        s[r * (F / 128) + c / 16] = (uint8_t)(e + 127);
+                }
+            }
+        }
+    }
+}
+
+} // namespace fgb
+
+using namespace fgb;
+
+extern "C" size_t permute_pad_workspace_size(int64_t T, int topk, int G)
+{
+    (void)topk;
+    if (T < 0 || G < 1)
+        return 0;
+    return (2 * pp_nchunks(T) * (size_t)G + (size_t)G) * sizeof(int32_t);
+}
+
+extern "C" int permute_pad(const uint8_t *xq, const uint8_t *xs, const int32_t *topk_idx,
+                           int64_t T, int topk, int G, int64_t H, int pad_multiple,
+                           uint8_t *out_q, uint8_t *out_s, int32_t *row_map,
+                           int32_t *group_offsets, int64_t M_cap, void *workspace,
+                           size_t ws_bytes, void *stream)
+{
+    clear_error();
+    FGB_REQUIRE(xq && xs && topk_idx && out_q && out_s && row_map && group_offsets, FGB_EINVAL,
+                "permute_pad: null pointer");
+    FGB_REQUIRE(T >= 0 && topk >= 1 && topk <= 64 && G >= 1 && G <= 1024, FGB_EINVAL,
+                "permute_pad: need T >= 0, 1 <= topk <= 64, 1 <= G <= 1024");
+    FGB_REQUIRE(H > 0 && H % 128 == 0, FGB_EINVAL, "permute_pad: H must be a positive multiple of 128");
+    FGB_REQUIRE(pad_multiple >= 1 && pad_multiple <= 256, FGB_EINVAL,
+                "permute_pad: pad_multiple must be in [1, 256]");
+    FGB_REQUIRE(M_cap >= T * topk + (int64_t)(pad_multiple - 1) * G, FGB_EINVAL,
+                "permute_pad: M_cap must be >= T*topk + (pad_multiple-1)*G");
+    FGB_REQUIRE(M_cap < (1ll << 31), FGB_EINVAL, "permute_pad: M_cap must fit in int32");
+    FGB_REQUIRE(aligned16(xq) && aligned16(out_q), FGB_EINVAL,
+                "permute_pad: xq and out_q must be 16-byte aligned");
+    size_t need = permute_pad_workspace_size(T, topk, G);
+    FGB_REQUIRE(workspace && ws_bytes >= need, FGB_EWORKSPACE,
+                "permute_pad: workspace of %zu bytes required", need);
+    hipStream_t st = (hipStream_t)stream;
+    PPWorkspace w = pp_carve(workspace, T, G);
+    int nchunks = (int)pp_nchunks(T);
+    if (nchunks > 0) {
+        pp_count_kernel<<<nchunks, 256, G * sizeof(int32_t), st>>>(topk_idx, T, topk, G, w.cnt);
+        FGB_LAUNCHED("permute_pad/count");
+    }
+    pp_scan_kernel<<<1, 256, (2 * G + 1) * sizeof(int32_t), st>>>(w.cnt, nchunks, G, pad_multiple,
+                                                                 w.base, w.total, group_offsets);
+    FGB_LAUNCHED("permute_pad/scan");
+    if (nchunks > 0) {
+        pp_rowmap_kernel<<<nchunks, 256, 5 * G * sizeof(int32_t), st>>>(topk_idx, T, topk, G, w.base, row_map);
+        FGB_LAUNCHED("permute_pad/rowmap");
+    }
+    int64_t tok_blocks = (T + 3) / 4;
+    int64_t pad_blocks = ((int64_t)(pad_multiple - 1) * G + 3) / 4;
+    int64_t grid = tok_blocks + pad_blocks;
+    if (grid > 0) {
+        pp_copy_kernel<<<(unsigned)grid, 256, 0, st>>>(xq, xs, row_map, T, topk, G, H, pad_multiple,
+                                                      w.total, group_offsets, out_q, out_s, tok_blocks, M_cap);
+        FGB_LAUNCHED("permute_pad/copy");
+    }
+    return FGB_OK;
+}
+
+extern "C" int unpermute_unpad(const void *y, const int32_t *row_map, const float *probs,
+                               int64_t T, int topk, int64_t H, void *out, void *stream)
+{
+    clear_error();
+    FGB_REQUIRE(y && row_map && out, FGB_EINVAL, "unpermute_unpad: null pointer");
+    FGB_REQUIRE(T >= 0 && topk >= 1 && topk <= 64, FGB_EINVAL, "unpermute_unpad: need 1 <= topk <= 64");
+    FGB_REQUIRE(H > 0 && H % 8 == 0, FGB_EINVAL, "unpermute_unpad: H must be a positive multiple of 8");
+    FGB_REQUIRE(aligned16(y) && aligned16(out), FGB_EINVAL, "unpermute_unpad: y and out must be 16-byte aligned");
+    if (T == 0)
+        return FGB_OK;
+    int64_t grid = (T + 3) / 4;
+    grid = grid < 8192 ? grid : 8192;
+    unpermute_kernel<<<(unsigned)grid, 256, 0, (hipStream_t)stream>>>((const uint16_t *)y, row_map, probs,
+                                                                      T, topk, H, (uint16_t *)out);
+    FGB_LAUNCHED("unpermute_unpad");
+    return FGB_OK;
+}
+
+extern "C" int swiglu_quant(const void *h, int64_t M, int64_t F, int64_t ldh,
+                            const int32_t *group_offsets, int G, uint8_t *q, uint8_t *s,
+                            void *stream)
+{
+    clear_error();
+    FGB_REQUIRE(h && q && s, FGB_EINVAL, "swiglu_quant: null pointer");
+    FGB_REQUIRE(M >= 0 && F > 0 && F % 128 == 0, FGB_EINVAL, "swiglu_quant: F must be a positive multiple of 128");
+    FGB_REQUIRE(ldh >= 2 * F && ldh % 8 == 0, FGB_EINVAL, "swiglu_quant: ldh must be >= 2F and a multiple of 8");
+    FGB_REQUIRE(!group_offsets || G >= 1, FGB_EINVAL, "swiglu_quant: G must be >= 1 with group_offsets");
+    FGB_REQUIRE(aligned16(h) && aligned16(q), FGB_EINVAL, "swiglu_quant: h and q must be 16-byte aligned");
+    if (M == 0)
+        return FGB_OK;
+    int64_t grid = (M + 3) / 4;
+    grid = grid < 16384 ? grid : 16384;
+    swiglu_quant_kernel<<<(unsigned)grid, 256, 0, (hipStream_t)stream>>>((const uint8_t *)h, M, F, ldh * 2,
+                                                                         group_offsets, G, q, s);
+    FGB_LAUNCHED("swiglu_quant");
+    return FGB_OK;
+}

@@ -1,0 +1,140 @@
+// transpose.hip -- scaling-aware direct transpose of row-wise FP8.
+//
+// awesome-system-papers, "FP8-Flow-MoE: A Casting-Free FP8 Recipe without
+// Double Quantization Error", "Core method" and key observation 2: with
+// power-of-two scales, converting row-wise (1x128) FP8 into column-wise FP8
+// needs only, inside each 128x128 block, the block's largest scale Smax and an
+// exponent shift of every code by k = log2(Smax / S_row), recombining the
+// mantissa when the result leaves the normal range.  The result equals
+// requantizing the dequantized block at Smax -- without a dequantize /
+// requantize pass.
+//
+// gfx950 mapping: one wave per 128x128 block.  Lane (tsub = lane & 7,
+// csub = lane >> 3) owns the 16x16 byte sub-tile at rows tsub*16.., columns
+// csub*16..: 16 row loads of 16 bytes (8 lanes cover one 128-byte row
+// segment), the shift applied in the row domain where k is uniform per row,
+// a 16x16 byte transpose in registers with v_perm_b32, and 16 column stores of
+// 16 bytes (8 lanes cover one 128-byte output row segment).  No LDS, no bank
+// conflicts; HBM-bound.
+//
+// The shift decodes two codes to fp32 (exact), multiplies by 2^-k (exact) and
+// converts back with round-to-nearest-even; for E - k >= 1 that is the plain
+// exponent decrement, below it the subnormal re-rounding.
+#include "fgb_internal.h"
+
+namespace fgb {
+
+// 4x4 byte transpose: rows a,b,c,d (byte i = column i) -> columns.
+__device__ __forceinline__ void tr4x4(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t &o0,
+                                      uint32_t &o1, uint32_t &o2, uint32_t &o3)
+{
+    uint32_t ab_lo = __builtin_amdgcn_perm(b, a, 0x05010400u); // a0 b0 a1 b1
+    uint32_t ab_hi = __builtin_amdgcn_perm(b, a, 0x07030602u); // a2 b2 a3 b3
+    uint32_t cd_lo = __builtin_amdgcn_perm(d, c, 0x05010400u); // c0 d0 c1 d1
+    uint32_t cd_hi = __builtin_amdgcn_perm(d, c, 0x07030602u); // c2 d2 c3 d3
+    o0 = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u);     // a0 b0 c0 d0
+    o1 = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u);     // a1 b1 c1 d1
+    o2 = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u);     // a2 b2 c2 d2
+    o3 = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u);     // a3 b3 c3 d3
+}
+
+__device__ __forceinline__ uint32_t shift_word(uint32_t w, float f)
+{
+    float2 a = dec2_lo(w), b = dec2_hi(w);
+    return cvt4_e4m3(a.x * f, a.y * f, b.x * f, b.y * f);
+}
+
+template <bool ROWSCALE>
+__global__ __launch_bounds__(256) void direct_transpose_kernel(const uint8_t *__restrict__ q,
+                                                               const uint8_t *__restrict__ s,
+                                                               int64_t T, int64_t C,
+                                                               uint8_t *__restrict__ qt,
+                                                               uint8_t *__restrict__ st,
+                                                               int64_t nblocks)
+{
+    const int lane = lane_id();
+    const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (blk >= nblocks)
+        return;
+    const int64_t ncb = C / 128, ntb = T / 128;
+    const int64_t tb = blk / ncb, cb = blk % ncb;
+    const int tsub = lane & 7, csub = lane >> 3;
+    const int64_t t0 = tb * 128 + tsub * 16;
+    const int64_t c0 = cb * 128 + csub * 16;
+
+    uint32_t w[16][4];
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+        uint4 v = *reinterpret_cast<const uint4 *>(q + (t0 + j) * C + c0);
+        w[j][0] = v.x;
+        w[j][1] = v.y;
+        w[j][2] = v.z;
+        w[j][3] = v.w;
+    }
+    int emax = 0;
+    if constexpr (ROWSCALE) {
+        int e[16];
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            e[j] = s[(t0 + j) * ncb + cb];
+            m = max(m, (uint32_t)e[j]);
+        }
+        emax = (int)group_max_u32<8>(m); // lanes with equal csub hold all 128 rows
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            int k = min(emax - e[j], 31);
+            float f = pow2f(-k);
+#pragma unroll
+            for (int x = 0; x < 4; x++)
+                w[j][x] = shift_word(w[j][x], f);
+        }
+    }
+    uint32_t o[16][4]; // o[c][i]: column c0+c, rows t0+4i .. t0+4i+3
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int x = 0; x < 4; x++)
+            tr4x4(w[4 * i + 0][x], w[4 * i + 1][x], w[4 * i + 2][x], w[4 * i + 3][x], o[4 * x + 0][i],
+                  o[4 * x + 1][i], o[4 * x + 2][i], o[4 * x + 3][i]);
+#pragma unroll
+    for (int c = 0; c < 16; c++)
+        *reinterpret_cast<uint4 *>(qt + (c0 + c) * T + t0) = make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]);
+    if constexpr (ROWSCALE) {
+        st[(cb * 128 + lane) * ntb + tb] = (uint8_t)emax;
+        st[(cb * 128 + 64 + lane) * ntb + tb] = (uint8_t)emax;
+    } else {
+        if (lane == 0)
+            st[cb * ntb + tb] = s[tb * ncb + cb];
+    }
+}
+
+} // namespace fgb
+
+using namespace fgb;
+
+extern "C" int fp8_direct_transpose(const uint8_t *q, const uint8_t *s, int s_gran, int64_t rows,
+                                    int64_t cols, uint8_t *qt, uint8_t *st, void *stream)
+{
+    clear_error();
+    FGB_REQUIRE(q && s && qt && st, FGB_EINVAL, "fp8_direct_transpose: null pointer");
+    FGB_REQUIRE(s_gran == FGB_ROW1x128 || s_gran == FGB_BLOCK128, FGB_EUNSUPPORTED,
+                "fp8_direct_transpose: s_gran must be FGB_ROW1x128 or FGB_BLOCK128");
+    FGB_REQUIRE(rows >= 0 && cols >= 0 && rows % 128 == 0 && cols % 128 == 0, FGB_EINVAL,
+                "fp8_direct_transpose: rows and cols must be multiples of 128 (rows=%lld cols=%lld)",
+                (long long)rows, (long long)cols);
+    FGB_REQUIRE(aligned16(q) && aligned16(qt), FGB_EINVAL,
+                "fp8_direct_transpose: q and qt must be 16-byte aligned");
+    int64_t nb = (rows / 128) * (cols / 128);
+    if (nb == 0)
+        return FGB_OK;
+    int64_t grid = (nb + 3) / 4;
+    FGB_REQUIRE(grid < (1ll << 31), FGB_EINVAL, "fp8_direct_transpose: too many blocks");
+    hipStream_t stm = (hipStream_t)stream;
+    if (s_gran == FGB_ROW1x128)
+        direct_transpose_kernel<true><<<(int)grid, 256, 0, stm>>>(q, s, rows, cols, qt, st, nb);
+    else
+        direct_transpose_kernel<false><<<(int)grid, 256, 0, stm>>>(q, s, rows, cols, qt, st, nb);
+    FGB_LAUNCHED("fp8_direct_transpose");
+    return FGB_OK;
+}

@@ -1,0 +1,246 @@
+/*
+ * fgb.h -- C ABI of libfgb.so: fine-grained blockwise FP8 (E4M3 codes with
+ * power-of-two UE8M0 scales) for AMD Instinct MI355X (gfx950).
+ *
+ * Sources cited below (page title, section):
+ *   [DSV3]  llm-infra-atlas, "01 · DeepSeek FP8 and DeepGEMM: Hopper software recipe"
+ *   [LP]    llm-infra-atlas, "Low precision" chapter index
+ *   [FLOW]  awesome-system-papers, "FP8-Flow-MoE: A Casting-Free FP8 Recipe without
+ *           Double Quantization Error (MLSys 2026)"
+ *   [MOSS]  xllm-io paper review, "MOSS: Efficient and Accurate FP8 LLM Training with
+ *           Microscaling and Automatic Scaling"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Codes are uint8 OCP E4M3FN ([LP] §2: 1/4/3 bits, max 448, no Inf): bias 7,
+ *    NaN only at 0x7F/0xFF.  Conversions round to nearest even and keep the
+ *    sign (negative underflow gives 0x80).
+ *  - A scale is one byte b = e + 127 meaning the power of two 2^e; a value is
+ *    decode(code) * 2^e ([DSV3] §3 multiplier convention, §8 UE8M0).  For an
+ *    amax over a group, e is the smallest integer with amax <= 448 * 2^e,
+ *    floored at -22 for 128-element groups ([DSV3] §3, the 1e-4 amax clamp)
+ *    and at -127 for 32-element groups (E8M0 range, [MOSS] §3).
+ *  - Matrices are row-major.  ld* arguments are leading dimensions in
+ *    elements.  Every data pointer is a device pointer owned by the caller;
+ *    the library allocates nothing, keeps no pointer after return and holds
+ *    no global state.
+ *  - stream is a hipStream_t (NULL = the null stream).  Every call only
+ *    enqueues work: no host synchronisation, no implicit copies.  Results are
+ *    deterministic (no floating-point atomics).
+ *  - Return value: FGB_OK or an error code; arguments are validated on the
+ *    host before anything is enqueued, so an error leaves the outputs
+ *    untouched.  fgb_last_error() gives a thread-local message.
+ *  - Data pointers must be 16-byte aligned, and every ld* times the element
+ *    size must be a multiple of 16 bytes, except where stated.
+ *  - Inputs are assumed finite; non-finite inputs give unspecified outputs.
+ */
+#ifndef FGB_H
+#define FGB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define FGB_OK 0
+#define FGB_EINVAL 1       /* null pointer, bad size, misalignment, bad ld */
+#define FGB_EUNSUPPORTED 2 /* dtype / granularity combination not provided */
+#define FGB_EWORKSPACE 3   /* workspace missing or too small */
+#define FGB_EHIP 4         /* a HIP runtime call failed (launch error) */
+
+/* element types */
+#define FGB_F32 0
+#define FGB_BF16 1
+
+/* scale granularities */
+#define FGB_ROW1x128 0 /* one scale per row per 128 columns: s[rows, cols/128] */
+#define FGB_ROW1x32 1  /* one scale per row per 32 columns:  s[rows, cols/32] */
+#define FGB_BLOCK128 2 /* one scale per 128x128 block: s[ceil(rows/128), cols/128] */
+
+/* Thread-local text of the last error raised on this thread ("" if none). */
+const char *fgb_last_error(void);
+
+/* Library version string. */
+const char *fgb_version(void);
+
+/*
+ * fp8_quant_rowwise -- 1 x group activation quantization.
+ * [DSV3] §2 (online quantization: amax of every 1x128 activation tile is
+ * computed at run time) and §3 (per token per 128 channels, scale tensor
+ * [T, C/128]); group 32 is the MX single-level activation scaling of [MOSS] §3.
+ *   x      [rows, cols], ld ldx, dtype x_dtype (FGB_F32 or FGB_BF16)
+ *   group  128 or 32; cols % group == 0
+ *   q      [rows, cols] E4M3 codes, ld ldq (bytes; multiple of 16)
+ *   s      [rows, cols/group] scale bytes, ld lds (any ld >= cols/group)
+ * For each row and group: e = scale exponent of the group's amax, q = E4M3
+ * of x * 2^-e (an exact product, |x * 2^-e| <= 448), s = e + 127.
+ */
+int fp8_quant_rowwise(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                      int group, uint8_t *q, int64_t ldq, uint8_t *s, int64_t lds, void *stream);
+
+/*
+ * fp8_quant_blockwise -- 128 x 128 weight-block quantization.
+ * [DSV3] §3: per 128 input channels x 128 output channels; scale tensor
+ * [Cout/128, Cin/128].  The last row block may be partial (rows % 128 != 0,
+ * e.g. Cout = 2112 in [DSV3] §5.7); its amax covers the rows present.
+ *   w  [rows, cols], ld ldw, FGB_F32 or FGB_BF16; cols % 128 == 0
+ *   q  [rows, cols], ld ldq;  s [ceil(rows/128), cols/128], ld lds
+ */
+int fp8_quant_blockwise(const void *w, int w_dtype, int64_t rows, int64_t cols, int64_t ldw,
+                        uint8_t *q, int64_t ldq, uint8_t *s, int64_t lds, void *stream);
+
+/*
+ * fp8_dequant -- decode(q) * 2^(s - 127) into FP32 or BF16 (diagnostic helper).
+ *   q [rows, cols] dense; s dense in the layout gran names; out [rows, cols]
+ *   dense, dtype out_dtype.  BF16 output rounds to nearest even.
+ */
+int fp8_dequant(const uint8_t *q, const uint8_t *s, int gran, int64_t rows, int64_t cols,
+                void *out, int out_dtype, void *stream);
+
+/*
+ * fgb_e4m3_encode -- E4M3 of each fp32 value (round to nearest even,
+ * saturating at +-448, sign kept).  Exposes the device conversion the
+ * kernels use, for exhaustive checks.  x, q dense, n elements.
+ */
+int fgb_e4m3_encode(const float *x, int64_t n, uint8_t *q, void *stream);
+
+/*
+ * fp8_direct_transpose -- scaling-aware transpose ([FLOW] "Core method" and
+ * key observation 2): inside each 128x128 block the block's largest scale
+ * e_max is taken, and each code of row t is shifted by k_t = e_max - e_t in
+ * the exponent (with round-to-nearest-even when the result falls into the
+ * subnormal range), i.e. the result equals requantizing the dequantized
+ * block at 2^e_max, with no dequantize/requantize pass.
+ *   s_gran = FGB_ROW1x128: q [rows=T, cols=C] with s [T, C/128]
+ *            -> qt [C, T], st [C, T/128] (all 128 entries of a block equal);
+ *   s_gran = FGB_BLOCK128: the k = 0 case for weights, an exact byte
+ *            transpose: s [T/128, C/128] -> st [C/128, T/128].
+ *   rows % 128 == 0 and cols % 128 == 0; all tensors dense.
+ */
+int fp8_direct_transpose(const uint8_t *q, const uint8_t *s, int s_gran, int64_t rows,
+                         int64_t cols, uint8_t *qt, uint8_t *st, void *stream);
+
+/*
+ * fp8_block_gemm -- blockwise-scaled FP8 GEMM, D = A * B^T ("NT": A [M,K] and
+ * B [N,K] both K-contiguous, [DSV3] §5.7).  Covers a Linear's three GEMMs
+ * ([DSV3] §1): Fprop A = X, B = W; Dgrad A = dY, B = W^T (block transpose);
+ * Wgrad A = dY^T, B = X^T (both from fp8_direct_transpose, 1x128 scales).
+ * Accumulation is FP32; the scale product of A's and B's group is applied to
+ * each 128-element (or 32-element) K group's partial sum ([DSV3] §4, §5.3).
+ *   a, sa, a_gran : A codes [M, K] (ld lda) and scales, FGB_ROW1x128 -> sa
+ *                   [M, K/128], FGB_ROW1x32 -> sa [M, K/32] (dense)
+ *   b, sb, b_gran : B codes [N, K] (ld ldb) and scales, FGB_BLOCK128 -> sb
+ *                   [ceil(N/128), K/128], FGB_ROW1x128 -> sb [N, K/128],
+ *                   FGB_ROW1x32 -> sb [N, K/32] (dense).  ROW1x32 must be
+ *                   paired with ROW1x32.
+ *   b_l1, g1      : optional [MOSS] §3 level-1 FP32 factor per column of D,
+ *                   b_l1 [N] (dense), applied to the FP32 result; requires
+ *                   K <= g1 (one level-1 group along K); NULL = none.
+ *   d, d_dtype    : D [M, N], ld ldd, FGB_F32 or FGB_BF16 (round to nearest
+ *                   even).  accumulate != 0 (FP32 only): D += A * B^T.
+ *   workspace     : unused, may be NULL (ws_bytes ignored).
+ * K % 128 == 0; M, N >= 1.
+ */
+int fp8_block_gemm(const uint8_t *a, const uint8_t *sa, int a_gran, const uint8_t *b,
+                   const uint8_t *sb, int b_gran, const float *b_l1, int64_t g1, int64_t M,
+                   int64_t N, int64_t K, int64_t lda, int64_t ldb, void *d, int d_dtype,
+                   int64_t ldd, int accumulate, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * fp8_grouped_gemm -- M-grouped contiguous FP8 GEMM for MoE experts ([DSV3]
+ * §5.6: experts concatenated along M, each expert's 128x128 weight scales
+ * picked by its group; [FLOW] assumption 2: the expert linears emit BF16).
+ *   a  [M_cap, K] codes, sa [M_cap, K/128] (1x128 scales), dense
+ *   b  [G, N, K] codes, sb [G, ceil(N/128), K/128] (128x128 scales), dense
+ *   group_offsets : device int32 [G+1], non-decreasing, off[0] = 0,
+ *                   off[G] <= M_cap (as written by permute_pad).  Rows
+ *                   [off[g], off[g+1]) use expert g.  Read on the device:
+ *                   no host synchronisation.
+ *   d  [M_cap, N], dense, FGB_BF16 or FGB_F32.  Rows >= off[G] are neither
+ *      read nor written.
+ * K % 128 == 0.
+ */
+int fp8_grouped_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t *b, const uint8_t *sb,
+                     const int32_t *group_offsets, int G, int64_t M_cap, int64_t N, int64_t K,
+                     void *d, int d_dtype, void *stream);
+
+/*
+ * permute_pad -- fused permute + pad ([FLOW] "Core method": expert reordering
+ * fused with 16-aligned padding, on row-wise FP8 with its scales).
+ *   xq [T, H] codes, xs [T, H/128] scales, topk_idx [T, topk] int32 (device)
+ *   Rows are grouped by expert id ascending and, inside an expert, by
+ *   (token, slot) ascending; each expert's segment is padded at its end to a
+ *   multiple of pad_multiple rows with code 0x00 and scale byte 127.  A slot
+ *   whose id lies outside [0, G) is dropped (row_map = -1).
+ *   out_q [M_cap, H], out_s [M_cap, H/128]: rows >= off[G] untouched.
+ *   row_map [T, topk] int32: destination row of each slot, or -1.
+ *   group_offsets [G+1] int32: segment starts (multiples of pad_multiple).
+ *   M_cap must be >= T*topk + (pad_multiple-1)*G (the host-side bound).
+ *   workspace: device memory of permute_pad_workspace_size(T, topk, G)
+ *   bytes; its contents on entry do not matter.
+ * H % 128 == 0, 1 <= G <= 1024, pad_multiple in [1, 256].
+ */
+int permute_pad(const uint8_t *xq, const uint8_t *xs, const int32_t *topk_idx, int64_t T, int topk,
+                int G, int64_t H, int pad_multiple, uint8_t *out_q, uint8_t *out_s,
+                int32_t *row_map, int32_t *group_offsets, int64_t M_cap, void *workspace,
+                size_t ws_bytes, void *stream);
+
+/* Workspace bytes permute_pad needs for these sizes. */
+size_t permute_pad_workspace_size(int64_t T, int topk, int G);
+
+/*
+ * unpermute_unpad -- inverse of permute_pad on the expert output ([FLOW]
+ * "Core method": fused unpermute + unpadding).
+ *   out[t][h] = bf16_rne( fold k = 0..topk-1 of acc = fmaf(w, y[row_map[t][k]][h], acc) )
+ *   with acc starting at 0, w = probs[t][k] (or 1 when probs == NULL), slots
+ *   with row_map < 0 skipped; padding rows are never read.
+ *   y [*, H] bf16 dense; row_map [T, topk] int32; probs [T, topk] fp32 or
+ *   NULL; out [T, H] bf16 dense.  H % 8 == 0.
+ */
+int unpermute_unpad(const void *y, const int32_t *row_map, const float *probs, int64_t T,
+                    int topk, int64_t H, void *out, void *stream);
+
+/*
+ * swiglu_quant -- fused SwiGLU + 1x128 quantization ([FLOW] "Core method":
+ * the activation emits FP8 directly; assumption 2: the first linear's
+ * output is BF16).
+ *   h [M, 2F] bf16, ld ldh, gate columns [0, F), up columns [F, 2F).
+ *   a = (g / (1 + exp(-g))) * u, each operation rounded to fp32; exp is the
+ *   library's own fp32 function (Cody-Waite reduction with a two-part ln2,
+ *   degree-7 Taylor polynomial in Horner form with fused multiply-adds,
+ *   scaling by 2^n in two exact steps), so results are reproducible
+ *   bit for bit.  Then 1x128 quantization of a into q [M, F] (dense) and
+ *   s [M, F/128] (dense).
+ *   group_offsets: NULL, or device int32 [G+1]; rows >= off[G] are skipped.
+ * F % 128 == 0.
+ */
+int swiglu_quant(const void *h, int64_t M, int64_t F, int64_t ldh, const int32_t *group_offsets,
+                 int G, uint8_t *q, uint8_t *s, void *stream);
+
+/*
+ * mx2_quant -- MOSS two-level microscaling ([MOSS] §3 two-level
+ * microscaling, Fig. 2): level 1 is an FP32 factor alpha1 per g1 contiguous
+ * elements of a row (last group partial), alpha1 = fp32(amax / 448), or 1
+ * for an all-zero group; y = fp32(x / alpha1) (correctly rounded division);
+ * level 2 is an E8M0 scale per 32 elements of y (floor -127); elements E4M3.
+ *   x [R, C] bf16 dense; q [R, C]; s2 [R, C/32]; s1 [R, ceil(C/g1)] fp32.
+ * C % 32 == 0, g1 % 32 == 0.
+ */
+int mx2_quant(const void *x, int64_t R, int64_t C, int64_t g1, uint8_t *q, uint8_t *s2, float *s1,
+              void *stream);
+
+/*
+ * mx2_dequant -- x_hat = fp32( fp32(decode(q) * 2^(s2 - 127)) * alpha1 ).
+ *   out [R, C] fp32 dense.
+ */
+int mx2_dequant(const uint8_t *q, const uint8_t *s2, const float *s1, int64_t R, int64_t C,
+                int64_t g1, float *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FGB_H */

@@ -1,0 +1,114 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host with the documented
+status codes before anything is enqueued."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "fgb.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z0-9_]+)\s*\(", src)) - {"defined"})
+
+
+def test_header_symbols_exported():
+    import fine_grained_blockwise_amd as fgb
+    names = header_functions()
+    assert len(names) >= 14
+    L = fgb.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(fgb.symbols()) == set(names)
+    assert fgb.lib().fgb_version().decode().startswith("fgb")
+
+
+def test_library_has_gfx950_code_object():
+    from fine_grained_blockwise_amd import LIB_PATH
+    blob = open(LIB_PATH, "rb").read()
+    assert b"gfx950" in blob
+
+
+P = C.c_void_p
+
+
+def _fake(addr=0x1000):
+    return C.c_void_p(addr)
+
+
+def test_quant_rowwise_validation():
+    import fine_grained_blockwise_amd as fgb
+    L = fgb.lib()
+    assert L.fp8_quant_rowwise(None, 1, 4, 128, 128, 128, _fake(), 128, _fake(), 1, None) == 1
+    assert b"null" in L.fgb_last_error()
+    assert L.fp8_quant_rowwise(_fake(), 7, 4, 128, 128, 128, _fake(), 128, _fake(), 1, None) == 2
+    assert L.fp8_quant_rowwise(_fake(), 1, 4, 100, 128, 128, _fake(), 128, _fake(), 1, None) == 1
+    assert L.fp8_quant_rowwise(_fake(), 1, 4, 128, 128, 64, _fake(), 128, _fake(), 1, None) == 2
+    assert L.fp8_quant_rowwise(_fake(), 1, 4, 128, 120, 128, _fake(), 128, _fake(), 1, None) == 1
+    assert L.fp8_quant_rowwise(_fake(0x1001), 1, 4, 128, 128, 128, _fake(), 128, _fake(), 1, None) == 1
+    assert b"aligned" in L.fgb_last_error()
+    # rows == 0 is a no-op that touches nothing
+    assert L.fp8_quant_rowwise(_fake(), 1, 0, 128, 128, 128, _fake(), 128, _fake(), 1, None) == 0
+
+
+def test_gemm_validation():
+    import fine_grained_blockwise_amd as fgb
+    L = fgb.lib()
+    f = _fake()
+    args = dict(a=f, sa=f, ag=0, b=f, sb=f, bg=2, l1=None, g1=0, M=256, N=256, K=512, lda=512,
+                ldb=512, d=f, dt=1, ldd=256, acc=0)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.fp8_block_gemm(a["a"], a["sa"], a["ag"], a["b"], a["sb"], a["bg"], a["l1"], a["g1"],
+                                a["M"], a["N"], a["K"], a["lda"], a["ldb"], a["d"], a["dt"],
+                                a["ldd"], a["acc"], None, 0, None)
+    assert call(K=500) == 1
+    assert call(M=0) == 1
+    assert call(lda=500, K=256) == 1
+    assert call(ag=2) == 2          # BLOCK128 A scales are not a mode
+    assert call(ag=1, bg=2) == 2    # 1x32 must pair with 1x32
+    assert call(acc=1, dt=1) == 2   # accumulate needs FP32 output
+    assert call(l1=f, g1=256) == 2  # level-1 factor needs K <= g1
+    assert call(a=None) == 1
+    assert L.fp8_grouped_gemm(f, f, f, f, f, 0, 100, 256, 512, f, 1, None) == 1
+
+
+def test_transpose_and_moe_validation():
+    import fine_grained_blockwise_amd as fgb
+    L = fgb.lib()
+    f = _fake()
+    assert L.fp8_direct_transpose(f, f, 0, 200, 256, f, f, None) == 1
+    assert L.fp8_direct_transpose(f, f, 1, 256, 256, f, f, None) == 2
+    ws = fgb.permute_pad_workspace_size(16384, 8, 32)
+    assert ws > 0
+    # M_cap below the host-side bound
+    assert L.permute_pad(f, f, f, 100, 8, 32, 7168, 16, f, f, f, f, 800, f, ws, None) == 1
+    # workspace too small
+    assert L.permute_pad(f, f, f, 100, 8, 32, 7168, 16, f, f, f, f, 800 + 15 * 32, f, 4, None) == 3
+    assert L.unpermute_unpad(f, f, None, 10, 8, 7, f, None) == 1
+    assert L.swiglu_quant(f, 10, 100, 200, None, 0, f, f, None) == 1
+    assert L.mx2_quant(f, 4, 64, 48, f, f, f, None) == 2
+    assert L.mx2_quant(f, 4, 48, 64, f, f, f, None) == 1
+
+
+def test_oracle_and_library_share_nothing():
+    """The oracle never includes or loads the HIP library, and the library never
+    includes, imports or loads the oracle."""
+    osrc = open(os.path.join(ROOT, "oracle", "fgb_oracle.c")).read()
+    includes = re.findall(r"#include\s*[<\"]([^>\"]+)", osrc)
+    assert all(not (i.startswith("hip") or "fgb" in i) for i in includes), includes
+    for fn in os.listdir(os.path.join(ROOT, "oracle")):
+        if fn.endswith(".py"):
+            txt = open(os.path.join(ROOT, "oracle", fn)).read()
+            assert "fine_grained_blockwise_amd" not in txt and "libfgb" not in txt
+    pkg = os.path.join(ROOT, "fine_grained_blockwise_amd")
+    for dp, _, fns in os.walk(pkg):
+        for fn in fns:
+            if fn.endswith((".py", ".hip", ".h")):
+                txt = open(os.path.join(dp, fn)).read()
+                assert not re.search(r"import\s+oracle|from\s+oracle|liboracle|fgb_oracle", txt), fn

@@ -1,0 +1,442 @@
+"""GPU parity: every HIP entry point against the CPU oracle on the same bytes.
+
+Bit-exact for codes, scales, data movement and the bf16 unpermute fold; GEMMs
+within max|d - ref| / max|ref| <= 1e-5 (FP32 output) or, elementwise, one bf16
+ulp of |ref| or 1e-5 * max|ref| (BF16 output)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def fgb():
+    import fine_grained_blockwise_amd as m
+    return m
+
+
+def np_(t):
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def bits(t):
+    """bf16 CPU tensor -> uint16 numpy bits."""
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def ulp_bf16(x):
+    x = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.maximum(x, 2.0 ** -133)))
+    return np.exp2(np.maximum(e, -133) - 7)
+
+
+def check_fp32(got, ref, tol=1e-5):
+    got = np.asarray(got, np.float64)
+    scale = np.max(np.abs(ref))
+    err = np.max(np.abs(got - ref)) / scale if scale > 0 else np.max(np.abs(got))
+    assert err <= tol, f"max rel err {err:.3e}"
+    return err
+
+
+def check_bf16(got_bits, ref):
+    got = torch.from_numpy(got_bits.view(np.int16)).view(torch.bfloat16).float().numpy().astype(np.float64)
+    d = np.abs(got - ref)
+    ok = (d <= ulp_bf16(ref)) | (d <= 1e-5 * np.max(np.abs(ref)))
+    assert ok.all(), f"{(~ok).sum()} elements beyond 1 bf16 ulp; worst {d[~ok].max() if (~ok).any() else 0}"
+
+
+def rand_codes(shape, seed):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randint(0, 256, shape, generator=g, dtype=torch.int32).to(torch.uint8)
+    q[(q & 0x7F) == 0x7F] ^= 1  # no NaN codes
+    return q
+
+
+def rand_scales(shape, lo, hi, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randint(lo + 127, hi + 128, shape, generator=g, dtype=torch.int32).to(torch.uint8)
+
+
+# ---------------------------------------------------------------------------
+# E4M3 device conversion
+# ---------------------------------------------------------------------------
+def test_device_encode_all_bf16_and_ties(fgb):
+    say("encode: all bf16, every tie and neighbours")
+    b = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
+    b = b[np.isfinite(b)]
+    tab = O.e4m3_decode_table()
+    mags = np.sort(np.unique(np.abs(tab[np.isfinite(tab)])))
+    mids = ((mags[1:] + mags[:-1]) / 2).astype(np.float32)
+    near = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9)),
+                           mags.astype(np.float32)])
+    x = np.concatenate([b, near, -near, np.float32([0.0, -0.0, 448, 449, 500, -1e30, 1e-40, -1e-40])])
+    x = x.astype(np.float32)
+    got = np_(fgb.fgb_e4m3_encode(torch.from_numpy(x).to(DEV)))
+    assert np.array_equal(got, O.e4m3_encode(x))
+
+
+def test_device_encode_dense_fp32_range(fgb):
+    say("encode: strided sweep of fp32 in [2^-12, 2^9]")
+    lo = int(np.float32(2.0 ** -12).view(np.uint32))
+    hi = int(np.float32(2.0 ** 9).view(np.uint32))
+    bitsv = np.arange(lo, hi, 5, dtype=np.uint32)
+    x = bitsv.view(np.float32)
+    x = np.concatenate([x, -x[::7]])
+    got = np_(fgb.fgb_e4m3_encode(torch.from_numpy(x).to(DEV)))
+    assert np.array_equal(got, O.e4m3_encode(x))
+
+
+# ---------------------------------------------------------------------------
+# 1 x g quantization
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("group", [128, 32])
+@pytest.mark.parametrize("rows,cols", [(1, 128), (3, 384), (67, 1024), (257, 7168)])
+def test_quant_rowwise_small(fgb, dtype, group, rows, cols):
+    say("quant_rowwise", dtype, group, rows, cols)
+    g = torch.Generator().manual_seed(rows * 31 + cols)
+    x = torch.randn(rows, cols, generator=g) * torch.exp2(torch.randint(-30, 30, (rows, 1), generator=g).float())
+    x[0, :group] = 0.0
+    if rows > 2:
+        x[1, :group] = -0.0
+        x[2, :min(cols, 256)] *= 1e-38  # subnormal fp32 / bf16 values
+    x = x.to(dtype)
+    q, s = fgb.fp8_quant_rowwise(x.to(DEV), group)
+    xr = bits(x) if dtype == torch.bfloat16 else x.numpy()
+    oq, os_ = O.quant_rowwise(xr, group)
+    assert np.array_equal(np_(q), oq) and np.array_equal(np_(s), os_)
+
+
+def test_quant_rowwise_strided_ld(fgb):
+    say("quant_rowwise ld != cols")
+    x = torch.randn(100, 1024).to(torch.bfloat16)
+    xs = x[:, :640]
+    q = torch.full((100, 768), 0xAA, dtype=torch.uint8, device=DEV)
+    s = torch.full((100, 9), 0xAA, dtype=torch.uint8, device=DEV)
+    fgb.fp8_quant_rowwise(x.to(DEV)[:, :640], 128, q[:, :640], s[:, :5])
+    oq, os_ = O.quant_rowwise(bits(xs.contiguous()), 128)
+    assert np.array_equal(np_(q)[:, :640], oq) and np.all(np_(q)[:, 640:] == 0xAA)
+    assert np.array_equal(np_(s)[:, :5], os_) and np.all(np_(s)[:, 5:] == 0xAA)
+
+
+def test_quant_linear_tiny(fgb):
+    say("quant: tiny linear X, dY (fp32), W (fp32 blocks)")
+    X, W, dY = synth.linear_tiny(0)
+    for t in (X, dY):
+        q, s = fgb.fp8_quant_rowwise(t.to(DEV))
+        oq, os_ = O.quant_rowwise(t.numpy())
+        assert np.array_equal(np_(q), oq) and np.array_equal(np_(s), os_)
+    q, s = fgb.fp8_quant_blockwise(W.to(DEV))
+    oq, os_ = O.quant_blockwise(W.numpy())
+    assert np.array_equal(np_(q), oq) and np.array_equal(np_(s), os_)
+
+
+def test_quant_dsv3_full(fgb):
+    say("quant: DeepSeek-V3 X [8192, 7168] bf16 rowwise, W [2048, 7168] blockwise")
+    X, W, dY = synth.linear_dsv3(0)
+    q, s = fgb.fp8_quant_rowwise(X.to(DEV))
+    oq, os_ = O.quant_rowwise(bits(X))
+    assert np.array_equal(np_(s), os_)
+    assert np.array_equal(np_(q), oq)
+    q, s = fgb.fp8_quant_blockwise(W.to(DEV))
+    oq, os_ = O.quant_blockwise(bits(W))
+    assert np.array_equal(np_(q), oq) and np.array_equal(np_(s), os_)
+
+
+@pytest.mark.parametrize("rows", [1, 100, 2112])
+def test_quant_blockwise_partial(fgb, rows):
+    say("quant_blockwise rows", rows)
+    g = torch.Generator().manual_seed(rows)
+    w = (torch.randn(rows, 512, generator=g) * 0.02).to(torch.bfloat16)
+    q, s = fgb.fp8_quant_blockwise(w.to(DEV))
+    oq, os_ = O.quant_blockwise(bits(w))
+    assert np.array_equal(np_(q), oq) and np.array_equal(np_(s), os_)
+
+
+def test_dequant(fgb):
+    say("dequant")
+    q = rand_codes((256, 512), 1)
+    for gran, sshape in [(fgb.ROW1x128, (256, 4)), (fgb.ROW1x32, (256, 16)), (fgb.BLOCK128, (2, 4))]:
+        s = rand_scales(sshape, -40, 40, 2)
+        ref = O.dequant(q.numpy(), s.numpy(), gran)
+        out = np_(fgb.fp8_dequant(q.to(DEV), s.to(DEV), gran, torch.float32))
+        assert np.array_equal(out.astype(np.float64), ref)
+
+
+# ---------------------------------------------------------------------------
+# direct transpose
+# ---------------------------------------------------------------------------
+def test_transpose_exhaustive_codes_and_shifts(fgb):
+    say("transpose: 256 codes x k in 0..127")
+    q = torch.arange(256, dtype=torch.int32).to(torch.uint8).repeat(256, 1)  # [256 rows, 256 cols]
+    s = torch.zeros((256, 2), dtype=torch.uint8)
+    for t in range(256):
+        k = t % 128
+        s[t, :] = 240 - k
+    qt, st = fgb.fp8_direct_transpose(q.to(DEV), s.to(DEV))
+    oqt, ost = O.direct_transpose(q.numpy(), s.numpy())
+    nan = np.isin(np.arange(256), [0x7F, 0xFF])
+    assert np.array_equal(np_(qt)[~nan], oqt[~nan])
+    assert np.array_equal(np_(st), ost)
+
+
+@pytest.mark.parametrize("T,C", [(128, 128), (256, 512), (384, 2048)])
+def test_transpose_random(fgb, T, C):
+    say("transpose", T, C)
+    q, s = synth.wgrad_codes(T, C, seed=T + C)
+    qt, st = fgb.fp8_direct_transpose(q.to(DEV), s.to(DEV))
+    oqt, ost = O.direct_transpose(q.numpy(), s.numpy())
+    assert np.array_equal(np_(qt), oqt) and np.array_equal(np_(st), ost)
+
+
+def test_transpose_wgrad_dy_full(fgb):
+    say("transpose: Wgrad dY codes [32768, 2048] with scales 2^-20..2^4")
+    q, s = synth.wgrad_codes(32768, 2048, seed=0, stream=42)
+    qt, st = fgb.fp8_direct_transpose(q.to(DEV), s.to(DEV))
+    oqt, ost = O.direct_transpose(q.numpy(), s.numpy())
+    assert np.array_equal(np_(st), ost)
+    assert np.array_equal(np_(qt), oqt)
+
+
+def test_transpose_block_weights(fgb):
+    say("transpose: 128x128-block weight transpose")
+    q = rand_codes((2048, 1024), 5)
+    s = rand_scales((16, 8), -30, 10, 6)
+    qt, st = fgb.fp8_direct_transpose(q.to(DEV), s.to(DEV), fgb.BLOCK128)
+    assert np.array_equal(np_(qt), q.numpy().T) and np.array_equal(np_(st), s.numpy().T)
+
+
+# ---------------------------------------------------------------------------
+# GEMMs
+# ---------------------------------------------------------------------------
+def test_gemm_linear_tiny_three_gemms(fgb):
+    say("gemm: tiny linear Fprop / Dgrad / Wgrad (fp32 out)")
+    X, W, dY = synth.linear_tiny(0)
+    oxq, oxs = O.quant_rowwise(X.numpy())
+    owq, ows = O.quant_blockwise(W.numpy())
+    ogq, ogs = O.quant_rowwise(dY.numpy())
+    oxqt, oxst = O.direct_transpose(oxq, oxs)
+    ogqt, ogst = O.direct_transpose(ogq, ogs)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    y = fgb.fp8_block_gemm(t(oxq), t(oxs), fgb.ROW1x128, t(owq), t(ows), fgb.BLOCK128, out_dtype=torch.float32)
+    check_fp32(np_(y), O.block_gemm(oxq, oxs, O.ROW1x128, owq, ows, O.BLOCK128))
+    dx = fgb.fp8_block_gemm(t(ogq), t(ogs), fgb.ROW1x128, t(owq.T), t(ows.T), fgb.BLOCK128, out_dtype=torch.float32)
+    check_fp32(np_(dx), O.block_gemm(ogq, ogs, O.ROW1x128, owq.T.copy(), ows.T.copy(), O.BLOCK128))
+    dw = fgb.fp8_block_gemm(t(ogqt), t(ogst), fgb.ROW1x128, t(oxqt), t(oxst), fgb.ROW1x128, out_dtype=torch.float32)
+    check_fp32(np_(dw), O.block_gemm(ogqt, ogst, O.ROW1x128, oxqt, oxst, O.ROW1x128))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (300, 2112, 512), (513, 260, 384)])
+@pytest.mark.parametrize("bg", ["block", "row"])
+def test_gemm_ragged(fgb, M, N, K, bg):
+    say("gemm ragged", M, N, K, bg)
+    a = rand_codes((M, K), M)
+    b = rand_codes((N, K), N)
+    sa = rand_scales((M, K // 128), -10, 10, 3)
+    if bg == "block":
+        sb = rand_scales(((N + 127) // 128, K // 128), -10, 10, 4)
+        gran = fgb.BLOCK128
+    else:
+        sb = rand_scales((N, K // 128), -10, 10, 4)
+        gran = fgb.ROW1x128
+    ref = O.block_gemm(a.numpy(), sa.numpy(), O.ROW1x128, b.numpy(), sb.numpy(), gran)
+    d = fgb.fp8_block_gemm(a.to(DEV), sa.to(DEV), fgb.ROW1x128, b.to(DEV), sb.to(DEV), gran, out_dtype=torch.float32)
+    check_fp32(np_(d), ref)
+    d16 = fgb.fp8_block_gemm(a.to(DEV), sa.to(DEV), fgb.ROW1x128, b.to(DEV), sb.to(DEV), gran, out_dtype=torch.bfloat16)
+    check_bf16(np_(d16), ref)
+
+
+def test_gemm_accumulate_and_ldd(fgb):
+    say("gemm accumulate into strided fp32 D")
+    M, N, K = 256, 384, 256
+    a, b = rand_codes((M, K), 1), rand_codes((N, K), 2)
+    sa, sb = rand_scales((M, 2), -5, 5, 3), rand_scales((N, 2), -5, 5, 4)
+    ref = O.block_gemm(a.numpy(), sa.numpy(), O.ROW1x128, b.numpy(), sb.numpy(), O.ROW1x128)
+    base = torch.randn(M, 512, dtype=torch.float32)
+    d = base.clone().to(DEV)
+    fgb.fp8_block_gemm(a.to(DEV), sa.to(DEV), fgb.ROW1x128, b.to(DEV), sb.to(DEV), fgb.ROW1x128,
+                       d=d[:, :N], accumulate=True)
+    got = np_(d)
+    check_fp32(got[:, :N] - base.numpy()[:, :N].astype(np.float64), ref, tol=1e-5)
+    assert np.array_equal(got[:, N:], base.numpy()[:, N:])
+
+
+def test_gemm_k4096_accumulation_control(fgb):
+    say("gemm: K=4096 random FP8 precision control")
+    g = torch.Generator().manual_seed(9)
+    x = torch.randn(256, 4096, generator=g)
+    y = torch.randn(512, 4096, generator=g)
+    qa, sa = O.quant_rowwise(x.numpy())
+    qb, sb = O.quant_rowwise(y.numpy())
+    ref = O.block_gemm(qa, sa, O.ROW1x128, qb, sb, O.ROW1x128)
+    t = lambda a: torch.from_numpy(a).to(DEV)
+    d = fgb.fp8_block_gemm(t(qa), t(sa), fgb.ROW1x128, t(qb), t(sb), fgb.ROW1x128, out_dtype=torch.float32)
+    err = check_fp32(np_(d), ref, tol=1e-5)
+    say("K=4096 max relative error", err)
+
+
+def test_gemm_mx_per32_with_level1(fgb):
+    say("gemm: 1x32 E8M0 scales on both sides + fp32 level-1 factor")
+    M, N, K = 192, 320, 1024
+    a, b = rand_codes((M, K), 11), rand_codes((N, K), 12)
+    sa, sb = rand_scales((M, K // 32), -20, 20, 13), rand_scales((N, K // 32), -20, 20, 14)
+    l1 = torch.rand(N, generator=torch.Generator().manual_seed(15)) * 2 + 0.1
+    ref = O.block_gemm(a.numpy(), sa.numpy(), O.ROW1x32, b.numpy(), sb.numpy(), O.ROW1x32,
+                       l1.numpy().reshape(N, 1), 10240)
+    d = fgb.fp8_block_gemm(a.to(DEV), sa.to(DEV), fgb.ROW1x32, b.to(DEV), sb.to(DEV), fgb.ROW1x32,
+                           b_l1=l1.to(DEV), g1=10240, out_dtype=torch.float32)
+    check_fp32(np_(d), ref)
+
+
+def _sample(M, N, n, seed):
+    rng = np.random.default_rng(seed)
+    mi = np.concatenate([rng.integers(0, M, n), [0, M - 1, M - 1]])
+    ni = np.concatenate([rng.integers(0, N, n), [0, N - 1, 0]])
+    return mi, ni
+
+
+def test_gemm_dsv3_fprop_sampled(fgb):
+    say("gemm: DeepSeek-V3 Fprop 8192x2048x7168, bf16 out, sampled")
+    M, N, K = 8192, 2048, 7168
+    a, b = rand_codes((M, K), 21), rand_codes((N, K), 22)
+    sa, sb = rand_scales((M, K // 128), -8, 2, 23), rand_scales((N // 128, K // 128), -12, -4, 24)
+    d = np_(fgb.fp8_block_gemm(a.to(DEV), sa.to(DEV), fgb.ROW1x128, b.to(DEV), sb.to(DEV), fgb.BLOCK128))
+    mi, ni = _sample(M, N, 3000, 1)
+    ref = O.block_gemm_sampled(a.numpy(), sa.numpy(), O.ROW1x128, b.numpy(), sb.numpy(), O.BLOCK128, mi, ni)
+    check_bf16(d[mi, ni], ref)
+
+
+# ---------------------------------------------------------------------------
+# MoE
+# ---------------------------------------------------------------------------
+def _moe_small(T=700, topk=4, G=6, H=512, seed=0):
+    g = torch.Generator().manual_seed(seed)
+    xq = rand_codes((T, H), seed + 1)
+    xs = rand_scales((T, H // 128), -20, 4, seed + 2)
+    idx = torch.stack([torch.randperm(G, generator=g)[:topk] for _ in range(T)]).to(torch.int32)
+    idx[idx == 2] = -1  # expert 2 empty, slots dropped
+    return xq, xs, idx
+
+
+def test_permute_pad_small(fgb):
+    say("permute_pad small (empty expert, dropped slots)")
+    xq, xs, idx = _moe_small()
+    G = 6
+    oq, os_, orm, ooff, used = O.permute_pad(xq.numpy(), xs.numpy(), idx.numpy(), G, 16)
+    q, s, rm, off = fgb.permute_pad(xq.to(DEV), xs.to(DEV), idx.to(DEV), G, 16)
+    assert np.array_equal(np_(off), ooff) and np.array_equal(np_(rm), orm)
+    assert np.array_equal(np_(q)[:used], oq[:used]) and np.array_equal(np_(s)[:used], os_[:used])
+
+
+def test_permute_pad_moe_full(fgb):
+    say("permute_pad: 16384 tokens top-8 of 32 experts, H=7168")
+    T, H, G = 16384, 7168, 32
+    idx, probs = synth.routing(T, G, 8, 1.1, 0)
+    xq = rand_codes((T, H), 31)
+    xs = rand_scales((T, H // 128), -20, 4, 32)
+    oq, os_, orm, ooff, used = O.permute_pad(xq.numpy(), xs.numpy(), idx, G, 16)
+    q, s, rm, off = fgb.permute_pad(xq.to(DEV), xs.to(DEV), torch.from_numpy(idx).to(DEV), G, 16)
+    assert np.array_equal(np_(off), ooff) and np.array_equal(np_(rm), orm)
+    assert np.array_equal(np_(s)[:used], os_[:used])
+    assert np.array_equal(np_(q)[:used], oq[:used])
+
+
+def test_unpermute_small_and_full(fgb):
+    for T, topk, H, with_p in [(50, 3, 64, False), (300, 8, 7168, True), (16384, 8, 7168, True)]:
+        say("unpermute", T, topk, H, with_p)
+        g = torch.Generator().manual_seed(T)
+        M = T * topk + 15 * 8
+        y = torch.randn(M, H, generator=g).to(torch.bfloat16)
+        rm = torch.randperm(M, generator=g)[: T * topk].reshape(T, topk).to(torch.int32)
+        rm[0, 0] = -1
+        probs = torch.rand(T, topk, generator=g) if with_p else None
+        out = fgb.unpermute_unpad(y.to(DEV), rm.to(DEV), None if probs is None else probs.to(DEV))
+        ref = O.unpermute_unpad(bits(y), rm.numpy(), None if probs is None else probs.numpy())
+        assert np.array_equal(np_(out), ref)
+
+
+def test_swiglu_quant(fgb):
+    for M, F, use_off in [(64, 256, False), (1000, 2048, True)]:
+        say("swiglu_quant", M, F, use_off)
+        g = torch.Generator().manual_seed(M)
+        h = (torch.randn(M, 2 * F, generator=g) * 4).to(torch.bfloat16)
+        h[0, :F] = 0.0
+        h[1, :F] = -100.0  # exp(-g) overflows
+        off = torch.tensor([0, 48, 96, 96, M - 40], dtype=torch.int32) if use_off else None
+        q0 = torch.zeros((M, F), dtype=torch.uint8, device=DEV)
+        s0 = torch.zeros((M, F // 128), dtype=torch.uint8, device=DEV)
+        q, s = fgb.swiglu_quant(h.to(DEV), None if off is None else off.to(DEV), q0, s0)
+        oq, os_ = O.swiglu_quant(bits(h), None if off is None else off.numpy())
+        assert np.array_equal(np_(s), os_)
+        assert np.array_equal(np_(q), oq)
+
+
+def test_grouped_gemm_small(fgb):
+    say("grouped gemm small, one empty expert, ragged segments")
+    G, N, K = 4, 384, 512
+    off = np.array([0, 48, 48, 336, 352], np.int32)
+    M_cap = 400
+    a = rand_codes((M_cap, K), 41)
+    sa = rand_scales((M_cap, K // 128), -6, 6, 42)
+    b = rand_codes((G, N, K), 43)
+    sb = rand_scales((G, (N + 127) // 128, K // 128), -6, 6, 44)
+    d = torch.full((M_cap, N), 7.0, dtype=torch.float32, device=DEV)
+    fgb.fp8_grouped_gemm(a.to(DEV), sa.to(DEV), b.to(DEV), sb.to(DEV), torch.from_numpy(off).to(DEV), d=d)
+    got = np_(d)
+    mi = np.repeat(np.arange(352), N)
+    ni = np.tile(np.arange(N), 352)
+    ref = O.grouped_gemm_sampled(a.numpy(), sa.numpy(), b.numpy(), sb.numpy(), off, mi, ni).reshape(352, N)
+    check_fp32(got[:352], ref)
+    assert np.all(got[352:] == 7.0)
+
+
+def test_grouped_gemm_moe_fc1_sampled(fgb):
+    say("grouped gemm: fc1 of the 32-expert layer (N=4096, K=7168), sampled")
+    T, G, N, K = 16384, 32, 4096, 7168
+    idx, _ = synth.routing(T, G, 8, 1.1, 0)
+    counts = np.bincount(idx.ravel(), minlength=G)
+    off = np.concatenate([[0], np.cumsum((counts + 15) // 16 * 16)]).astype(np.int32)
+    M_cap = T * 8 + 15 * G
+    a = rand_codes((M_cap, K), 51)
+    sa = rand_scales((M_cap, K // 128), -8, 2, 52)
+    b = rand_codes((G, N, K), 53)
+    sb = rand_scales((G, N // 128, K // 128), -12, -4, 54)
+    d = np_(fgb.fp8_grouped_gemm(a.to(DEV), sa.to(DEV), b.to(DEV), sb.to(DEV), torch.from_numpy(off).to(DEV)))
+    rng = np.random.default_rng(3)
+    mi = np.concatenate([rng.integers(0, off[G], 3000), off[1:G] - 1, off[:G]])
+    mi = mi[mi < off[G]]
+    ni = rng.integers(0, N, mi.size)
+    ref = O.grouped_gemm_sampled(a.numpy(), sa.numpy(), b.numpy(), sb.numpy(), off, mi, ni)
+    check_bf16(d[mi, ni], ref)
+
+
+# ---------------------------------------------------------------------------
+# MOSS two-level
+# ---------------------------------------------------------------------------
+def test_mx2_small_and_rows_of_full(fgb):
+    for R, Cc, g1 in [(5, 1024 + 96, 512), (64, 28672, 10240)]:
+        say("mx2", R, Cc, g1)
+        W, _ = synth.moss(seed=0, R=R, C=Cc, M=1)
+        W[1, :g1] = 0.0
+        q, s2, s1 = fgb.mx2_quant(W.to(DEV), g1)
+        oq, os2, os1 = O.mx2_quant(bits(W), g1)
+        assert np.array_equal(np_(s1), os1) and np.array_equal(np_(s2), os2)
+        assert np.array_equal(np_(q), oq)
+        xh = np_(fgb.mx2_dequant(q, s2, s1, g1))
+        assert np.array_equal(xh, O.mx2_dequant(oq, os2, os1, g1))
