@@ -17,7 +17,7 @@ __all__ = [
     "fp8_quant_rowwise", "fp8_quant_blockwise", "fp8_dequant", "fgb_e4m3_encode",
     "fp8_direct_transpose", "fp8_block_gemm", "fp8_grouped_gemm", "permute_pad",
     "permute_pad_workspace_size", "unpermute_unpad", "swiglu_quant", "mx2_quant", "mx2_dequant",
-    "F32", "BF16", "ROW1x128", "ROW1x32", "BLOCK128",
+    "F32", "BF16", "ROW1x128", "ROW1x32", "BLOCK128", "GEMM_EXACT", "GEMM_FAST",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(HERE, "libfgb.so")
 
 F32, BF16 = 0, 1
 ROW1x128, ROW1x32, BLOCK128 = 0, 1, 2
+GEMM_EXACT, GEMM_FAST = 0, 1
 
 SYMBOLS = [
     "fgb_last_error", "fgb_version", "fp8_quant_rowwise", "fp8_quant_blockwise", "fp8_dequant",
@@ -55,8 +56,8 @@ _SIG = {
     "fgb_e4m3_encode": (_i32, [_p, _i64, _p, _p]),
     "fp8_direct_transpose": (_i32, [_p, _p, _i32, _i64, _i64, _p, _p, _p]),
     "fp8_block_gemm": (_i32, [_p, _p, _i32, _p, _p, _i32, _p, _i64, _i64, _i64, _i64, _i64, _i64,
-                              _p, _i32, _i64, _i32, _p, _sz, _p]),
-    "fp8_grouped_gemm": (_i32, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, _i32, _p]),
+                              _p, _i32, _i64, _i32, _i32, _p, _sz, _p]),
+    "fp8_grouped_gemm": (_i32, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, _i32, _i32, _p]),
     "permute_pad": (_i32, [_p, _p, _p, _i64, _i32, _i32, _i64, _i32, _p, _p, _p, _p, _i64, _p,
                            _sz, _p]),
     "permute_pad_workspace_size": (_sz, [_i64, _i32, _i32]),
@@ -183,7 +184,7 @@ def fp8_direct_transpose(q, s, s_gran=ROW1x128):
 
 
 def fp8_block_gemm(a, sa, a_gran, b, sb, b_gran, b_l1=None, g1=0, out_dtype=torch.bfloat16,
-                   d=None, accumulate=False):
+                   d=None, accumulate=False, mode=GEMM_EXACT):
     """D = A * B^T with blockwise scales (A [M,K], B [N,K] codes) -> D [M, N]."""
     _check_dev(a, sa, b, sb, b_l1, d)
     M, K = a.shape
@@ -192,11 +193,12 @@ def fp8_block_gemm(a, sa, a_gran, b, sb, b_gran, b_l1=None, g1=0, out_dtype=torc
         d = torch.empty((M, N), dtype=out_dtype, device=a.device)
     _call("fp8_block_gemm", _ptr(a), _ptr(sa.contiguous()), a_gran, _ptr(b), _ptr(sb.contiguous()),
           b_gran, _ptr(b_l1), g1, M, N, K, _row_ld(a), _row_ld(b), _ptr(d), _dtype_code(d),
-          _row_ld(d), int(bool(accumulate)), None, 0, _stream(a))
+          _row_ld(d), int(bool(accumulate)), mode, None, 0, _stream(a))
     return d
 
 
-def fp8_grouped_gemm(a, sa, b, sb, group_offsets, out_dtype=torch.bfloat16, d=None):
+def fp8_grouped_gemm(a, sa, b, sb, group_offsets, out_dtype=torch.bfloat16, d=None,
+                     mode=GEMM_EXACT):
     """M-grouped contiguous GEMM: a [M_cap, K], b [G, N, K], offsets [G+1] (device) -> d [M_cap, N]."""
     _check_dev(a, sa, b, sb, group_offsets, d)
     M_cap, K = a.shape
@@ -205,7 +207,7 @@ def fp8_grouped_gemm(a, sa, b, sb, group_offsets, out_dtype=torch.bfloat16, d=No
         d = torch.empty((M_cap, N), dtype=out_dtype, device=a.device)
     _call("fp8_grouped_gemm", _ptr(a.contiguous()), _ptr(sa.contiguous()), _ptr(b.contiguous()),
           _ptr(sb.contiguous()), _ptr(group_offsets), G, M_cap, N, K, _ptr(d), _dtype_code(d),
-          _stream(a))
+          mode, _stream(a))
     return d
 
 

@@ -55,6 +55,10 @@ extern "C" {
 #define FGB_F32 0
 #define FGB_BF16 1
 
+/* GEMM arithmetic modes */
+#define FGB_GEMM_EXACT 0 /* FP32 accumulation of exact products (bf16 matrix unit) */
+#define FGB_GEMM_FAST 1  /* FP8 matrix unit with its own product-sum precision */
+
 /* scale granularities */
 #define FGB_ROW1x128 0 /* one scale per row per 128 columns: s[rows, cols/128] */
 #define FGB_ROW1x32 1  /* one scale per row per 32 columns:  s[rows, cols/32] */
@@ -128,26 +132,35 @@ int fp8_direct_transpose(const uint8_t *q, const uint8_t *s, int s_gran, int64_t
  * B [N,K] both K-contiguous, [DSV3] §5.7).  Covers a Linear's three GEMMs
  * ([DSV3] §1): Fprop A = X, B = W; Dgrad A = dY, B = W^T (block transpose);
  * Wgrad A = dY^T, B = X^T (both from fp8_direct_transpose, 1x128 scales).
- * Accumulation is FP32; the scale product of A's and B's group is applied to
- * each 128-element (or 32-element) K group's partial sum ([DSV3] §4, §5.3).
+ * Every K group's product sum is scaled by 2^(ea + eb) and accumulated in
+ * FP32 ([DSV3] §4, §5.3).
  *   a, sa, a_gran : A codes [M, K] (ld lda) and scales, FGB_ROW1x128 -> sa
  *                   [M, K/128], FGB_ROW1x32 -> sa [M, K/32] (dense)
  *   b, sb, b_gran : B codes [N, K] (ld ldb) and scales, FGB_BLOCK128 -> sb
  *                   [ceil(N/128), K/128], FGB_ROW1x128 -> sb [N, K/128],
  *                   FGB_ROW1x32 -> sb [N, K/32] (dense).  ROW1x32 must be
- *                   paired with ROW1x32.
+ *                   paired with ROW1x32; 1x32 scale tensors 4-byte aligned.
  *   b_l1, g1      : optional [MOSS] §3 level-1 FP32 factor per column of D,
  *                   b_l1 [N] (dense), applied to the FP32 result; requires
  *                   K <= g1 (one level-1 group along K); NULL = none.
  *   d, d_dtype    : D [M, N], ld ldd, FGB_F32 or FGB_BF16 (round to nearest
  *                   even).  accumulate != 0 (FP32 only): D += A * B^T.
+ *   mode          : FGB_GEMM_EXACT -- products are exact and summed in FP32
+ *                   (round to nearest even), matching an FP32 accumulation
+ *                   of the dequantized operands.  FGB_GEMM_FAST -- the FP8
+ *                   matrix unit with E8M0 scales, twice the rate; within
+ *                   each run of 8 consecutive K its products are summed
+ *                   with each cut (toward zero) to 13 bits below the run's
+ *                   largest, so |error| <= 2^-10 * sum over runs of the
+ *                   run's largest |scaled product| plus FP32 rounding.
  *   workspace     : unused, may be NULL (ws_bytes ignored).
- * K % 128 == 0; M, N >= 1.
+ * K % 128 == 0; M, N >= 1; 256 * lda and 256 * ldb below 2^32.
  */
 int fp8_block_gemm(const uint8_t *a, const uint8_t *sa, int a_gran, const uint8_t *b,
                    const uint8_t *sb, int b_gran, const float *b_l1, int64_t g1, int64_t M,
                    int64_t N, int64_t K, int64_t lda, int64_t ldb, void *d, int d_dtype,
-                   int64_t ldd, int accumulate, void *workspace, size_t ws_bytes, void *stream);
+                   int64_t ldd, int accumulate, int mode, void *workspace, size_t ws_bytes,
+                   void *stream);
 
 /*
  * fp8_grouped_gemm -- M-grouped contiguous FP8 GEMM for MoE experts ([DSV3]
@@ -161,11 +174,12 @@ int fp8_block_gemm(const uint8_t *a, const uint8_t *sa, int a_gran, const uint8_
  *                   no host synchronisation.
  *   d  [M_cap, N], dense, FGB_BF16 or FGB_F32.  Rows >= off[G] are neither
  *      read nor written.
+ *   mode: FGB_GEMM_EXACT or FGB_GEMM_FAST as for fp8_block_gemm.
  * K % 128 == 0.
  */
 int fp8_grouped_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t *b, const uint8_t *sb,
                      const int32_t *group_offsets, int G, int64_t M_cap, int64_t N, int64_t K,
-                     void *d, int d_dtype, void *stream);
+                     void *d, int d_dtype, int mode, void *stream);
 
 /*
  * permute_pad -- fused permute + pad ([FLOW] "Core method": expert reordering

@@ -43,6 +43,8 @@ def lib():
         L.orc_block_gemm.argtypes = [p, p, i32, p, p, i32, p, i64, i64, i64, i64, i64, i64, p]
         L.orc_block_gemm_sampled.argtypes = [p, p, i32, p, p, i32, p, i64, i64, i64, i64, i64,
                                              p, p, i64, p]
+        L.orc_gemm_run_bounds_sampled.argtypes = [p, p, i32, p, p, i32, p, i64, i64, i64, i64, p, p,
+                                                  i64, i32, p, p]
         L.orc_grouped_gemm_sampled.argtypes = [p, p, p, p, p, i32, i64, i64, p, p, i64, p]
         L.orc_permute_pad.restype = C.c_int64
         L.orc_permute_pad.argtypes = [p, p, p, i64, i32, i32, i64, i32, p, p, p, p, i64]
@@ -209,6 +211,28 @@ def block_gemm_sampled(a, sa, a_gran, b, sb, b_gran, mi, ni, b_l1=None, g1=0):
     lib().orc_block_gemm_sampled(_p(a), _p(sa), a_gran, _p(b), _p(sb), b_gran, _p(b_l1), g1, N,
                                  K, K, K, _p(mi), _p(ni), mi.size, _p(out))
     return out
+
+
+def gemm_run_bounds_sampled(a, sa, a_gran, b, sb, b_gran, mi, ni, run=8, b_l1=None):
+    """orc_gemm_run_bounds_sampled -> (sum of per-run max |p|, sum |p|) at (mi, ni).
+
+    Test tolerance helper for a matrix unit that sums runs of `run`
+    consecutive K products with limited precision."""
+    a = _c(a, np.uint8)
+    b = _c(b, np.uint8)
+    sa = _c(sa, np.uint8)
+    sb = _c(sb, np.uint8)
+    if b_l1 is not None:
+        b_l1 = _c(b_l1, np.float32)
+    mi = _c(np.asarray(mi, np.int64), np.int64)
+    ni = _c(np.asarray(ni, np.int64), np.int64)
+    K = a.shape[1]
+    N = b.shape[0]
+    rm = np.empty(mi.shape, np.float64)
+    asum = np.empty(mi.shape, np.float64)
+    lib().orc_gemm_run_bounds_sampled(_p(a), _p(sa), a_gran, _p(b), _p(sb), b_gran, _p(b_l1), N,
+                                      K, K, K, _p(mi), _p(ni), mi.size, run, _p(rm), _p(asum))
+    return rm, asum
 
 
 def grouped_gemm_sampled(a, sa, b, sb, off, mi, ni):

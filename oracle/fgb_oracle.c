@@ -338,6 +338,43 @@ void orc_block_gemm_sampled(const uint8_t *a, const uint8_t *sa, int a_gran, con
         out[i] = gemm_one(a, sa, a_gran, b, sb, b_gran, b_l1, g1, N, K, lda, ldb, mi[i], ni[i]);
 }
 
+/* Tolerance helper for a GEMM whose matrix unit sums runs of `run`
+ * consecutive K products with each product cut to a fixed number of bits
+ * below the run's largest: for each sample returns
+ *   runmax[i] = sum over runs of max_{k in run} |scaled product k|,
+ *   abssum[i] = sum over k of |scaled product k|
+ * (both times |b_l1| when given).  Plain definitions, fp64. */
+void orc_gemm_run_bounds_sampled(const uint8_t *a, const uint8_t *sa, int a_gran, const uint8_t *b,
+                                 const uint8_t *sb, int b_gran, const float *b_l1, int64_t N,
+                                 int64_t K, int64_t lda, int64_t ldb, const int64_t *mi,
+                                 const int64_t *ni, int64_t ns, int run, double *runmax,
+                                 double *abssum)
+{
+    dec_table();
+    int ga = gran_size(a_gran), gb = gran_size(b_gran);
+    for (int64_t i = 0; i < ns; i++) {
+        int64_t m = mi[i], n = ni[i];
+        double rm = 0.0, as = 0.0;
+        for (int64_t k0 = 0; k0 < K; k0 += run) {
+            double mx = 0.0;
+            for (int64_t k = k0; k < k0 + run && k < K; k++) {
+                int ea = (int)sa[m * (K / ga) + k / ga] - 127;
+                int eb = (b_gran == ORC_BLOCK128) ? (int)sb[(n / 128) * (K / 128) + k / 128] - 127
+                                                  : (int)sb[n * (K / gb) + k / gb] - 127;
+                double pr = fabs(ldexp(g_dec[a[m * lda + k]] * g_dec[b[n * ldb + k]], ea + eb));
+                as += pr;
+                if (pr > mx)
+                    mx = pr;
+            }
+            rm += mx;
+        }
+        double f = b_l1 ? fabs((double)b_l1[n]) : 1.0;
+        runmax[i] = rm * f;
+        abssum[i] = as * f;
+    }
+    (void)N;
+}
+
 /* M-grouped contiguous GEMM ([DSV3] §5.6): rows [off[g], off[g+1]) of A are */
 /* multiplied by expert g's B_g [N, K] with its 128x128 block scales.        */
 /* Rows of D outside every segment are not written.  out: [M_rows, N] fp64. */

@@ -66,7 +66,7 @@ def test_gemm_validation():
         a = dict(args, **kw)
         return L.fp8_block_gemm(a["a"], a["sa"], a["ag"], a["b"], a["sb"], a["bg"], a["l1"], a["g1"],
                                 a["M"], a["N"], a["K"], a["lda"], a["ldb"], a["d"], a["dt"],
-                                a["ldd"], a["acc"], None, 0, None)
+                                a["ldd"], a["acc"], a.get("mode", 0), None, 0, None)
     assert call(K=500) == 1
     assert call(M=0) == 1
     assert call(lda=500, K=256) == 1
@@ -75,7 +75,10 @@ def test_gemm_validation():
     assert call(acc=1, dt=1) == 2   # accumulate needs FP32 output
     assert call(l1=f, g1=256) == 2  # level-1 factor needs K <= g1
     assert call(a=None) == 1
-    assert L.fp8_grouped_gemm(f, f, f, f, f, 0, 100, 256, 512, f, 1, None) == 1
+    assert call(mode=2) == 2
+    assert call(ag=1, bg=1, sa=_fake(0x1001)) == 1  # 1x32 scales need 4-byte alignment
+    assert L.fp8_grouped_gemm(f, f, f, f, f, 0, 100, 256, 512, f, 1, 0, None) == 1
+    assert L.fp8_grouped_gemm(f, f, f, f, f, 4, 100, 256, 512, f, 1, 5, None) == 2
 
 
 def test_transpose_and_moe_validation():
