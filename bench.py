@@ -1,0 +1,366 @@
+#!/usr/bin/env python3
+"""Benchmark of the fine-grained blockwise FP8 hot path on one MI355X.
+
+One step is one pass of every hot-path operation over one batch of seeded
+synthetic input, already resident in HBM:
+  linear  DeepSeek-V3-shaped Linear, T=8192, Cin=7168, Cout=2048 (bf16 in):
+          1x128 quant of X and dY, 128x128 quant of W, block transpose of W,
+          direct transposes of Xq and dYq, Fprop / Dgrad / Wgrad (bf16 out)
+  moe     one GPU's 32 local experts, 16384 tokens x 7168, top-8: quant of X,
+          128x128 quant of W1 [32x4096x7168] and W2 [32x7168x2048],
+          permute+pad-16, grouped fc1, SwiGLU+quant, grouped fc2,
+          unpermute+unpad
+  wgrad   direct transposes of row-wise codes [32768, 7168] and [32768, 2048]
+          (scales 2^-20..2^4) and the Wgrad GEMM over K=32768 (fp32 out)
+  moss    two-level microscaling of W^T [28672, 8192] (quant + dequant),
+          1x32 quant of A [4096, 8192], MX-scaled GEMM (fp32 out)
+
+Reported value: the step's roofline efficiency in percent -- the sum over the
+step's kernels of their roofline floor time (algorithmic bytes at 8 TB/s HBM
+for the data-movement kernels, flops at the matrix unit's dense peak for the
+GEMMs: bf16 2.5 PFLOP/s for the exact mode, fp8 5.0 PFLOP/s for the fast
+mode) divided by the measured step time.  Per-kernel figures come from HIP
+events recorded on the launch stream around every kernel of the timed steps.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--gemm-mode exact|fast]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"exact": 2500.0, "fast": 5000.0}  # dense bf16 / dense fp8
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--gemm-mode", choices=["exact", "fast"], default="exact")
+    ap.add_argument("--parts", default="linear,moe,wgrad,moss")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    return ap.parse_args()
+
+
+class Recorder:
+    """HIP events around each kernel on torch's current stream (the launch stream)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.on = False
+        self.ev = {}
+        self.meta = {}
+
+    def __call__(self, name, kind, work, fn, *a, **kw):
+        if not self.on:
+            return fn(*a, **kw)
+        t = self.torch
+        e0 = t.cuda.Event(enable_timing=True)
+        e1 = t.cuda.Event(enable_timing=True)
+        e0.record()
+        out = fn(*a, **kw)
+        e1.record()
+        self.ev.setdefault(name, []).append((e0, e1))
+        self.meta[name] = (kind, work)
+        return out
+
+    def results(self):
+        res = {}
+        for name, lst in self.ev.items():
+            ms = sum(a.elapsed_time(b) for a, b in lst) / len(lst)
+            res[name] = (ms,) + self.meta[name]
+        return res
+
+
+def build(fgb, torch, synth, dev, seed, parts):
+    """All inputs and weights, resident on the GPU (untimed)."""
+    W = {}
+    if "linear" in parts:
+        X, Wl, dY = synth.linear_dsv3(seed, device=dev)
+        W["lin"] = dict(X=X, W=Wl, dY=dY)
+    if "moe" in parts:
+        X, idx, probs, W1, W2 = synth.moe(seed, device=dev)
+        T, topk, G, H = X.shape[0], idx.shape[1], 32, X.shape[1]
+        M_cap = T * topk + 15 * G
+        W["moe"] = dict(X=X, idx=torch.from_numpy(idx).to(dev), probs=torch.from_numpy(probs).to(dev),
+                        W1=W1.reshape(-1, H), W2=W2.reshape(-1, W2.shape[2]), G=G, M_cap=M_cap,
+                        F=W1.shape[1] // 2, N1=W1.shape[1], N2=W2.shape[1],
+                        ws=torch.empty(fgb.permute_pad_workspace_size(T, topk, G), dtype=torch.uint8,
+                                       device=dev),
+                        counts=torch.from_numpy(__import__("numpy").bincount(idx.ravel(), minlength=G)))
+    if "wgrad" in parts:
+        xq, xs = synth.wgrad_codes(32768, 7168, seed, 41, device=dev)
+        gq, gs = synth.wgrad_codes(32768, 2048, seed, 42, device=dev)
+        W["wg"] = dict(xq=xq, xs=xs, gq=gq, gs=gs)
+    if "moss" in parts:
+        Wm, A = synth.moss(seed, device=dev)
+        W["moss"] = dict(Wt=Wm.t().contiguous(), A=A)
+        del Wm
+    torch.cuda.synchronize()
+    return W
+
+
+def step(fgb, torch, W, rec, mode):
+    gm = fgb.GEMM_EXACT if mode == "exact" else fgb.GEMM_FAST
+    out = {}
+    if "lin" in W:
+        L = W["lin"]
+        T, Cin = L["X"].shape
+        Cout = L["W"].shape[0]
+        xq, xs = rec("lin.quant_rowwise X", "hbm", T * Cin * 3 + T * Cin // 128, fgb.fp8_quant_rowwise, L["X"])
+        wq, ws = rec("lin.quant_blockwise W", "hbm", Cout * Cin * 3 + (Cout * Cin) // 16384,
+                     fgb.fp8_quant_blockwise, L["W"])
+        gq, gs = rec("lin.quant_rowwise dY", "hbm", T * Cout * 3 + T * Cout // 128, fgb.fp8_quant_rowwise, L["dY"])
+        y = rec("lin.gemm fprop", "mfma", 2 * T * Cout * Cin, fgb.fp8_block_gemm, xq, xs, fgb.ROW1x128, wq, ws,
+                fgb.BLOCK128, mode=gm)
+        wqt, wst = rec("lin.transpose W (block)", "hbm", 2 * Cout * Cin + 2 * (Cout * Cin) // 16384,
+                       fgb.fp8_direct_transpose, wq, ws, fgb.BLOCK128)
+        dx = rec("lin.gemm dgrad", "mfma", 2 * T * Cin * Cout, fgb.fp8_block_gemm, gq, gs, fgb.ROW1x128, wqt, wst,
+                 fgb.BLOCK128, mode=gm)
+        xqt, xst = rec("lin.direct_transpose Xq", "hbm", 2 * (T * Cin + T * Cin // 128), fgb.fp8_direct_transpose,
+                       xq, xs)
+        gqt, gst = rec("lin.direct_transpose dYq", "hbm", 2 * (T * Cout + T * Cout // 128),
+                       fgb.fp8_direct_transpose, gq, gs)
+        dw = rec("lin.gemm wgrad", "mfma", 2 * Cout * Cin * T, fgb.fp8_block_gemm, gqt, gst, fgb.ROW1x128, xqt, xst,
+                 fgb.ROW1x128, mode=gm)
+        out["lin"] = (y, dx, dw)
+    if "moe" in W:
+        E = W["moe"]
+        T, H = E["X"].shape
+        topk = E["idx"].shape[1]
+        G, M_cap, F, N1, N2 = E["G"], E["M_cap"], E["F"], E["N1"], E["N2"]
+        rows = int(E["counts"].sum())
+        pad_rows = int(((E["counts"] + 15) // 16 * 16).sum())
+        xq, xs = rec("moe.quant_rowwise X", "hbm", T * H * 3 + T * H // 128, fgb.fp8_quant_rowwise, E["X"])
+        w1q, w1s = rec("moe.quant_blockwise W1", "hbm", E["W1"].numel() * 3 + E["W1"].numel() // 16384,
+                       fgb.fp8_quant_blockwise, E["W1"])
+        w2q, w2s = rec("moe.quant_blockwise W2", "hbm", E["W2"].numel() * 3 + E["W2"].numel() // 16384,
+                       fgb.fp8_quant_blockwise, E["W2"])
+        pq, ps, rmap, offs = rec("moe.permute_pad", "hbm",
+                                 T * H * (1 + 1 / 128) + pad_rows * H * (1 + 1 / 128) + 8 * T * topk,
+                                 fgb.permute_pad, xq, xs, E["idx"], G, 16, M_cap, E["ws"])
+        h = rec("moe.grouped_gemm fc1", "mfma", 2 * rows * N1 * H, fgb.fp8_grouped_gemm, pq, ps,
+                w1q.view(G, N1, H), w1s.view(G, N1 // 128, H // 128), offs, mode=gm)
+        aq, as_ = rec("moe.swiglu_quant", "hbm", pad_rows * (2 * F * 2 + F * (1 + 1 / 128)), fgb.swiglu_quant,
+                      h, offs)
+        y = rec("moe.grouped_gemm fc2", "mfma", 2 * rows * N2 * F, fgb.fp8_grouped_gemm, aq, as_,
+                w2q.view(G, N2, F), w2s.view(G, N2 // 128, F // 128), offs, mode=gm)
+        o = rec("moe.unpermute_unpad", "hbm", T * topk * H * 2 + T * H * 2 + 8 * T * topk, fgb.unpermute_unpad,
+                y, rmap, E["probs"])
+        out["moe"] = (o, offs)
+    if "wg" in W:
+        Wg = W["wg"]
+        T, Cin = Wg["xq"].shape
+        Cout = Wg["gq"].shape[1]
+        xqt, xst = rec("wgrad.direct_transpose X", "hbm", 2 * (T * Cin + T * Cin // 128), fgb.fp8_direct_transpose,
+                       Wg["xq"], Wg["xs"])
+        gqt, gst = rec("wgrad.direct_transpose dY", "hbm", 2 * (T * Cout + T * Cout // 128),
+                       fgb.fp8_direct_transpose, Wg["gq"], Wg["gs"])
+        dw = rec("wgrad.gemm K=32768", "mfma", 2 * Cout * Cin * T, fgb.fp8_block_gemm, gqt, gst, fgb.ROW1x128, xqt,
+                 xst, fgb.ROW1x128, out_dtype=torch.float32, mode=gm)
+        out["wg"] = dw
+    if "moss" in W:
+        Mo = W["moss"]
+        R, Cc = Mo["Wt"].shape
+        M = Mo["A"].shape[0]
+        g1 = 10240
+        q, s2, s1 = rec("moss.mx2_quant W^T", "hbm", R * Cc * (3 + 1 / 32) + 4 * R * ((Cc + g1 - 1) // g1),
+                        fgb.mx2_quant, Mo["Wt"], g1)
+        xh = rec("moss.mx2_dequant", "hbm", R * Cc * (1 + 4 + 1 / 32) + 4 * R * ((Cc + g1 - 1) // g1),
+                 fgb.mx2_dequant, q, s2, s1, g1)
+        aq, as_ = rec("moss.quant_rowwise A 1x32", "hbm", M * Cc * 3 + M * Cc // 32, fgb.fp8_quant_rowwise,
+                      Mo["A"], 32)
+        y = rec("moss.gemm MX", "mfma", 2 * M * R * Cc, fgb.fp8_block_gemm, aq, as_, fgb.ROW1x32, q, s2,
+                fgb.ROW1x32, b_l1=s1.view(-1), g1=g1, out_dtype=torch.float32, mode=gm)
+        out["moss"] = (xh, y)
+    return out
+
+
+def source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel_name, launches_bytes):
+    """HBM bytes per launch from committed rocprofv3 counter runs, when the
+    kernel's sources are unchanged since; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel_name)
+        if not rec or rec.get("source_sha") != source_sha(rec["sources"]):
+            return None
+        return rec["traffic_bytes_per_launch"]
+    except Exception:
+        return None
+
+
+def cpu_baseline(torch, synth, seed, kernel_results, step_floor_s):
+    """The oracle, as it stands, on a bounded sample of each op; the whole step's
+    CPU time is extrapolated from the per-op rates (single thread)."""
+    import numpy as np
+
+    import oracle as O
+
+    rates = {}  # units of work per second, per op family
+    t_all = time.perf_counter()
+    X, Wl, dY = synth.linear_dsv3(seed, T=256)
+    xb = synth.bf16_bits(X)
+    t = time.perf_counter(); xq, xs = O.quant_rowwise(xb); rates["quant_rowwise"] = xb.size * 3 / (time.perf_counter() - t)
+    wb = synth.bf16_bits(Wl[:256])
+    t = time.perf_counter(); O.quant_blockwise(wb); rates["quant_blockwise"] = wb.size * 3 / (time.perf_counter() - t)
+    t = time.perf_counter(); O.direct_transpose(xq, xs); rates["transpose"] = 2 * xq.size / (time.perf_counter() - t)
+    wq, ws = O.quant_blockwise(synth.bf16_bits(Wl))
+    mi = np.arange(2000) % 256
+    ni = (np.arange(2000) * 7) % 2048
+    t = time.perf_counter(); O.block_gemm_sampled(xq, xs, O.ROW1x128, wq, ws, O.BLOCK128, mi, ni)
+    rates["gemm"] = 2 * 2000 * 7168 / (time.perf_counter() - t)
+    Xm, idx, probs, _, _ = synth.moe(seed, T=2048, weights=False)
+    xmq, xms = O.quant_rowwise(synth.bf16_bits(Xm))
+    t = time.perf_counter(); pq, ps, rm, off, used = O.permute_pad(xmq, xms, idx, 32, 16)
+    rates["permute"] = (xmq.size + used * 7168) / (time.perf_counter() - t)
+    y = synth.bf16_bits(torch.randn(used, 7168).to(torch.bfloat16))
+    t = time.perf_counter(); O.unpermute_unpad(y, rm, probs); rates["unpermute"] = (2048 * 8 * 7168 * 2) / (time.perf_counter() - t)
+    h = synth.bf16_bits(torch.randn(512, 4096).to(torch.bfloat16))
+    t = time.perf_counter(); O.swiglu_quant(h); rates["swiglu"] = h.size * 2 * 1.25 / (time.perf_counter() - t)
+    Wm, _ = synth.moss(seed, R=64, C=8192, M=1)
+    wmb = synth.bf16_bits(Wm)
+    t = time.perf_counter(); q, s2, s1 = O.mx2_quant(wmb, 10240); rates["mx2"] = wmb.size * 3 / (time.perf_counter() - t)
+    sample_s = time.perf_counter() - t_all
+
+    def fam(name):
+        for key, f in [("gemm", "gemm"), ("transpose", "transpose"), ("quant_blockwise", "quant_blockwise"),
+                       ("quant_rowwise", "quant_rowwise"), ("permute_pad", "permute"), ("unpermute", "unpermute"),
+                       ("swiglu", "swiglu"), ("mx2", "mx2")]:
+            if key in name:
+                return f
+        return None
+
+    cpu_step_s = 0.0
+    for name, (ms, kind, work) in kernel_results.items():
+        f = fam(name)
+        cpu_step_s += work / rates[f]
+    value = 100.0 * step_floor_s / cpu_step_s
+    return {"value": value, "unit": "% of MI355X roofline (step, extrapolated)", "cores": 1, "kind": "oracle",
+            "step_seconds_extrapolated": cpu_step_s,
+            "rates": {"quant_rowwise_GBps": rates["quant_rowwise"] / 1e9, "transpose_GBps": rates["transpose"] / 1e9,
+                      "gemm_GFLOPs": rates["gemm"] / 1e9, "permute_GBps": rates["permute"] / 1e9,
+                      "unpermute_GBps": rates["unpermute"] / 1e9, "swiglu_GBps": rates["swiglu"] / 1e9,
+                      "mx2_GBps": rates["mx2"] / 1e9, "quant_blockwise_GBps": rates["quant_blockwise"] / 1e9},
+            "sample": ("single-threaded oracle on: 256x7168 bf16 quant (row and block) and direct transpose, "
+                       "2000 sampled outputs of the 7168-deep Fprop, permute_pad of 2048 tokens top-8, "
+                       "unpermute of 2048 tokens, SwiGLU+quant of 512x4096, MOSS quant of 64x8192; "
+                       f"{sample_s:.1f} s; step time extrapolated from the per-op rates")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (sharding is a design note only)"}))
+        sys.exit(2)
+    import torch
+
+    import fine_grained_blockwise_amd as fgb
+    import synth
+
+    dev = torch.device("cuda:0")
+    parts = set(args.parts.split(","))
+    W = build(fgb, torch, synth, dev, args.seed, parts)
+    log(f"inputs resident: parts={sorted(parts)} gemm_mode={args.gemm_mode}")
+    rec = Recorder(torch)
+    for _ in range(args.warmup):
+        step(fgb, torch, W, rec, args.gemm_mode)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
+    rec.on = True
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        out = step(fgb, torch, W, rec, args.gemm_mode)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    rec.on = False
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    res = rec.results()
+
+    kernels = {}
+    floor_s = 0.0
+    for name, (ms, kind, work) in res.items():
+        if kind == "hbm":
+            ach = work / (ms * 1e-3) / 1e9
+            peak = HBM_PEAK_GBS
+            unit = "GB/s"
+        else:
+            ach = work / (ms * 1e-3) / 1e12
+            peak = MFMA_PEAK_TFLOPS[args.gemm_mode]
+            unit = "TFLOP/s"
+        fl = work / (peak * (1e9 if kind == "hbm" else 1e12))
+        floor_s += fl
+        kernels[name] = {"ms": round(ms, 4), "achieved": round(ach, 1), "unit": unit, "frac": round(ach / peak, 4),
+                         "work": work}
+    value = 100.0 * floor_s / (ms_step * 1e-3)
+    dom = max(res.items(), key=lambda kv: kv[1][0])
+    dname, (dms, dkind, dwork) = dom
+    dpeak = HBM_PEAK_GBS if dkind == "hbm" else MFMA_PEAK_TFLOPS[args.gemm_mode]
+    dach = dwork / (dms * 1e-3) / (1e9 if dkind == "hbm" else 1e12)
+    roofline = {"bound": dkind, "achieved": round(dach, 1), "peak": dpeak,
+                "unit": "GB/s" if dkind == "hbm" else "TFLOP/s", "frac": round(dach / dpeak, 4),
+                "traffic": traffic_for(dname, dwork), "kernel": dname}
+
+    extra = {}
+    if "moss" in out:
+        xh, _ = out["moss"]
+        Wt = W["moss"]["Wt"].float()
+        num = (Wt.double() ** 2).sum()
+        den = ((Wt.double() - xh.double()) ** 2).sum()
+        extra["moss_snr_db"] = round(float(10 * torch.log10(num / den)), 3)
+
+    log(f"timed: {ms_step:.3f} ms/step")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(torch, synth, args.seed, res, floor_s)
+        log("cpu baseline done")
+
+    line = {
+        "metric": "blockwise-FP8 GEMM TFLOP/s & quant/transpose GB/s, % of MI355X roofline",
+        "value": round(value, 2),
+        "unit": "% of MI355X roofline (step)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3",
+        "data": "synthetic (seeded; shapes and distributions of the DeepSeek-V3 / MoE / MOSS layers)",
+        "config": {"workload": ("dsv3-linear T8192 Cin7168 Cout2048 (fwd+bwd) + moe 16384 tok top-8 of 32 "
+                                "experts H7168 F2048 (fwd) + wgrad T32768 Cin7168 Cout2048 + moss W^T 28672x8192 "
+                                "A 4096x8192"),
+                   "parts": sorted(parts), "gemm_mode": args.gemm_mode,
+                   "gemm_contraction": "bf16 MFMA on exact scaled fp8->bf16 operands" if args.gemm_mode == "exact"
+                   else "fp8 scaled MFMA"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        **extra,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
