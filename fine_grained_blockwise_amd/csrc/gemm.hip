@@ -31,10 +31,10 @@
 // copied HBM -> LDS with global_load_lds_dwordx4 into a double buffer
 // (2 x 64 KB).  LDS rows are 128 bytes with the 16-byte chunk index
 // XOR-swizzled by f(row) = (row ^ row>>3) & 7 so the operand reads of 32
-// consecutive rows hit distinct banks.  All fragment reads of a K step are
-// issued before the next step's copies, so no wait on those copies ever
-// stands in front of an LDS read.  Tiles are mapped to XCDs in contiguous
-// ranges so neighbouring tiles share an XCD's L2.
+// consecutive rows hit distinct banks.  The K loop is software-pipelined by
+// half steps (see the main loop) so the matrix units work right after every
+// barrier while LDS reads and HBM copies are in flight.  Tiles are mapped to
+// XCDs in contiguous ranges so neighbouring tiles share an XCD's L2.
 //
 // Fragment layout, per lane (row r = lane%32 of a 32-row tile, half h =
 // lane/32), per 128-byte K step: the four 16-byte chunks h, h+2, h+4, h+6.
@@ -55,7 +55,8 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 constexpr int BM = 256, BN = 256, BK = 128;
 constexpr int TILE_BYTES = BM * BK; // one operand tile: 32 KB
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;
-constexpr int LDS_BYTES = 2 * STAGE_BYTES; // double buffer: 128 KB
+constexpr int EPI_BYTES = 4 * 128 * (128 * 2 + 16); // epilogue staging, 4 waves (bf16; fp32 halves fit too)
+constexpr int LDS_BYTES = 2 * STAGE_BYTES > EPI_BYTES ? 2 * STAGE_BYTES : EPI_BYTES; // 136 KB
 
 enum { MODE_EXACT = 0, MODE_FAST = 1 };
 enum { AG_ROW128 = 0, AG_ROW32 = 1 };
@@ -82,20 +83,15 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t nb)
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
-// 16 E4M3 codes -> two 8-element bf16 operands, each value times 2^e (sc = 2^e).
-__device__ __forceinline__ void cvt16_bf16(uint4 w, float sc, v8bf &lo, v8bf &hi)
+// 8 E4M3 codes (two words) -> one 8-element bf16 operand, each value times 2^e (sc = 2^e).
+__device__ __forceinline__ v8bf cvt8_bf16(uint32_t w0, uint32_t w1, float sc)
 {
-    uint4 a, b;
-    a.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, sc, false));
-    a.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, sc, true));
-    a.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, sc, false));
-    a.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, sc, true));
-    b.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.z, sc, false));
-    b.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.z, sc, true));
-    b.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.w, sc, false));
-    b.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.w, sc, true));
-    lo = __builtin_bit_cast(v8bf, a);
-    hi = __builtin_bit_cast(v8bf, b);
+    uint4 a;
+    a.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, false));
+    a.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, true));
+    a.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, false));
+    a.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, true));
+    return __builtin_bit_cast(v8bf, a);
 }
 
 // Scale byte -> the fp32 whose exponent field it is (byte 0 is taken as 1).
@@ -124,16 +120,25 @@ gemm_fp8_kernel(GemmArgs p)
     const int64_t N = p.N;
 
     // ---- tile -> (m0, n0) ------------------------------------------------
+    // Within an XCD's contiguous range, tiles run in bands of GM m-tiles:
+    // consecutive tiles walk down a band first, so the ~32 tiles an XCD runs
+    // at once form a GM x 8 block sharing A rows and B columns in L2.
     int64_t tile = xcd_remap(blockIdx.x, gridDim.x);
-    int64_t m0 = 0, m_end = 0, tn;
+    int64_t tm, tn;
+    {
+        constexpr int64_t GM = 4;
+        const int64_t tiles_m = gridDim.x / p.tiles_n;
+        const int64_t band = tile / (GM * p.tiles_n), in = tile % (GM * p.tiles_n);
+        const int64_t bm = min(GM, tiles_m - band * GM); // rows in this (possibly last) band
+        tm = band * GM + in % bm;
+        tn = in / bm;
+    }
+    int64_t m0 = 0, m_end = 0;
     const uint8_t *B = p.b, *SB = p.sb;
     if constexpr (!GROUPED) {
-        m0 = (tile / p.tiles_n) * BM;
-        tn = tile % p.tiles_n;
+        m0 = tm * BM;
         m_end = p.M;
     } else {
-        int64_t tm = tile / p.tiles_n;
-        tn = tile % p.tiles_n;
         int e = -1;
         int64_t base = 0;
         for (int g = 0; g < p.G; g++) {
@@ -170,15 +175,24 @@ gemm_fp8_kernel(GemmArgs p)
         a_off[i] = (uint32_t)(ar * p.lda + chunk * 16);
         b_off[i] = (uint32_t)(br * p.ldb + chunk * 16);
     }
+    // One 16-byte-per-lane HBM -> LDS copy; M0 holds the wave-uniform LDS
+    // base, lane l lands at M0 + 16*l.  Issued as inline asm so that the
+    // compiler does not place a wait on it in front of unrelated LDS reads:
+    // the kernel itself waits for all copies (s_waitcnt vmcnt(0)) before the
+    // barrier that precedes reading a stage.
+    auto dma16 = [](const uint8_t *g, uint32_t lds_addr) {
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :
+                     : "s"(lds_addr), "v"(g)
+                     : "memory", "m0");
+    };
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
     auto issue_copy = [&](int stage, int64_t ks) {
-        uint8_t *sa_ = smem + stage * STAGE_BYTES;
-        uint8_t *sb_ = sa_ + TILE_BYTES;
+        const uint32_t sa_ = lds_base + stage * STAGE_BYTES, sb_ = sa_ + TILE_BYTES;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            __builtin_amdgcn_global_load_lds(a_base + a_off[i] + ks * BK,
-                                             (__attribute__((address_space(3))) void *)(sa_ + (wave * 8 + i) * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(b_base + b_off[i] + ks * BK,
-                                             (__attribute__((address_space(3))) void *)(sb_ + (wave * 8 + i) * 1024), 16, 0, 0);
+            dma16(a_base + a_off[i] + ks * BK, __builtin_amdgcn_readfirstlane(sa_ + (wave * 8 + i) * 1024));
+            dma16(b_base + b_off[i] + ks * BK, __builtin_amdgcn_readfirstlane(sb_ + (wave * 8 + i) * 1024));
         }
     };
 
@@ -186,7 +200,7 @@ gemm_fp8_kernel(GemmArgs p)
     // Per K step and operand tile t, a lane needs the scale(s) of its row of
     // that tile: one byte (128-element groups) or the four consecutive bytes
     // of the step's 32-element blocks, read as one dword.  They are loaded one
-    // step ahead into raw registers and decoded after the next barrier.
+    // step ahead and consumed after the next barrier.
     constexpr bool A32 = AG == AG_ROW32, B32 = BG == BG_ROW32;
     const int64_t sa_row = A32 ? K / 32 : K / 128;
     const int64_t sb_row = B32 ? K / 32 : K / 128;
@@ -217,31 +231,42 @@ gemm_fp8_kernel(GemmArgs p)
             sb_off[t] = (uint32_t)(c * sb_row);
         }
     }
-    uint32_t raw_a[4], raw_b[4];
-    auto load_scales = [&](int64_t ks) {
+    auto load_scales = [&](int64_t ks, uint32_t(&ra)[4], uint32_t(&rb)[4]) {
 #pragma unroll
         for (int t = 0; t < 4; t++) {
-            raw_a[t] = A32 ? *reinterpret_cast<const uint32_t *>(sa_base + sa_off[t] + ks * 4)
-                           : (uint32_t)sa_base[sa_off[t] + ks];
+            ra[t] = A32 ? *reinterpret_cast<const uint32_t *>(sa_base + sa_off[t] + ks * 4)
+                        : (uint32_t)sa_base[sa_off[t] + ks];
             if constexpr (BG == BG_BLOCK)
-                raw_b[t] = t == 0 ? (uint32_t)sb_base[ks] : 0u;
+                rb[t] = t == 0 ? (uint32_t)sb_base[ks] : 0u;
             else
-                raw_b[t] = B32 ? *reinterpret_cast<const uint32_t *>(sb_base + sb_off[t] + ks * 4)
-                               : (uint32_t)sb_base[sb_off[t] + ks];
+                rb[t] = B32 ? *reinterpret_cast<const uint32_t *>(sb_base + sb_off[t] + ks * 4)
+                            : (uint32_t)sb_base[sb_off[t] + ks];
         }
     };
 
     // ---- fragment addressing ---------------------------------------------------
     // operand row r = t*32 + lane%32 within the wave's 128 rows (the wave's
-    // 128-row offset leaves swz unchanged); chunk 2q + h.
-    int frag_off[4][4];
+    // 128-row offset leaves swz unchanged); chunk 2q + h.  swz(r) for odd t is
+    // swz for even t with bit 2 flipped, i.e. chunk 2q+h of an odd tile sits
+    // where chunk 2(q^2)+h of an even tile does; t*4096 is an immediate.
+    int qoff[4];
 #pragma unroll
-    for (int t = 0; t < 4; t++) {
-        int r = t * 32 + l32;
+    for (int q = 0; q < 4; q++)
+        qoff[q] = l32 * 128 + (((2 * q + hk) ^ swz(l32)) * 16);
+    // half hf of a K step = chunks q = 2hf, 2hf+1 of every A and B tile
+    auto read_half = [&](int stage, int hf, uint4(&fa)[4][2], uint4(&fb)[4][2]) {
+        const uint8_t *la = smem + stage * STAGE_BYTES + wm * 128 * 128;
+        const uint8_t *lb = smem + stage * STAGE_BYTES + TILE_BYTES + wn * 128 * 128;
 #pragma unroll
-        for (int q = 0; q < 4; q++)
-            frag_off[t][q] = r * 128 + (((2 * q + hk) ^ swz(r)) * 16);
-    }
+        for (int qq = 0; qq < 2; qq++)
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const int q = 2 * hf + qq;
+                const int off = qoff[(t & 1) ? (q ^ 2) : q] + t * 4096;
+                fa[t][qq] = *reinterpret_cast<const uint4 *>(la + off);
+                fb[t][qq] = *reinterpret_cast<const uint4 *>(lb + off);
+            }
+    };
 
     v16f acc[4][4];
 #pragma unroll
@@ -250,110 +275,209 @@ gemm_fp8_kernel(GemmArgs p)
         for (int j = 0; j < 4; j++)
             acc[i][j] = (v16f){0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
-    load_scales(0);
-    issue_copy(0, 0);
-
-    for (int64_t ks = 0; ks < nk; ks++) {
-        const int cur = (int)(ks & 1);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        uint32_t ca[4], cb[4];
+    // MFMAs of half hf of a K step whose scales are ca/cb.
+    // Scales of one K step, compact: for a 128-element group operand one
+    // word with byte t = tile t; for 1x32 one word per tile (byte = 32-block
+    // of the step); for 128x128 B one byte.
+    constexpr int NA = A32 ? 4 : 1, NB = B32 ? 4 : 1;
+    auto pack = [&](const uint32_t(&ra)[4], const uint32_t(&rb)[4], uint32_t(&wa)[NA], uint32_t(&wb)[NB]) {
+        if constexpr (A32) {
 #pragma unroll
-        for (int t = 0; t < 4; t++) {
-            ca[t] = raw_a[t];
-            cb[t] = raw_b[t];
+            for (int t = 0; t < 4; t++)
+                wa[t] = ra[t];
+        } else {
+            wa[0] = ra[0] | (ra[1] << 8) | (ra[2] << 16) | (ra[3] << 24);
         }
-        const uint8_t *la = smem + cur * STAGE_BYTES + wm * 128 * 128;
-        const uint8_t *lb = smem + cur * STAGE_BYTES + TILE_BYTES + wn * 128 * 128;
-        uint4 fa[4][4], fb[4][4];
+        if constexpr (B32) {
 #pragma unroll
-        for (int q = 0; q < 4; q++)
-#pragma unroll
-            for (int t = 0; t < 4; t++) {
-                fa[t][q] = *reinterpret_cast<const uint4 *>(la + frag_off[t][q]);
-                fb[t][q] = *reinterpret_cast<const uint4 *>(lb + frag_off[t][q]);
-            }
-        if (ks + 1 < nk) {
-            load_scales(ks + 1);
-            issue_copy(cur ^ 1, ks + 1);
+            for (int t = 0; t < 4; t++)
+                wb[t] = rb[t];
+        } else if constexpr (BG == BG_BLOCK) {
+            wb[0] = rb[0];
+        } else {
+            wb[0] = rb[0] | (rb[1] << 8) | (rb[2] << 16) | (rb[3] << 24);
         }
+    };
+    auto compute_half = [&](int hf, const uint4(&fa)[4][2], const uint4(&fb)[4][2], const uint32_t(&ca)[NA],
+                            const uint32_t(&cb)[NB]) {
         if constexpr (MODE == MODE_FAST) {
-#pragma unroll
-            for (int s = 0; s < 2; s++) {
-                // scale words: byte t = tile t's scale for this lane's 32-block
-                uint32_t wa = 0, wb = 0;
-                const int sh = A32 ? 8 * (2 * s + hk) : 0;
+            const int s = hf; // 64-wide sub-step
+            uint32_t wa = 0, wb = 0;
+            if constexpr (A32) {
+                const int sh = 8 * (2 * s + hk);
 #pragma unroll
                 for (int t = 0; t < 4; t++)
                     wa |= ((ca[t] >> sh) & 0xFFu) << (8 * t);
-                if constexpr (BG == BG_BLOCK) {
-                    wb = cb[0];
-                } else {
-                    const int shb = B32 ? 8 * (2 * s + hk) : 0;
+            } else {
+                wa = ca[0];
+            }
+            if constexpr (B32) {
+                const int shb = 8 * (2 * s + hk);
 #pragma unroll
-                    for (int t = 0; t < 4; t++)
-                        wb |= ((cb[t] >> shb) & 0xFFu) << (8 * t);
-                }
-                v8i av[4], bv[4];
+                for (int t = 0; t < 4; t++)
+                    wb |= ((cb[t] >> shb) & 0xFFu) << (8 * t);
+            } else {
+                wb = cb[0];
+            }
+            v8i av[4], bv[4];
 #pragma unroll
-                for (int t = 0; t < 4; t++) {
-                    av[t] = cat(fa[t][2 * s], fa[t][2 * s + 1]);
-                    bv[t] = cat(fb[t][2 * s], fb[t][2 * s + 1]);
-                }
+            for (int t = 0; t < 4; t++) {
+                av[t] = cat(fa[t][0], fa[t][1]);
+                bv[t] = cat(fb[t][0], fb[t][1]);
+            }
 #define FGB_J(I, J) acc[I][J] = mfma_scaled<I, (BG == BG_BLOCK ? 0 : J)>(av[I], bv[J], acc[I][J], wa, wb);
 #define FGB_I(I) FGB_J(I, 0) FGB_J(I, 1) FGB_J(I, 2) FGB_J(I, 3)
-                FGB_I(0) FGB_I(1) FGB_I(2) FGB_I(3)
+            FGB_I(0) FGB_I(1) FGB_I(2) FGB_I(3)
 #undef FGB_I
 #undef FGB_J
-            }
         } else {
 #pragma unroll
-            for (int q = 0; q < 4; q++) {
-                v8bf alo[4], ahi[4], blo[4], bhi[4];
+            for (int qq = 0; qq < 2; qq++) {
+                const int q = 2 * hf + qq; // 32-wide pair
+                float sa_f[4], sb_f[4];
 #pragma unroll
                 for (int t = 0; t < 4; t++) {
-                    uint32_t ba = A32 ? (ca[t] >> (8 * q)) & 0xFFu : ca[t];
-                    cvt16_bf16(fa[t][q], scale_f32(ba), alo[t], ahi[t]);
-                    uint32_t bb = BG == BG_BLOCK ? cb[0] : (B32 ? (cb[t] >> (8 * q)) & 0xFFu : cb[t]);
-                    cvt16_bf16(fb[t][q], scale_f32(bb), blo[t], bhi[t]);
+                    sa_f[t] = scale_f32(A32 ? (ca[t] >> (8 * q)) & 0xFFu : (ca[0] >> (8 * t)) & 0xFFu);
+                    sb_f[t] = scale_f32(B32 ? (cb[t] >> (8 * q)) & 0xFFu
+                                            : (BG == BG_BLOCK ? cb[0] : (cb[0] >> (8 * t)) & 0xFFu));
                 }
+                // bytes 0-7 of the chunk feed sub-step 2q, bytes 8-15 sub-step 2q+1
 #pragma unroll
-                for (int i = 0; i < 4; i++)
+                for (int sub = 0; sub < 2; sub++) {
+                    v8bf av[4], bv[4];
 #pragma unroll
-                    for (int j = 0; j < 4; j++) {
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[i], blo[j], acc[i][j], 0, 0, 0);
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[i], bhi[j], acc[i][j], 0, 0, 0);
+                    for (int t = 0; t < 4; t++) {
+                        av[t] = sub == 0 ? cvt8_bf16(fa[t][qq].x, fa[t][qq].y, sa_f[t])
+                                         : cvt8_bf16(fa[t][qq].z, fa[t][qq].w, sa_f[t]);
+                        bv[t] = sub == 0 ? cvt8_bf16(fb[t][qq].x, fb[t][qq].y, sb_f[t])
+                                         : cvt8_bf16(fb[t][qq].z, fb[t][qq].w, sb_f[t]);
                     }
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+#pragma unroll
+                        for (int j = 0; j < 4; j++)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0); // keep each sub-step's converts next to its MFMAs
+                }
             }
         }
+    };
+
+    // ---- main loop ---------------------------------------------------------------
+    // Iteration j: wait for stage j's copy and sync; start the copy of step
+    // j+1 into the other stage (free: every wave finished reading it before
+    // this barrier); read half 0 of step j; multiply half 1 of step j-1
+    // (already in registers); read half 1 of step j; multiply half 0 of step j.
+    // The matrix units start right after each barrier, LDS reads overlap the
+    // MFMAs of the other half, and each copy has a full step to land.
+    uint4 f0a[4][2], f0b[4][2], f1a[4][2], f1b[4][2];
+    uint32_t ca_cur[NA], cb_cur[NB], ca_prev[NA], cb_prev[NB], ra[4], rb[4];
+    load_scales(0, ra, rb);
+    issue_copy(0, 0);
+    for (int64_t ks = 0; ks < nk; ks++) {
+        const int cur = (int)(ks & 1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        pack(ra, rb, ca_cur, cb_cur);
+        if (ks + 1 < nk) {
+            issue_copy(cur ^ 1, ks + 1);
+            load_scales(ks + 1, ra, rb);
+        }
+        read_half(cur, 0, f0a, f0b);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks > 0)
+            compute_half(1, f1a, f1b, ca_prev, cb_prev);
+        __builtin_amdgcn_sched_barrier(0);
+        read_half(cur, 1, f1a, f1b);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_half(0, f0a, f0b, ca_cur, cb_cur);
+#pragma unroll
+        for (int t = 0; t < NA; t++)
+            ca_prev[t] = ca_cur[t];
+#pragma unroll
+        for (int t = 0; t < NB; t++)
+            cb_prev[t] = cb_cur[t];
     }
+    compute_half(1, f1a, f1b, ca_prev, cb_prev);
 
     // ---- epilogue --------------------------------------------------------------
     // 32x32 accumulator layout: lane l, register r -> row (r/4)*8 + (l/32)*4 + r%4,
-    // column l%32.
+    // column l%32.  The tile is staged through LDS (free after the last
+    // barrier) so that global stores are 16 bytes per lane along rows: each
+    // wave writes its 128x128 block, 64 rows at a time, as [row][128 + pad]
+    // and reads it back row-contiguous.
+    __syncthreads();
+    constexpr int ESZ = OUT_BF16 ? 2 : 4;
+    constexpr int ROWB = 128 * ESZ + 16;   // padded LDS row (bytes)
+    constexpr int EPI_ROWS = OUT_BF16 ? 128 : 64;
+    uint8_t *ep = smem + wave * (EPI_ROWS * ROWB);
+    float l1v[4];
 #pragma unroll
     for (int j = 0; j < 4; j++) {
         int64_t col = n0 + wn * 128 + j * 32 + l32;
-        if (col >= N)
-            continue;
-        float l1 = p.l1 ? p.l1[col] : 1.0f;
+        l1v[j] = (p.l1 && col < N) ? p.l1[col] : 1.0f;
+    }
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+    for (int part = 0; part < 128 / EPI_ROWS; part++) {
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                int64_t row = m0 + wm * 128 + i * 32 + (r / 4) * 8 + hk * 4 + (r % 4);
-                if (row >= m_end)
-                    continue;
-                float v = acc[i][j][r];
-                if (p.l1)
-                    v *= l1;
-                if constexpr (OUT_BF16) {
-                    ((uint16_t *)p.d)[row * p.ldd + col] = (uint16_t)bf16_rne(v);
+        for (int ii = 0; ii < EPI_ROWS / 32; ii++) {
+            const int i = part * (EPI_ROWS / 32) + ii;
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    int row = ii * 32 + (r / 4) * 8 + hk * 4 + (r % 4);
+                    int col = j * 32 + l32;
+                    float v = acc[i][j][r];
+                    if (p.l1)
+                        v *= l1v[j];
+                    if constexpr (OUT_BF16)
+                        *reinterpret_cast<uint16_t *>(ep + row * ROWB + col * 2) = (uint16_t)bf16_rne(v);
+                    else
+                        *reinterpret_cast<float *>(ep + row * ROWB + col * 4) = v;
+                }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0): this wave's LDS writes done
+        __builtin_amdgcn_wave_barrier();
+        // read back: one row segment of 16 bytes per lane
+        constexpr int LPR = 128 * ESZ / 16; // lanes per row
+        constexpr int RPI = 64 / LPR;       // rows per instruction
+        const int lr = lane / LPR, lc = lane % LPR;
+#pragma unroll
+        for (int rr = 0; rr < EPI_ROWS; rr += RPI) {
+            const int row_l = rr + lr;
+            const int64_t row = m0 + wm * 128 + part * EPI_ROWS + row_l;
+            const int64_t col0 = n0 + wn * 128 + lc * (16 / ESZ);
+            uint4 v = *reinterpret_cast<const uint4 *>(ep + row_l * ROWB + lc * 16);
+            if (row >= m_end || col0 >= N)
+                continue;
+            uint8_t *dst = (uint8_t *)p.d + (row * p.ldd + col0) * ESZ;
+            const bool full = col0 + 16 / ESZ <= N && (((uintptr_t)dst & 15) == 0);
+            if constexpr (OUT_BF16) {
+                if (full) {
+                    *reinterpret_cast<uint4 *>(dst) = v;
                 } else {
-                    float *dst = (float *)p.d + row * p.ldd + col;
-                    *dst = p.accumulate ? *dst + v : v;
+                    uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+                    for (int e = 0; e < 8 && col0 + e < N; e++)
+                        reinterpret_cast<uint16_t *>(dst)[e] = (uint16_t)(w4[e / 2] >> (16 * (e & 1)));
+                }
+            } else {
+                float f4[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+                float *fd = reinterpret_cast<float *>(dst);
+                if (full) {
+                    if (p.accumulate) {
+                        float4 o = *reinterpret_cast<const float4 *>(fd);
+                        f4[0] += o.x; f4[1] += o.y; f4[2] += o.z; f4[3] += o.w;
+                    }
+                    *reinterpret_cast<float4 *>(fd) = make_float4(f4[0], f4[1], f4[2], f4[3]);
+                } else {
+                    for (int e = 0; e < 4 && col0 + e < N; e++)
+                        fd[e] = p.accumulate ? fd[e] + f4[e] : f4[e];
                 }
             }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
