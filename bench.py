@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--parts", default="linear,moe,wgrad,moss")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB read + 1 GiB write elementwise kernel 3 times (the reference "
+                         "point for scaling HBM byte counters), then exit")
     return ap.parse_args()
 
 
@@ -195,15 +198,18 @@ def source_sha(paths):
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel_name, launches_bytes):
-    """HBM bytes per launch from committed rocprofv3 counter runs, when the
-    kernel's sources are unchanged since; else None."""
+def traffic_for(kernel_name, mode):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) from
+    committed rocprofv3 counter runs, when the kernel's sources and GEMM mode
+    are unchanged since; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path)).get(kernel_name)
         if not rec or rec.get("source_sha") != source_sha(rec["sources"]):
+            return None
+        if rec.get("gemm_mode", mode) != mode:
             return None
         return rec["traffic_bytes_per_launch"]
     except Exception:
@@ -279,6 +285,16 @@ def main():
     import synth
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = 1 << 28  # float32 elements: 1 GiB in, 1 GiB out per launch
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"launches": 3, "read_bytes_per_launch": 4 * n,
+                                               "write_bytes_per_launch": 4 * n}}))
+        return
     parts = set(args.parts.split(","))
     W = build(fgb, torch, synth, dev, args.seed, parts)
     log(f"inputs resident: parts={sorted(parts)} gemm_mode={args.gemm_mode}")
@@ -319,7 +335,7 @@ def main():
     dach = dwork / (dms * 1e-3) / (1e9 if dkind == "hbm" else 1e12)
     roofline = {"bound": dkind, "achieved": round(dach, 1), "peak": dpeak,
                 "unit": "GB/s" if dkind == "hbm" else "TFLOP/s", "frac": round(dach / dpeak, 4),
-                "traffic": traffic_for(dname, dwork), "kernel": dname}
+                "traffic": traffic_for(dname, args.gemm_mode), "kernel": dname}
 
     extra = {}
     if "moss" in out:
