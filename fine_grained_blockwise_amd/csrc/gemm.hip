@@ -27,23 +27,27 @@
 //   precision (see above); accumulation across K groups is FP32.
 //
 // Tiling: 256x256 output tile per workgroup of 4 waves (each wave 128x128 =
-// 4x4 tiles of 32x32), K step 128.  A and B tiles (256 rows x 128 bytes) are
-// copied HBM -> LDS with global_load_lds_dwordx4 into a double buffer
-// (2 x 64 KB).  LDS rows are 128 bytes with the 16-byte chunk index
-// XOR-swizzled by f(row) = (row ^ row>>3) & 7 so the operand reads of 32
-// consecutive rows hit distinct banks.  The K loop is software-pipelined by
-// half steps (see the main loop) so the matrix units work right after every
-// barrier while LDS reads and HBM copies are in flight.  Tiles are mapped to
-// XCDs in contiguous ranges so neighbouring tiles share an XCD's L2.
+// 4x4 tiles of 32x32), K step 128 split into two 64-deep half-steps.  A and
+// B tiles go HBM -> LDS with global_load_lds (16 bytes per lane) through a
+// ring of 4 half-step buffers; each wave issues two copy instructions per
+// 16 (exact) or 4 (fast) MFMAs, so the copies of half-step h+4 trickle out
+// during half-step h and have three half-steps to land, and a barrier comes
+// once per half-step.  The scale bytes travel the same way (one dword per
+// tile row or column, in two K-step tables).  LDS rows are 64 bytes with
+// the 16-byte chunk index XOR-swizzled by (row >> 2) & 3, so the operand
+// reads of 16 consecutive rows hit distinct banks and each copy instruction
+// has per-lane offsets that do not depend on which 16 rows it moves.  Tiles
+// are mapped to XCDs in contiguous ranges, in bands of 4 m-tiles, so
+// neighbouring tiles share an XCD's L2.
 //
 // Fragment layout, per lane (row r = lane%32 of a 32-row tile, half h =
-// lane/32), per 128-byte K step: the four 16-byte chunks h, h+2, h+4, h+6.
-//   FAST : 64-wide sub-step s uses chunks 4s+h (bytes 0-15, hardware K block
-//          0) and 4s+2+h (bytes 16-31, block 1); the hardware takes block
-//          b's scale from lane r + 32b, so lane half h supplies the scale of
-//          logical 32-block 2s+h.
-//   EXACT: 32-wide pair p uses chunk 2p+h; its bytes 0-7 feed the bf16 MFMA
-//          of sub-step 2p and bytes 8-15 that of sub-step 2p+1.
+// lane/32), per 64-byte half-step: chunks h and 2+h.
+//   FAST : one 64-wide MFMA step per half-step: chunk h is bytes 0-15
+//          (hardware K block 0), chunk 2+h bytes 16-31 (block 1); the
+//          hardware takes block b's scale from lane r + 32b, so lane half h
+//          supplies the scale of the half-step's 32-block h.
+//   EXACT: 32-wide pair p' (0, 1) of the half-step uses chunk 2p'+h; its
+//          bytes 0-7 feed one bf16 MFMA sub-step and bytes 8-15 the next.
 #include "fgb_internal.h"
 
 namespace fgb {
@@ -53,10 +57,12 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int TILE_BYTES = BM * BK; // one operand tile: 32 KB
-constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+constexpr int NBUF = 4;                              // ring of half-step (K = 64) buffers
+constexpr int HALF_BYTES = BM * 64;                  // one operand tile of a half-step: 16 KB
+constexpr int BUF_BYTES = 2 * HALF_BYTES;            // A and B: 32 KB
 constexpr int EPI_BYTES = 4 * 128 * (128 * 2 + 16); // epilogue staging, 4 waves (bf16; fp32 halves fit too)
-constexpr int LDS_BYTES = 2 * STAGE_BYTES > EPI_BYTES ? 2 * STAGE_BYTES : EPI_BYTES; // 136 KB
+constexpr int MAIN_BYTES = NBUF * BUF_BYTES + 2 * 2 * 256 * 4; // ring + two K steps of scale tables
+constexpr int LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES; // 136 KB
 
 enum { MODE_EXACT = 0, MODE_FAST = 1 };
 enum { AG_ROW128 = 0, AG_ROW32 = 1 };
@@ -81,7 +87,6 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t nb)
     return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
 // 8 E4M3 codes (two words) -> one 8-element bf16 operand, each value times 2^e (sc = 2^e).
 __device__ __forceinline__ v8bf cvt8_bf16(uint32_t w0, uint32_t w1, float sc)
@@ -158,115 +163,176 @@ gemm_fp8_kernel(GemmArgs p)
     }
     const int64_t n0 = tn * BN;
 
-    // ---- global -> LDS copy plan -----------------------------------------
-    // Operand tile = 32 groups of 8 rows (1 KB each); wave w copies groups
-    // w*8 .. w*8+7 of A and of B.  Lane l lands at LDS offset l*16 of its
-    // group: row g*8 + l/8, physical chunk l%8, which holds logical chunk
-    // (l%8) ^ swz(row).  Rows past the end re-read the last valid row.
+    // ---- LDS layout ----------------------------------------------------------
+    // Ring of 4 half-step buffers (K = 64 each): buffer b holds the A tile
+    // (256 rows x 64 bytes) at b*32K and the B tile at b*32K + 16K.  Row r's
+    // 16-byte chunk c sits at r*64 + 16*(c ^ ((r >> 2) & 3)): the reads of 16
+    // consecutive rows at one chunk then cover all 64 banks once.  Scale
+    // tables (one dword per tile row of A and per tile column of B, the scale
+    // byte zero-extended, or the 4 bytes of the step's 32-element blocks) for
+    // two K steps follow the ring.
+    // Half-step h uses buffer h % 4 and is copied with the 8 copy
+    // instructions of each wave (4 for A, 4 for B), plus, for the first half
+    // of K step j, one scale copy per operand into scale slot j % 2.  The
+    // copy of half-step h+4 is issued over the slots of half-step h, after
+    // the barrier that follows the last read of buffer h % 4; it must land by
+    // the barrier before half-step h+3 is read, three half-steps later.
+    constexpr int RING_BYTES = NBUF * BUF_BYTES;
+    constexpr int SC_SLOT = 2 * 256 * 4; // A and B tables of one K step
+
+    // ---- copy plan ---------------------------------------------------------
+    // Instruction g (0..3) of wave w copies tile rows w*64 + g*16 .. +15: lane
+    // l lands at LDS (w*64 + g*16)*64 + 16*l, i.e. row +l/4, position l%4,
+    // which holds chunk (l%4) ^ ((l/16) % 4) of that row.  Rows past the end
+    // re-read the last valid row (those outputs are never stored).
     const uint8_t *a_base = p.a + m0 * p.lda;
     const uint8_t *b_base = B + n0 * p.ldb;
-    uint32_t a_off[8], b_off[8];
+    uint32_t a_off[4], b_off[4];
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        int r = (wave * 8 + i) * 8 + (lane >> 3);
-        int chunk = (lane & 7) ^ swz(r);
-        int64_t ar = m0 + r < m_end ? r : m_end - 1 - m0;
-        int64_t br = n0 + r < N ? r : N - 1 - n0;
-        a_off[i] = (uint32_t)(ar * p.lda + chunk * 16);
-        b_off[i] = (uint32_t)(br * p.ldb + chunk * 16);
+    for (int g = 0; g < 4; g++) {
+        const int r = wave * 64 + g * 16 + (lane >> 2);
+        const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
+        const int64_t ar = m0 + r < m_end ? r : m_end - 1 - m0;
+        const int64_t br = n0 + r < N ? r : N - 1 - n0;
+        a_off[g] = (uint32_t)(ar * p.lda + chunk * 16);
+        b_off[g] = (uint32_t)(br * p.ldb + chunk * 16);
     }
-    // One 16-byte-per-lane HBM -> LDS copy; M0 holds the wave-uniform LDS
-    // base, lane l lands at M0 + 16*l.  Issued as inline asm so that the
-    // compiler does not place a wait on it in front of unrelated LDS reads:
-    // the kernel itself waits for all copies (s_waitcnt vmcnt(0)) before the
-    // barrier that precedes reading a stage.
-    auto dma16 = [](const uint8_t *g, uint32_t lds_addr) {
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                     :
-                     : "s"(lds_addr), "v"(g)
-                     : "memory", "m0");
-    };
-    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
-    auto issue_copy = [&](int stage, int64_t ks) {
-        const uint32_t sa_ = lds_base + stage * STAGE_BYTES, sb_ = sa_ + TILE_BYTES;
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            dma16(a_base + a_off[i] + ks * BK, __builtin_amdgcn_readfirstlane(sa_ + (wave * 8 + i) * 1024));
-            dma16(b_base + b_off[i] + ks * BK, __builtin_amdgcn_readfirstlane(sb_ + (wave * 8 + i) * 1024));
-        }
-    };
-
-    // ---- scale plan ----------------------------------------------------------
-    // Per K step and operand tile t, a lane needs the scale(s) of its row of
-    // that tile: one byte (128-element groups) or the four consecutive bytes
-    // of the step's 32-element blocks, read as one dword.  They are loaded one
-    // step ahead and consumed after the next barrier.
+    // Scale copy: lane l of wave w fetches the scale of tile row (A) or tile
+    // column (B) w*64 + l for K step ks into dword w*64 + l of the step's table.
     constexpr bool A32 = AG == AG_ROW32, B32 = BG == BG_ROW32;
     const int64_t sa_row = A32 ? K / 32 : K / 128;
     const int64_t sb_row = B32 ? K / 32 : K / 128;
-    const uint8_t *sa_base = p.sa + m0 * sa_row;
-    uint32_t sa_off[4];
-#pragma unroll
-    for (int t = 0; t < 4; t++) {
-        int64_t r = wm * 128 + t * 32 + l32;
-        r = m0 + r < m_end ? r : m_end - 1 - m0;
-        sa_off[t] = (uint32_t)(r * sa_row);
-    }
-    const uint8_t *sb_base;
-    uint32_t sb_off[4];
-    if constexpr (BG == BG_BLOCK) {
-        // a wave's 128 columns lie in one 128-row block of B; past the last
-        // block (ragged N) clamp to it -- those columns are never stored
-        int64_t nb = (n0 + wn * 128) / 128, nb_last = (N - 1) / 128;
-        sb_base = SB + (nb < nb_last ? nb : nb_last) * (K / 128);
-#pragma unroll
-        for (int t = 0; t < 4; t++)
-            sb_off[t] = 0;
-    } else {
-        sb_base = SB + n0 * sb_row;
-#pragma unroll
-        for (int t = 0; t < 4; t++) {
-            int64_t c = wn * 128 + t * 32 + l32;
-            c = n0 + c < N ? c : N - 1 - n0;
-            sb_off[t] = (uint32_t)(c * sb_row);
+    uint32_t sa_off, sb_off;
+    const uint8_t *sa_base = p.sa + m0 * sa_row, *sb_base;
+    {
+        const int64_t r = wave * 64 + lane;
+        const int64_t rc = m0 + r < m_end ? r : m_end - 1 - m0;
+        sa_off = (uint32_t)(rc * sa_row);
+        const int64_t c = n0 + r < N ? r : N - 1 - n0;
+        if constexpr (BG == BG_BLOCK) {
+            sb_base = SB;
+            sb_off = (uint32_t)(((n0 + c) / 128) * (K / 128));
+        } else {
+            sb_base = SB + n0 * sb_row;
+            sb_off = (uint32_t)(c * sb_row);
         }
     }
-    auto load_scales = [&](int64_t ks, uint32_t(&ra)[4], uint32_t(&rb)[4]) {
+
+    // One copy instruction: M0 holds the wave-uniform LDS destination (lane l
+    // lands at M0 + 16*l, or M0 + 4*l for the 1- and 4-byte forms); the global
+    // address is a uniform 64-bit base (SGPRs) plus the lane's 32-bit offset.
+    // Issued as inline asm so that the compiler does not place waits on them
+    // in front of unrelated LDS reads; the kernel counts them itself.
+    auto dma16 = [](const uint8_t *gbase, uint32_t off, uint32_t lds_addr) {
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :
+                     : "s"(lds_addr), "v"(off), "s"(gbase)
+                     : "memory", "m0");
+    };
+    auto dma4 = [](const uint8_t *gbase, uint32_t off, uint32_t lds_addr) {
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                     :
+                     : "s"(lds_addr), "v"(off), "s"(gbase)
+                     : "memory", "m0");
+    };
+    auto dma1 = [](const uint8_t *gbase, uint32_t off, uint32_t lds_addr) {
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_ubyte %1, %2"
+                     :
+                     : "s"(lds_addr), "v"(off), "s"(gbase)
+                     : "memory", "m0");
+    };
+    auto uniform = [](const uint8_t *q) {
+        const uint64_t v = (uint64_t)(uintptr_t)q;
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+        return (const uint8_t *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+    };
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
+    const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const uint8_t *a_base_u = uniform(a_base), *b_base_u = uniform(b_base);
+    const uint8_t *sa_base_u = uniform(sa_base), *sb_base_u = uniform(sb_base);
+    const int64_t nh = 2 * nk; // half-steps
+    // Copy instruction i (0..7: A g=0..3, then B g=0..3) of half-step h
+    // (clamped to the last one: copies past the end refill a free buffer
+    // with data nothing reads).
+    auto dma_tile = [&](int64_t h, int i) {
+        const int64_t hc = h < nh ? h : nh - 1;
+        const uint32_t dst = lds_base + (uint32_t)(hc & 3) * BUF_BYTES + (i >= 4 ? HALF_BYTES : 0) +
+                             (wave_u * 64 + (i & 3) * 16) * 64;
+        if (i < 4)
+            dma16(a_base_u + hc * 64, a_off[i & 3], dst);
+        else
+            dma16(b_base_u + hc * 64, b_off[i & 3], dst);
+    };
+    // The two scale copies of K step ks (clamped likewise).
+    auto dma_scales = [&](int64_t ks) {
+        const int64_t kc = ks < nk ? ks : nk - 1;
+        const uint32_t dst = lds_base + RING_BYTES + (uint32_t)(kc & 1) * SC_SLOT + wave_u * 256;
+        if constexpr (A32)
+            dma4(sa_base_u + kc * 4, sa_off, dst);
+        else
+            dma1(sa_base_u + kc, sa_off, dst);
+        if constexpr (B32)
+            dma4(sb_base_u + kc * 4, sb_off, dst + 1024);
+        else
+            dma1(sb_base_u + kc, sb_off, dst + 1024);
+    };
+    // All copies of half-step h (the prologue's batches).
+    auto dma_half = [&](int64_t h, int first, int last) {
+        if (first == 0 && (h & 1) == 0)
+            dma_scales(h >> 1);
+        for (int i = first; i <= last; i++)
+            dma_tile(h, i);
+    };
+    // Wait until at most n copy instructions are outstanding, then sync.
+#define FGB_WAIT_SYNC(n)                                                                                               \
+    do {                                                                                                               \
+        asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory");                                                          \
+        __syncthreads();                                                                                               \
+    } while (0)
+
+    // ---- scales of one K step, from its LDS table ---------------------------
+    // A: word per tile of the wave (1x32: the 4 block bytes; 1x128: the byte),
+    // packed for 1x128 into one word with byte t = tile t; likewise B, whose
+    // 128x128 form is one byte (the wave's 128 columns lie in one block).
+    constexpr int NA = A32 ? 4 : 1, NB = B32 ? 4 : 1;
+    auto read_scales = [&](int64_t ks, uint32_t(&wa)[NA], uint32_t(&wb)[NB]) {
+        const uint32_t *ta = reinterpret_cast<const uint32_t *>(smem + RING_BYTES + (ks & 1) * SC_SLOT);
+        const uint32_t *tb = ta + 256;
+        uint32_t va[4], vb[4];
 #pragma unroll
         for (int t = 0; t < 4; t++) {
-            ra[t] = A32 ? *reinterpret_cast<const uint32_t *>(sa_base + sa_off[t] + ks * 4)
-                        : (uint32_t)sa_base[sa_off[t] + ks];
-            if constexpr (BG == BG_BLOCK)
-                rb[t] = t == 0 ? (uint32_t)sb_base[ks] : 0u;
-            else
-                rb[t] = B32 ? *reinterpret_cast<const uint32_t *>(sb_base + sb_off[t] + ks * 4)
-                            : (uint32_t)sb_base[sb_off[t] + ks];
+            va[t] = ta[wm * 128 + t * 32 + l32];
+            vb[t] = BG == BG_BLOCK ? (t == 0 ? tb[wn * 128] : 0u) : tb[wn * 128 + t * 32 + l32];
+        }
+        if constexpr (A32) {
+#pragma unroll
+            for (int t = 0; t < 4; t++)
+                wa[t] = va[t];
+        } else {
+            wa[0] = va[0] | (va[1] << 8) | (va[2] << 16) | (va[3] << 24);
+        }
+        if constexpr (B32) {
+#pragma unroll
+            for (int t = 0; t < 4; t++)
+                wb[t] = vb[t];
+        } else if constexpr (BG == BG_BLOCK) {
+            wb[0] = vb[0];
+        } else {
+            wb[0] = vb[0] | (vb[1] << 8) | (vb[2] << 16) | (vb[3] << 24);
         }
     };
 
     // ---- fragment addressing ---------------------------------------------------
-    // operand row r = t*32 + lane%32 within the wave's 128 rows (the wave's
-    // 128-row offset leaves swz unchanged); chunk 2q + h.  swz(r) for odd t is
-    // swz for even t with bit 2 flipped, i.e. chunk 2q+h of an odd tile sits
-    // where chunk 2(q^2)+h of an even tile does; t*4096 is an immediate.
+    // The wave's row t*32 + l32 of an operand tile (offset wm*128 or wn*128
+    // rows); chunk c of it at qoff[c] + t*2048 (the swizzle depends on l32
+    // only).
     int qoff[4];
 #pragma unroll
-    for (int q = 0; q < 4; q++)
-        qoff[q] = l32 * 128 + (((2 * q + hk) ^ swz(l32)) * 16);
-    // half hf of a K step = chunks q = 2hf, 2hf+1 of every A and B tile
-    auto read_half = [&](int stage, int hf, uint4(&fa)[4][2], uint4(&fb)[4][2]) {
-        const uint8_t *la = smem + stage * STAGE_BYTES + wm * 128 * 128;
-        const uint8_t *lb = smem + stage * STAGE_BYTES + TILE_BYTES + wn * 128 * 128;
-#pragma unroll
-        for (int qq = 0; qq < 2; qq++)
-#pragma unroll
-            for (int t = 0; t < 4; t++) {
-                const int q = 2 * hf + qq;
-                const int off = qoff[(t & 1) ? (q ^ 2) : q] + t * 4096;
-                fa[t][qq] = *reinterpret_cast<const uint4 *>(la + off);
-                fb[t][qq] = *reinterpret_cast<const uint4 *>(lb + off);
-            }
-    };
+    for (int c = 0; c < 4; c++)
+        qoff[c] = l32 * 64 + ((c ^ ((l32 >> 2) & 3)) * 16);
+    auto lds_a = [&](int64_t h) { return smem + (h & 3) * BUF_BYTES + wm * 128 * 64; };
+    auto lds_b = [&](int64_t h) { return smem + (h & 3) * BUF_BYTES + HALF_BYTES + wn * 128 * 64; };
 
     v16f acc[4][4];
 #pragma unroll
@@ -275,36 +341,42 @@ gemm_fp8_kernel(GemmArgs p)
         for (int j = 0; j < 4; j++)
             acc[i][j] = (v16f){0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
-    // MFMAs of half hf of a K step whose scales are ca/cb.
-    // Scales of one K step, compact: for a 128-element group operand one
-    // word with byte t = tile t; for 1x32 one word per tile (byte = 32-block
-    // of the step); for 128x128 B one byte.
-    constexpr int NA = A32 ? 4 : 1, NB = B32 ? 4 : 1;
-    auto pack = [&](const uint32_t(&ra)[4], const uint32_t(&rb)[4], uint32_t(&wa)[NA], uint32_t(&wb)[NB]) {
-        if constexpr (A32) {
+    // ---- prologue ----------------------------------------------------------------
+    // Half-steps 0..2 and the first six instructions of half-step 3 in flight;
+    // wait for half-step 0 (24 instructions issued after it) and sync.
+    dma_half(0, 0, 7);
+    dma_half(1, 0, 7);
+    dma_half(2, 0, 7);
+    dma_half(3, 0, 5);
+    FGB_WAIT_SYNC(24);
+    uint32_t ca[NA], cb[NB], can[NA], cbn[NB];
+    read_scales(0, ca, cb);
+
+    // ---- main loop ----------------------------------------------------------------
+    // A K step is 8 slots; slot s of step j issues 2 copy instructions
+    // (half-step 2j+3's last two in slot 0, 2j+4's in slots 1-4 with step
+    // j+2's scale copies, 2j+5's first six in slots 5-7).  The barriers
+    // before slots 1 and 5 wait for half-steps 2j+1 and 2j+2 (18 copy
+    // instructions issued after them in either case).
+    if constexpr (MODE == MODE_FAST) {
+        // A half-step is one 64-deep MFMA sub-step: 16 scaled MFMAs, 4 per
+        // slot; its fragments (chunks hk and 2+hk of each tile row: hardware
+        // K blocks 0 and 1) are read in the first two slots after the barrier
+        // that precedes it.
+        uint4 f[2][2][4][2]; // [half-step parity][A/B][tile][chunk]
+        auto read_frag = [&](int64_t h, int op, uint4(&x)[4][2]) {
+            const uint8_t *base = op == 0 ? lds_a(h) : lds_b(h);
 #pragma unroll
-            for (int t = 0; t < 4; t++)
-                wa[t] = ra[t];
-        } else {
-            wa[0] = ra[0] | (ra[1] << 8) | (ra[2] << 16) | (ra[3] << 24);
-        }
-        if constexpr (B32) {
-#pragma unroll
-            for (int t = 0; t < 4; t++)
-                wb[t] = rb[t];
-        } else if constexpr (BG == BG_BLOCK) {
-            wb[0] = rb[0];
-        } else {
-            wb[0] = rb[0] | (rb[1] << 8) | (rb[2] << 16) | (rb[3] << 24);
-        }
-    };
-    auto compute_half = [&](int hf, const uint4(&fa)[4][2], const uint4(&fb)[4][2], const uint32_t(&ca)[NA],
-                            const uint32_t(&cb)[NB]) {
-        if constexpr (MODE == MODE_FAST) {
-            const int s = hf; // 64-wide sub-step
+            for (int t = 0; t < 4; t++) {
+                x[t][0] = *reinterpret_cast<const uint4 *>(base + qoff[hk] + t * 2048);
+                x[t][1] = *reinterpret_cast<const uint4 *>(base + qoff[2 + hk] + t * 2048);
+            }
+        };
+        // MFMAs of row tile i for half-step parity hs (32-blocks 2hs, 2hs+1 of the step)
+        auto mfma_row = [&](int hs, int i, const uint4(&xa)[4][2], const uint4(&xb)[4][2]) {
             uint32_t wa = 0, wb = 0;
             if constexpr (A32) {
-                const int sh = 8 * (2 * s + hk);
+                const int sh = 8 * (2 * hs + hk);
 #pragma unroll
                 for (int t = 0; t < 4; t++)
                     wa |= ((ca[t] >> sh) & 0xFFu) << (8 * t);
@@ -312,93 +384,208 @@ gemm_fp8_kernel(GemmArgs p)
                 wa = ca[0];
             }
             if constexpr (B32) {
-                const int shb = 8 * (2 * s + hk);
+                const int sh = 8 * (2 * hs + hk);
 #pragma unroll
                 for (int t = 0; t < 4; t++)
-                    wb |= ((cb[t] >> shb) & 0xFFu) << (8 * t);
+                    wb |= ((cb[t] >> sh) & 0xFFu) << (8 * t);
             } else {
                 wb = cb[0];
             }
-            v8i av[4], bv[4];
-#pragma unroll
-            for (int t = 0; t < 4; t++) {
-                av[t] = cat(fa[t][0], fa[t][1]);
-                bv[t] = cat(fb[t][0], fb[t][1]);
-            }
-#define FGB_J(I, J) acc[I][J] = mfma_scaled<I, (BG == BG_BLOCK ? 0 : J)>(av[I], bv[J], acc[I][J], wa, wb);
+            const v8i av = cat(xa[i][0], xa[i][1]);
+#define FGB_J(I, J)                                                                                                    \
+    if (i == I)                                                                                                        \
+        acc[I][J] = mfma_scaled<I, (BG == BG_BLOCK ? 0 : J)>(av, cat(xb[J][0], xb[J][1]), acc[I][J], wa, wb);
 #define FGB_I(I) FGB_J(I, 0) FGB_J(I, 1) FGB_J(I, 2) FGB_J(I, 3)
             FGB_I(0) FGB_I(1) FGB_I(2) FGB_I(3)
 #undef FGB_I
 #undef FGB_J
-        } else {
+        };
+        read_frag(0, 0, f[0][0]);
+        read_frag(0, 1, f[0][1]);
+        for (int64_t ks = 0; ks < nk; ks++) {
+            const int64_t h0 = 2 * ks;
+            // slot 0
+            dma_tile(h0 + 3, 6);
+            dma_tile(h0 + 3, 7);
+            mfma_row(0, 0, f[0][0], f[0][1]);
+            __builtin_amdgcn_sched_barrier(0);
+            // slot 1
+            FGB_WAIT_SYNC(18);
+            dma_scales(ks + 2);
+            dma_tile(h0 + 4, 0);
+            dma_tile(h0 + 4, 1);
+            read_frag(h0 + 1, 0, f[1][0]);
+            mfma_row(0, 1, f[0][0], f[0][1]);
+            __builtin_amdgcn_sched_barrier(0);
+            // slot 2
+            dma_tile(h0 + 4, 2);
+            dma_tile(h0 + 4, 3);
+            read_frag(h0 + 1, 1, f[1][1]);
+            mfma_row(0, 2, f[0][0], f[0][1]);
+            __builtin_amdgcn_sched_barrier(0);
+            // slot 3
+            dma_tile(h0 + 4, 4);
+            dma_tile(h0 + 4, 5);
+            mfma_row(0, 3, f[0][0], f[0][1]);
+            __builtin_amdgcn_sched_barrier(0);
+            // slot 4
+            dma_tile(h0 + 4, 6);
+            dma_tile(h0 + 4, 7);
+            mfma_row(1, 0, f[1][0], f[1][1]);
+            __builtin_amdgcn_sched_barrier(0);
+            // slot 5
+            FGB_WAIT_SYNC(18);
+            read_scales(ks + 1, can, cbn);
+            dma_tile(h0 + 5, 0);
+            dma_tile(h0 + 5, 1);
+            read_frag(h0 + 2, 0, f[0][0]);
+            mfma_row(1, 1, f[1][0], f[1][1]);
+            __builtin_amdgcn_sched_barrier(0);
+            // slot 6
+            dma_tile(h0 + 5, 2);
+            dma_tile(h0 + 5, 3);
+            read_frag(h0 + 2, 1, f[0][1]);
+            mfma_row(1, 2, f[1][0], f[1][1]);
+            __builtin_amdgcn_sched_barrier(0);
+            // slot 7
+            dma_tile(h0 + 5, 4);
+            dma_tile(h0 + 5, 5);
+            mfma_row(1, 3, f[1][0], f[1][1]);
 #pragma unroll
-            for (int qq = 0; qq < 2; qq++) {
-                const int q = 2 * hf + qq; // 32-wide pair
-                float sa_f[4], sb_f[4];
+            for (int t = 0; t < NA; t++)
+                ca[t] = can[t];
 #pragma unroll
-                for (int t = 0; t < 4; t++) {
-                    sa_f[t] = scale_f32(A32 ? (ca[t] >> (8 * q)) & 0xFFu : (ca[0] >> (8 * t)) & 0xFFu);
-                    sb_f[t] = scale_f32(B32 ? (cb[t] >> (8 * q)) & 0xFFu
-                                            : (BG == BG_BLOCK ? cb[0] : (cb[0] >> (8 * t)) & 0xFFu));
-                }
-                // bytes 0-7 of the chunk feed sub-step 2q, bytes 8-15 sub-step 2q+1
+            for (int t = 0; t < NB; t++)
+                cb[t] = cbn[t];
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        // Exact mode: a slot is one 16-deep sub-step: its 16 bf16 MFMAs
+        // interleaved with the 32 conversions of the next sub-step (two per
+        // MFMA), so the conversion work runs while the matrix unit is busy.
+        // Sub-step s of a step takes bytes 0-7 (s even) or 8-15 (s odd) of
+        // chunk 2q' + hk of its half-step, q = s/2 the 32-wide pair, q' = q%2.
+        // Pair q+1's LDS reads are issued two slots before its first
+        // conversion (pairs 2, 3 after the barrier before slot 1, the next
+        // step's pairs 0, 1 after the one before slot 5).
+        uint4 rA[2][4], rB[2][4]; // FP8 fragments of two pairs
+        v8bf cA[2][4], cB[2][4];  // bf16 operands of two sub-steps
+        float sfA[4], sfB[4];     // scale factors of the pair being converted
+        auto read_pair = [&](int64_t h, int qq, uint4(&xa)[4], uint4(&xb)[4]) {
+            const uint8_t *la = lds_a(h), *lb = lds_b(h);
+            const int c = 2 * qq + hk;
 #pragma unroll
-                for (int sub = 0; sub < 2; sub++) {
-                    v8bf av[4], bv[4];
-#pragma unroll
-                    for (int t = 0; t < 4; t++) {
-                        av[t] = sub == 0 ? cvt8_bf16(fa[t][qq].x, fa[t][qq].y, sa_f[t])
-                                         : cvt8_bf16(fa[t][qq].z, fa[t][qq].w, sa_f[t]);
-                        bv[t] = sub == 0 ? cvt8_bf16(fb[t][qq].x, fb[t][qq].y, sb_f[t])
-                                         : cvt8_bf16(fb[t][qq].z, fb[t][qq].w, sb_f[t]);
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; i++)
-#pragma unroll
-                        for (int j = 0; j < 4; j++)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
-                    __builtin_amdgcn_sched_barrier(0); // keep each sub-step's converts next to its MFMAs
-                }
+            for (int t = 0; t < 4; t++) {
+                xa[t] = *reinterpret_cast<const uint4 *>(la + qoff[c] + t * 2048);
+                xb[t] = *reinterpret_cast<const uint4 *>(lb + qoff[c] + t * 2048);
             }
-        }
-    };
+        };
+        auto factors = [&](int q) {
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                if (A32 || q == 0)
+                    sfA[t] = scale_f32(A32 ? (ca[t] >> (8 * q)) & 0xFFu : (ca[0] >> (8 * t)) & 0xFFu);
+                if (B32 || q == 0)
+                    sfB[t] = scale_f32(B32 ? (cb[t] >> (8 * q)) & 0xFFu
+                                           : (BG == BG_BLOCK ? cb[0] : (cb[0] >> (8 * t)) & 0xFFu));
+            }
+        };
+        // half part (0/1) of the conversions of sub-step parity sub: A tiles
+        // (part 0) or B tiles (part 1)
+        auto convert = [&](int sub, int part, const uint4(&xa)[4], const uint4(&xb)[4], v8bf(&oa)[4], v8bf(&ob)[4]) {
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                if (part == 0)
+                    oa[t] = sub == 0 ? cvt8_bf16(xa[t].x, xa[t].y, sfA[t]) : cvt8_bf16(xa[t].z, xa[t].w, sfA[t]);
+                else
+                    ob[t] = sub == 0 ? cvt8_bf16(xb[t].x, xb[t].y, sfB[t]) : cvt8_bf16(xb[t].z, xb[t].w, sfB[t]);
+            }
+        };
+        // row tiles 2*part, 2*part+1: 8 MFMAs
+        auto mfmas = [&](int part, const v8bf(&xa)[4], const v8bf(&xb)[4]) {
+#pragma unroll
+            for (int i = 2 * part; i < 2 * part + 2; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
+        };
+        // one MFMA, then two VALU instructions, eight times
+        auto interleave = [&]() {
+#pragma unroll
+            for (int k = 0; k < 8; k++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+            }
+        };
+        // Half of a slot: 8 MFMAs on operand buffer MB, half of the next
+        // conversion (CONV), one copy instruction (DMA) issued after them.
+#define FGB_HALFSLOT(MB, PART, CONV, DMA)                                                                              \
+    do {                                                                                                               \
+        mfmas(PART, cA[MB], cB[MB]);                                                                                   \
+        CONV;                                                                                                          \
+        interleave();                                                                                                  \
+        __builtin_amdgcn_sched_barrier(0);                                                                             \
+        DMA;                                                                                                           \
+        __builtin_amdgcn_sched_barrier(0);                                                                             \
+    } while (0)
+#define FGB_SLOT(MB, SUB, RX, OB, D0, D1)                                                                              \
+    do {                                                                                                               \
+        FGB_HALFSLOT(MB, 0, convert(SUB, 0, rA[RX], rB[RX], cA[OB], cB[OB]), D0);                                      \
+        FGB_HALFSLOT(MB, 1, convert(SUB, 1, rA[RX], rB[RX], cA[OB], cB[OB]), D1);                                      \
+    } while (0)
 
-    // ---- main loop ---------------------------------------------------------------
-    // Iteration j: wait for stage j's copy and sync; start the copy of step
-    // j+1 into the other stage (free: every wave finished reading it before
-    // this barrier); read half 0 of step j; multiply half 1 of step j-1
-    // (already in registers); read half 1 of step j; multiply half 0 of step j.
-    // The matrix units start right after each barrier, LDS reads overlap the
-    // MFMAs of the other half, and each copy has a full step to land.
-    uint4 f0a[4][2], f0b[4][2], f1a[4][2], f1b[4][2];
-    uint32_t ca_cur[NA], cb_cur[NB], ca_prev[NA], cb_prev[NB], ra[4], rb[4];
-    load_scales(0, ra, rb);
-    issue_copy(0, 0);
-    for (int64_t ks = 0; ks < nk; ks++) {
-        const int cur = (int)(ks & 1);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        pack(ra, rb, ca_cur, cb_cur);
-        if (ks + 1 < nk) {
-            issue_copy(cur ^ 1, ks + 1);
-            load_scales(ks + 1, ra, rb);
+        // prologue: pairs 0 and 1 of step 0 read, sub-step 0 converted
+        read_pair(0, 0, rA[0], rB[0]);
+        read_pair(0, 1, rA[1], rB[1]);
+        factors(0);
+        convert(0, 0, rA[0], rB[0], cA[0], cB[0]);
+        convert(0, 1, rA[0], rB[0], cA[0], cB[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        for (int64_t ks = 0; ks < nk; ks++) {
+            const int64_t h0 = 2 * ks;
+            // slot 0: sub-step 0; convert sub-step 1 (pair 0)
+            FGB_SLOT(0, 1, 0, 1, dma_tile(h0 + 3, 6), dma_tile(h0 + 3, 7));
+            // slot 1: half-step h0+1 landed; read pair 2; convert sub-step 2 (pair 1)
+            FGB_WAIT_SYNC(18);
+            dma_scales(ks + 2);
+            read_pair(h0 + 1, 0, rA[0], rB[0]);
+            factors(1);
+            FGB_SLOT(1, 0, 1, 0, dma_tile(h0 + 4, 0), dma_tile(h0 + 4, 1));
+            // slot 2: convert sub-step 3 (pair 1)
+            FGB_SLOT(0, 1, 1, 1, dma_tile(h0 + 4, 2), dma_tile(h0 + 4, 3));
+            // slot 3: read pair 3; convert sub-step 4 (pair 2)
+            read_pair(h0 + 1, 1, rA[1], rB[1]);
+            factors(2);
+            FGB_SLOT(1, 0, 0, 0, dma_tile(h0 + 4, 4), dma_tile(h0 + 4, 5));
+            // slot 4: convert sub-step 5 (pair 2)
+            FGB_SLOT(0, 1, 0, 1, dma_tile(h0 + 4, 6), dma_tile(h0 + 4, 7));
+            // slot 5: half-step h0+2 landed; next step's scales and pair 0;
+            // convert sub-step 6 (pair 3)
+            FGB_WAIT_SYNC(18);
+            read_scales(ks + 1, can, cbn);
+            read_pair(h0 + 2, 0, rA[0], rB[0]);
+            factors(3);
+            FGB_SLOT(1, 0, 1, 0, dma_tile(h0 + 5, 0), dma_tile(h0 + 5, 1));
+            // slot 6: convert sub-step 7 (pair 3)
+            FGB_SLOT(0, 1, 1, 1, dma_tile(h0 + 5, 2), dma_tile(h0 + 5, 3));
+            // slot 7: read the next step's pair 1; convert its sub-step 0.
+            // After the last step the reads and conversion touch only LDS and
+            // registers and are discarded.
+            read_pair(h0 + 2, 1, rA[1], rB[1]);
+#pragma unroll
+            for (int t = 0; t < NA; t++)
+                ca[t] = can[t];
+#pragma unroll
+            for (int t = 0; t < NB; t++)
+                cb[t] = cbn[t];
+            factors(0);
+            FGB_SLOT(1, 0, 0, 0, dma_tile(h0 + 5, 4), dma_tile(h0 + 5, 5));
         }
-        read_half(cur, 0, f0a, f0b);
-        __builtin_amdgcn_sched_barrier(0);
-        if (ks > 0)
-            compute_half(1, f1a, f1b, ca_prev, cb_prev);
-        __builtin_amdgcn_sched_barrier(0);
-        read_half(cur, 1, f1a, f1b);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_half(0, f0a, f0b, ca_cur, cb_cur);
-#pragma unroll
-        for (int t = 0; t < NA; t++)
-            ca_prev[t] = ca_cur[t];
-#pragma unroll
-        for (int t = 0; t < NB; t++)
-            cb_prev[t] = cb_cur[t];
+#undef FGB_SLOT
+#undef FGB_HALFSLOT
     }
-    compute_half(1, f1a, f1b, ca_prev, cb_prev);
+#undef FGB_WAIT_SYNC
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); // trailing copies land before LDS is reused
 
     // ---- epilogue --------------------------------------------------------------
     // 32x32 accumulator layout: lane l, register r -> row (r/4)*8 + (l/32)*4 + r%4,
