@@ -34,9 +34,10 @@
 // during half-step h and have three half-steps to land, and a barrier comes
 // once per half-step.  The scale bytes travel the same way (one dword per
 // tile row or column, in two K-step tables).  LDS rows are 64 bytes with
-// the 16-byte chunk index XOR-swizzled by (row >> 2) & 3, so the operand
-// reads of 16 consecutive rows hit distinct banks and each copy instruction
-// has per-lane offsets that do not depend on which 16 rows it moves.  Tiles
+// the 16-byte chunk index XOR-swizzled by a function of row % 16, so the
+// operand reads of 8 or 16 consecutive rows hit distinct banks and each copy
+// instruction has per-lane offsets that do not depend on which 16 rows it
+// moves.  Tiles
 // are mapped to XCDs in contiguous ranges, in bands of 4 m-tiles, so
 // neighbouring tiles share an XCD's L2.
 //
@@ -87,6 +88,13 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t nb)
     return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
+
+// LDS chunk swizzle of a 64-byte tile row: chunk c of row r sits at position
+// c ^ swz(r & 15).  Bit 0 = r bit 2, bit 1 = r bit 1 ^ r bit 3: for 16
+// consecutive rows the pairs (r % 4, position) are all distinct, and so are
+// the pairs (r % 2, position) within each 8 consecutive rows, so 16-byte
+// reads of one chunk over 8 or 16 consecutive rows touch every bank once.
+__device__ __forceinline__ int swz(int r) { return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1); }
 
 // 8 E4M3 codes (two words) -> one 8-element bf16 operand, each value times 2^e (sc = 2^e).
 __device__ __forceinline__ v8bf cvt8_bf16(uint32_t w0, uint32_t w1, float sc)
@@ -166,8 +174,7 @@ gemm_fp8_kernel(GemmArgs p)
     // ---- LDS layout ----------------------------------------------------------
     // Ring of 4 half-step buffers (K = 64 each): buffer b holds the A tile
     // (256 rows x 64 bytes) at b*32K and the B tile at b*32K + 16K.  Row r's
-    // 16-byte chunk c sits at r*64 + 16*(c ^ ((r >> 2) & 3)): the reads of 16
-    // consecutive rows at one chunk then cover all 64 banks once.  Scale
+    // 16-byte chunk c sits at r*64 + 16*(c ^ swz(r & 15)).  Scale
     // tables (one dword per tile row of A and per tile column of B, the scale
     // byte zero-extended, or the 4 bytes of the step's 32-element blocks) for
     // two K steps follow the ring.
@@ -183,7 +190,7 @@ gemm_fp8_kernel(GemmArgs p)
     // ---- copy plan ---------------------------------------------------------
     // Instruction g (0..3) of wave w copies tile rows w*64 + g*16 .. +15: lane
     // l lands at LDS (w*64 + g*16)*64 + 16*l, i.e. row +l/4, position l%4,
-    // which holds chunk (l%4) ^ ((l/16) % 4) of that row.  Rows past the end
+    // which holds chunk (l%4) ^ swz(l/4) of that row.  Rows past the end
     // re-read the last valid row (those outputs are never stored).
     const uint8_t *a_base = p.a + m0 * p.lda;
     const uint8_t *b_base = B + n0 * p.ldb;
@@ -191,7 +198,7 @@ gemm_fp8_kernel(GemmArgs p)
 #pragma unroll
     for (int g = 0; g < 4; g++) {
         const int r = wave * 64 + g * 16 + (lane >> 2);
-        const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
+        const int chunk = (lane & 3) ^ swz(lane >> 2);
         const int64_t ar = m0 + r < m_end ? r : m_end - 1 - m0;
         const int64_t br = n0 + r < N ? r : N - 1 - n0;
         a_off[g] = (uint32_t)(ar * p.lda + chunk * 16);
@@ -251,34 +258,34 @@ gemm_fp8_kernel(GemmArgs p)
     const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
     const uint8_t *a_base_u = uniform(a_base), *b_base_u = uniform(b_base);
     const uint8_t *sa_base_u = uniform(sa_base), *sb_base_u = uniform(sb_base);
-    const int64_t nh = 2 * nk; // half-steps
+    const int nk32 = (int)nk, nh = 2 * nk32; // K steps, half-steps (K < 2^24)
     // Copy instruction i (0..7: A g=0..3, then B g=0..3) of half-step h
     // (clamped to the last one: copies past the end refill a free buffer
     // with data nothing reads).
-    auto dma_tile = [&](int64_t h, int i) {
-        const int64_t hc = h < nh ? h : nh - 1;
+    auto dma_tile = [&](int h, int i) {
+        const int hc = h < nh ? h : nh - 1;
         const uint32_t dst = lds_base + (uint32_t)(hc & 3) * BUF_BYTES + (i >= 4 ? HALF_BYTES : 0) +
                              (wave_u * 64 + (i & 3) * 16) * 64;
         if (i < 4)
-            dma16(a_base_u + hc * 64, a_off[i & 3], dst);
+            dma16(a_base_u + (uint32_t)hc * 64u, a_off[i & 3], dst);
         else
-            dma16(b_base_u + hc * 64, b_off[i & 3], dst);
+            dma16(b_base_u + (uint32_t)hc * 64u, b_off[i & 3], dst);
     };
     // The two scale copies of K step ks (clamped likewise).
-    auto dma_scales = [&](int64_t ks) {
-        const int64_t kc = ks < nk ? ks : nk - 1;
+    auto dma_scales = [&](int ks) {
+        const int kc = ks < nk32 ? ks : nk32 - 1;
         const uint32_t dst = lds_base + RING_BYTES + (uint32_t)(kc & 1) * SC_SLOT + wave_u * 256;
         if constexpr (A32)
-            dma4(sa_base_u + kc * 4, sa_off, dst);
+            dma4(sa_base_u + (uint32_t)kc * 4u, sa_off, dst);
         else
-            dma1(sa_base_u + kc, sa_off, dst);
+            dma1(sa_base_u + (uint32_t)kc, sa_off, dst);
         if constexpr (B32)
-            dma4(sb_base_u + kc * 4, sb_off, dst + 1024);
+            dma4(sb_base_u + (uint32_t)kc * 4u, sb_off, dst + 1024);
         else
-            dma1(sb_base_u + kc, sb_off, dst + 1024);
+            dma1(sb_base_u + (uint32_t)kc, sb_off, dst + 1024);
     };
     // All copies of half-step h (the prologue's batches).
-    auto dma_half = [&](int64_t h, int first, int last) {
+    auto dma_half = [&](int h, int first, int last) {
         if (first == 0 && (h & 1) == 0)
             dma_scales(h >> 1);
         for (int i = first; i <= last; i++)
@@ -296,15 +303,18 @@ gemm_fp8_kernel(GemmArgs p)
     // packed for 1x128 into one word with byte t = tile t; likewise B, whose
     // 128x128 form is one byte (the wave's 128 columns lie in one block).
     constexpr int NA = A32 ? 4 : 1, NB = B32 ? 4 : 1;
-    auto read_scales = [&](int64_t ks, uint32_t(&wa)[NA], uint32_t(&wb)[NB]) {
+    // read_scales issues the LDS reads (raw dwords); pack_scales combines them
+    // and is placed a few slots later so the reads have landed by then.
+    auto read_scales = [&](int ks, uint32_t(&va)[4], uint32_t(&vb)[4]) {
         const uint32_t *ta = reinterpret_cast<const uint32_t *>(smem + RING_BYTES + (ks & 1) * SC_SLOT);
         const uint32_t *tb = ta + 256;
-        uint32_t va[4], vb[4];
 #pragma unroll
         for (int t = 0; t < 4; t++) {
             va[t] = ta[wm * 128 + t * 32 + l32];
             vb[t] = BG == BG_BLOCK ? (t == 0 ? tb[wn * 128] : 0u) : tb[wn * 128 + t * 32 + l32];
         }
+    };
+    auto pack_scales = [&](const uint32_t(&va)[4], const uint32_t(&vb)[4], uint32_t(&wa)[NA], uint32_t(&wb)[NB]) {
         if constexpr (A32) {
 #pragma unroll
             for (int t = 0; t < 4; t++)
@@ -325,14 +335,14 @@ gemm_fp8_kernel(GemmArgs p)
 
     // ---- fragment addressing ---------------------------------------------------
     // The wave's row t*32 + l32 of an operand tile (offset wm*128 or wn*128
-    // rows); chunk c of it at qoff[c] + t*2048 (the swizzle depends on l32
-    // only).
+    // rows); chunk c of it at qoff[c] + t*2048 (the swizzle depends on
+    // l32 % 16 only).
     int qoff[4];
 #pragma unroll
     for (int c = 0; c < 4; c++)
-        qoff[c] = l32 * 64 + ((c ^ ((l32 >> 2) & 3)) * 16);
-    auto lds_a = [&](int64_t h) { return smem + (h & 3) * BUF_BYTES + wm * 128 * 64; };
-    auto lds_b = [&](int64_t h) { return smem + (h & 3) * BUF_BYTES + HALF_BYTES + wn * 128 * 64; };
+        qoff[c] = l32 * 64 + ((c ^ swz(l32 & 15)) * 16);
+    auto lds_a = [&](int h) { return smem + (h & 3) * BUF_BYTES + wm * 128 * 64; };
+    auto lds_b = [&](int h) { return smem + (h & 3) * BUF_BYTES + HALF_BYTES + wn * 128 * 64; };
 
     v16f acc[4][4];
 #pragma unroll
@@ -349,8 +359,9 @@ gemm_fp8_kernel(GemmArgs p)
     dma_half(2, 0, 7);
     dma_half(3, 0, 5);
     FGB_WAIT_SYNC(24);
-    uint32_t ca[NA], cb[NB], can[NA], cbn[NB];
-    read_scales(0, ca, cb);
+    uint32_t ca[NA], cb[NB], sva[4], svb[4];
+    read_scales(0, sva, svb);
+    pack_scales(sva, svb, ca, cb);
 
     // ---- main loop ----------------------------------------------------------------
     // A K step is 8 slots; slot s of step j issues 2 copy instructions
@@ -364,7 +375,7 @@ gemm_fp8_kernel(GemmArgs p)
         // K blocks 0 and 1) are read in the first two slots after the barrier
         // that precedes it.
         uint4 f[2][2][4][2]; // [half-step parity][A/B][tile][chunk]
-        auto read_frag = [&](int64_t h, int op, uint4(&x)[4][2]) {
+        auto read_frag = [&](int h, int op, uint4(&x)[4][2]) {
             const uint8_t *base = op == 0 ? lds_a(h) : lds_b(h);
 #pragma unroll
             for (int t = 0; t < 4; t++) {
@@ -402,8 +413,8 @@ gemm_fp8_kernel(GemmArgs p)
         };
         read_frag(0, 0, f[0][0]);
         read_frag(0, 1, f[0][1]);
-        for (int64_t ks = 0; ks < nk; ks++) {
-            const int64_t h0 = 2 * ks;
+        for (int ks = 0; ks < nk32; ks++) {
+            const int h0 = 2 * ks;
             // slot 0
             dma_tile(h0 + 3, 6);
             dma_tile(h0 + 3, 7);
@@ -415,12 +426,12 @@ gemm_fp8_kernel(GemmArgs p)
             dma_tile(h0 + 4, 0);
             dma_tile(h0 + 4, 1);
             read_frag(h0 + 1, 0, f[1][0]);
+            read_frag(h0 + 1, 1, f[1][1]);
             mfma_row(0, 1, f[0][0], f[0][1]);
             __builtin_amdgcn_sched_barrier(0);
             // slot 2
             dma_tile(h0 + 4, 2);
             dma_tile(h0 + 4, 3);
-            read_frag(h0 + 1, 1, f[1][1]);
             mfma_row(0, 2, f[0][0], f[0][1]);
             __builtin_amdgcn_sched_barrier(0);
             // slot 3
@@ -435,28 +446,24 @@ gemm_fp8_kernel(GemmArgs p)
             __builtin_amdgcn_sched_barrier(0);
             // slot 5
             FGB_WAIT_SYNC(18);
-            read_scales(ks + 1, can, cbn);
+            read_scales(ks + 1, sva, svb);
             dma_tile(h0 + 5, 0);
             dma_tile(h0 + 5, 1);
             read_frag(h0 + 2, 0, f[0][0]);
+            read_frag(h0 + 2, 1, f[0][1]);
             mfma_row(1, 1, f[1][0], f[1][1]);
             __builtin_amdgcn_sched_barrier(0);
             // slot 6
             dma_tile(h0 + 5, 2);
             dma_tile(h0 + 5, 3);
-            read_frag(h0 + 2, 1, f[0][1]);
             mfma_row(1, 2, f[1][0], f[1][1]);
             __builtin_amdgcn_sched_barrier(0);
-            // slot 7
+            // slot 7: the next step's scales replace the current ones after
+            // this slot's MFMAs
             dma_tile(h0 + 5, 4);
             dma_tile(h0 + 5, 5);
             mfma_row(1, 3, f[1][0], f[1][1]);
-#pragma unroll
-            for (int t = 0; t < NA; t++)
-                ca[t] = can[t];
-#pragma unroll
-            for (int t = 0; t < NB; t++)
-                cb[t] = cbn[t];
+            pack_scales(sva, svb, ca, cb);
             __builtin_amdgcn_sched_barrier(0);
         }
     } else {
@@ -471,7 +478,7 @@ gemm_fp8_kernel(GemmArgs p)
         uint4 rA[2][4], rB[2][4]; // FP8 fragments of two pairs
         v8bf cA[2][4], cB[2][4];  // bf16 operands of two sub-steps
         float sfA[4], sfB[4];     // scale factors of the pair being converted
-        auto read_pair = [&](int64_t h, int qq, uint4(&xa)[4], uint4(&xb)[4]) {
+        auto read_pair = [&](int h, int qq, uint4(&xa)[4], uint4(&xb)[4]) {
             const uint8_t *la = lds_a(h), *lb = lds_b(h);
             const int c = 2 * qq + hk;
 #pragma unroll
@@ -541,8 +548,8 @@ gemm_fp8_kernel(GemmArgs p)
         convert(0, 0, rA[0], rB[0], cA[0], cB[0]);
         convert(0, 1, rA[0], rB[0], cA[0], cB[0]);
         __builtin_amdgcn_sched_barrier(0);
-        for (int64_t ks = 0; ks < nk; ks++) {
-            const int64_t h0 = 2 * ks;
+        for (int ks = 0; ks < nk32; ks++) {
+            const int h0 = 2 * ks;
             // slot 0: sub-step 0; convert sub-step 1 (pair 0)
             FGB_SLOT(0, 1, 0, 1, dma_tile(h0 + 3, 6), dma_tile(h0 + 3, 7));
             // slot 1: half-step h0+1 landed; read pair 2; convert sub-step 2 (pair 1)
@@ -562,7 +569,7 @@ gemm_fp8_kernel(GemmArgs p)
             // slot 5: half-step h0+2 landed; next step's scales and pair 0;
             // convert sub-step 6 (pair 3)
             FGB_WAIT_SYNC(18);
-            read_scales(ks + 1, can, cbn);
+            read_scales(ks + 1, sva, svb);
             read_pair(h0 + 2, 0, rA[0], rB[0]);
             factors(3);
             FGB_SLOT(1, 0, 1, 0, dma_tile(h0 + 5, 0), dma_tile(h0 + 5, 1));
@@ -572,12 +579,7 @@ gemm_fp8_kernel(GemmArgs p)
             // After the last step the reads and conversion touch only LDS and
             // registers and are discarded.
             read_pair(h0 + 2, 1, rA[1], rB[1]);
-#pragma unroll
-            for (int t = 0; t < NA; t++)
-                ca[t] = can[t];
-#pragma unroll
-            for (int t = 0; t < NB; t++)
-                cb[t] = cbn[t];
+            pack_scales(sva, svb, ca, cb);
             factors(0);
             FGB_SLOT(1, 0, 0, 0, dma_tile(h0 + 5, 4), dma_tile(h0 + 5, 5));
         }
