@@ -104,6 +104,28 @@ __device__ __forceinline__ uint32_t group_max_u32(uint32_t v)
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
+// Streaming loads and stores (nontemporal: the data is touched once, so it
+// should not displace cached lines) of 16, 8 and 4 bytes.
+typedef uint32_t fgb_u4v __attribute__((ext_vector_type(4)));
+typedef uint32_t fgb_u2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld_stream16(const void *p)
+{
+    const fgb_u4v v = __builtin_nontemporal_load(reinterpret_cast<const fgb_u4v *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_stream16(void *p, uint4 v)
+{
+    __builtin_nontemporal_store((fgb_u4v){v.x, v.y, v.z, v.w}, reinterpret_cast<fgb_u4v *>(p));
+}
+__device__ __forceinline__ void st_stream8(void *p, uint2 v)
+{
+    __builtin_nontemporal_store((fgb_u2v){v.x, v.y}, reinterpret_cast<fgb_u2v *>(p));
+}
+__device__ __forceinline__ void st_stream4(void *p, uint32_t v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<uint32_t *>(p));
+}
+
 } // namespace fgb
 
 #define FGB_REQUIRE(cond, code, ...)                                                              \

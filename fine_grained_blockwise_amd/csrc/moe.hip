@@ -173,7 +173,7 @@ __global__ __launch_bounds__(256) void pp_copy_kernel(const uint8_t *__restrict_
 #pragma unroll
             for (int u = 0; u < 8; u++) {
                 int64_t c = c0 + u * 64 + lane;
-                v[u] = c < H16 ? *reinterpret_cast<const uint4 *>(src + c * 16) : make_uint4(0, 0, 0, 0);
+                v[u] = c < H16 ? ld_stream16(src + c * 16) : make_uint4(0, 0, 0, 0);
             }
             for (int k = 0; k < topk; k++) {
                 int32_t r = __shfl(my_row, k);
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256) void pp_copy_kernel(const uint8_t *__restrict_
                 for (int u = 0; u < 8; u++) {
                     int64_t c = c0 + u * 64 + lane;
                     if (c < H16)
-                        *reinterpret_cast<uint4 *>(dst + c * 16) = v[u];
+                        st_stream16(dst + c * 16, v[u]);
                 }
             }
         }
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void pp_copy_kernel(const uint8_t *__restrict_
             return;
         uint8_t *dst = out_q + r * H;
         for (int64_t c = lane; c < H16; c += 64)
-            *reinterpret_cast<uint4 *>(dst + c * 16) = make_uint4(0, 0, 0, 0);
+            st_stream16(dst + c * 16, make_uint4(0, 0, 0, 0));
         for (int64_t c = lane; c < H128; c += 64)
             out_s[r * H128 + c] = 127;
     }
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const uint16_t *__restri
                     for (int u = 0; u < 2; u++) {
                         int64_t c = c0 + u * 64 + lane;
                         v[kk][u] = (rr[kk] >= 0 && c < H8)
-                                       ? *reinterpret_cast<const uint4 *>(y + (int64_t)rr[kk] * H + c * 8)
+                                       ? ld_stream16(y + (int64_t)rr[kk] * H + c * 8)
                                        : make_uint4(0, 0, 0, 0);
                     }
                 }
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const uint16_t *__restri
                     o.y = bf16_rne(acc[u][2]) | (bf16_rne(acc[u][3]) << 16);
                     o.z = bf16_rne(acc[u][4]) | (bf16_rne(acc[u][5]) << 16);
                     o.w = bf16_rne(acc[u][6]) | (bf16_rne(acc[u][7]) << 16);
-                    *reinterpret_cast<uint4 *>(out + t * H + c * 8) = o;
+                    st_stream16(out + t * H + c * 8, o);
                 }
             }
         }
@@ -326,6 +326,7 @@ __device__ __forceinline__ float silu_mul(float g, float u)
 
 // One wave per row; lane owns 8 gate and the matching 8 up values (16-byte
 // loads); 16 lanes form one 128-element output group.
+constexpr int SW_U = 4; // 16-byte chunks of gate and of up in flight per lane
 __global__ __launch_bounds__(256) void swiglu_quant_kernel(const uint8_t *__restrict__ h, int64_t M,
                                                            int64_t F, int64_t ldh_bytes,
                                                            const int32_t *__restrict__ offs, int G,
@@ -339,16 +340,16 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(const uint8_t *__rest
     const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
     for (int64_t r = wave; r < rows && r < M; r += nwaves) {
         const uint8_t *hr = h + r * ldh_bytes;
-        for (int64_t c0 = 0; c0 < F8; c0 += 64 * 2) {
-            uint4 gv[2], uv[2];
+        for (int64_t c0 = 0; c0 < F8; c0 += 64 * SW_U) {
+            uint4 gv[SW_U], uv[SW_U];
 #pragma unroll
-            for (int u = 0; u < 2; u++) {
+            for (int u = 0; u < SW_U; u++) {
                 int64_t c = c0 + u * 64 + lane;
-                gv[u] = c < F8 ? *reinterpret_cast<const uint4 *>(hr + c * 16) : make_uint4(0, 0, 0, 0);
-                uv[u] = c < F8 ? *reinterpret_cast<const uint4 *>(hr + F * 2 + c * 16) : make_uint4(0, 0, 0, 0);
+                gv[u] = c < F8 ? ld_stream16(hr + c * 16) : make_uint4(0, 0, 0, 0);
+                uv[u] = c < F8 ? ld_stream16(hr + F * 2 + c * 16) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
-            for (int u = 0; u < 2; u++) {
+            for (int u = 0; u < SW_U; u++) {
                 int64_t c = c0 + u * 64 + lane;
                 uint32_t gw[4] = {gv[u].x, gv[u].y, gv[u].z, gv[u].w};
                 uint32_t uw[4] = {uv[u].x, uv[u].y, uv[u].z, uv[u].w};
@@ -368,7 +369,7 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(const uint8_t *__rest
                     uint2 o;
                     o.x = cvt4_e4m3(a[0] * sc, a[1] * sc, a[2] * sc, a[3] * sc);
                     o.y = cvt4_e4m3(a[4] * sc, a[5] * sc, a[6] * sc, a[7] * sc);
-                    *reinterpret_cast<uint2 *>(q + r * F + c * 8) = o;
+                    st_stream8(q + r * F + c * 8, o);
                     if ((lane & 15) == 0)
                         s[r * (F / 128) + c / 16] = (uint8_t)(e + 127);
                 }

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void mx2_quant_kernel(const uint16_t *__restri
 #pragma unroll
     for (int i = 0; i < MX_MAXCH; i++) {
         int64_t c = (int64_t)i * 256 + t;
-        v[i] = c < nch ? *reinterpret_cast<const uint4 *>(xr + c * 8) : make_uint4(0, 0, 0, 0);
+        v[i] = c < nch ? ld_stream16(xr + c * 8) : make_uint4(0, 0, 0, 0);
         uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
         for (int k = 0; k < 4; k++)
@@ -51,6 +51,12 @@ __global__ __launch_bounds__(256) void mx2_quant_kernel(const uint16_t *__restri
     const float alpha = m != 0 ? amax / 448.0f : 1.0f;
     if (t == 0)
         s1[r * ng + g] = alpha;
+    // y = RN32(x / alpha) as RN32(RN64(x * RN64(1 / alpha))): the product is
+    // within 2^-51.9 relative of x / alpha, while a quotient of a bf16 by an
+    // fp32 lies more than 2^-49 relative from every fp32 rounding boundary
+    // (the boundary times alpha has at most 49 significant bits and cannot
+    // equal x), so both roundings land where the one correct rounding does.
+    const double rinv = 1.0 / (double)alpha;
 #pragma unroll
     for (int i = 0; i < MX_MAXCH; i++) {
         int64_t c = (int64_t)i * 256 + t;
@@ -61,8 +67,8 @@ __global__ __launch_bounds__(256) void mx2_quant_kernel(const uint16_t *__restri
         uint32_t m2 = 0;
 #pragma unroll
         for (int k = 0; k < 4; k++) {
-            y[2 * k] = bf16lo(w4[k]) / alpha;
-            y[2 * k + 1] = bf16hi(w4[k]) / alpha;
+            y[2 * k] = (float)((double)bf16lo(w4[k]) * rinv);
+            y[2 * k + 1] = (float)((double)bf16hi(w4[k]) * rinv);
             m2 = max(m2, __float_as_uint(y[2 * k]) & 0x7FFFFFFFu);
             m2 = max(m2, __float_as_uint(y[2 * k + 1]) & 0x7FFFFFFFu);
         }
@@ -73,34 +79,47 @@ __global__ __launch_bounds__(256) void mx2_quant_kernel(const uint16_t *__restri
             uint2 o;
             o.x = cvt4_e4m3(y[0] * sc, y[1] * sc, y[2] * sc, y[3] * sc);
             o.y = cvt4_e4m3(y[4] * sc, y[5] * sc, y[6] * sc, y[7] * sc);
-            *reinterpret_cast<uint2 *>(q + r * C + c0 + c * 8) = o;
+            st_stream8(q + r * C + c0 + c * 8, o);
             if ((t & 3) == 0)
                 s2[r * (C / 32) + (c0 + c * 8) / 32] = (uint8_t)(e + 127);
         }
     }
 }
 
-// Each thread: 16 codes (16 bytes) -> 16 fp32.
+// Workgroup (x, y) decodes row y (and every gridDim.y-th after it), codes
+// [4096 x, 4096 x + 4096): each thread takes 4 runs of 4 codes, 256 runs
+// apart, so every load and store instruction covers one contiguous span.
 __global__ __launch_bounds__(256) void mx2_dequant_kernel(const uint8_t *__restrict__ q,
                                                           const uint8_t *__restrict__ s2,
                                                           const float *__restrict__ s1, int64_t R,
                                                           int64_t C, int64_t g1, int64_t ng,
                                                           float *__restrict__ out)
 {
-    const int64_t nch = R * (C / 16);
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nch;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        int64_t r = i / (C / 16), c = (i % (C / 16)) * 16;
-        int e = (int)s2[r * (C / 32) + c / 32] - 127;
-        float alpha = s1[r * ng + c / g1];
-        uint4 v = *reinterpret_cast<const uint4 *>(q + r * C + c);
-        uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        float4 *dst = reinterpret_cast<float4 *>(out + r * C + c);
+    const int64_t C4 = C / 4;
+    for (int64_t r = blockIdx.y; r < R; r += gridDim.y) {
+        const uint8_t *qr = q + r * C;
+        float *orow = out + r * C;
+        uint32_t w[4];
+        float al[4];
+        int e[4];
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            float2 a = dec2_lo(w[j]), b = dec2_hi(w[j]);
-            dst[j] = make_float4(ldexpf(a.x, e) * alpha, ldexpf(a.y, e) * alpha,
-                                 ldexpf(b.x, e) * alpha, ldexpf(b.y, e) * alpha);
+        for (int u = 0; u < 4; u++) {
+            const int64_t j = (int64_t)blockIdx.x * 1024 + u * 256 + threadIdx.x; // run index
+            if (j < C4) {
+                w[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(qr + j * 4));
+                e[u] = (int)s2[r * (C / 32) + j / 8] - 127;
+                al[u] = s1[r * ng + (j * 4) / g1];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int64_t j = (int64_t)blockIdx.x * 1024 + u * 256 + threadIdx.x;
+            if (j < C4) {
+                const float2 a = dec2_lo(w[u]), b = dec2_hi(w[u]);
+                st_stream16(orow + j * 4,
+                            make_uint4(__float_as_uint(ldexpf(a.x, e[u]) * al[u]), __float_as_uint(ldexpf(a.y, e[u]) * al[u]),
+                                       __float_as_uint(ldexpf(b.x, e[u]) * al[u]), __float_as_uint(ldexpf(b.y, e[u]) * al[u])));
+            }
         }
     }
 }
@@ -138,10 +157,8 @@ extern "C" int mx2_dequant(const uint8_t *q, const uint8_t *s2, const float *s1,
     if (R == 0)
         return FGB_OK;
     int64_t ng = (C + g1 - 1) / g1;
-    int64_t nch = R * (C / 16);
-    int64_t grid = (nch + 255) / 256;
-    grid = grid < 65536 ? grid : 65536;
-    mx2_dequant_kernel<<<(unsigned)grid, 256, 0, (hipStream_t)stream>>>(q, s2, s1, R, C, g1, ng, out);
+    const dim3 grid((unsigned)((C / 4 + 1023) / 1024), (unsigned)(R < 65535 ? R : 65535));
+    mx2_dequant_kernel<<<grid, 256, 0, (hipStream_t)stream>>>(q, s2, s1, R, C, g1, ng, out);
     FGB_LAUNCHED("mx2_dequant");
     return FGB_OK;
 }

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void quant_rowwise_kernel(const uint8_t *__res
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 int64_t c = c0 + u * 64 + lane;
-                v[u] = c < cpr ? *reinterpret_cast<const uint4 *>(xr + c * 16) : make_uint4(0, 0, 0, 0);
+                v[u] = c < cpr ? ld_stream16(xr + c * 16) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int u = 0; u < U; u++) {
@@ -83,9 +83,9 @@ __global__ __launch_bounds__(256) void quant_rowwise_kernel(const uint8_t *__res
                 float sc = pow2f(-e);
                 if (c < cpr) {
                     if constexpr (BF16)
-                        *reinterpret_cast<uint2 *>(qr + c * 8) = chunk_codes_bf16(v[u], sc);
+                        st_stream8(qr + c * 8, chunk_codes_bf16(v[u], sc));
                     else
-                        *reinterpret_cast<uint32_t *>(qr + c * 4) = chunk_codes_f32(v[u], sc);
+                        st_stream4(qr + c * 4, chunk_codes_f32(v[u], sc));
                     if (lane % LPG == 0)
                         sr[c / LPG] = (uint8_t)(e + 127);
                 }
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void quant_blockwise_kernel(const uint8_t *__r
 #pragma unroll
     for (int i = 0; i < NP; i++) {
         int64_t r = rb * 128 + r0 + i * RPP;
-        v[i] = r < rows ? *reinterpret_cast<const uint4 *>(w + r * ldw_bytes + (cb * 128 + ch * EPC) * (BF16 ? 2 : 4))
+        v[i] = r < rows ? ld_stream16(w + r * ldw_bytes + (cb * 128 + ch * EPC) * (BF16 ? 2 : 4))
                         : make_uint4(0, 0, 0, 0);
         m = max(m, chunk_amax_bits<BF16>(v[i]));
     }
@@ -133,9 +133,9 @@ __global__ __launch_bounds__(256) void quant_blockwise_kernel(const uint8_t *__r
         if (r < rows) {
             uint8_t *dst = q + r * ldq + cb * 128 + ch * EPC;
             if constexpr (BF16)
-                *reinterpret_cast<uint2 *>(dst) = chunk_codes_bf16(v[i], sc);
+                st_stream8(dst, chunk_codes_bf16(v[i], sc));
             else
-                *reinterpret_cast<uint32_t *>(dst) = chunk_codes_f32(v[i], sc);
+                st_stream4(dst, chunk_codes_f32(v[i], sc));
         }
     }
     if (t == 0)

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void direct_transpose_kernel(const uint8_t *__
     uint32_t w[16][4];
 #pragma unroll
     for (int j = 0; j < 16; j++) {
-        uint4 v = *reinterpret_cast<const uint4 *>(q + (t0 + j) * C + c0);
+        uint4 v = ld_stream16(q + (t0 + j) * C + c0);
         w[j][0] = v.x;
         w[j][1] = v.y;
         w[j][2] = v.z;
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void direct_transpose_kernel(const uint8_t *__
                   o[4 * x + 1][i], o[4 * x + 2][i], o[4 * x + 3][i]);
 #pragma unroll
     for (int c = 0; c < 16; c++)
-        *reinterpret_cast<uint4 *>(qt + (c0 + c) * T + t0) = make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]);
+        st_stream16(qt + (c0 + c) * T + t0, make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]));
     if constexpr (ROWSCALE) {
         st[(cb * 128 + lane) * ntb + tb] = (uint8_t)emax;
         st[(cb * 128 + 64 + lane) * ntb + tb] = (uint8_t)emax;
