@@ -66,6 +66,11 @@ constexpr int MAIN_BYTES = NBUF * BUF_BYTES + 2 * 2 * 256 * 4; // ring + two K s
 constexpr int LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES; // 136 KB
 
 enum { MODE_EXACT = 0, MODE_FAST = 1 };
+// Waves per workgroup: exact mode runs two waves per SIMD (its conversion
+// work hides behind the other wave's MFMAs), fast mode one.
+template <int MODE> struct Waves {
+    static constexpr int NW = MODE == MODE_EXACT ? 8 : 4;
+};
 enum { AG_ROW128 = 0, AG_ROW32 = 1 };
 enum { BG_ROW128 = 0, BG_ROW32 = 1, BG_BLOCK = 2 };
 
@@ -122,12 +127,15 @@ __device__ __forceinline__ v16f mfma_scaled(v8i a, v8i b, v16f c, uint32_t sa, u
 }
 
 template <int MODE, int AG, int BG, bool OUT_BF16, bool GROUPED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+__global__ __launch_bounds__(Waves<MODE>::NW * 64) __attribute__((amdgpu_waves_per_eu(Waves<MODE>::NW / 4, Waves<MODE>::NW / 4))) void
 gemm_fp8_kernel(GemmArgs p)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    // NW waves: a 2 x NW/2 grid of 128 x WNC sub-tiles (TJ column tiles of 32)
+    constexpr int NW = Waves<MODE>::NW, WNC = 256 / (NW / 2), TJ = WNC / 32;
+    constexpr int RPW = 256 / NW, IPO = RPW / 16; // copy rows and instructions per wave and operand
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / (NW / 2), wn = wave % (NW / 2);
     const int l32 = lane & 31, hk = lane >> 5;
     const int64_t K = p.K, nk = K / BK;
     const int64_t N = p.N;
@@ -188,16 +196,16 @@ gemm_fp8_kernel(GemmArgs p)
     constexpr int SC_SLOT = 2 * 256 * 4; // A and B tables of one K step
 
     // ---- copy plan ---------------------------------------------------------
-    // Instruction g (0..3) of wave w copies tile rows w*64 + g*16 .. +15: lane
-    // l lands at LDS (w*64 + g*16)*64 + 16*l, i.e. row +l/4, position l%4,
-    // which holds chunk (l%4) ^ swz(l/4) of that row.  Rows past the end
+    // Instruction g (0..IPO-1) of wave w copies tile rows w*RPW + g*16 .. +15:
+    // lane l lands at LDS (w*RPW + g*16)*64 + 16*l, i.e. row +l/4, position
+    // l%4, which holds chunk (l%4) ^ swz(l/4) of that row.  Rows past the end
     // re-read the last valid row (those outputs are never stored).
     const uint8_t *a_base = p.a + m0 * p.lda;
     const uint8_t *b_base = B + n0 * p.ldb;
-    uint32_t a_off[4], b_off[4];
+    uint32_t a_off[IPO], b_off[IPO];
 #pragma unroll
-    for (int g = 0; g < 4; g++) {
-        const int r = wave * 64 + g * 16 + (lane >> 2);
+    for (int g = 0; g < IPO; g++) {
+        const int r = wave * RPW + g * 16 + (lane >> 2);
         const int chunk = (lane & 3) ^ swz(lane >> 2);
         const int64_t ar = m0 + r < m_end ? r : m_end - 1 - m0;
         const int64_t br = n0 + r < N ? r : N - 1 - n0;
@@ -205,14 +213,16 @@ gemm_fp8_kernel(GemmArgs p)
         b_off[g] = (uint32_t)(br * p.ldb + chunk * 16);
     }
     // Scale copy: lane l of wave w fetches the scale of tile row (A) or tile
-    // column (B) w*64 + l for K step ks into dword w*64 + l of the step's table.
+    // column (B) sw*64 + l for K step ks into dword sw*64 + l of the step's
+    // table, sw = w % 4 (with 8 waves, waves 0-3 copy the A scales and waves
+    // 4-7 the B scales; with 4 waves each wave copies both).
     constexpr bool A32 = AG == AG_ROW32, B32 = BG == BG_ROW32;
     const int64_t sa_row = A32 ? K / 32 : K / 128;
     const int64_t sb_row = B32 ? K / 32 : K / 128;
     uint32_t sa_off, sb_off;
     const uint8_t *sa_base = p.sa + m0 * sa_row, *sb_base;
     {
-        const int64_t r = wave * 64 + lane;
+        const int64_t r = (wave & 3) * 64 + lane;
         const int64_t rc = m0 + r < m_end ? r : m_end - 1 - m0;
         sa_off = (uint32_t)(rc * sa_row);
         const int64_t c = n0 + r < N ? r : N - 1 - n0;
@@ -259,33 +269,46 @@ gemm_fp8_kernel(GemmArgs p)
     const uint8_t *a_base_u = uniform(a_base), *b_base_u = uniform(b_base);
     const uint8_t *sa_base_u = uniform(sa_base), *sb_base_u = uniform(sb_base);
     const int nk32 = (int)nk, nh = 2 * nk32; // K steps, half-steps (K < 2^24)
-    // Copy instruction i (0..7: A g=0..3, then B g=0..3) of half-step h
+    // Copy instruction i (0..2*IPO-1: A g=0..IPO-1, then B) of half-step h
     // (clamped to the last one: copies past the end refill a free buffer
     // with data nothing reads).
     auto dma_tile = [&](int h, int i) {
         const int hc = h < nh ? h : nh - 1;
-        const uint32_t dst = lds_base + (uint32_t)(hc & 3) * BUF_BYTES + (i >= 4 ? HALF_BYTES : 0) +
-                             (wave_u * 64 + (i & 3) * 16) * 64;
-        if (i < 4)
-            dma16(a_base_u + (uint32_t)hc * 64u, a_off[i & 3], dst);
+        const uint32_t dst = lds_base + (uint32_t)(hc & 3) * BUF_BYTES + (i >= IPO ? HALF_BYTES : 0) +
+                             (wave_u * RPW + (i % IPO) * 16) * 64;
+        if (i < IPO)
+            dma16(a_base_u + (uint32_t)hc * 64u, a_off[i % IPO], dst);
         else
-            dma16(b_base_u + (uint32_t)hc * 64u, b_off[i & 3], dst);
+            dma16(b_base_u + (uint32_t)hc * 64u, b_off[i % IPO], dst);
     };
-    // The two scale copies of K step ks (clamped likewise).
+    // The scale copies of K step ks (clamped likewise).  Both operands use
+    // the same copy size (1x32 scales come on both sides or on neither).
     auto dma_scales = [&](int ks) {
         const int kc = ks < nk32 ? ks : nk32 - 1;
-        const uint32_t dst = lds_base + RING_BYTES + (uint32_t)(kc & 1) * SC_SLOT + wave_u * 256;
-        if constexpr (A32)
-            dma4(sa_base_u + (uint32_t)kc * 4u, sa_off, dst);
-        else
-            dma1(sa_base_u + (uint32_t)kc, sa_off, dst);
-        if constexpr (B32)
-            dma4(sb_base_u + (uint32_t)kc * 4u, sb_off, dst + 1024);
-        else
-            dma1(sb_base_u + (uint32_t)kc, sb_off, dst + 1024);
+        const uint32_t dst = lds_base + RING_BYTES + (uint32_t)(kc & 1) * SC_SLOT + (wave_u & 3) * 256;
+        const uint32_t ka = A32 ? (uint32_t)kc * 4u : (uint32_t)kc, kb = B32 ? (uint32_t)kc * 4u : (uint32_t)kc;
+        if constexpr (NW == 4) {
+            if constexpr (A32)
+                dma4(sa_base_u + ka, sa_off, dst);
+            else
+                dma1(sa_base_u + ka, sa_off, dst);
+            if constexpr (B32)
+                dma4(sb_base_u + kb, sb_off, dst + 1024);
+            else
+                dma1(sb_base_u + kb, sb_off, dst + 1024);
+        } else {
+            // one instruction per wave, no branch: waves 0-3 copy A's, 4-7 B's
+            const bool is_a = wave_u < 4;
+            const uint8_t *g = is_a ? sa_base_u + ka : sb_base_u + kb;
+            const uint32_t off = is_a ? sa_off : sb_off;
+            if constexpr (A32)
+                dma4(g, off, dst + (is_a ? 0u : 1024u));
+            else
+                dma1(g, off, dst + (is_a ? 0u : 1024u));
+        }
     };
     // All copies of half-step h (the prologue's batches).
-    auto dma_half = [&](int h, int first, int last) {
+    auto dma_half = [&](int h, int first, int last) { // instructions first..last
         if (first == 0 && (h & 1) == 0)
             dma_scales(h >> 1);
         for (int i = first; i <= last; i++)
@@ -300,9 +323,10 @@ gemm_fp8_kernel(GemmArgs p)
 
     // ---- scales of one K step, from its LDS table ---------------------------
     // A: word per tile of the wave (1x32: the 4 block bytes; 1x128: the byte),
-    // packed for 1x128 into one word with byte t = tile t; likewise B, whose
-    // 128x128 form is one byte (the wave's 128 columns lie in one block).
-    constexpr int NA = A32 ? 4 : 1, NB = B32 ? 4 : 1;
+    // packed for 1x128 into one word with byte t = tile t; likewise B (TJ
+    // tiles), whose 128x128 form is one byte (the wave's columns lie in one
+    // block).
+    constexpr int NA = A32 ? 4 : 1, NB = B32 ? TJ : 1;
     // read_scales issues the LDS reads (raw dwords); pack_scales combines them
     // and is placed a few slots later so the reads have landed by then.
     auto read_scales = [&](int ks, uint32_t(&va)[4], uint32_t(&vb)[4]) {
@@ -311,7 +335,7 @@ gemm_fp8_kernel(GemmArgs p)
 #pragma unroll
         for (int t = 0; t < 4; t++) {
             va[t] = ta[wm * 128 + t * 32 + l32];
-            vb[t] = BG == BG_BLOCK ? (t == 0 ? tb[wn * 128] : 0u) : tb[wn * 128 + t * 32 + l32];
+            vb[t] = (BG == BG_BLOCK || t >= TJ) ? (t == 0 ? tb[wn * WNC] : 0u) : tb[wn * WNC + t * 32 + l32];
         }
     };
     auto pack_scales = [&](const uint32_t(&va)[4], const uint32_t(&vb)[4], uint32_t(&wa)[NA], uint32_t(&wb)[NB]) {
@@ -324,7 +348,7 @@ gemm_fp8_kernel(GemmArgs p)
         }
         if constexpr (B32) {
 #pragma unroll
-            for (int t = 0; t < 4; t++)
+            for (int t = 0; t < TJ; t++)
                 wb[t] = vb[t];
         } else if constexpr (BG == BG_BLOCK) {
             wb[0] = vb[0];
@@ -342,23 +366,28 @@ gemm_fp8_kernel(GemmArgs p)
     for (int c = 0; c < 4; c++)
         qoff[c] = l32 * 64 + ((c ^ swz(l32 & 15)) * 16);
     auto lds_a = [&](int h) { return smem + (h & 3) * BUF_BYTES + wm * 128 * 64; };
-    auto lds_b = [&](int h) { return smem + (h & 3) * BUF_BYTES + HALF_BYTES + wn * 128 * 64; };
+    auto lds_b = [&](int h) { return smem + (h & 3) * BUF_BYTES + HALF_BYTES + wn * WNC * 64; };
 
-    v16f acc[4][4];
+    v16f acc[4][TJ];
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int j = 0; j < TJ; j++)
             acc[i][j] = (v16f){0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
     // ---- prologue ----------------------------------------------------------------
-    // Half-steps 0..2 and the first six instructions of half-step 3 in flight;
-    // wait for half-step 0 (24 instructions issued after it) and sync.
-    dma_half(0, 0, 7);
-    dma_half(1, 0, 7);
-    dma_half(2, 0, 7);
-    dma_half(3, 0, 5);
-    FGB_WAIT_SYNC(24);
+    // Half-steps 0..2 and part of half-step 3 in flight (the rest is issued in
+    // the first slots of the main loop); wait for half-step 0 and sync.
+    dma_half(0, 0, 2 * IPO - 1);
+    dma_half(1, 0, 2 * IPO - 1);
+    dma_half(2, 0, 2 * IPO - 1);
+    if constexpr (NW == 4) {
+        dma_half(3, 0, 5);
+        FGB_WAIT_SYNC(24); // 8 + 10 + 6 instructions issued after half-step 0
+    } else {
+        dma_half(3, 0, 1);
+        FGB_WAIT_SYNC(11); // 4 + 5 + 2
+    }
     uint32_t ca[NA], cb[NB], sva[4], svb[4];
     read_scales(0, sva, svb);
     pack_scales(sva, svb, ca, cb);
@@ -467,124 +496,100 @@ gemm_fp8_kernel(GemmArgs p)
             __builtin_amdgcn_sched_barrier(0);
         }
     } else {
-        // Exact mode: a slot is one 16-deep sub-step: its 16 bf16 MFMAs
-        // interleaved with the 32 conversions of the next sub-step (two per
-        // MFMA), so the conversion work runs while the matrix unit is busy.
+        // Exact mode, 8 waves (two per SIMD, each 128 x 64): a slot is one
+        // 16-deep sub-step -- the 24 conversions of its FP8 fragments (4 A
+        // tiles, 2 B tiles; the scale folded in) and its 8 bf16 MFMAs; while
+        // one wave of a SIMD converts, the other keeps the matrix unit busy.
         // Sub-step s of a step takes bytes 0-7 (s even) or 8-15 (s odd) of
         // chunk 2q' + hk of its half-step, q = s/2 the 32-wide pair, q' = q%2.
         // Pair q+1's LDS reads are issued two slots before its first
-        // conversion (pairs 2, 3 after the barrier before slot 1, the next
-        // step's pairs 0, 1 after the one before slot 5).
-        uint4 rA[2][4], rB[2][4]; // FP8 fragments of two pairs
-        v8bf cA[2][4], cB[2][4];  // bf16 operands of two sub-steps
-        float sfA[4], sfB[4];     // scale factors of the pair being converted
-        auto read_pair = [&](int h, int qq, uint4(&xa)[4], uint4(&xb)[4]) {
+        // conversion.  Each slot issues one copy instruction: half-step
+        // 2j+3's last two in slots 0-1, 2j+4's (with step j+2's scale copy)
+        // in slots 2-5, 2j+5's first two in slots 6-7.  The barriers before
+        // slots 2 and 6 wait for half-steps 2j+1 and 2j+2 (9 copy
+        // instructions issued after them in either case).
+        static_assert(NW == 8, "exact mode runs 8 waves");
+        uint4 rA[2][4], rB[2][TJ]; // FP8 fragments of two pairs
+        v8bf cA[4], cB[TJ];        // bf16 operands of the current sub-step
+        float sfA[4], sfB[TJ];     // scale factors of the pair being converted
+        auto read_pair = [&](int h, int qq, uint4(&xa)[4], uint4(&xb)[TJ]) {
             const uint8_t *la = lds_a(h), *lb = lds_b(h);
             const int c = 2 * qq + hk;
 #pragma unroll
-            for (int t = 0; t < 4; t++) {
+            for (int t = 0; t < 4; t++)
                 xa[t] = *reinterpret_cast<const uint4 *>(la + qoff[c] + t * 2048);
+#pragma unroll
+            for (int t = 0; t < TJ; t++)
                 xb[t] = *reinterpret_cast<const uint4 *>(lb + qoff[c] + t * 2048);
-            }
         };
         auto factors = [&](int q) {
 #pragma unroll
-            for (int t = 0; t < 4; t++) {
+            for (int t = 0; t < 4; t++)
                 if (A32 || q == 0)
                     sfA[t] = scale_f32(A32 ? (ca[t] >> (8 * q)) & 0xFFu : (ca[0] >> (8 * t)) & 0xFFu);
+#pragma unroll
+            for (int t = 0; t < TJ; t++)
                 if (B32 || q == 0)
                     sfB[t] = scale_f32(B32 ? (cb[t] >> (8 * q)) & 0xFFu
                                            : (BG == BG_BLOCK ? cb[0] : (cb[0] >> (8 * t)) & 0xFFu));
-            }
         };
-        // half part (0/1) of the conversions of sub-step parity sub: A tiles
-        // (part 0) or B tiles (part 1)
-        auto convert = [&](int sub, int part, const uint4(&xa)[4], const uint4(&xb)[4], v8bf(&oa)[4], v8bf(&ob)[4]) {
+        auto convert = [&](int sub, const uint4(&xa)[4], const uint4(&xb)[TJ]) {
 #pragma unroll
-            for (int t = 0; t < 4; t++) {
-                if (part == 0)
-                    oa[t] = sub == 0 ? cvt8_bf16(xa[t].x, xa[t].y, sfA[t]) : cvt8_bf16(xa[t].z, xa[t].w, sfA[t]);
-                else
-                    ob[t] = sub == 0 ? cvt8_bf16(xb[t].x, xb[t].y, sfB[t]) : cvt8_bf16(xb[t].z, xb[t].w, sfB[t]);
-            }
+            for (int t = 0; t < 4; t++)
+                cA[t] = sub == 0 ? cvt8_bf16(xa[t].x, xa[t].y, sfA[t]) : cvt8_bf16(xa[t].z, xa[t].w, sfA[t]);
+#pragma unroll
+            for (int t = 0; t < TJ; t++)
+                cB[t] = sub == 0 ? cvt8_bf16(xb[t].x, xb[t].y, sfB[t]) : cvt8_bf16(xb[t].z, xb[t].w, sfB[t]);
         };
-        // row tiles 2*part, 2*part+1: 8 MFMAs
-        auto mfmas = [&](int part, const v8bf(&xa)[4], const v8bf(&xb)[4]) {
+        auto mfmas = [&]() {
 #pragma unroll
-            for (int i = 2 * part; i < 2 * part + 2; i++)
+            for (int i = 0; i < 4; i++)
 #pragma unroll
-                for (int j = 0; j < 4; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < TJ; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cA[i], cB[j], acc[i][j], 0, 0, 0);
         };
-        // one MFMA, then two VALU instructions, eight times
-        auto interleave = [&]() {
-#pragma unroll
-            for (int k = 0; k < 8; k++) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-            }
-        };
-        // Half of a slot: 8 MFMAs on operand buffer MB, half of the next
-        // conversion (CONV), one copy instruction (DMA) issued after them.
-#define FGB_HALFSLOT(MB, PART, CONV, DMA)                                                                              \
+#define FGB_SLOT(SUB, RX, DMA)                                                                                         \
     do {                                                                                                               \
-        mfmas(PART, cA[MB], cB[MB]);                                                                                   \
-        CONV;                                                                                                          \
-        interleave();                                                                                                  \
+        convert(SUB, rA[RX], rB[RX]);                                                                                  \
+        mfmas();                                                                                                       \
         __builtin_amdgcn_sched_barrier(0);                                                                             \
         DMA;                                                                                                           \
         __builtin_amdgcn_sched_barrier(0);                                                                             \
     } while (0)
-#define FGB_SLOT(MB, SUB, RX, OB, D0, D1)                                                                              \
-    do {                                                                                                               \
-        FGB_HALFSLOT(MB, 0, convert(SUB, 0, rA[RX], rB[RX], cA[OB], cB[OB]), D0);                                      \
-        FGB_HALFSLOT(MB, 1, convert(SUB, 1, rA[RX], rB[RX], cA[OB], cB[OB]), D1);                                      \
-    } while (0)
 
-        // prologue: pairs 0 and 1 of step 0 read, sub-step 0 converted
         read_pair(0, 0, rA[0], rB[0]);
-        read_pair(0, 1, rA[1], rB[1]);
         factors(0);
-        convert(0, 0, rA[0], rB[0], cA[0], cB[0]);
-        convert(0, 1, rA[0], rB[0], cA[0], cB[0]);
-        __builtin_amdgcn_sched_barrier(0);
         for (int ks = 0; ks < nk32; ks++) {
             const int h0 = 2 * ks;
-            // slot 0: sub-step 0; convert sub-step 1 (pair 0)
-            FGB_SLOT(0, 1, 0, 1, dma_tile(h0 + 3, 6), dma_tile(h0 + 3, 7));
-            // slot 1: half-step h0+1 landed; read pair 2; convert sub-step 2 (pair 1)
-            FGB_WAIT_SYNC(18);
+            // slots 0-1: read pair 1; sub-steps 0, 1 (pair 0)
+            read_pair(h0, 1, rA[1], rB[1]);
+            FGB_SLOT(0, 0, dma_tile(h0 + 3, 2));
+            FGB_SLOT(1, 0, dma_tile(h0 + 3, 3));
+            // slots 2-3: half-step h0+1 landed; read pair 2; sub-steps 2, 3 (pair 1)
+            FGB_WAIT_SYNC(9);
             dma_scales(ks + 2);
             read_pair(h0 + 1, 0, rA[0], rB[0]);
             factors(1);
-            FGB_SLOT(1, 0, 1, 0, dma_tile(h0 + 4, 0), dma_tile(h0 + 4, 1));
-            // slot 2: convert sub-step 3 (pair 1)
-            FGB_SLOT(0, 1, 1, 1, dma_tile(h0 + 4, 2), dma_tile(h0 + 4, 3));
-            // slot 3: read pair 3; convert sub-step 4 (pair 2)
+            FGB_SLOT(0, 1, dma_tile(h0 + 4, 0));
+            FGB_SLOT(1, 1, dma_tile(h0 + 4, 1));
+            // slots 4-5: read pair 3; sub-steps 4, 5 (pair 2)
             read_pair(h0 + 1, 1, rA[1], rB[1]);
             factors(2);
-            FGB_SLOT(1, 0, 0, 0, dma_tile(h0 + 4, 4), dma_tile(h0 + 4, 5));
-            // slot 4: convert sub-step 5 (pair 2)
-            FGB_SLOT(0, 1, 0, 1, dma_tile(h0 + 4, 6), dma_tile(h0 + 4, 7));
-            // slot 5: half-step h0+2 landed; next step's scales and pair 0;
-            // convert sub-step 6 (pair 3)
-            FGB_WAIT_SYNC(18);
+            FGB_SLOT(0, 0, dma_tile(h0 + 4, 2));
+            FGB_SLOT(1, 0, dma_tile(h0 + 4, 3));
+            // slots 6-7: half-step h0+2 landed; the next step's scales and pair 0;
+            // sub-steps 6, 7 (pair 3).  After the last step these reads touch
+            // only LDS and are discarded.
+            FGB_WAIT_SYNC(9);
             read_scales(ks + 1, sva, svb);
             read_pair(h0 + 2, 0, rA[0], rB[0]);
             factors(3);
-            FGB_SLOT(1, 0, 1, 0, dma_tile(h0 + 5, 0), dma_tile(h0 + 5, 1));
-            // slot 6: convert sub-step 7 (pair 3)
-            FGB_SLOT(0, 1, 1, 1, dma_tile(h0 + 5, 2), dma_tile(h0 + 5, 3));
-            // slot 7: read the next step's pair 1; convert its sub-step 0.
-            // After the last step the reads and conversion touch only LDS and
-            // registers and are discarded.
-            read_pair(h0 + 2, 1, rA[1], rB[1]);
+            FGB_SLOT(0, 1, dma_tile(h0 + 5, 0));
+            FGB_SLOT(1, 1, dma_tile(h0 + 5, 1));
             pack_scales(sva, svb, ca, cb);
             factors(0);
-            FGB_SLOT(1, 0, 0, 0, dma_tile(h0 + 5, 4), dma_tile(h0 + 5, 5));
         }
 #undef FGB_SLOT
-#undef FGB_HALFSLOT
     }
 #undef FGB_WAIT_SYNC
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); // trailing copies land before LDS is reused
@@ -593,17 +598,17 @@ gemm_fp8_kernel(GemmArgs p)
     // 32x32 accumulator layout: lane l, register r -> row (r/4)*8 + (l/32)*4 + r%4,
     // column l%32.  The tile is staged through LDS (free after the last
     // barrier) so that global stores are 16 bytes per lane along rows: each
-    // wave writes its 128x128 block, 64 rows at a time, as [row][128 + pad]
-    // and reads it back row-contiguous.
+    // wave writes its 128 x WNC block, EPI_ROWS rows at a time, as
+    // [row][WNC + pad] and reads it back row-contiguous.
     __syncthreads();
     constexpr int ESZ = OUT_BF16 ? 2 : 4;
-    constexpr int ROWB = 128 * ESZ + 16;   // padded LDS row (bytes)
-    constexpr int EPI_ROWS = OUT_BF16 ? 128 : 64;
+    constexpr int ROWB = WNC * ESZ + 16; // padded LDS row (bytes)
+    constexpr int EPI_ROWS = NW * 128 * ROWB <= LDS_BYTES ? 128 : NW * 64 * ROWB <= LDS_BYTES ? 64 : 32;
     uint8_t *ep = smem + wave * (EPI_ROWS * ROWB);
-    float l1v[4];
+    float l1v[TJ];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        int64_t col = n0 + wn * 128 + j * 32 + l32;
+    for (int j = 0; j < TJ; j++) {
+        int64_t col = n0 + wn * WNC + j * 32 + l32;
         l1v[j] = (p.l1 && col < N) ? p.l1[col] : 1.0f;
     }
 #pragma unroll
@@ -612,7 +617,7 @@ gemm_fp8_kernel(GemmArgs p)
         for (int ii = 0; ii < EPI_ROWS / 32; ii++) {
             const int i = part * (EPI_ROWS / 32) + ii;
 #pragma unroll
-            for (int j = 0; j < 4; j++)
+            for (int j = 0; j < TJ; j++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
                     int row = ii * 32 + (r / 4) * 8 + hk * 4 + (r % 4);
@@ -629,14 +634,14 @@ gemm_fp8_kernel(GemmArgs p)
         __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0): this wave's LDS writes done
         __builtin_amdgcn_wave_barrier();
         // read back: one row segment of 16 bytes per lane
-        constexpr int LPR = 128 * ESZ / 16; // lanes per row
+        constexpr int LPR = WNC * ESZ / 16; // lanes per row
         constexpr int RPI = 64 / LPR;       // rows per instruction
         const int lr = lane / LPR, lc = lane % LPR;
 #pragma unroll
         for (int rr = 0; rr < EPI_ROWS; rr += RPI) {
             const int row_l = rr + lr;
             const int64_t row = m0 + wm * 128 + part * EPI_ROWS + row_l;
-            const int64_t col0 = n0 + wn * 128 + lc * (16 / ESZ);
+            const int64_t col0 = n0 + wn * WNC + lc * (16 / ESZ);
             uint4 v = *reinterpret_cast<const uint4 *>(ep + row_l * ROWB + lc * 16);
             if (row >= m_end || col0 >= N)
                 continue;
@@ -681,7 +686,7 @@ static int launch_one(const GemmArgs &p, int64_t grid, hipStream_t st)
             return set_error(FGB_EHIP, "gemm: hipFuncSetAttribute failed: %s", hipGetErrorString(e));
         attr_set = true;
     }
-    kern<<<(unsigned)grid, 256, LDS_BYTES, st>>>(p);
+    kern<<<(unsigned)grid, Waves<MODE>::NW * 64, LDS_BYTES, st>>>(p);
     FGB_LAUNCHED("gemm_fp8_kernel");
     return FGB_OK;
 }
