@@ -50,6 +50,7 @@ def parse():
     ap.add_argument("--gemm-mode", choices=["exact", "fast"], default="exact")
     ap.add_argument("--parts", default="linear,moe,wgrad,moss")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-study", action="store_true", help="skip the untimed transpose comparison")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB read + 1 GiB write elementwise kernel 3 times (the reference "
@@ -344,6 +345,31 @@ def main():
         num = (Wt.double() ** 2).sum()
         den = ((Wt.double() - xh.double()) ** 2).sum()
         extra["moss_snr_db"] = round(float(10 * torch.log10(num / den)), 3)
+
+    if "wg" in W and not args.no_study:
+        # Outside the step: the direct transpose against the three-pass conversion it replaces
+        # (dequantize, transpose, requantize) on the Wgrad-path tensors.
+        study = {}
+        for key, qk, sk in (("X [32768, 7168]", "xq", "xs"), ("dY [32768, 2048]", "gq", "gs")):
+            q, sc = W["wg"][qk], W["wg"][sk]
+            wsb = torch.empty(fgb.fp8_naive_transpose_workspace_size(*q.shape), dtype=torch.uint8, device=dev)
+            times = {}
+            for name, fn in (("direct", lambda: fgb.fp8_direct_transpose(q, sc)),
+                             ("three_pass", lambda: fgb.fp8_naive_transpose(q, sc, wsb))):
+                for _ in range(3):
+                    fn()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(10):
+                    fn()
+                e1.record()
+                torch.cuda.synchronize()
+                times[name] = e0.elapsed_time(e1) / 10 * 1e3
+            study[key] = {"direct_us": round(times["direct"], 1), "three_pass_us": round(times["three_pass"], 1),
+                          "speedup": round(times["three_pass"] / times["direct"], 2)}
+            del wsb
+        extra["direct_vs_three_pass_transpose"] = study
+        log(f"transpose study: {study}")
 
     log(f"timed: {ms_step:.3f} ms/step")
     cpu = None

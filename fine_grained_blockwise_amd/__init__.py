@@ -15,7 +15,8 @@ import torch
 __all__ = [
     "lib", "symbols", "FgbError",
     "fp8_quant_rowwise", "fp8_quant_blockwise", "fp8_dequant", "fgb_e4m3_encode",
-    "fp8_direct_transpose", "fp8_block_gemm", "fp8_grouped_gemm", "permute_pad",
+    "fp8_direct_transpose", "fp8_naive_transpose", "fp8_naive_transpose_workspace_size",
+    "fp8_block_gemm", "fp8_grouped_gemm", "permute_pad",
     "permute_pad_workspace_size", "unpermute_unpad", "swiglu_quant", "mx2_quant", "mx2_dequant",
     "F32", "BF16", "ROW1x128", "ROW1x32", "BLOCK128", "GEMM_EXACT", "GEMM_FAST",
 ]
@@ -31,7 +32,7 @@ SYMBOLS = [
     "fgb_last_error", "fgb_version", "fp8_quant_rowwise", "fp8_quant_blockwise", "fp8_dequant",
     "fgb_e4m3_encode", "fp8_direct_transpose", "fp8_block_gemm", "fp8_grouped_gemm",
     "permute_pad", "permute_pad_workspace_size", "unpermute_unpad", "swiglu_quant", "mx2_quant",
-    "mx2_dequant",
+    "mx2_dequant", "fp8_naive_transpose", "fp8_naive_transpose_workspace_size",
 ]
 
 
@@ -55,6 +56,8 @@ _SIG = {
     "fp8_dequant": (_i32, [_p, _p, _i32, _i64, _i64, _p, _i32, _p]),
     "fgb_e4m3_encode": (_i32, [_p, _i64, _p, _p]),
     "fp8_direct_transpose": (_i32, [_p, _p, _i32, _i64, _i64, _p, _p, _p]),
+    "fp8_naive_transpose": (_i32, [_p, _p, _i64, _i64, _p, _p, _p, _sz, _p]),
+    "fp8_naive_transpose_workspace_size": (_sz, [_i64, _i64]),
     "fp8_block_gemm": (_i32, [_p, _p, _i32, _p, _p, _i32, _p, _i64, _i64, _i64, _i64, _i64, _i64,
                               _p, _i32, _i64, _i32, _i32, _p, _sz, _p]),
     "fp8_grouped_gemm": (_i32, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, _i32, _i32, _p]),
@@ -180,6 +183,24 @@ def fp8_direct_transpose(q, s, s_gran=ROW1x128):
         st = torch.empty((Cc // 128, T // 128), dtype=torch.uint8, device=q.device)
     _call("fp8_direct_transpose", _ptr(q.contiguous()), _ptr(s.contiguous()), s_gran, T, Cc,
           _ptr(qt), _ptr(st), _stream(q))
+    return qt, st
+
+
+def fp8_naive_transpose_workspace_size(rows, cols):
+    return int(_lib.fp8_naive_transpose_workspace_size(rows, cols))
+
+
+def fp8_naive_transpose(q, s, workspace=None):
+    """Three-pass baseline (dequantize, transpose, requantize): (q [T, C], s) -> (qt [C, T], st)."""
+    _check_dev(q, s)
+    T, Cc = q.shape
+    qt = torch.empty((Cc, T), dtype=torch.uint8, device=q.device)
+    st = torch.empty((Cc, T // 128), dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(fp8_naive_transpose_workspace_size(T, Cc), dtype=torch.uint8,
+                                device=q.device)
+    _call("fp8_naive_transpose", _ptr(q.contiguous()), _ptr(s.contiguous()), T, Cc, _ptr(qt), _ptr(st),
+          _ptr(workspace), workspace.numel(), _stream(q))
     return qt, st
 
 

@@ -109,6 +109,43 @@ __global__ __launch_bounds__(256) void direct_transpose_kernel(const uint8_t *__
     }
 }
 
+// ---- three-pass baseline ------------------------------------------------------
+// The conversion the direct transpose replaces (FP8-Flow-MoE "Core method",
+// Fig. 1): dequantize to bf16, transpose, requantize 1x128.  The middle pass
+// is this 2-byte transpose: one wave per 64x64 tile; lane (rg = lane / 8,
+// cg = lane % 8) loads rows rg*8.. of columns cg*8.. (8 lanes cover one
+// 128-byte row segment), swaps 16-bit halves across row pairs with v_perm_b32,
+// and stores 8 output rows of 16 bytes (8 lanes cover one 128-byte segment).
+__global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t *__restrict__ x, int64_t R,
+                                                          int64_t C, uint16_t *__restrict__ xt,
+                                                          int64_t ntc, int64_t ntiles)
+{
+    const int lane = lane_id();
+    const int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (tile >= ntiles)
+        return;
+    const int64_t r0 = (tile / ntc) * 64 + (lane >> 3) * 8, c0 = (tile % ntc) * 64 + (lane & 7) * 8;
+    uint32_t w[8][4];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const uint4 v = ld_stream16(x + (r0 + j) * C + c0);
+        w[j][0] = v.x;
+        w[j][1] = v.y;
+        w[j][2] = v.z;
+        w[j][3] = v.w;
+    }
+    // output row c0+i, dword m = input rows r0+2m (low half), r0+2m+1 (high half)
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t o[4];
+#pragma unroll
+        for (int m = 0; m < 4; m++)
+            o[m] = __builtin_amdgcn_perm(w[2 * m + 1][i >> 1], w[2 * m][i >> 1], sel);
+        st_stream16(xt + (c0 + i) * R + r0, make_uint4(o[0], o[1], o[2], o[3]));
+    }
+}
+
 } // namespace fgb
 
 using namespace fgb;
@@ -137,4 +174,38 @@ extern "C" int fp8_direct_transpose(const uint8_t *q, const uint8_t *s, int s_gr
         direct_transpose_kernel<false><<<(int)grid, 256, 0, stm>>>(q, s, rows, cols, qt, st, nb);
     FGB_LAUNCHED("fp8_direct_transpose");
     return FGB_OK;
+}
+
+extern "C" size_t fp8_naive_transpose_workspace_size(int64_t rows, int64_t cols)
+{
+    return rows > 0 && cols > 0 ? (size_t)(4 * rows * cols) : 0;
+}
+
+extern "C" int fp8_naive_transpose(const uint8_t *q, const uint8_t *s, int64_t rows, int64_t cols,
+                                   uint8_t *qt, uint8_t *st, void *workspace, size_t ws_bytes,
+                                   void *stream)
+{
+    clear_error();
+    FGB_REQUIRE(q && s && qt && st, FGB_EINVAL, "fp8_naive_transpose: null pointer");
+    FGB_REQUIRE(rows >= 0 && cols >= 0 && rows % 128 == 0 && cols % 128 == 0, FGB_EINVAL,
+                "fp8_naive_transpose: rows and cols must be multiples of 128 (rows=%lld cols=%lld)",
+                (long long)rows, (long long)cols);
+    FGB_REQUIRE(aligned16(q) && aligned16(qt), FGB_EINVAL,
+                "fp8_naive_transpose: q and qt must be 16-byte aligned");
+    if (rows == 0 || cols == 0)
+        return FGB_OK;
+    const size_t need = fp8_naive_transpose_workspace_size(rows, cols);
+    FGB_REQUIRE(workspace && ws_bytes >= need && aligned16(workspace), FGB_EWORKSPACE,
+                "fp8_naive_transpose: workspace must be 16-byte aligned and >= %zu bytes", need);
+    uint16_t *x = (uint16_t *)workspace, *xt = x + rows * cols;
+    // pass 1: dequantize to bf16 (exact for power-of-two scales)
+    int rc = fp8_dequant(q, s, FGB_ROW1x128, rows, cols, x, FGB_BF16, stream);
+    if (rc != FGB_OK)
+        return rc;
+    // pass 2: transpose
+    const int64_t ntc = cols / 64, ntiles = (rows / 64) * ntc;
+    transpose16_kernel<<<(unsigned)((ntiles + 3) / 4), 256, 0, (hipStream_t)stream>>>(x, rows, cols, xt, ntc, ntiles);
+    FGB_LAUNCHED("fp8_naive_transpose");
+    // pass 3: requantize the rows of the transposed copy
+    return fp8_quant_rowwise(xt, FGB_BF16, cols, rows, rows, 128, qt, rows, st, rows / 128, stream);
 }

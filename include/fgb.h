@@ -128,6 +128,24 @@ int fp8_direct_transpose(const uint8_t *q, const uint8_t *s, int s_gran, int64_t
                          int64_t cols, uint8_t *qt, uint8_t *st, void *stream);
 
 /*
+ * fp8_naive_transpose -- the three-pass conversion that the direct transpose
+ * replaces ([FLOW] "Core method" and Fig. 1, the baseline it is 2-3x faster
+ * than): dequantize the row-wise codes to bf16 (exact for power-of-two
+ * scales), transpose, and requantize 1x128 along the new rows (power-of-two
+ * scales, the rule of fp8_quant_rowwise).  Provided as the measured baseline;
+ * its result can differ from fp8_direct_transpose (column scales instead of
+ * block-max scales).
+ *   q [rows=T, cols=C], s [T, C/128] -> qt [C, T], st [C, T/128]; all dense;
+ *   rows % 128 == 0, cols % 128 == 0.
+ *   workspace: >= fp8_naive_transpose_workspace_size(rows, cols) bytes
+ *   (4*rows*cols: the bf16 copy and its transpose), 16-byte aligned, owned by
+ *   the caller; FGB_EWORKSPACE if too small.  Three kernels on `stream`.
+ */
+int fp8_naive_transpose(const uint8_t *q, const uint8_t *s, int64_t rows, int64_t cols,
+                        uint8_t *qt, uint8_t *st, void *workspace, size_t ws_bytes, void *stream);
+size_t fp8_naive_transpose_workspace_size(int64_t rows, int64_t cols);
+
+/*
  * fp8_block_gemm -- blockwise-scaled FP8 GEMM, D = A * B^T ("NT": A [M,K] and
  * B [N,K] both K-contiguous, [DSV3] §5.7).  Covers a Linear's three GEMMs
  * ([DSV3] §1): Fprop A = X, B = W; Dgrad A = dY, B = W^T (block transpose);

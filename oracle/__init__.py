@@ -40,6 +40,10 @@ def lib():
         L.orc_dequant.argtypes = [p, p, i32, i64, i64, p]
         L.orc_direct_transpose.argtypes = [p, p, i64, i64, p, p]
         L.orc_block_transpose.argtypes = [p, p, i64, i64, p, p]
+        L.orc_naive_transpose.argtypes = [p, p, i64, i64, p, p]
+        L.orc_quant_rowwise_sf.argtypes = [p, i64, i64, p, p]
+        L.orc_dequant_sf.argtypes = [p, p, i64, i64, p]
+        L.orc_naive_transpose_sf.argtypes = [p, p, i64, i64, p, p]
         L.orc_block_gemm.argtypes = [p, p, i32, p, p, i32, p, i64, i64, i64, i64, i64, i64, p]
         L.orc_block_gemm_sampled.argtypes = [p, p, i32, p, p, i32, p, i64, i64, i64, i64, i64,
                                              p, p, i64, p]
@@ -176,6 +180,47 @@ def block_transpose(q, s):
     st = np.empty((cols // 128, rows // 128), np.uint8)
     lib().orc_block_transpose(_p(q), _p(s), rows, cols, _p(qt), _p(st))
     return qt, st
+
+
+def naive_transpose(q, s):
+    """orc_naive_transpose: dequantize, transpose, requantize 1x128 (power-of-two scales)."""
+    q = _c(q, np.uint8)
+    s = _c(s, np.uint8)
+    T, Cc = q.shape
+    qt = np.empty((Cc, T), np.uint8)
+    st = np.empty((Cc, T // 128), np.uint8)
+    lib().orc_naive_transpose(_p(q), _p(s), T, Cc, _p(qt), _p(st))
+    return qt, st
+
+
+def quant_rowwise_sf(x):
+    """orc_quant_rowwise_sf: 1x128 with fp32 scales sf = amax/448 (study only) -> (q, sf)."""
+    x = _c(x, np.float32)
+    rows, cols = x.shape
+    q = np.empty((rows, cols), np.uint8)
+    sf = np.empty((rows, cols // 128), np.float32)
+    lib().orc_quant_rowwise_sf(_p(x), rows, cols, _p(q), _p(sf))
+    return q, sf
+
+
+def dequant_sf(q, sf):
+    q = _c(q, np.uint8)
+    sf = _c(sf, np.float32)
+    rows, cols = q.shape
+    out = np.empty((rows, cols), np.float32)
+    lib().orc_dequant_sf(_p(q), _p(sf), rows, cols, _p(out))
+    return out
+
+
+def naive_transpose_sf(q, sf):
+    """orc_naive_transpose_sf: the three passes with sf = amax/448 scaling (study only)."""
+    q = _c(q, np.uint8)
+    sf = _c(sf, np.float32)
+    T, Cc = q.shape
+    qt = np.empty((Cc, T), np.uint8)
+    sft = np.empty((Cc, T // 128), np.float32)
+    lib().orc_naive_transpose_sf(_p(q), _p(sf), T, Cc, _p(qt), _p(sft))
+    return qt, sft
 
 
 # ---- GEMMs ---------------------------------------------------------------

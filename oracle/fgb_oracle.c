@@ -251,6 +251,80 @@ void orc_direct_transpose(const uint8_t *q, const uint8_t *s, int64_t T, int64_t
         }
 }
 
+/* ------------------------------------------------------------------------ */
+/* The three-pass conversion the direct transpose replaces ([FLOW] "Core    */
+/* method" and Fig. 1: dequantize, transpose, requantize).  Steps in that   */
+/* order: x = decode(q) * 2^e (exact), x^T, then the 1x128 rule of          */
+/* orc_quant_rowwise on the rows of x^T (power-of-two scales, floor -22).   */
+/*   q: [T, C], s: [T, C/128] -> qt: [C, T], st: [C, T/128].                */
+/* ------------------------------------------------------------------------ */
+void orc_naive_transpose(const uint8_t *q, const uint8_t *s, int64_t T, int64_t C,
+                         uint8_t *qt, uint8_t *st)
+{
+    double *xt = (double *)malloc((size_t)(T * C) * sizeof(double));
+    for (int64_t t = 0; t < T; t++)
+        for (int64_t c = 0; c < C; c++)
+            xt[c * T + t] = ldexp(orc_e4m3_decode(q[t * C + c]), (int)s[t * (C / 128) + c / 128] - 127);
+    for (int64_t c = 0; c < C; c++)
+        for (int64_t j = 0; j < T / 128; j++) {
+            double amax = 0.0;
+            for (int64_t k = 0; k < 128; k++)
+                if (fabs(xt[c * T + j * 128 + k]) > amax)
+                    amax = fabs(xt[c * T + j * 128 + k]);
+            int e = orc_scale_exp(amax, -22);
+            for (int64_t k = 0; k < 128; k++)
+                qt[c * T + j * 128 + k] = orc_e4m3_encode(ldexp(xt[c * T + j * 128 + k], -e));
+            st[c * (T / 128) + j] = (uint8_t)(e + 127);
+        }
+    free(xt);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Non-power-of-two scaling, for the double-quantization study only.        */
+/* [DSV3] §3: sf = amax / 448 is an fp32 multiplier per 1x128 tile (1 for   */
+/* an all-zero tile); a code is E4M3(RN32(x / sf)) and decodes to           */
+/* RN32(decode(code) * sf).  orc_naive_transpose_sf runs the three passes   */
+/* with this rule (dequantized values kept in fp32).                        */
+/*   x: [rows, cols] fp32; q: [rows, cols]; sf: [rows, cols/128] fp32.      */
+/* ------------------------------------------------------------------------ */
+void orc_quant_rowwise_sf(const float *x, int64_t rows, int64_t cols, uint8_t *q, float *sf)
+{
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t j = 0; j < cols / 128; j++) {
+            float amax = 0.0f;
+            for (int64_t k = 0; k < 128; k++)
+                if (fabsf(x[r * cols + j * 128 + k]) > amax)
+                    amax = fabsf(x[r * cols + j * 128 + k]);
+            float f = amax > 0.0f ? amax / 448.0f : 1.0f;
+            for (int64_t k = 0; k < 128; k++) {
+                float y = x[r * cols + j * 128 + k] / f;
+                q[r * cols + j * 128 + k] = orc_e4m3_encode((double)y);
+            }
+            sf[r * (cols / 128) + j] = f;
+        }
+}
+
+void orc_dequant_sf(const uint8_t *q, const float *sf, int64_t rows, int64_t cols, float *out)
+{
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t c = 0; c < cols; c++)
+            out[r * cols + c] = (float)orc_e4m3_decode(q[r * cols + c]) * sf[r * (cols / 128) + c / 128];
+}
+
+void orc_naive_transpose_sf(const uint8_t *q, const float *sf, int64_t T, int64_t C, uint8_t *qt,
+                            float *sft)
+{
+    float *x = (float *)malloc((size_t)(T * C) * sizeof(float));
+    float *xt = (float *)malloc((size_t)(T * C) * sizeof(float));
+    orc_dequant_sf(q, sf, T, C, x);
+    for (int64_t t = 0; t < T; t++)
+        for (int64_t c = 0; c < C; c++)
+            xt[c * T + t] = x[t * C + c];
+    orc_quant_rowwise_sf(xt, C, T, qt, sft);
+    free(x);
+    free(xt);
+}
+
 /* Weight-block transpose for Dgrad: W[rows, cols] with 128x128 block      */
 /* scales becomes W^T[cols, rows] with transposed block scales; exact.     */
 /* ([DSV3] §1: Dgrad multiplies by W, so the NT GEMM needs W^T K-major.)    */

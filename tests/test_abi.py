@@ -87,6 +87,11 @@ def test_transpose_and_moe_validation():
     f = _fake()
     assert L.fp8_direct_transpose(f, f, 0, 200, 256, f, f, None) == 1
     assert L.fp8_direct_transpose(f, f, 1, 256, 256, f, f, None) == 2
+    # three-pass baseline: shape and workspace checks
+    assert fgb.fp8_naive_transpose_workspace_size(256, 384) == 4 * 256 * 384
+    assert L.fp8_naive_transpose(f, f, 200, 256, f, f, f, 1 << 20, None) == 1
+    assert L.fp8_naive_transpose(f, f, 256, 256, f, f, f, 1000, None) == 3
+    assert L.fp8_naive_transpose(f, f, 256, 256, f, f, None, 1 << 20, None) == 3
     ws = fgb.permute_pad_workspace_size(16384, 8, 32)
     assert ws > 0
     # M_cap below the host-side bound

@@ -208,6 +208,16 @@ def test_transpose_wgrad_dy_full(fgb):
     assert np.array_equal(np_(qt), oqt)
 
 
+@pytest.mark.parametrize("T,C", [(128, 128), (256, 512), (384, 2048), (32768, 2048)])
+def test_naive_transpose(fgb, T, C):
+    say("three-pass transpose", T, C)
+    q, s = synth.wgrad_codes(T, C, seed=T + C + 1)
+    qt, st = fgb.fp8_naive_transpose(q.to(DEV), s.to(DEV))
+    oqt, ost = O.naive_transpose(q.numpy(), s.numpy())
+    assert np.array_equal(np_(st), ost)
+    assert np.array_equal(np_(qt), oqt)
+
+
 def test_transpose_block_weights(fgb):
     say("transpose: 128x128-block weight transpose")
     q = rand_codes((2048, 1024), 5)

@@ -340,6 +340,98 @@ def test_direct_transpose_invariants():
     assert np.array_equal(qtt, qt.T)
 
 
+# --------------------------------------------------------------------------
+# three-pass (naive) transpose, and the sf = amax/448 rule of the study
+# --------------------------------------------------------------------------
+def brute_rowwise_pow2(x):
+    """1x128 power-of-two quantization of a float64 array whose tile maxima are
+    fp32 numbers: closed-form exponent and brute-force encoding."""
+    rows, cols = x.shape
+    tiles = x.reshape(rows, -1, 128)
+    amax = np.abs(tiles).max(-1)
+    e = np.full(amax.shape, -22, np.int64)
+    nz = amax > 0
+    e[nz] = np.maximum(scale_exp_bits(amax[nz].astype(np.float32)), -22)
+    q = brute_encode(tiles * np.ldexp(1.0, -e)[..., None]).reshape(rows, cols)
+    return q, (e + 127).astype(np.uint8)
+
+
+def test_naive_transpose_is_dequant_transpose_requant():
+    rng = np.random.default_rng(81)
+    T, Cc = 256, 384
+    x = (rng.standard_normal((T, Cc)) * np.float32(10.0) ** rng.integers(-3, 3, (T, 1))).astype(np.float32)
+    q, s = O.quant_rowwise(x)
+    qt, st = O.naive_transpose(q, s)
+    xh = torch_decode_table()[q] * np.ldexp(1.0, np.repeat(s.astype(np.int64) - 127, 128, axis=1))
+    qe, se = brute_rowwise_pow2(np.ascontiguousarray(xh.T))
+    assert np.array_equal(qt, qe) and np.array_equal(st, se)
+
+
+def test_naive_equals_direct_when_every_column_reaches_the_block_max():
+    # every column of each 128x128 block holds a 448 and the block's rows share
+    # one scale: the column scale is the block scale, nothing is re-rounded,
+    # and both conversions give the byte transpose
+    rng = np.random.default_rng(82)
+    T, Cc = 256, 256
+    q = (rng.integers(0, 0x7F, (T, Cc)) | (rng.integers(0, 2, (T, Cc)) << 7)).astype(np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0
+    q[5, :] = 0x7E
+    q[128 + 77, :] = 0xFE
+    s = np.repeat(rng.integers(106, 140, (2, Cc // 128)), 128, axis=0).astype(np.uint8)  # e >= -21, above the floor
+    qn, sn = O.naive_transpose(q, s)
+    qd, sd = O.direct_transpose(q, s)
+    assert np.array_equal(qn, q.T) and np.array_equal(qn, qd) and np.array_equal(sn, sd)
+
+
+def test_naive_scale_never_exceeds_the_direct_block_scale():
+    # the column maximum of a dequantized block is at most the block maximum, so
+    # the three-pass scales are <= the direct transpose's block-max scales and
+    # its dequantized result is at least as close to the input, element by element
+    rng = np.random.default_rng(83)
+    x = (rng.standard_normal((256, 256)) * np.exp(rng.standard_normal((256, 1)) * 3)).astype(np.float32)
+    q, s = O.quant_rowwise(x)
+    qn, sn = O.naive_transpose(q, s)
+    qd, sd = O.direct_transpose(q, s)
+    assert np.all(sn <= sd)
+    ref = O.dequant(q, s, O.ROW1x128).T
+    en = np.abs(O.dequant(qn, sn, O.ROW1x128) - ref)
+    ed = np.abs(O.dequant(qd, sd, O.ROW1x128) - ref)
+    assert np.all(en <= ed)
+
+
+def test_quant_rowwise_sf_rule():
+    rng = np.random.default_rng(84)
+    x = (rng.standard_normal((8, 256)) * np.float32(10.0) ** rng.integers(-4, 4, (8, 1))).astype(np.float32)
+    x[2, :128] = 0.0
+    q, sf = O.quant_rowwise_sf(x)
+    tiles = x.reshape(8, 2, 128)
+    amax = np.abs(tiles).max(-1)
+    f = np.where(amax > 0, (amax / np.float32(448.0)).astype(np.float32), np.float32(1.0)).astype(np.float32)
+    assert np.array_equal(sf, f)
+    y = (tiles / f[..., None]).astype(np.float32)  # fp32 division, correctly rounded
+    assert np.array_equal(q, brute_encode(y.astype(np.float64)).reshape(8, 256))
+    big = np.abs(tiles).argmax(-1)
+    for r in range(8):
+        for j in range(2):
+            if amax[r, j] > 0:
+                assert q[r, j * 128 + big[r, j]] & 0x7F == 0x7E  # the tile maximum codes to 448
+    xd = O.dequant_sf(q, sf)
+    assert np.array_equal(xd, (torch_decode_table()[q].astype(np.float32) * np.repeat(sf, 128, axis=1)).astype(np.float32))
+
+
+def test_naive_transpose_sf_composition():
+    rng = np.random.default_rng(85)
+    x = (rng.standard_normal((256, 384)) * 3).astype(np.float32)
+    q, sf = O.quant_rowwise_sf(x)
+    qt, sft = O.naive_transpose_sf(q, sf)
+    xt = np.ascontiguousarray((torch_decode_table()[q].astype(np.float32) * np.repeat(sf, 128, axis=1)).astype(np.float32).T)
+    tiles = xt.reshape(384, 2, 128)
+    amax = np.abs(tiles).max(-1)
+    f = np.where(amax > 0, (amax / np.float32(448.0)).astype(np.float32), np.float32(1.0)).astype(np.float32)
+    assert np.array_equal(sft, f)
+    assert np.array_equal(qt, brute_encode((tiles / f[..., None]).astype(np.float32).astype(np.float64)).reshape(384, 256))
+
+
 def test_block_transpose_exact():
     rng = np.random.default_rng(22)
     q = rng.integers(0, 256, (256, 384)).astype(np.uint8)
