@@ -371,6 +371,36 @@ def main():
         extra["direct_vs_three_pass_transpose"] = study
         log(f"transpose study: {study}")
 
+    if "moe" in W and "moe" in out and not args.no_study:
+        # Outside the step: SwiGLU backward from the FP8-cached fc1 output, at the expert-MLP size.
+        E = W["moe"]
+        offs = out["moe"][1]
+        F = E["F"]
+        g = torch.Generator(device=dev)
+        g.manual_seed(args.seed + 5)
+        h = (torch.randn((E["M_cap"], 2 * F), generator=g, device=dev) * 3).to(torch.bfloat16)
+        hq, hs = fgb.fp8_quant_rowwise(h)
+        del h
+        da = torch.randn((E["M_cap"], F), generator=g, device=dev).to(torch.bfloat16)
+        dq = torch.empty_like(hq)
+        ds = torch.empty_like(hs)
+        for _ in range(3):
+            fgb.dswiglu_quant(hq, hs, da, offs, dq, ds)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fgb.dswiglu_quant(hq, hs, da, offs, dq, ds)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / 10 * 1e3
+        rows = int(((E["counts"] + 15) // 16 * 16).sum())
+        nbytes = rows * (6 * F + 4 * F // 128)
+        extra["dswiglu_quant"] = {"us": round(us, 1), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                                  "frac_of_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                  "rows": rows, "F": F}
+        del hq, hs, da, dq, ds
+        log(f"dswiglu study: {extra['dswiglu_quant']}")
+
     log(f"timed: {ms_step:.3f} ms/step")
     cpu = None
     if not args.no_cpu_baseline:

@@ -17,8 +17,8 @@ __all__ = [
     "fp8_quant_rowwise", "fp8_quant_blockwise", "fp8_dequant", "fgb_e4m3_encode",
     "fp8_direct_transpose", "fp8_naive_transpose", "fp8_naive_transpose_workspace_size",
     "fp8_block_gemm", "fp8_grouped_gemm", "permute_pad",
-    "permute_pad_workspace_size", "unpermute_unpad", "swiglu_quant", "mx2_quant", "mx2_dequant",
-    "F32", "BF16", "ROW1x128", "ROW1x32", "BLOCK128", "GEMM_EXACT", "GEMM_FAST",
+    "permute_pad_workspace_size", "unpermute_unpad", "swiglu_quant", "dswiglu_quant", "mx2_quant",
+    "mx2_dequant", "F32", "BF16", "ROW1x128", "ROW1x32", "BLOCK128", "GEMM_EXACT", "GEMM_FAST",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -32,7 +32,7 @@ SYMBOLS = [
     "fgb_last_error", "fgb_version", "fp8_quant_rowwise", "fp8_quant_blockwise", "fp8_dequant",
     "fgb_e4m3_encode", "fp8_direct_transpose", "fp8_block_gemm", "fp8_grouped_gemm",
     "permute_pad", "permute_pad_workspace_size", "unpermute_unpad", "swiglu_quant", "mx2_quant",
-    "mx2_dequant", "fp8_naive_transpose", "fp8_naive_transpose_workspace_size",
+    "mx2_dequant", "fp8_naive_transpose", "fp8_naive_transpose_workspace_size", "dswiglu_quant",
 ]
 
 
@@ -66,6 +66,7 @@ _SIG = {
     "permute_pad_workspace_size": (_sz, [_i64, _i32, _i32]),
     "unpermute_unpad": (_i32, [_p, _p, _p, _i64, _i32, _i64, _p, _p]),
     "swiglu_quant": (_i32, [_p, _i64, _i64, _i64, _p, _i32, _p, _p, _p]),
+    "dswiglu_quant": (_i32, [_p, _p, _p, _i64, _i64, _p, _i32, _p, _p, _p]),
     "mx2_quant": (_i32, [_p, _i64, _i64, _i64, _p, _p, _p, _p]),
     "mx2_dequant": (_i32, [_p, _p, _p, _i64, _i64, _i64, _p, _p]),
 }
@@ -285,6 +286,20 @@ def swiglu_quant(h, group_offsets=None, q=None, s=None):
     _call("swiglu_quant", _ptr(h), M, F, _row_ld(h), _ptr(group_offsets), G, _ptr(q), _ptr(s),
           _stream(h))
     return q, s
+
+
+def dswiglu_quant(hq, hs, da, group_offsets=None, dq=None, ds=None):
+    """SwiGLU backward from the FP8-cached input: (hq [M,2F], hs, da bf16 [M,F]) -> (dq [M,2F], ds)."""
+    _check_dev(hq, hs, da, group_offsets)
+    M, F2 = hq.shape
+    if dq is None:
+        dq = torch.empty((M, F2), dtype=torch.uint8, device=hq.device)
+    if ds is None:
+        ds = torch.empty((M, F2 // 128), dtype=torch.uint8, device=hq.device)
+    G = 0 if group_offsets is None else group_offsets.numel() - 1
+    _call("dswiglu_quant", _ptr(hq.contiguous()), _ptr(hs.contiguous()), _ptr(da.contiguous()), M, F2 // 2,
+          _ptr(group_offsets), G, _ptr(dq), _ptr(ds), _stream(hq))
+    return dq, ds
 
 
 def mx2_quant(x, g1=10240):

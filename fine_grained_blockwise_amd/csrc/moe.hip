@@ -378,6 +378,99 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(const uint8_t *__rest
     }
 }
 
+// SwiGLU backward + 1x128 quantization from the FP8-cached input.  One wave
+// per row; lane owns 8 consecutive columns of g and u (8 code bytes each, one
+// scale byte each) and of da (16 bytes of bf16); 16 lanes form one
+// 128-element group of dg and of du.  The fp32 operations follow the
+// definition in include/fgb.h one by one (no contraction).
+constexpr int DS_U = 2;
+__global__ __launch_bounds__(256) void dswiglu_quant_kernel(const uint8_t *__restrict__ hq,
+                                                            const uint8_t *__restrict__ hs,
+                                                            const uint16_t *__restrict__ da, int64_t M,
+                                                            int64_t F, const int32_t *__restrict__ offs,
+                                                            int G, uint8_t *__restrict__ dq,
+                                                            uint8_t *__restrict__ ds)
+{
+    const int lane = lane_id();
+    const int64_t rows = offs ? (int64_t)offs[G] : M;
+    const int64_t F8 = F / 8, S = F / 64; // chunks of 8 per half-row, scale bytes per row
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    for (int64_t r = wave; r < rows && r < M; r += nwaves) {
+        const uint8_t *hr = hq + r * 2 * F;
+        for (int64_t c0 = 0; c0 < F8; c0 += 64 * DS_U) {
+            uint2 gq[DS_U], uq[DS_U];
+            uint4 av[DS_U];
+            int eg[DS_U], eu[DS_U];
+#pragma unroll
+            for (int u = 0; u < DS_U; u++) {
+                const int64_t c = c0 + u * 64 + lane;
+                if (c < F8) {
+                    gq[u] = *reinterpret_cast<const uint2 *>(hr + c * 8);
+                    uq[u] = *reinterpret_cast<const uint2 *>(hr + F + c * 8);
+                    av[u] = ld_stream16(da + r * F + c * 8);
+                    eg[u] = (int)hs[r * S + c / 16] - 127;
+                    eu[u] = (int)hs[r * S + F / 128 + c / 16] - 127;
+                } else {
+                    gq[u] = make_uint2(0, 0);
+                    uq[u] = make_uint2(0, 0);
+                    av[u] = make_uint4(0, 0, 0, 0);
+                    eg[u] = eu[u] = 0;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < DS_U; u++) {
+                const int64_t c = c0 + u * 64 + lane;
+                const float fg = pow2f(eg[u]), fu = pow2f(eu[u]);
+                const uint32_t gw[2] = {gq[u].x, gq[u].y}, uw[2] = {uq[u].x, uq[u].y};
+                const uint32_t aw[4] = {av[u].x, av[u].y, av[u].z, av[u].w};
+                float g[8], uu[8], a[8], dg[8], du[8];
+#pragma unroll
+                for (int k = 0; k < 2; k++) {
+                    const float2 g0 = dec2_lo(gw[k]), g1 = dec2_hi(gw[k]);
+                    const float2 u0 = dec2_lo(uw[k]), u1 = dec2_hi(uw[k]);
+                    g[4 * k + 0] = g0.x * fg; g[4 * k + 1] = g0.y * fg; g[4 * k + 2] = g1.x * fg; g[4 * k + 3] = g1.y * fg;
+                    uu[4 * k + 0] = u0.x * fu; uu[4 * k + 1] = u0.y * fu; uu[4 * k + 2] = u1.x * fu; uu[4 * k + 3] = u1.y * fu;
+                }
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    a[2 * k] = bf16lo(aw[k]);
+                    a[2 * k + 1] = bf16hi(aw[k]);
+                }
+                uint32_t mg = 0, mu = 0;
+#pragma unroll
+                for (int k = 0; k < 8; k++) {
+                    const float e = fgb_expf(-g[k]);
+                    const float d = 1.0f + e;
+                    const float sg = 1.0f / d;
+                    const float silu = g[k] / d;
+                    du[k] = a[k] * silu;
+                    const float dsilu = sg * (1.0f + g[k] * (1.0f - sg));
+                    dg[k] = (a[k] * uu[k]) * dsilu;
+                    mg = max(mg, __float_as_uint(dg[k]) & 0x7FFFFFFFu);
+                    mu = max(mu, __float_as_uint(du[k]) & 0x7FFFFFFFu);
+                }
+                mg = group_max_u32<16>(mg);
+                mu = group_max_u32<16>(mu);
+                const int sgx = scale_exp_from_bits(mg, -22), sux = scale_exp_from_bits(mu, -22);
+                const float scg = pow2f(-sgx), scu = pow2f(-sux);
+                if (c < F8) {
+                    st_stream8(dq + r * 2 * F + c * 8,
+                               make_uint2(cvt4_e4m3(dg[0] * scg, dg[1] * scg, dg[2] * scg, dg[3] * scg),
+                                          cvt4_e4m3(dg[4] * scg, dg[5] * scg, dg[6] * scg, dg[7] * scg)));
+                    st_stream8(dq + r * 2 * F + F + c * 8,
+                               make_uint2(cvt4_e4m3(du[0] * scu, du[1] * scu, du[2] * scu, du[3] * scu),
+                                          cvt4_e4m3(du[4] * scu, du[5] * scu, du[6] * scu, du[7] * scu)));
+                    if ((lane & 15) == 0) {
+                        ds[r * S + c / 16] = (uint8_t)(sgx + 127);
+                        ds[r * S + F / 128 + c / 16] = (uint8_t)(sux + 127);
+                    }
+                }
+            }
+        }
+    }
+}
+
 } // namespace fgb
 
 using namespace fgb;
@@ -472,5 +565,24 @@ extern "C" int swiglu_quant(const void *h, int64_t M, int64_t F, int64_t ldh,
     swiglu_quant_kernel<<<(unsigned)grid, 256, 0, (hipStream_t)stream>>>((const uint8_t *)h, M, F, ldh * 2,
                                                                          group_offsets, G, q, s);
     FGB_LAUNCHED("swiglu_quant");
+    return FGB_OK;
+}
+
+extern "C" int dswiglu_quant(const uint8_t *hq, const uint8_t *hs, const void *da, int64_t M, int64_t F,
+                             const int32_t *group_offsets, int G, uint8_t *dq, uint8_t *ds, void *stream)
+{
+    clear_error();
+    FGB_REQUIRE(hq && hs && da && dq && ds, FGB_EINVAL, "dswiglu_quant: null pointer");
+    FGB_REQUIRE(M >= 0 && F > 0 && F % 128 == 0, FGB_EINVAL, "dswiglu_quant: F must be a positive multiple of 128");
+    FGB_REQUIRE(!group_offsets || G >= 1, FGB_EINVAL, "dswiglu_quant: G must be >= 1 with group_offsets");
+    FGB_REQUIRE(aligned16(da) && ((uintptr_t)hq & 7) == 0 && ((uintptr_t)dq & 7) == 0, FGB_EINVAL,
+                "dswiglu_quant: da must be 16-byte and hq, dq 8-byte aligned");
+    if (M == 0)
+        return FGB_OK;
+    int64_t grid = (M + 3) / 4;
+    grid = grid < 16384 ? grid : 16384;
+    dswiglu_quant_kernel<<<(unsigned)grid, 256, 0, (hipStream_t)stream>>>(hq, hs, (const uint16_t *)da, M, F,
+                                                                          group_offsets, G, dq, ds);
+    FGB_LAUNCHED("dswiglu_quant");
     return FGB_OK;
 }

@@ -253,6 +253,25 @@ int swiglu_quant(const void *h, int64_t M, int64_t F, int64_t ldh, const int32_t
                  int G, uint8_t *q, uint8_t *s, void *stream);
 
 /*
+ * dswiglu_quant -- SwiGLU backward from the FP8-cached input, emitting FP8
+ * ([DSV3] §3, low-precision activations: the MoE SwiGLU input is cached in
+ * FP8 and the activation recomputed in the backward pass; [FLOW] "Core
+ * method": activation boundaries emit FP8).  With g, u the dequantized cached
+ * input and da the gradient of a = silu(g) * u, each operation one fp32
+ * rounding in this order:
+ *   e = exp(-g) (the library exponential of swiglu_quant), d = 1 + e,
+ *   sg = 1 / d, silu = g / d, du = da * silu,
+ *   dsilu = sg * (1 + g * (1 - sg)), dg = (da * u) * dsilu;
+ * then 1x128 quantization (the rule of fp8_quant_rowwise) of the row [dg | du].
+ *   hq [M, 2F] codes (gate first) with hs [M, 2F/128] 1x128 scales; da bf16
+ *   [M, F]; dq [M, 2F], ds [M, 2F/128]; all dense; F % 128 == 0.
+ *   group_offsets (device, may be NULL) as in swiglu_quant: rows >= offsets[G]
+ *   are not written.  da 16-byte, hq and dq 8-byte aligned.
+ */
+int dswiglu_quant(const uint8_t *hq, const uint8_t *hs, const void *da, int64_t M, int64_t F,
+                  const int32_t *group_offsets, int G, uint8_t *dq, uint8_t *ds, void *stream);
+
+/*
  * mx2_quant -- MOSS two-level microscaling ([MOSS] §3 two-level
  * microscaling, Fig. 2): level 1 is an FP32 factor alpha1 per g1 contiguous
  * elements of a row (last group partial), alpha1 = fp32(amax / 448), or 1

@@ -57,6 +57,7 @@ def lib():
         L.orc_expf.argtypes = [C.c_float]
         L.orc_expf_bulk.argtypes = [p, i64, p]
         L.orc_swiglu_quant.argtypes = [p, i64, i64, i64, p, i32, p, p]
+        L.orc_dswiglu_quant.argtypes = [p, p, p, i64, i64, p, i32, p, p]
         L.orc_mx2_quant.argtypes = [p, i64, i64, i64, p, p, p]
         L.orc_mx2_dequant.argtypes = [p, p, p, i64, i64, i64, p]
         L.orc_snr_db.restype = C.c_double
@@ -348,6 +349,26 @@ def swiglu_quant(h, off=None):
 
 
 # ---- MOSS two-level ------------------------------------------------------
+def dswiglu_quant(hq, hs, da, off=None):
+    """orc_dswiglu_quant: FP8-cached SwiGLU input (hq [M,2F], hs [M,2F/128]) and bf16 bits
+    da [M,F] -> 1x128 codes and scales of [dg | du] (dq [M,2F], ds [M,2F/128])."""
+    hq = _c(hq, np.uint8)
+    hs = _c(hs, np.uint8)
+    da = _c(da, np.uint16)
+    M, F2 = hq.shape
+    F = F2 // 2
+    dq = np.zeros((M, F2), np.uint8)
+    ds = np.zeros((M, F2 // 128), np.uint8)
+    offp = None
+    G = 0
+    if off is not None:
+        off = _c(off, np.int32)
+        offp = _p(off)
+        G = len(off) - 1
+    lib().orc_dswiglu_quant(_p(hq), _p(hs), _p(da), M, F, offp, G, _p(dq), _p(ds))
+    return dq, ds
+
+
 def mx2_quant(x, g1=10240):
     """orc_mx2_quant: x bf16 bits [R, C] -> (q, s2 [R, C/32], s1 [R, ceil(C/g1)])."""
     x = _c(x, np.uint16)

@@ -627,6 +627,48 @@ void orc_swiglu_quant(const uint16_t *h, int64_t M, int64_t F, int64_t ldh, cons
 }
 
 /* ------------------------------------------------------------------------ */
+/* Fused SwiGLU backward + 1x128 quantization.  [DSV3] §3 (low-precision    */
+/* activations): the MoE SwiGLU input is cached in FP8 and the activation   */
+/* is recomputed in the backward pass; [FLOW] "Core method": the activation */
+/* boundary emits FP8.  With g, u the dequantized cached input (exact in    */
+/* fp32) and da the gradient of a = silu(g) * u, in this order, each        */
+/* operation one fp32 rounding:                                             */
+/*   e = exp(-g), d = 1 + e, sg = 1 / d, silu = g / d, du = da * silu,      */
+/*   dsilu = sg * (1 + g * (1 - sg)), dg = (da * u) * dsilu                 */
+/* (dsilu is the derivative of g * sigmoid(g)); then 1x128 quantization of  */
+/* the row [dg | du].                                                       */
+/*   hq: [M, 2F] codes with hs [M, 2F/128] (1x128 scales); da: bf16 [M, F]; */
+/*   dq: [M, 2F], ds: [M, 2F/128].  Rows r >= off[G] (when off given) are   */
+/*   skipped.                                                               */
+/* ------------------------------------------------------------------------ */
+void orc_dswiglu_quant(const uint8_t *hq, const uint8_t *hs, const uint16_t *da, int64_t M,
+                       int64_t F, const int32_t *off, int G, uint8_t *dq, uint8_t *ds)
+{
+    int64_t rows = off ? off[G] : M;
+    float *dh = malloc((size_t)(2 * F) * sizeof(float));
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t j = 0; j < F; j++) {
+            float g = (float)ldexp(orc_e4m3_decode(hq[r * 2 * F + j]), (int)hs[r * (2 * F / 128) + j / 128] - 127);
+            float u = (float)ldexp(orc_e4m3_decode(hq[r * 2 * F + F + j]),
+                                   (int)hs[r * (2 * F / 128) + (F + j) / 128] - 127);
+            float a = (float)bf16_value(da[r * F + j]);
+            float e = orc_expf(-g);
+            float d = 1.0f + e;
+            float sg = 1.0f / d;
+            float silu = g / d;
+            float du = a * silu;
+            float dsilu = sg * (1.0f + g * (1.0f - sg));
+            float dg = (a * u) * dsilu;
+            dh[j] = dg;
+            dh[F + j] = du;
+        }
+        orc_quant_rowwise(dh, ORC_F32, 1, 2 * F, 2 * F, 128, -22, dq + r * 2 * F, 2 * F,
+                          ds + r * (2 * F / 128), 2 * F / 128);
+    }
+    free(dh);
+}
+
+/* ------------------------------------------------------------------------ */
 /* MOSS two-level microscaling ([MOSS] §3 "two-level microscaling" and Fig. */
 /* 2): level 1 is an FP32 factor alpha1 = max|X| / 448 over a group of about */
 /* 10K elements; level 2 is an E8M0 power-of-two scale per 32 elements of   */

@@ -100,6 +100,9 @@ def test_transpose_and_moe_validation():
     assert L.permute_pad(f, f, f, 100, 8, 32, 7168, 16, f, f, f, f, 800 + 15 * 32, f, 4, None) == 3
     assert L.unpermute_unpad(f, f, None, 10, 8, 7, f, None) == 1
     assert L.swiglu_quant(f, 10, 100, 200, None, 0, f, f, None) == 1
+    assert L.dswiglu_quant(f, f, f, 10, 100, None, 0, f, f, None) == 1
+    assert L.dswiglu_quant(f, f, _fake(0x1008), 10, 128, None, 0, f, f, None) == 1  # da not 16-byte aligned
+    assert L.dswiglu_quant(f, f, f, 10, 128, f, 0, f, f, None) == 1  # offsets without G
     assert L.mx2_quant(f, 4, 64, 48, f, f, f, None) == 2
     assert L.mx2_quant(f, 4, 48, 64, f, f, f, None) == 1
 

@@ -491,6 +491,22 @@ def test_swiglu_quant(fgb):
         assert np.array_equal(np_(q), oq)
 
 
+@pytest.mark.parametrize("M,F,use_off", [(37, 256, True), (4096, 2048, False)])
+def test_dswiglu_quant(fgb, M, F, use_off):
+    say("dswiglu_quant", M, F, use_off)
+    g = torch.Generator().manual_seed(M + F)
+    h = (torch.randn((M, 2 * F), generator=g) * 3).to(torch.bfloat16)
+    hq, hs = O.quant_rowwise(bits(h), 128)
+    da = (torch.randn((M, F), generator=g) * 0.1).to(torch.bfloat16)
+    off = np.array([0, 16, 24, 32], np.int32) if use_off else None
+    dq, ds = fgb.dswiglu_quant(torch.from_numpy(hq).to(DEV), torch.from_numpy(hs).to(DEV), da.to(DEV),
+                               None if off is None else torch.from_numpy(off).to(DEV))
+    oq, os_ = O.dswiglu_quant(hq, hs, bits(da), off)
+    rows = M if off is None else int(off[-1])
+    assert np.array_equal(np_(ds)[:rows], os_[:rows])
+    assert np.array_equal(np_(dq)[:rows], oq[:rows])
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_grouped_gemm_small(fgb, mode):
     say("grouped gemm small, one empty expert, ragged segments", mode)

@@ -707,6 +707,75 @@ def test_swiglu_quant_composition():
     assert np.array_equal(q2[:32], q[:32]) and np.all(q2[32:] == 0)
 
 
+def _dswiglu_inputs(seed, M, F):
+    rng = np.random.default_rng(seed)
+    h = (rng.standard_normal((M, 2 * F)) * 3).astype(np.float32)
+    hq, hs = O.quant_rowwise(h, 128)
+    da = torch.from_numpy(rng.standard_normal((M, F)).astype(np.float32)).to(torch.bfloat16)
+    return hq, hs, da
+
+
+def test_dswiglu_formula_is_the_derivative():
+    """sg * (1 + g * (1 - sg)) with sg = 1/(1+e^-g) is d/dg [g * sigmoid(g)]:
+    central differences in fp64 over a wide range of g."""
+    g = np.linspace(-30, 30, 2001)
+    silu = lambda x: x / (1.0 + np.exp(-x))
+    h = 1e-5
+    fd = (silu(g + h) - silu(g - h)) / (2 * h)
+    sg = 1.0 / (1.0 + np.exp(-g))
+    assert np.max(np.abs(sg * (1 + g * (1 - sg)) - fd)) < 1e-8
+
+
+def test_dswiglu_quant_against_fp64_gradient():
+    """Dequantized [dg | du] is within the E4M3 rounding bound of the fp64
+    gradient of a = silu(g) * u at the dequantized cached input."""
+    M, F = 24, 384
+    hq, hs, da = _dswiglu_inputs(61, M, F)
+    dab = da.view(torch.int16).numpy().view(np.uint16)
+    dq, ds = O.dswiglu_quant(hq, hs, dab)
+    h = O.dequant(hq, hs, O.ROW1x128)
+    g, u = h[:, :F], h[:, F:]
+    a = da.double().numpy()
+    sg = 1.0 / (1.0 + np.exp(-g))
+    exact = np.concatenate([a * u * sg * (1 + g * (1 - sg)), a * g * sg], axis=1)
+    got = O.dequant(dq, ds, O.ROW1x128)
+    step = np.ldexp(1.0, np.repeat(ds.astype(np.int64) - 127, 128, axis=1))  # 2^e per element
+    bound = np.maximum(np.abs(exact) * 2.0 ** -4, step * 2.0 ** -10) * (1 + 1e-5) + np.abs(exact) * 1e-6
+    assert np.all(np.abs(got - exact) <= bound)
+
+
+def test_dswiglu_quant_composition_and_special_cases():
+    """Layout and operation order: the gradient formed with numpy fp32 operations
+    around the oracle's exp, dg then du, quantized 1x128."""
+    M, F = 16, 256
+    hq, hs, da = _dswiglu_inputs(62, M, F)
+    dab = da.view(torch.int16).numpy().view(np.uint16)
+    h = O.dequant(hq, hs, O.ROW1x128).astype(np.float32)
+    g, u = h[:, :F], h[:, F:]
+    a = da.float().numpy()
+    one = np.float32(1.0)
+    d = (one + O.expf(-g)).astype(np.float32)
+    sg = (one / d).astype(np.float32)
+    silu = (g / d).astype(np.float32)
+    du = (a * silu).astype(np.float32)
+    dsilu = (sg * (one + (g * (one - sg)).astype(np.float32)).astype(np.float32)).astype(np.float32)
+    dg = ((a * u).astype(np.float32) * dsilu).astype(np.float32)
+    q_ref, s_ref = O.quant_rowwise(np.concatenate([dg, du], axis=1), 128)
+    dq, ds = O.dswiglu_quant(hq, hs, dab)
+    assert np.array_equal(dq, q_ref) and np.array_equal(ds, s_ref)
+    # g = 0: silu = 0 (du = 0) and dsilu = 1/2 exactly
+    hz = hq.copy()
+    hz[:, :F] = 0
+    dq0, ds0 = O.dswiglu_quant(hz, hs, dab)
+    assert np.all((dq0[:, F:] & 0x7F) == 0)  # +-0 (the sign of da is kept)
+    ref0, rs0 = O.quant_rowwise((a * O.dequant(hz, hs, O.ROW1x128)[:, F:].astype(np.float32) * np.float32(0.5)).astype(np.float32), 128)
+    assert np.array_equal(dq0[:, :F], ref0) and np.array_equal(ds0[:, :F // 128], rs0)
+    # rows past off[G] are not written
+    off = np.array([0, 8, 12], np.int32)
+    dq2, _ = O.dswiglu_quant(hq, hs, dab, off)
+    assert np.array_equal(dq2[:12], dq[:12]) and np.all(dq2[12:] == 0)
+
+
 # --------------------------------------------------------------------------
 # MOSS two-level
 # --------------------------------------------------------------------------
