@@ -18,7 +18,7 @@ __all__ = [
     "fp8_direct_transpose", "fp8_naive_transpose", "fp8_naive_transpose_workspace_size",
     "fp8_block_gemm", "fp8_grouped_gemm", "permute_pad",
     "permute_pad_workspace_size", "unpermute_unpad", "swiglu_quant", "dswiglu_quant", "mx2_quant",
-    "mx2_dequant", "F32", "BF16", "ROW1x128", "ROW1x32", "BLOCK128", "GEMM_EXACT", "GEMM_FAST",
+    "mx2_dequant", "unpermute_backward", "unpermute_backward_workspace_size", "F32", "BF16", "ROW1x128", "ROW1x32", "BLOCK128", "GEMM_EXACT", "GEMM_FAST",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,6 +33,7 @@ SYMBOLS = [
     "fgb_e4m3_encode", "fp8_direct_transpose", "fp8_block_gemm", "fp8_grouped_gemm",
     "permute_pad", "permute_pad_workspace_size", "unpermute_unpad", "swiglu_quant", "mx2_quant",
     "mx2_dequant", "fp8_naive_transpose", "fp8_naive_transpose_workspace_size", "dswiglu_quant",
+    "unpermute_backward", "unpermute_backward_workspace_size",
 ]
 
 
@@ -65,6 +66,8 @@ _SIG = {
                            _sz, _p]),
     "permute_pad_workspace_size": (_sz, [_i64, _i32, _i32]),
     "unpermute_unpad": (_i32, [_p, _p, _p, _i64, _i32, _i64, _p, _p]),
+    "unpermute_backward": (_i32, [_p, _p, _p, _i64, _i32, _i64, _i64, _p, _p, _sz, _p]),
+    "unpermute_backward_workspace_size": (_sz, [_i64]),
     "swiglu_quant": (_i32, [_p, _i64, _i64, _i64, _p, _i32, _p, _p, _p]),
     "dswiglu_quant": (_i32, [_p, _p, _p, _i64, _i64, _p, _i32, _p, _p, _p]),
     "mx2_quant": (_i32, [_p, _i64, _i64, _i64, _p, _p, _p, _p]),
@@ -271,6 +274,26 @@ def unpermute_unpad(y, row_map, probs=None, out=None):
     _call("unpermute_unpad", _ptr(y.contiguous()), _ptr(row_map.contiguous()),
           _ptr(None if probs is None else probs.contiguous()), T, topk, H, _ptr(out), _stream(y))
     return out
+
+
+def unpermute_backward_workspace_size(M_cap):
+    return int(_lib.unpermute_backward_workspace_size(M_cap))
+
+
+def unpermute_backward(dout, row_map, probs, M_cap, dy=None, workspace=None):
+    """Gradient of unpermute_unpad: dout bf16 [T, H] -> dy bf16 [M_cap, H] (padding rows zero)."""
+    _check_dev(dout, row_map, probs)
+    T, H = dout.shape
+    topk = row_map.shape[1]
+    if dy is None:
+        dy = torch.empty((M_cap, H), dtype=torch.bfloat16, device=dout.device)
+    if workspace is None:
+        workspace = torch.empty(max(unpermute_backward_workspace_size(M_cap), 1), dtype=torch.uint8,
+                                device=dout.device)
+    _call("unpermute_backward", _ptr(dout.contiguous()), _ptr(row_map.contiguous()),
+          _ptr(None if probs is None else probs.contiguous()), T, topk, H, M_cap, _ptr(dy), _ptr(workspace),
+          workspace.numel(), _stream(dout))
+    return dy
 
 
 def swiglu_quant(h, group_offsets=None, q=None, s=None):

@@ -471,6 +471,68 @@ __global__ __launch_bounds__(256) void dswiglu_quant_kernel(const uint8_t *__res
     }
 }
 
+// ---- backward of unpermute_unpad ------------------------------------------------
+// dy[row_map[t,k]] = bf16(w[t,k] * dout[t]); rows no slot maps to are zero.
+// Three passes: inverse map filled with -1, slot index scattered into it,
+// then one wave per destination row gathers (or zeroes) its row.
+__global__ __launch_bounds__(256) void ub_fill_kernel(int32_t *__restrict__ inv, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        inv[i] = -1;
+}
+
+__global__ __launch_bounds__(256) void ub_scatter_kernel(const int32_t *__restrict__ row_map, int64_t n,
+                                                         int64_t M_cap, int32_t *__restrict__ inv)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t r = row_map[i];
+        if (r >= 0 && r < M_cap)
+            inv[r] = (int32_t)i;
+    }
+}
+
+__global__ __launch_bounds__(256) void ub_gather_kernel(const uint16_t *__restrict__ dout,
+                                                        const int32_t *__restrict__ inv,
+                                                        const float *__restrict__ probs, int topk, int64_t H,
+                                                        int64_t M_cap, uint16_t *__restrict__ dy)
+{
+    const int lane = lane_id();
+    const int64_t H8 = H / 8;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    for (int64_t r = wave; r < M_cap; r += nwaves) {
+        const int32_t si = inv[r];
+        uint16_t *dst = dy + r * H;
+        if (si < 0) {
+            for (int64_t c = lane; c < H8; c += 64)
+                st_stream16(dst + c * 8, make_uint4(0, 0, 0, 0));
+            continue;
+        }
+        const float w = probs ? probs[si] : 1.0f;
+        const uint16_t *src = dout + (int64_t)(si / topk) * H;
+        for (int64_t c0 = 0; c0 < H8; c0 += 64 * 4) {
+            uint4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const int64_t c = c0 + u * 64 + lane;
+                v[u] = c < H8 ? *reinterpret_cast<const uint4 *>(src + c * 8) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const int64_t c = c0 + u * 64 + lane;
+                if (c < H8) {
+                    const uint32_t x4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+                    uint32_t o[4];
+#pragma unroll
+                    for (int k = 0; k < 4; k++)
+                        o[k] = bf16_rne(w * bf16lo(x4[k])) | (bf16_rne(w * bf16hi(x4[k])) << 16);
+                    st_stream16(dst + c * 8, make_uint4(o[0], o[1], o[2], o[3]));
+                }
+            }
+        }
+    }
+}
+
 } // namespace fgb
 
 using namespace fgb;
@@ -584,5 +646,41 @@ extern "C" int dswiglu_quant(const uint8_t *hq, const uint8_t *hs, const void *d
     dswiglu_quant_kernel<<<(unsigned)grid, 256, 0, (hipStream_t)stream>>>(hq, hs, (const uint16_t *)da, M, F,
                                                                           group_offsets, G, dq, ds);
     FGB_LAUNCHED("dswiglu_quant");
+    return FGB_OK;
+}
+
+extern "C" size_t unpermute_backward_workspace_size(int64_t M_cap)
+{
+    return M_cap > 0 ? (size_t)(4 * M_cap) : 0;
+}
+
+extern "C" int unpermute_backward(const void *dout, const int32_t *row_map, const float *probs, int64_t T,
+                                  int topk, int64_t H, int64_t M_cap, void *dy, void *workspace, size_t ws_bytes,
+                                  void *stream)
+{
+    clear_error();
+    FGB_REQUIRE(dout && row_map && dy, FGB_EINVAL, "unpermute_backward: null pointer");
+    FGB_REQUIRE(T >= 0 && topk >= 1 && topk <= 64 && H > 0 && H % 8 == 0 && M_cap >= 0, FGB_EINVAL,
+                "unpermute_backward: need topk in [1, 64] and H a positive multiple of 8");
+    FGB_REQUIRE(T * topk < (1ll << 31) && M_cap < (1ll << 31), FGB_EINVAL, "unpermute_backward: too many rows");
+    FGB_REQUIRE(aligned16(dout) && aligned16(dy), FGB_EINVAL, "unpermute_backward: dout and dy must be 16-byte aligned");
+    if (M_cap == 0)
+        return FGB_OK;
+    FGB_REQUIRE(workspace && ws_bytes >= unpermute_backward_workspace_size(M_cap), FGB_EWORKSPACE,
+                "unpermute_backward: workspace must hold %zu bytes", unpermute_backward_workspace_size(M_cap));
+    hipStream_t st = (hipStream_t)stream;
+    int32_t *inv = (int32_t *)workspace;
+    int64_t g1 = (M_cap + 255) / 256;
+    ub_fill_kernel<<<(unsigned)(g1 < 4096 ? g1 : 4096), 256, 0, st>>>(inv, M_cap);
+    FGB_LAUNCHED("unpermute_backward");
+    if (T > 0) {
+        int64_t g2 = (T * topk + 255) / 256;
+        ub_scatter_kernel<<<(unsigned)(g2 < 4096 ? g2 : 4096), 256, 0, st>>>(row_map, T * topk, M_cap, inv);
+        FGB_LAUNCHED("unpermute_backward");
+    }
+    int64_t g3 = (M_cap + 3) / 4;
+    ub_gather_kernel<<<(unsigned)(g3 < 16384 ? g3 : 16384), 256, 0, st>>>((const uint16_t *)dout, inv, probs, topk,
+                                                                           H, M_cap, (uint16_t *)dy);
+    FGB_LAUNCHED("unpermute_backward");
     return FGB_OK;
 }

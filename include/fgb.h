@@ -236,6 +236,21 @@ int unpermute_unpad(const void *y, const int32_t *row_map, const float *probs, i
                     int topk, int64_t H, void *out, void *stream);
 
 /*
+ * unpermute_backward -- gradient of unpermute_unpad for the MoE expert
+ * backward ([FLOW] "Core method", the fused unpermute): out[t] = sum_k
+ * w[t,k] * y[row_map[t,k]] gives dy[row_map[t,k]] = bf16(fp32(w[t,k] *
+ * dout[t])) (round to nearest even; w = 1 when probs is NULL); rows that no
+ * slot maps to (the padding) are written as zeros.
+ *   dout bf16 [T, H]; row_map, probs [T, topk] (device); dy bf16 [M_cap, H].
+ *   workspace: >= unpermute_backward_workspace_size(M_cap) bytes (an inverse
+ *   map), caller-owned, contents on entry irrelevant.  H % 8 == 0, topk <= 64;
+ *   dout and dy 16-byte aligned.  Three kernels on `stream`.
+ */
+int unpermute_backward(const void *dout, const int32_t *row_map, const float *probs, int64_t T, int topk,
+                       int64_t H, int64_t M_cap, void *dy, void *workspace, size_t ws_bytes, void *stream);
+size_t unpermute_backward_workspace_size(int64_t M_cap);
+
+/*
  * swiglu_quant -- fused SwiGLU + 1x128 quantization ([FLOW] "Core method":
  * the activation emits FP8 directly; assumption 2: the first linear's
  * output is BF16).

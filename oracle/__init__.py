@@ -53,6 +53,7 @@ def lib():
         L.orc_permute_pad.restype = C.c_int64
         L.orc_permute_pad.argtypes = [p, p, p, i64, i32, i32, i64, i32, p, p, p, p, i64]
         L.orc_unpermute_unpad.argtypes = [p, p, p, i64, i32, i64, p]
+        L.orc_unpermute_backward.argtypes = [p, p, p, i64, i32, i64, i64, p]
         L.orc_expf.restype = C.c_float
         L.orc_expf.argtypes = [C.c_float]
         L.orc_expf_bulk.argtypes = [p, i64, p]
@@ -329,6 +330,21 @@ def unpermute_unpad(y, row_map, probs=None):
     out = np.empty((T, H), np.uint16)
     lib().orc_unpermute_unpad(_p(y), _p(row_map), _p(probs), T, topk, H, _p(out))
     return out
+
+
+def unpermute_backward(dout, row_map, probs, M_cap):
+    """orc_unpermute_backward: dout bf16 bits [T,H] -> dy bf16 bits [M_cap, H]."""
+    dout = _c(dout, np.uint16)
+    row_map = _c(row_map, np.int32)
+    T, H = dout.shape
+    topk = row_map.shape[1]
+    dy = np.empty((M_cap, H), np.uint16)
+    pp = None
+    if probs is not None:
+        probs = _c(probs, np.float32)
+        pp = _p(probs)
+    lib().orc_unpermute_backward(_p(dout), _p(row_map), pp, T, topk, H, M_cap, _p(dy))
+    return dy
 
 
 def swiglu_quant(h, off=None):

@@ -552,6 +552,29 @@ void orc_unpermute_unpad(const uint16_t *y, const int32_t *row_map, const float 
 }
 
 /* ------------------------------------------------------------------------ */
+/* Backward of unpermute_unpad, for the MoE expert backward ([FLOW] "Core   */
+/* method": the fused unpermute; its gradient brings the output gradient   */
+/* back into the permuted, padded expert layout).  out[t] = sum_k w[t,k] *  */
+/* y[row_map[t,k]] gives dy[row_map[t,k]] = RN_bf16(fp32(w[t,k] * dout[t]))  */
+/* (w = 1 without probs); rows no slot maps to (the padding) are zero.      */
+/*   dout bf16 [T, H]; row_map, probs [T, topk]; dy bf16 [M_cap, H].         */
+/* ------------------------------------------------------------------------ */
+void orc_unpermute_backward(const uint16_t *dout, const int32_t *row_map, const float *probs,
+                            int64_t T, int topk, int64_t H, int64_t M_cap, uint16_t *dy)
+{
+    memset(dy, 0, (size_t)(M_cap * H) * sizeof(uint16_t));
+    for (int64_t t = 0; t < T; t++)
+        for (int k = 0; k < topk; k++) {
+            int32_t r = row_map[t * topk + k];
+            if (r < 0 || r >= M_cap)
+                continue;
+            float w = probs ? probs[t * topk + k] : 1.0f;
+            for (int64_t h = 0; h < H; h++)
+                dy[(int64_t)r * H + h] = bf16_round(w * (float)bf16_value(dout[t * H + h]));
+        }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Exponential used by SwiGLU.  The pages fix no exp; this one is the       */
 /* library's own definition so that both implementations round alike:      */
 /* Cody-Waite argument reduction x = n ln2 + r (Cody & Waite, "Software     */

@@ -99,6 +99,9 @@ def test_transpose_and_moe_validation():
     # workspace too small
     assert L.permute_pad(f, f, f, 100, 8, 32, 7168, 16, f, f, f, f, 800 + 15 * 32, f, 4, None) == 3
     assert L.unpermute_unpad(f, f, None, 10, 8, 7, f, None) == 1
+    assert fgb.unpermute_backward_workspace_size(1000) == 4000
+    assert L.unpermute_backward(f, f, None, 10, 8, 7, 200, f, f, 4096, None) == 1  # H % 8
+    assert L.unpermute_backward(f, f, None, 10, 8, 128, 200, f, f, 16, None) == 3  # workspace
     assert L.swiglu_quant(f, 10, 100, 200, None, 0, f, f, None) == 1
     assert L.dswiglu_quant(f, f, f, 10, 100, None, 0, f, f, None) == 1
     assert L.dswiglu_quant(f, f, _fake(0x1008), 10, 128, None, 0, f, f, None) == 1  # da not 16-byte aligned

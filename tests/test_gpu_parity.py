@@ -475,6 +475,24 @@ def test_unpermute_small_and_full(fgb):
         assert np.array_equal(np_(out), ref)
 
 
+@pytest.mark.parametrize("T,H,weighted", [(64, 256, True), (2048, 7168, True), (300, 512, False)])
+def test_unpermute_backward(fgb, T, H, weighted):
+    say("unpermute_backward", T, H, weighted)
+    topk, G = 8, 32
+    idx, probs = synth.routing(T=T, E=G, topk=topk, seed=T)
+    xq = torch.zeros((T, H), dtype=torch.uint8, device=DEV)
+    xs = torch.zeros((T, H // 128), dtype=torch.uint8, device=DEV)
+    M_cap = T * topk + 15 * G
+    ws = torch.empty(fgb.permute_pad_workspace_size(T, topk, G), dtype=torch.uint8, device=DEV)
+    _, _, rmap, offs = fgb.permute_pad(xq, xs, torch.from_numpy(idx).to(DEV), G, 16, M_cap, ws)
+    g = torch.Generator().manual_seed(T + H)
+    dout = torch.randn((T, H), generator=g).to(torch.bfloat16)
+    pr = torch.from_numpy(probs).to(DEV) if weighted else None
+    dy = fgb.unpermute_backward(dout.to(DEV), rmap, pr, M_cap)
+    ref = O.unpermute_backward(bits(dout), np_(rmap), probs if weighted else None, M_cap)
+    assert np.array_equal(np_(dy), ref)
+
+
 def test_swiglu_quant(fgb):
     for M, F, use_off in [(64, 256, False), (1000, 2048, True)]:
         say("swiglu_quant", M, F, use_off)

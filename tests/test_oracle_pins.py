@@ -617,6 +617,36 @@ def test_unpermute_inverts_permute():
     assert np.array_equal(O.unpermute_unpad(y, rm), xb)
 
 
+def test_unpermute_backward_is_the_adjoint():
+    """dy = unpermute_backward(dout) satisfies <unpermute_unpad(y), dout> =
+    <y, dy> for the exact linear maps (checked in fp64 with bf16-exact weights
+    and values, where no rounding occurs), copies dout exactly without probs,
+    and leaves every padding row zero."""
+    rng = np.random.default_rng(43)
+    T, topk, G, H = 96, 4, 8, 128
+    idx = np.stack([rng.permutation(G)[:topk] for _ in range(T)]).astype(np.int32)
+    _, _, rm, off, used = O.permute_pad(np.zeros((T, H), np.uint8), np.zeros((T, 1), np.uint8), idx, G, 16)
+    M_cap = T * topk + 15 * G
+    # small-integer bf16 values and power-of-two probs: every product and sum is exact
+    dout = torch.from_numpy(rng.integers(-8, 9, (T, H)).astype(np.float32)).to(torch.bfloat16)
+    db = dout.view(torch.int16).numpy().view(np.uint16)
+    probs = np.ldexp(1.0, rng.integers(-3, 1, (T, topk))).astype(np.float32)
+    dy = O.unpermute_backward(db, rm, probs, M_cap)
+    dyf = torch.from_numpy(dy.view(np.int16)).view(torch.bfloat16).double().numpy()
+    y = torch.from_numpy(rng.integers(-8, 9, (M_cap, H)).astype(np.float32)).to(torch.bfloat16)
+    out = O.unpermute_unpad(y.view(torch.int16).numpy().view(np.uint16), rm, probs)
+    outf = torch.from_numpy(out.view(np.int16)).view(torch.bfloat16).double().numpy()
+    assert np.sum(outf * dout.double().numpy()) == np.sum(y.double().numpy() * dyf)
+    # without probs: the rows are copies; padding rows (and rows past used) are zero
+    dy1 = O.unpermute_backward(db, rm, None, M_cap)
+    for t in range(T):
+        for k in range(topk):
+            assert np.array_equal(dy1[rm[t, k]], db[t])
+    mask = np.zeros(M_cap, bool)
+    mask[rm.ravel()] = True
+    assert np.all(dy1[~mask] == 0) and np.all(dy[~mask] == 0)
+
+
 def test_unpermute_weighted_fold_small_integers_and_fma():
     # small integers: every fma exact, result exact
     T, topk, H = 3, 3, 8
