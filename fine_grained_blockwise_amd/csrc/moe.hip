@@ -15,7 +15,8 @@
 //           of the same expert, in (token, slot) order -> row_map
 //   copy    one wave per token: the 16-byte chunks of the code row and the
 //           scale row are read once and written to each destination; extra
-//           waves fill the padding rows (code 0, scale byte 127).
+//           waves fill the padding rows (code 0, scale byte 105 -- what
+//           the 1x128 rule gives an all-zero tile).
 #include "fgb_internal.h"
 
 namespace fgb {
@@ -209,7 +210,7 @@ __global__ __launch_bounds__(256) void pp_copy_kernel(const uint8_t *__restrict_
         for (int64_t c = lane; c < H16; c += 64)
             st_stream16(dst + c * 16, make_uint4(0, 0, 0, 0));
         for (int64_t c = lane; c < H128; c += 64)
-            out_s[r * H128 + c] = 127;
+            out_s[r * H128 + c] = 105;
     }
 }
 

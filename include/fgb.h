@@ -205,7 +205,9 @@ int fp8_grouped_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t *b, cons
  *   xq [T, H] codes, xs [T, H/128] scales, topk_idx [T, topk] int32 (device)
  *   Rows are grouped by expert id ascending and, inside an expert, by
  *   (token, slot) ascending; each expert's segment is padded at its end to a
- *   multiple of pad_multiple rows with code 0x00 and scale byte 127.  A slot
+ *   multiple of pad_multiple rows with code 0x00 and scale byte 105 (the
+ *   scale the 1x128 rule gives an all-zero tile, so padding never raises a
+ *   block-max scale when a segment is transposed).  A slot
  *   whose id lies outside [0, G) is dropped (row_map = -1).
  *   out_q [M_cap, H], out_s [M_cap, H/128]: rows >= off[G] untouched.
  *   row_map [T, topk] int32: destination row of each slot, or -1.

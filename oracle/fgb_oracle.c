@@ -479,7 +479,9 @@ void orc_grouped_gemm_sampled(const uint8_t *a, const uint8_t *sa, const uint8_t
 /* reordering merged with 16-row alignment padding).  Rows are grouped by   */
 /* expert id ascending; inside an expert, by (token, slot) ascending; each  */
 /* expert segment is padded at its end to a multiple of pad_multiple rows   */
-/* with code 0x00 and scale byte 127.  A slot whose expert id lies outside  */
+/* with code 0x00 and scale byte 105: exactly what the 1x128 rule gives an  */
+/* all-zero tile (e = -22), so a padding row never raises the block-max     */
+/* scale of a transposed segment.  A slot whose expert id lies outside      */
 /* [0, G) is dropped (row_map = -1).                                        */
 /*   xq [T, H], xs [T, H/128], topk_idx [T, topk];                          */
 /*   out_q [M_cap, H], out_s [M_cap, H/128], row_map [T, topk], off [G+1].  */
@@ -520,7 +522,7 @@ int64_t orc_permute_pad(const uint8_t *xq, const uint8_t *xs, const int32_t *top
     for (int e = 0; e < G; e++)
         for (int64_t r = off[e] + cnt[e]; r < off[e + 1]; r++) {
             memset(out_q + r * H, 0x00, (size_t)H);
-            memset(out_s + r * H128, 127, (size_t)H128);
+            memset(out_s + r * H128, 105, (size_t)H128);
         }
     free(cnt);
     free(cur);

@@ -598,7 +598,10 @@ def test_permute_pad_invariants():
         toks = np.nonzero((idx == e).any(1))[0]
         assert np.array_equal(rm[toks][idx[toks] == e], np.arange(off[e], off[e] + counts[e]))
         pad = slice(off[e] + counts[e], off[e + 1])
-        assert np.all(out_q[pad] == 0) and np.all(out_s[pad] == 127)
+        assert np.all(out_q[pad] == 0) and np.all(out_s[pad] == 105)
+        # the padding looks exactly like a quantized all-zero row
+        zq, zs = O.quant_rowwise(np.zeros((1, H), np.float32), 128)
+        assert np.all(out_q[pad] == zq) and np.all(out_s[pad] == zs)
         assert not seen[pad].any()
     assert np.all(out_q[used:] == 0xCD)  # rows past the end untouched
 
