@@ -18,7 +18,8 @@ __all__ = [
     "fp8_direct_transpose", "fp8_naive_transpose", "fp8_naive_transpose_workspace_size",
     "fp8_block_gemm", "fp8_grouped_gemm", "permute_pad",
     "permute_pad_workspace_size", "unpermute_unpad", "swiglu_quant", "dswiglu_quant", "mx2_quant",
-    "mx2_dequant", "unpermute_backward", "unpermute_backward_workspace_size", "F32", "BF16", "ROW1x128", "ROW1x32", "BLOCK128", "GEMM_EXACT", "GEMM_FAST",
+    "mx2_dequant", "unpermute_backward", "unpermute_backward_workspace_size",
+    "fp8_block_transpose_batched", "fp8_grouped_direct_transpose", "F32", "BF16", "ROW1x128", "ROW1x32", "BLOCK128", "GEMM_EXACT", "GEMM_FAST",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,7 +34,8 @@ SYMBOLS = [
     "fgb_e4m3_encode", "fp8_direct_transpose", "fp8_block_gemm", "fp8_grouped_gemm",
     "permute_pad", "permute_pad_workspace_size", "unpermute_unpad", "swiglu_quant", "mx2_quant",
     "mx2_dequant", "fp8_naive_transpose", "fp8_naive_transpose_workspace_size", "dswiglu_quant",
-    "unpermute_backward", "unpermute_backward_workspace_size",
+    "unpermute_backward", "unpermute_backward_workspace_size", "fp8_block_transpose_batched",
+    "fp8_grouped_direct_transpose",
 ]
 
 
@@ -58,6 +60,8 @@ _SIG = {
     "fgb_e4m3_encode": (_i32, [_p, _i64, _p, _p]),
     "fp8_direct_transpose": (_i32, [_p, _p, _i32, _i64, _i64, _p, _p, _p]),
     "fp8_naive_transpose": (_i32, [_p, _p, _i64, _i64, _p, _p, _p, _sz, _p]),
+    "fp8_block_transpose_batched": (_i32, [_p, _p, _i32, _i64, _i64, _p, _p, _p]),
+    "fp8_grouped_direct_transpose": (_i32, [_p, _p, _i64, _i64, _p, _i32, _p, _p, _i64, _p, _p]),
     "fp8_naive_transpose_workspace_size": (_sz, [_i64, _i64]),
     "fp8_block_gemm": (_i32, [_p, _p, _i32, _p, _p, _i32, _p, _i64, _i64, _i64, _i64, _i64, _i64,
                               _p, _i32, _i64, _i32, _i32, _p, _sz, _p]),
@@ -188,6 +192,37 @@ def fp8_direct_transpose(q, s, s_gran=ROW1x128):
     _call("fp8_direct_transpose", _ptr(q.contiguous()), _ptr(s.contiguous()), s_gran, T, Cc,
           _ptr(qt), _ptr(st), _stream(q))
     return qt, st
+
+
+def fp8_block_transpose_batched(q, s):
+    """Per-matrix 128x128-block transposes: q [G, rows, cols] -> qt [G, cols, rows]."""
+    _check_dev(q, s)
+    G, rows, cols = q.shape
+    qt = torch.empty((G, cols, rows), dtype=torch.uint8, device=q.device)
+    st = torch.empty((G, cols // 128, rows // 128), dtype=torch.uint8, device=q.device)
+    _call("fp8_block_transpose_batched", _ptr(q.contiguous()), _ptr(s.contiguous()), G, rows, cols, _ptr(qt),
+          _ptr(st), _stream(q))
+    return qt, st
+
+
+def grouped_k_cap(M_cap, G):
+    """Host bound on the columns of the per-expert transposed copy."""
+    return (M_cap + 127 * G + 127) // 128 * 128
+
+
+def fp8_grouped_direct_transpose(q, s, group_offsets, K_cap=None):
+    """Direct transpose of expert segments: q [M_cap, C] -> (qt [C, K_cap], st, k_offsets [G+1])."""
+    _check_dev(q, s, group_offsets)
+    M_cap, Cc = q.shape
+    G = group_offsets.numel() - 1
+    if K_cap is None:
+        K_cap = grouped_k_cap(M_cap, G)
+    qt = torch.empty((Cc, K_cap), dtype=torch.uint8, device=q.device)
+    st = torch.empty((Cc, K_cap // 128), dtype=torch.uint8, device=q.device)
+    koff = torch.empty(G + 1, dtype=torch.int32, device=q.device)
+    _call("fp8_grouped_direct_transpose", _ptr(q.contiguous()), _ptr(s.contiguous()), M_cap, Cc,
+          _ptr(group_offsets), G, _ptr(qt), _ptr(st), K_cap, _ptr(koff), _stream(q))
+    return qt, st, koff
 
 
 def fp8_naive_transpose_workspace_size(rows, cols):

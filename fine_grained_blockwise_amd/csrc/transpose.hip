@@ -58,6 +58,13 @@ __global__ __launch_bounds__(256) void direct_transpose_kernel(const uint8_t *__
         return;
     const int64_t ncb = C / 128, ntb = T / 128;
     const int64_t tb = blk / ncb, cb = blk % ncb;
+    { // matrix blockIdx.y of a dense batch
+        const int64_t e = blockIdx.y;
+        q += e * T * C;
+        qt += e * T * C;
+        s += e * (ROWSCALE ? T * ncb : ntb * ncb);
+        st += e * (ROWSCALE ? C * ntb : ntb * ncb);
+    }
     const int tsub = lane & 7, csub = lane >> 3;
     const int64_t t0 = tb * 128 + tsub * 16;
     const int64_t c0 = cb * 128 + csub * 16;
@@ -107,6 +114,85 @@ __global__ __launch_bounds__(256) void direct_transpose_kernel(const uint8_t *__
         if (lane == 0)
             st[cb * ntb + tb] = s[tb * ncb + cb];
     }
+}
+
+// ---- expert segments, for the expert backward's Wgrad --------------------------
+// koff[e+1] = koff[e] + ceil(len_e / 128) * 128 (one thread; G <= 1024).
+__global__ void koff_kernel(const int32_t *__restrict__ off, int G, int32_t *__restrict__ koff)
+{
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
+        int32_t k = 0;
+        koff[0] = 0;
+        for (int e = 0; e < G; e++) {
+            k += ((off[e + 1] - off[e] + 127) / 128) * 128;
+            koff[e + 1] = k;
+        }
+    }
+}
+
+// Direct transpose of expert segments: one wave per 128x128 output block
+// (column block kb of the transposed copy, row block cb of C), as in
+// direct_transpose_kernel, except that the block's source rows are the
+// segment's rows present (the last block of a segment may be short: its
+// absent rows count as code 0 and take no part in the block maximum).
+__global__ __launch_bounds__(256) void grouped_direct_transpose_kernel(
+    const uint8_t *__restrict__ q, const uint8_t *__restrict__ s, int64_t C, const int32_t *__restrict__ off,
+    const int32_t *__restrict__ koff, int G, uint8_t *__restrict__ qt, uint8_t *__restrict__ st, int64_t Kc,
+    int64_t nslots)
+{
+    const int lane = lane_id();
+    const int64_t slot = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (slot >= nslots)
+        return;
+    const int64_t ncb = C / 128, nkb = Kc / 128;
+    const int64_t kb = slot / ncb, cb = slot % ncb;
+    int ex = -1;
+    for (int g = 0; g < G; g++)
+        if (kb * 128 >= koff[g] && kb * 128 < koff[g + 1])
+            ex = g;
+    if (ex < 0)
+        return; // past the last segment (uniform per wave)
+    const int64_t r0 = off[ex] + (kb * 128 - koff[ex]);
+    const int64_t n = min((int64_t)128, (int64_t)off[ex + 1] - r0);
+    const int tsub = lane & 7, csub = lane >> 3;
+    const int tl = tsub * 16;
+    const int64_t c0 = cb * 128 + csub * 16;
+
+    uint32_t w[16][4];
+    int e[16];
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+        const bool present = tl + j < n;
+        const uint4 v = present ? ld_stream16(q + (r0 + tl + j) * C + c0) : make_uint4(0, 0, 0, 0);
+        w[j][0] = v.x;
+        w[j][1] = v.y;
+        w[j][2] = v.z;
+        w[j][3] = v.w;
+        e[j] = present ? s[(r0 + tl + j) * ncb + cb] : 0;
+        m = max(m, (uint32_t)e[j]);
+    }
+    const int emax = (int)group_max_u32<8>(m);
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+        const int k = min(emax - e[j], 31);
+        const float f = pow2f(-k);
+#pragma unroll
+        for (int x = 0; x < 4; x++)
+            w[j][x] = shift_word(w[j][x], f);
+    }
+    uint32_t o[16][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int x = 0; x < 4; x++)
+            tr4x4(w[4 * i + 0][x], w[4 * i + 1][x], w[4 * i + 2][x], w[4 * i + 3][x], o[4 * x + 0][i],
+                  o[4 * x + 1][i], o[4 * x + 2][i], o[4 * x + 3][i]);
+#pragma unroll
+    for (int c = 0; c < 16; c++)
+        st_stream16(qt + (c0 + c) * Kc + kb * 128 + tl, make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]));
+    st[(cb * 128 + lane) * nkb + kb] = (uint8_t)emax;
+    st[(cb * 128 + 64 + lane) * nkb + kb] = (uint8_t)emax;
 }
 
 // ---- three-pass baseline ------------------------------------------------------
@@ -208,4 +294,47 @@ extern "C" int fp8_naive_transpose(const uint8_t *q, const uint8_t *s, int64_t r
     FGB_LAUNCHED("fp8_naive_transpose");
     // pass 3: requantize the rows of the transposed copy
     return fp8_quant_rowwise(xt, FGB_BF16, cols, rows, rows, 128, qt, rows, st, rows / 128, stream);
+}
+
+extern "C" int fp8_block_transpose_batched(const uint8_t *q, const uint8_t *s, int G, int64_t rows, int64_t cols,
+                                           uint8_t *qt, uint8_t *st, void *stream)
+{
+    clear_error();
+    FGB_REQUIRE(q && s && qt && st, FGB_EINVAL, "fp8_block_transpose_batched: null pointer");
+    FGB_REQUIRE(G >= 1 && G <= 65535, FGB_EINVAL, "fp8_block_transpose_batched: G must be in [1, 65535]");
+    FGB_REQUIRE(rows >= 0 && cols >= 0 && rows % 128 == 0 && cols % 128 == 0, FGB_EINVAL,
+                "fp8_block_transpose_batched: rows and cols must be multiples of 128");
+    FGB_REQUIRE(aligned16(q) && aligned16(qt), FGB_EINVAL, "fp8_block_transpose_batched: q and qt must be 16-byte aligned");
+    const int64_t nb = (rows / 128) * (cols / 128);
+    if (nb == 0)
+        return FGB_OK;
+    const dim3 grid((unsigned)((nb + 3) / 4), (unsigned)G);
+    direct_transpose_kernel<false><<<grid, 256, 0, (hipStream_t)stream>>>(q, s, rows, cols, qt, st, nb);
+    FGB_LAUNCHED("fp8_block_transpose_batched");
+    return FGB_OK;
+}
+
+extern "C" int fp8_grouped_direct_transpose(const uint8_t *q, const uint8_t *s, int64_t M_cap, int64_t cols,
+                                            const int32_t *group_offsets, int G, uint8_t *qt, uint8_t *st,
+                                            int64_t K_cap, int32_t *k_offsets, void *stream)
+{
+    clear_error();
+    FGB_REQUIRE(q && s && qt && st && group_offsets && k_offsets, FGB_EINVAL,
+                "fp8_grouped_direct_transpose: null pointer");
+    FGB_REQUIRE(G >= 1 && G <= 1024, FGB_EINVAL, "fp8_grouped_direct_transpose: G must be in [1, 1024]");
+    FGB_REQUIRE(M_cap >= 0 && cols > 0 && cols % 128 == 0 && K_cap % 128 == 0, FGB_EINVAL,
+                "fp8_grouped_direct_transpose: cols and K_cap must be multiples of 128");
+    FGB_REQUIRE(K_cap >= ((M_cap + 127 * (int64_t)G + 127) / 128) * 128, FGB_EINVAL,
+                "fp8_grouped_direct_transpose: K_cap must be >= M_cap + 127*G rounded up to 128");
+    FGB_REQUIRE(aligned16(q) && aligned16(qt), FGB_EINVAL, "fp8_grouped_direct_transpose: q and qt must be 16-byte aligned");
+    hipStream_t stm = (hipStream_t)stream;
+    koff_kernel<<<1, 64, 0, stm>>>(group_offsets, G, k_offsets);
+    FGB_LAUNCHED("fp8_grouped_direct_transpose");
+    const int64_t nslots = (K_cap / 128) * (cols / 128);
+    if (nslots == 0)
+        return FGB_OK;
+    grouped_direct_transpose_kernel<<<(unsigned)((nslots + 3) / 4), 256, 0, stm>>>(q, s, cols, group_offsets,
+                                                                                   k_offsets, G, qt, st, K_cap, nslots);
+    FGB_LAUNCHED("fp8_grouped_direct_transpose");
+    return FGB_OK;
 }

@@ -128,6 +128,36 @@ int fp8_direct_transpose(const uint8_t *q, const uint8_t *s, int s_gran, int64_t
                          int64_t cols, uint8_t *qt, uint8_t *st, void *stream);
 
 /*
+ * fp8_block_transpose_batched -- fp8_direct_transpose with s_gran =
+ * FGB_BLOCK128 applied to each of G stacked matrices (the expert weights of
+ * the MoE Dgrad: [DSV3] §1, Dgrad multiplies by W, and the grouped NT GEMM
+ * needs each W_e^T K-major).  q [G, rows, cols], s [G, rows/128, cols/128]
+ * -> qt [G, cols, rows], st [G, cols/128, rows/128]; all dense; rows % 128 ==
+ * 0, cols % 128 == 0; exact byte transposes.  One kernel on `stream`.
+ */
+int fp8_block_transpose_batched(const uint8_t *q, const uint8_t *s, int G, int64_t rows, int64_t cols,
+                                uint8_t *qt, uint8_t *st, void *stream);
+
+/*
+ * fp8_grouped_direct_transpose -- the direct transpose applied to each expert
+ * segment of a permuted, padded row-wise FP8 activation, for the K-grouped
+ * Wgrad of the expert backward ([FLOW] "Core method", per 128x128 block;
+ * [DSV3] §5.6 grouped layouts).  Segment e = rows [off[e], off[e+1]) of q
+ * (off = group_offsets on the device, as from permute_pad); its transpose
+ * fills columns [koff[e], koff[e] + ceil(len_e/128)*128) of qt [cols, K_cap],
+ * koff[e+1] = koff[e] + ceil(len_e/128)*128 (written to k_offsets [G+1] on
+ * the device).  A segment's last 128-row block may be short: the block's
+ * scale is the largest over the rows present and the columns of the absent
+ * rows hold code 0.  st [cols, K_cap/128] (all 128 entries of a block
+ * equal).  Columns past koff[G] are not written.
+ *   q [M_cap, cols], s [M_cap, cols/128] 1x128 scales; cols % 128 == 0;
+ *   K_cap % 128 == 0 and K_cap >= M_cap + 127*G rounded up to 128; 1 <= G <= 1024.
+ */
+int fp8_grouped_direct_transpose(const uint8_t *q, const uint8_t *s, int64_t M_cap, int64_t cols,
+                                 const int32_t *group_offsets, int G, uint8_t *qt, uint8_t *st, int64_t K_cap,
+                                 int32_t *k_offsets, void *stream);
+
+/*
  * fp8_naive_transpose -- the three-pass conversion that the direct transpose
  * replaces ([FLOW] "Core method" and Fig. 1, the baseline it is 2-3x faster
  * than): dequantize the row-wise codes to bf16 (exact for power-of-two

@@ -41,6 +41,8 @@ def lib():
         L.orc_direct_transpose.argtypes = [p, p, i64, i64, p, p]
         L.orc_block_transpose.argtypes = [p, p, i64, i64, p, p]
         L.orc_naive_transpose.argtypes = [p, p, i64, i64, p, p]
+        L.orc_grouped_direct_transpose.argtypes = [p, p, i64, p, i32, p, p, i64, p]
+        L.orc_kgrouped_gemm_sampled.argtypes = [p, p, p, p, p, i64, p, p, p, i64, p]
         L.orc_quant_rowwise_sf.argtypes = [p, i64, i64, p, p]
         L.orc_dequant_sf.argtypes = [p, p, i64, i64, p]
         L.orc_naive_transpose_sf.argtypes = [p, p, i64, i64, p, p]
@@ -223,6 +225,39 @@ def naive_transpose_sf(q, sf):
     sft = np.empty((Cc, T // 128), np.float32)
     lib().orc_naive_transpose_sf(_p(q), _p(sf), T, Cc, _p(qt), _p(sft))
     return qt, sft
+
+
+def block_transpose_batched(q, s):
+    """Per-expert weight-block transposes: q [G, rows, cols], s [G, rows/128, cols/128]."""
+    outs = [block_transpose(q[e], s[e]) for e in range(q.shape[0])]
+    return np.stack([o[0] for o in outs]), np.stack([o[1] for o in outs])
+
+
+def grouped_direct_transpose(q, s, off, Kc):
+    """orc_grouped_direct_transpose: segments of q [M, C] -> (qt [C, Kc], st [C, Kc/128], koff [G+1])."""
+    q = _c(q, np.uint8)
+    s = _c(s, np.uint8)
+    off = _c(off, np.int32)
+    M, Cc = q.shape
+    G = len(off) - 1
+    qt = np.zeros((Cc, Kc), np.uint8)
+    st = np.zeros((Cc, Kc // 128), np.uint8)
+    koff = np.zeros(G + 1, np.int32)
+    lib().orc_grouped_direct_transpose(_p(q), _p(s), Cc, _p(off), G, _p(qt), _p(st), Kc, _p(koff))
+    return qt, st, koff
+
+
+def kgrouped_gemm_sampled(a, sa, b, sb, koff, ei, mi, ni):
+    a = _c(a, np.uint8)
+    sa = _c(sa, np.uint8)
+    b = _c(b, np.uint8)
+    sb = _c(sb, np.uint8)
+    koff = _c(koff, np.int32)
+    ei, mi, ni = (_c(v, np.int64) for v in (ei, mi, ni))
+    out = np.empty(len(mi), np.float64)
+    lib().orc_kgrouped_gemm_sampled(_p(a), _p(sa), _p(b), _p(sb), _p(koff), a.shape[1], _p(ei), _p(mi), _p(ni),
+                                   len(mi), _p(out))
+    return out
 
 
 # ---- GEMMs ---------------------------------------------------------------

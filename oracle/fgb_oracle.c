@@ -325,6 +325,53 @@ void orc_naive_transpose_sf(const uint8_t *q, const float *sf, int64_t T, int64_
     free(xt);
 }
 
+/* ------------------------------------------------------------------------ */
+/* Direct transpose of the expert segments of a permuted, padded activation */
+/* (the expert backward's Wgrad contracts over each expert's own rows;      */
+/* [FLOW] "Core method": the transpose is applied per 128x128 block).       */
+/* Segment e = rows [off[e], off[e+1]) of q; its transpose fills columns    */
+/* [koff[e], koff[e] + ceil(len_e/128)*128) of qt [C, Kc], with             */
+/* koff[e+1] = koff[e] + ceil(len_e/128)*128.  Each block takes the largest */
+/* scale over the rows present (the last block of a segment may be short); */
+/* the columns of absent rows hold code 0.  st [C, Kc/128].                 */
+/* Columns past koff[G] are not written.                                   */
+/* ------------------------------------------------------------------------ */
+void orc_grouped_direct_transpose(const uint8_t *q, const uint8_t *s, int64_t C, const int32_t *off,
+                                  int G, uint8_t *qt, uint8_t *st, int64_t Kc, int32_t *koff)
+{
+    koff[0] = 0;
+    for (int e = 0; e < G; e++) {
+        int64_t len = off[e + 1] - off[e];
+        koff[e + 1] = koff[e] + (int32_t)(((len + 127) / 128) * 128);
+    }
+    for (int e = 0; e < G; e++) {
+        for (int64_t b = 0; b < (koff[e + 1] - koff[e]) / 128; b++) {
+            int64_t t0 = off[e] + b * 128, n = off[e + 1] - t0 < 128 ? off[e + 1] - t0 : 128;
+            int64_t kc = koff[e] + b * 128;
+            for (int64_t cb = 0; cb < C / 128; cb++) {
+                int emax = -1000;
+                for (int64_t t = t0; t < t0 + n; t++) {
+                    int ee = (int)s[t * (C / 128) + cb] - 127;
+                    if (ee > emax)
+                        emax = ee;
+                }
+                for (int64_t c = cb * 128; c < cb * 128 + 128; c++)
+                    for (int64_t i = 0; i < 128; i++) {
+                        uint8_t code = 0;
+                        if (i < n) {
+                            int ee = (int)s[(t0 + i) * (C / 128) + cb] - 127;
+                            double v = ldexp(orc_e4m3_decode(q[(t0 + i) * C + c]), ee);
+                            code = orc_e4m3_encode(ldexp(v, -emax));
+                        }
+                        qt[c * Kc + kc + i] = code;
+                    }
+                for (int64_t c = cb * 128; c < cb * 128 + 128; c++)
+                    st[c * (Kc / 128) + kc / 128] = (uint8_t)(emax + 127);
+            }
+        }
+    }
+}
+
 /* Weight-block transpose for Dgrad: W[rows, cols] with 128x128 block      */
 /* scales becomes W^T[cols, rows] with transposed block scales; exact.     */
 /* ([DSV3] §1: Dgrad multiplies by W, so the NT GEMM needs W^T K-major.)    */
@@ -410,6 +457,30 @@ void orc_block_gemm_sampled(const uint8_t *a, const uint8_t *sa, int a_gran, con
     dec_table();
     for (int64_t i = 0; i < ns; i++)
         out[i] = gemm_one(a, sa, a_gran, b, sb, b_gran, b_l1, g1, N, K, lda, ldb, mi[i], ni[i]);
+}
+
+/* K-grouped GEMM for the expert Wgrad ([DSV3] §5.6 grouped GEMMs; each    */
+/* expert's weight gradient contracts over its own token segment, the 1D1D  */
+/* case of §5.2): D_e = A[:, k0:k1] * B[:, k0:k1]^T, k0 = koff[e],          */
+/* k1 = koff[e+1] (multiples of 128).  A [M, Kc], B [N, Kc] codes with      */
+/* 1x128 scales [M, Kc/128], [N, Kc/128]; exact 128-term partials scaled    */
+/* and summed in fp64.  Sampled outputs (ei, mi, ni).                      */
+void orc_kgrouped_gemm_sampled(const uint8_t *a, const uint8_t *sa, const uint8_t *b, const uint8_t *sb,
+                               const int32_t *koff, int64_t Kc, const int64_t *ei, const int64_t *mi,
+                               const int64_t *ni, int64_t ns, double *out)
+{
+    dec_table();
+    for (int64_t i = 0; i < ns; i++) {
+        int64_t e = ei[i], m = mi[i], n = ni[i];
+        double acc = 0.0;
+        for (int64_t kb = koff[e]; kb < koff[e + 1]; kb += 128) {
+            double part = 0.0;
+            for (int64_t k = kb; k < kb + 128; k++)
+                part += g_dec[a[m * Kc + k]] * g_dec[b[n * Kc + k]];
+            acc += ldexp(part, (int)sa[m * (Kc / 128) + kb / 128] + (int)sb[n * (Kc / 128) + kb / 128] - 254);
+        }
+        out[i] = acc;
+    }
 }
 
 /* Tolerance helper for a GEMM whose matrix unit sums runs of `run`

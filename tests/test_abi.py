@@ -87,6 +87,10 @@ def test_transpose_and_moe_validation():
     f = _fake()
     assert L.fp8_direct_transpose(f, f, 0, 200, 256, f, f, None) == 1
     assert L.fp8_direct_transpose(f, f, 1, 256, 256, f, f, None) == 2
+    assert L.fp8_block_transpose_batched(f, f, 0, 256, 256, f, f, None) == 1
+    assert L.fp8_block_transpose_batched(f, f, 4, 200, 256, f, f, None) == 1
+    assert L.fp8_grouped_direct_transpose(f, f, 1000, 256, f, 8, f, f, 1024, f, None) == 1  # K_cap too small
+    assert L.fp8_grouped_direct_transpose(f, f, 1000, 200, f, 8, f, f, 4096, f, None) == 1  # cols % 128
     # three-pass baseline: shape and workspace checks
     assert fgb.fp8_naive_transpose_workspace_size(256, 384) == 4 * 256 * 384
     assert L.fp8_naive_transpose(f, f, 200, 256, f, f, f, 1 << 20, None) == 1

@@ -218,6 +218,33 @@ def test_naive_transpose(fgb, T, C):
     assert np.array_equal(np_(qt), oqt)
 
 
+def test_block_transpose_batched(fgb):
+    say("transpose: batched expert weight blocks [8, 512, 256]")
+    q = rand_codes((8, 512, 256), 15)
+    s = rand_scales((8, 4, 2), -30, 10, 16)
+    qt, st = fgb.fp8_block_transpose_batched(q.to(DEV), s.to(DEV))
+    oqt, ost = O.block_transpose_batched(q.numpy(), s.numpy())
+    assert np.array_equal(np_(qt), oqt) and np.array_equal(np_(st), ost)
+
+
+@pytest.mark.parametrize("T,C", [(300, 256), (16384, 2048)])
+def test_grouped_direct_transpose(fgb, T, C):
+    say("grouped direct transpose of expert segments", T, C)
+    topk, G = 8, 32
+    idx, _ = synth.routing(T=T, E=G, topk=topk, seed=T + 7)
+    xq, xs = synth.wgrad_codes(T, C, seed=T + 8)
+    M_cap = T * topk + 15 * G
+    ws = torch.empty(fgb.permute_pad_workspace_size(T, topk, G), dtype=torch.uint8, device=DEV)
+    pq, ps, rmap, offs = fgb.permute_pad(xq.to(DEV), xs.to(DEV), torch.from_numpy(idx).to(DEV), G, 16, M_cap, ws)
+    qt, st, koff = fgb.fp8_grouped_direct_transpose(pq, ps, offs)
+    K_cap = qt.shape[1]
+    oqt, ost, okoff = O.grouped_direct_transpose(np_(pq), np_(ps), np_(offs), K_cap)
+    k = int(okoff[-1])
+    assert np.array_equal(np_(koff), okoff)
+    assert np.array_equal(np_(st)[:, :k // 128], ost[:, :k // 128])
+    assert np.array_equal(np_(qt)[:, :k], oqt[:, :k])
+
+
 def test_transpose_block_weights(fgb):
     say("transpose: 128x128-block weight transpose")
     q = rand_codes((2048, 1024), 5)

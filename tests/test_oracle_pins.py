@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import oracle as O
+import synth
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -430,6 +431,53 @@ def test_naive_transpose_sf_composition():
     f = np.where(amax > 0, (amax / np.float32(448.0)).astype(np.float32), np.float32(1.0)).astype(np.float32)
     assert np.array_equal(sft, f)
     assert np.array_equal(qt, brute_encode((tiles / f[..., None]).astype(np.float32).astype(np.float64)).reshape(384, 256))
+
+
+def test_grouped_direct_transpose_against_per_segment_direct_transpose():
+    """Each expert segment's block equals the direct transpose of that segment,
+    extended (when short) by absent rows of code 0 with scale byte 0, which can
+    never hold the block maximum; koff is the scan of the 128-rounded lengths."""
+    rng = np.random.default_rng(86)
+    lens = [256, 48, 0, 128, 144, 16]
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    M, Cc = int(off[-1]), 256
+    q, s = synth.wgrad_codes(M, Cc, seed=86)
+    q, s = q.numpy(), s.numpy()
+    Kc = 1024
+    qt, st, koff = O.grouped_direct_transpose(q, s, off, Kc)
+    assert list(koff) == list(np.concatenate([[0], np.cumsum([(l + 127) // 128 * 128 for l in lens])]))
+    for e, l in enumerate(lens):
+        if l == 0:
+            continue
+        n = (l + 127) // 128 * 128
+        qe = np.zeros((n, Cc), np.uint8)
+        se = np.zeros((n, Cc // 128), np.uint8)
+        qe[:l] = q[off[e]:off[e + 1]]
+        se[:l] = s[off[e]:off[e + 1]]
+        dq, ds = O.direct_transpose(qe, se)
+        assert np.array_equal(qt[:, koff[e]:koff[e] + n], dq)
+        assert np.array_equal(st[:, koff[e] // 128:(koff[e] + n) // 128], ds)
+
+
+def test_kgrouped_gemm_against_per_expert_block_gemm():
+    rng = np.random.default_rng(87)
+    koff = np.array([0, 256, 256, 640, 768], np.int32)
+    Kc, M, N = 896, 40, 24
+    a = rng.integers(0, 0x7F, (M, Kc)).astype(np.uint8)
+    b = (rng.integers(0, 0x7F, (N, Kc)) | 0x80 * rng.integers(0, 2, (N, Kc))).astype(np.uint8)
+    sa = rng.integers(110, 135, (M, Kc // 128)).astype(np.uint8)
+    sb = rng.integers(110, 135, (N, Kc // 128)).astype(np.uint8)
+    ei, mi, ni = np.meshgrid(np.arange(4), np.arange(M), np.arange(N), indexing="ij")
+    got = O.kgrouped_gemm_sampled(a, sa, b, sb, koff, ei.ravel(), mi.ravel(), ni.ravel()).reshape(4, M, N)
+    for e in range(4):
+        k0, k1 = koff[e], koff[e + 1]
+        if k1 == k0:
+            assert np.all(got[e] == 0)
+            continue
+        ref = O.block_gemm(np.ascontiguousarray(a[:, k0:k1]), np.ascontiguousarray(sa[:, k0 // 128:k1 // 128]),
+                           O.ROW1x128, np.ascontiguousarray(b[:, k0:k1]),
+                           np.ascontiguousarray(sb[:, k0 // 128:k1 // 128]), O.ROW1x128)
+        assert np.array_equal(got[e], ref)
 
 
 def test_block_transpose_exact():
