@@ -19,7 +19,7 @@ __all__ = [
     "fp8_block_gemm", "fp8_grouped_gemm", "permute_pad",
     "permute_pad_workspace_size", "unpermute_unpad", "swiglu_quant", "dswiglu_quant", "mx2_quant",
     "mx2_dequant", "unpermute_backward", "unpermute_backward_workspace_size",
-    "fp8_block_transpose_batched", "fp8_grouped_direct_transpose", "F32", "BF16", "ROW1x128", "ROW1x32", "BLOCK128", "GEMM_EXACT", "GEMM_FAST",
+    "fp8_block_transpose_batched", "fp8_grouped_direct_transpose", "fp8_kgrouped_gemm", "F32", "BF16", "ROW1x128", "ROW1x32", "BLOCK128", "GEMM_EXACT", "GEMM_FAST",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,7 +35,7 @@ SYMBOLS = [
     "permute_pad", "permute_pad_workspace_size", "unpermute_unpad", "swiglu_quant", "mx2_quant",
     "mx2_dequant", "fp8_naive_transpose", "fp8_naive_transpose_workspace_size", "dswiglu_quant",
     "unpermute_backward", "unpermute_backward_workspace_size", "fp8_block_transpose_batched",
-    "fp8_grouped_direct_transpose",
+    "fp8_grouped_direct_transpose", "fp8_kgrouped_gemm",
 ]
 
 
@@ -66,6 +66,8 @@ _SIG = {
     "fp8_block_gemm": (_i32, [_p, _p, _i32, _p, _p, _i32, _p, _i64, _i64, _i64, _i64, _i64, _i64,
                               _p, _i32, _i64, _i32, _i32, _p, _sz, _p]),
     "fp8_grouped_gemm": (_i32, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, _i32, _i32, _p]),
+    "fp8_kgrouped_gemm": (_i32, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, _i32, _i32, _i32,
+                                 _p]),
     "permute_pad": (_i32, [_p, _p, _p, _i64, _i32, _i32, _i64, _i32, _p, _p, _p, _p, _i64, _p,
                            _sz, _p]),
     "permute_pad_workspace_size": (_sz, [_i64, _i32, _i32]),
@@ -268,6 +270,27 @@ def fp8_grouped_gemm(a, sa, b, sb, group_offsets, out_dtype=torch.bfloat16, d=No
     _call("fp8_grouped_gemm", _ptr(a.contiguous()), _ptr(sa.contiguous()), _ptr(b.contiguous()),
           _ptr(sb.contiguous()), _ptr(group_offsets), G, M_cap, N, K, _ptr(d), _dtype_code(d),
           mode, _stream(a))
+    return d
+
+
+def fp8_kgrouped_gemm(a, sa, b, sb, k_offsets, out_dtype=torch.float32, d=None, accumulate=False,
+                      mode=GEMM_EXACT):
+    """K-grouped GEMM (expert Wgrad): a [M, K_cap], b [N, K_cap], k_offsets [G+1] (device) -> d [G, M, N]."""
+    _check_dev(a, sa, b, sb, k_offsets, d)
+    for t in (a, sa, b, sb, k_offsets):
+        if not t.is_contiguous():
+            raise ValueError("fp8_kgrouped_gemm: operands must be contiguous")
+    M, K_cap = a.shape
+    N = b.shape[0]
+    G = k_offsets.numel() - 1
+    if b.shape[1] != K_cap:
+        raise ValueError("fp8_kgrouped_gemm: a and b must have the same K capacity")
+    if d is None:
+        d = torch.empty((G, M, N), dtype=out_dtype, device=a.device)
+    elif not d.is_contiguous() or tuple(d.shape) != (G, M, N):
+        raise ValueError("fp8_kgrouped_gemm: d must be a contiguous [G, M, N] tensor")
+    _call("fp8_kgrouped_gemm", _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(k_offsets), G, M, N, K_cap,
+          _ptr(d), _dtype_code(d), int(bool(accumulate)), mode, _stream(a))
     return d
 
 

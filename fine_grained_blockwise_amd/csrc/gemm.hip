@@ -72,6 +72,7 @@ template <int MODE> struct Waves {
     static constexpr int NW = MODE == MODE_EXACT ? 8 : 4;
 };
 enum { AG_ROW128 = 0, AG_ROW32 = 1 };
+enum { GK_NONE = 0, GK_M = 1, GK_K = 2 }; // dense, M-grouped (experts' rows), K-grouped (experts' K ranges)
 enum { BG_ROW128 = 0, BG_ROW32 = 1, BG_BLOCK = 2 };
 
 struct GemmArgs {
@@ -83,7 +84,9 @@ struct GemmArgs {
     int tiles_n;
     const int32_t *offs; // grouped: group offsets [G+1]
     int G;
-    int64_t b_stride, sb_stride; // grouped: per-expert B / SB strides
+    int64_t b_stride, sb_stride; // M-grouped: per-expert B / SB strides
+    const int32_t *koffs;        // K-grouped: per-expert K offsets [G+1] (multiples of 128)
+    int64_t d_stride;            // K-grouped: per-expert output stride (elements)
 };
 
 // Contiguous tile ranges per XCD: workgroup b runs on XCD b % 8.
@@ -126,7 +129,7 @@ __device__ __forceinline__ v16f mfma_scaled(v8i a, v8i b, v16f c, uint32_t sa, u
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OPA, (int)sa, OPB, (int)sb);
 }
 
-template <int MODE, int AG, int BG, bool OUT_BF16, bool GROUPED>
+template <int MODE, int AG, int BG, bool OUT_BF16, int GK>
 __global__ __launch_bounds__(Waves<MODE>::NW * 64) __attribute__((amdgpu_waves_per_eu(Waves<MODE>::NW / 4, Waves<MODE>::NW / 4))) void
 gemm_fp8_kernel(GemmArgs p)
 {
@@ -137,7 +140,8 @@ gemm_fp8_kernel(GemmArgs p)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / (NW / 2), wn = wave % (NW / 2);
     const int l32 = lane & 31, hk = lane >> 5;
-    const int64_t K = p.K, nk = K / BK;
+    const int64_t K = p.K; // row length of A and B (K-grouped: the whole K capacity)
+    int64_t kbeg = 0, nk = K / BK;
     const int64_t N = p.N;
 
     // ---- tile -> (m0, n0) ------------------------------------------------
@@ -145,10 +149,19 @@ gemm_fp8_kernel(GemmArgs p)
     // consecutive tiles walk down a band first, so the ~32 tiles an XCD runs
     // at once form a GM x 8 block sharing A rows and B columns in L2.
     int64_t tile = xcd_remap(blockIdx.x, gridDim.x);
+    int64_t tiles_here = gridDim.x;
+    int ke = 0; // K-grouped: this workgroup's expert, whose K range is [koffs[ke], koffs[ke+1])
+    if constexpr (GK == GK_K) {
+        tiles_here = gridDim.x / p.G;
+        ke = (int)(tile / tiles_here);
+        tile %= tiles_here;
+        kbeg = p.koffs[ke];
+        nk = (p.koffs[ke + 1] - kbeg) / BK;
+    }
     int64_t tm, tn;
     {
         constexpr int64_t GM = 4;
-        const int64_t tiles_m = gridDim.x / p.tiles_n;
+        const int64_t tiles_m = tiles_here / p.tiles_n;
         const int64_t band = tile / (GM * p.tiles_n), in = tile % (GM * p.tiles_n);
         const int64_t bm = min(GM, tiles_m - band * GM); // rows in this (possibly last) band
         tm = band * GM + in % bm;
@@ -156,7 +169,7 @@ gemm_fp8_kernel(GemmArgs p)
     }
     int64_t m0 = 0, m_end = 0;
     const uint8_t *B = p.b, *SB = p.sb;
-    if constexpr (!GROUPED) {
+    if constexpr (GK != GK_M) {
         m0 = tm * BM;
         m_end = p.M;
     } else {
@@ -200,8 +213,8 @@ gemm_fp8_kernel(GemmArgs p)
     // lane l lands at LDS (w*RPW + g*16)*64 + 16*l, i.e. row +l/4, position
     // l%4, which holds chunk (l%4) ^ swz(l/4) of that row.  Rows past the end
     // re-read the last valid row (those outputs are never stored).
-    const uint8_t *a_base = p.a + m0 * p.lda;
-    const uint8_t *b_base = B + n0 * p.ldb;
+    const uint8_t *a_base = p.a + m0 * p.lda + kbeg;
+    const uint8_t *b_base = B + n0 * p.ldb + kbeg;
     uint32_t a_off[IPO], b_off[IPO];
 #pragma unroll
     for (int g = 0; g < IPO; g++) {
@@ -220,7 +233,7 @@ gemm_fp8_kernel(GemmArgs p)
     const int64_t sa_row = A32 ? K / 32 : K / 128;
     const int64_t sb_row = B32 ? K / 32 : K / 128;
     uint32_t sa_off, sb_off;
-    const uint8_t *sa_base = p.sa + m0 * sa_row, *sb_base;
+    const uint8_t *sa_base = p.sa + m0 * sa_row + kbeg / (A32 ? 32 : 128), *sb_base;
     {
         const int64_t r = (wave & 3) * 64 + lane;
         const int64_t rc = m0 + r < m_end ? r : m_end - 1 - m0;
@@ -230,7 +243,7 @@ gemm_fp8_kernel(GemmArgs p)
             sb_base = SB;
             sb_off = (uint32_t)(((n0 + c) / 128) * (K / 128));
         } else {
-            sb_base = SB + n0 * sb_row;
+            sb_base = SB + n0 * sb_row + kbeg / (B32 ? 32 : 128);
             sb_off = (uint32_t)(c * sb_row);
         }
     }
@@ -240,29 +253,29 @@ gemm_fp8_kernel(GemmArgs p)
     // address is a uniform 64-bit base (SGPRs) plus the lane's 32-bit offset.
     // Issued as inline asm so that the compiler does not place waits on them
     // in front of unrelated LDS reads; the kernel counts them itself.
-    auto dma16 = [](const uint8_t *gbase, uint32_t off, uint32_t lds_addr) {
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                     :
-                     : "s"(lds_addr), "v"(off), "s"(gbase)
-                     : "memory", "m0");
-    };
-    auto dma4 = [](const uint8_t *gbase, uint32_t off, uint32_t lds_addr) {
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
-                     :
-                     : "s"(lds_addr), "v"(off), "s"(gbase)
-                     : "memory", "m0");
-    };
-    auto dma1 = [](const uint8_t *gbase, uint32_t off, uint32_t lds_addr) {
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_ubyte %1, %2"
-                     :
-                     : "s"(lds_addr), "v"(off), "s"(gbase)
-                     : "memory", "m0");
-    };
     auto uniform = [](const uint8_t *q) {
         const uint64_t v = (uint64_t)(uintptr_t)q;
         const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
         const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
         return (const uint8_t *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+    };
+    auto dma16 = [&](const uint8_t *gbase, uint32_t off, uint32_t lds_addr) {
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :
+                     : "s"(lds_addr), "v"(off), "s"(uniform(gbase))
+                     : "memory", "m0");
+    };
+    auto dma4 = [&](const uint8_t *gbase, uint32_t off, uint32_t lds_addr) {
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                     :
+                     : "s"(lds_addr), "v"(off), "s"(uniform(gbase))
+                     : "memory", "m0");
+    };
+    auto dma1 = [&](const uint8_t *gbase, uint32_t off, uint32_t lds_addr) {
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_ubyte %1, %2"
+                     :
+                     : "s"(lds_addr), "v"(off), "s"(uniform(gbase))
+                     : "memory", "m0");
     };
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
     const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -375,6 +388,7 @@ gemm_fp8_kernel(GemmArgs p)
         for (int j = 0; j < TJ; j++)
             acc[i][j] = (v16f){0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
+    if (nk32 > 0) { // an expert of the K-grouped form may have no rows: the tile is zero
     // ---- prologue ----------------------------------------------------------------
     // Half-steps 0..2 and part of half-step 3 in flight (the rest is issued in
     // the first slots of the main loop); wait for half-step 0 and sync.
@@ -593,6 +607,7 @@ gemm_fp8_kernel(GemmArgs p)
     }
 #undef FGB_WAIT_SYNC
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); // trailing copies land before LDS is reused
+    } // nk32 > 0
 
     // ---- epilogue --------------------------------------------------------------
     // 32x32 accumulator layout: lane l, register r -> row (r/4)*8 + (l/32)*4 + r%4,
@@ -645,7 +660,7 @@ gemm_fp8_kernel(GemmArgs p)
             uint4 v = *reinterpret_cast<const uint4 *>(ep + row_l * ROWB + lc * 16);
             if (row >= m_end || col0 >= N)
                 continue;
-            uint8_t *dst = (uint8_t *)p.d + (row * p.ldd + col0) * ESZ;
+            uint8_t *dst = (uint8_t *)p.d + (ke * p.d_stride + row * p.ldd + col0) * ESZ;
             const bool full = col0 + 16 / ESZ <= N && (((uintptr_t)dst & 15) == 0);
             if constexpr (OUT_BF16) {
                 if (full) {
@@ -675,10 +690,10 @@ gemm_fp8_kernel(GemmArgs p)
     }
 }
 
-template <int MODE, int AG, int BG, bool OUT_BF16, bool GROUPED>
+template <int MODE, int AG, int BG, bool OUT_BF16, int GK>
 static int launch_one(const GemmArgs &p, int64_t grid, hipStream_t st)
 {
-    auto kern = gemm_fp8_kernel<MODE, AG, BG, OUT_BF16, GROUPED>;
+    auto kern = gemm_fp8_kernel<MODE, AG, BG, OUT_BF16, GK>;
     static bool attr_set = false; // per instantiation, set once per process
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
@@ -691,29 +706,37 @@ static int launch_one(const GemmArgs &p, int64_t grid, hipStream_t st)
     return FGB_OK;
 }
 
-template <int MODE, bool GROUPED>
+template <int MODE, int GK>
 static int dispatch_mode(int ag, int bg, bool bf16, const GemmArgs &p, int64_t grid, hipStream_t st)
 {
-    if (ag == AG_ROW128 && bg == BG_BLOCK)
-        return bf16 ? launch_one<MODE, AG_ROW128, BG_BLOCK, true, GROUPED>(p, grid, st)
-                    : launch_one<MODE, AG_ROW128, BG_BLOCK, false, GROUPED>(p, grid, st);
-    if constexpr (!GROUPED) {
+    if constexpr (GK == GK_M) {
+        if (ag == AG_ROW128 && bg == BG_BLOCK)
+            return bf16 ? launch_one<MODE, AG_ROW128, BG_BLOCK, true, GK_M>(p, grid, st)
+                        : launch_one<MODE, AG_ROW128, BG_BLOCK, false, GK_M>(p, grid, st);
+    } else if constexpr (GK == GK_K) {
         if (ag == AG_ROW128 && bg == BG_ROW128)
-            return bf16 ? launch_one<MODE, AG_ROW128, BG_ROW128, true, false>(p, grid, st)
-                        : launch_one<MODE, AG_ROW128, BG_ROW128, false, false>(p, grid, st);
+            return bf16 ? launch_one<MODE, AG_ROW128, BG_ROW128, true, GK_K>(p, grid, st)
+                        : launch_one<MODE, AG_ROW128, BG_ROW128, false, GK_K>(p, grid, st);
+    } else {
+        if (ag == AG_ROW128 && bg == BG_BLOCK)
+            return bf16 ? launch_one<MODE, AG_ROW128, BG_BLOCK, true, GK_NONE>(p, grid, st)
+                        : launch_one<MODE, AG_ROW128, BG_BLOCK, false, GK_NONE>(p, grid, st);
+        if (ag == AG_ROW128 && bg == BG_ROW128)
+            return bf16 ? launch_one<MODE, AG_ROW128, BG_ROW128, true, GK_NONE>(p, grid, st)
+                        : launch_one<MODE, AG_ROW128, BG_ROW128, false, GK_NONE>(p, grid, st);
         if (ag == AG_ROW32 && bg == BG_ROW32)
-            return bf16 ? launch_one<MODE, AG_ROW32, BG_ROW32, true, false>(p, grid, st)
-                        : launch_one<MODE, AG_ROW32, BG_ROW32, false, false>(p, grid, st);
+            return bf16 ? launch_one<MODE, AG_ROW32, BG_ROW32, true, GK_NONE>(p, grid, st)
+                        : launch_one<MODE, AG_ROW32, BG_ROW32, false, GK_NONE>(p, grid, st);
     }
     return set_error(FGB_EUNSUPPORTED, "gemm: unsupported scale granularity pair (%d, %d)", ag, bg);
 }
 
-template <bool GROUPED>
+template <int GK>
 static int dispatch(int mode, int ag, int bg, bool bf16, const GemmArgs &p, int64_t grid, hipStream_t st)
 {
     if (mode == FGB_GEMM_FAST)
-        return dispatch_mode<MODE_FAST, GROUPED>(ag, bg, bf16, p, grid, st);
-    return dispatch_mode<MODE_EXACT, GROUPED>(ag, bg, bf16, p, grid, st);
+        return dispatch_mode<MODE_FAST, GK>(ag, bg, bf16, p, grid, st);
+    return dispatch_mode<MODE_EXACT, GK>(ag, bg, bf16, p, grid, st);
 }
 
 } // namespace fgb
@@ -774,7 +797,7 @@ extern "C" int fp8_block_gemm(const uint8_t *a, const uint8_t *sa, int a_gran, c
     p.tiles_n = (int)((N + BN - 1) / BN);
     int64_t tiles = ((M + BM - 1) / BM) * p.tiles_n;
     FGB_REQUIRE(tiles < (1ll << 31), FGB_EINVAL, "fp8_block_gemm: too many tiles");
-    return dispatch<false>(mode, ag, bg, d_dtype == FGB_BF16, p, tiles, (hipStream_t)stream);
+    return dispatch<GK_NONE>(mode, ag, bg, d_dtype == FGB_BF16, p, tiles, (hipStream_t)stream);
 }
 
 extern "C" int fp8_grouped_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t *b,
@@ -807,5 +830,34 @@ extern "C" int fp8_grouped_gemm(const uint8_t *a, const uint8_t *sa, const uint8
     // sum over experts of ceil(rows_e / BM) <= ceil(M_cap / BM) + G
     int64_t tiles = ((M_cap + BM - 1) / BM + G) * p.tiles_n;
     FGB_REQUIRE(tiles < (1ll << 31), FGB_EINVAL, "fp8_grouped_gemm: too many tiles");
-    return dispatch<true>(mode, AG_ROW128, BG_BLOCK, d_dtype == FGB_BF16, p, tiles, (hipStream_t)stream);
+    return dispatch<GK_M>(mode, AG_ROW128, BG_BLOCK, d_dtype == FGB_BF16, p, tiles, (hipStream_t)stream);
+}
+
+extern "C" int fp8_kgrouped_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t *b, const uint8_t *sb,
+                                 const int32_t *k_offsets, int G, int64_t M, int64_t N, int64_t K_cap, void *d,
+                                 int d_dtype, int accumulate, int mode, void *stream)
+{
+    clear_error();
+    FGB_REQUIRE(a && sa && b && sb && d && k_offsets, FGB_EINVAL, "fp8_kgrouped_gemm: null pointer");
+    FGB_REQUIRE(G >= 1 && G <= 1024, FGB_EINVAL, "fp8_kgrouped_gemm: G must be in [1, 1024]");
+    FGB_REQUIRE(M > 0 && N > 0 && K_cap > 0 && K_cap % 128 == 0, FGB_EINVAL,
+                "fp8_kgrouped_gemm: need M, N > 0 and K_cap a positive multiple of 128");
+    FGB_REQUIRE(256 * K_cap < (1ll << 32), FGB_EINVAL, "fp8_kgrouped_gemm: K_cap too large");
+    FGB_REQUIRE(aligned16(a) && aligned16(b), FGB_EINVAL, "fp8_kgrouped_gemm: a and b must be 16-byte aligned");
+    FGB_REQUIRE(d_dtype == FGB_F32 || d_dtype == FGB_BF16, FGB_EUNSUPPORTED,
+                "fp8_kgrouped_gemm: d_dtype must be FGB_F32 or FGB_BF16");
+    FGB_REQUIRE(mode == FGB_GEMM_EXACT || mode == FGB_GEMM_FAST, FGB_EUNSUPPORTED,
+                "fp8_kgrouped_gemm: mode must be FGB_GEMM_EXACT or FGB_GEMM_FAST");
+    FGB_REQUIRE(!(accumulate && d_dtype != FGB_F32), FGB_EUNSUPPORTED, "fp8_kgrouped_gemm: accumulate needs FP32 output");
+    GemmArgs p{};
+    p.a = a; p.sa = sa; p.b = b; p.sb = sb; p.l1 = nullptr; p.d = d;
+    p.M = M; p.N = N; p.K = K_cap; p.lda = K_cap; p.ldb = K_cap; p.ldd = N;
+    p.accumulate = accumulate;
+    p.tiles_n = (int)((N + BN - 1) / BN);
+    p.G = G;
+    p.koffs = k_offsets;
+    p.d_stride = M * N;
+    const int64_t tiles = ((M + BM - 1) / BM) * p.tiles_n * G;
+    FGB_REQUIRE(tiles < (1ll << 31), FGB_EINVAL, "fp8_kgrouped_gemm: too many tiles");
+    return dispatch<GK_K>(mode, AG_ROW128, BG_ROW128, d_dtype == FGB_BF16, p, tiles, (hipStream_t)stream);
 }

@@ -230,6 +230,30 @@ int fp8_grouped_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t *b, cons
                      void *d, int d_dtype, int mode, void *stream);
 
 /*
+ * fp8_kgrouped_gemm -- K-grouped FP8 GEMM, the Wgrad of the MoE experts
+ * ([DSV3] §1: Wgrad multiplies dY^T by X, here per expert; §5.6 grouped
+ * layouts with the experts concatenated along K).  For each expert e,
+ *   D_e = A[:, koff[e]:koff[e+1]] * B[:, koff[e]:koff[e+1]]^T,
+ * with 1x128 scales on both operands (both as written by
+ * fp8_grouped_direct_transpose) and FP32 accumulation as in fp8_block_gemm.
+ *   a  [M, K_cap] codes, sa [M, K_cap/128] scales, dense (A_e = dY_e^T)
+ *   b  [N, K_cap] codes, sb [N, K_cap/128] scales, dense (B_e = X_e^T)
+ *   k_offsets : device int32 [G+1], non-decreasing multiples of 128,
+ *               k_offsets[0] >= 0, k_offsets[G] <= K_cap (as written by
+ *               fp8_grouped_direct_transpose).  Read on the device: no host
+ *               synchronisation and no check of these conditions.
+ *   d  [G, M, N] dense, FGB_F32 or FGB_BF16; an expert with an empty range
+ *      gets D_e = 0 (or keeps D_e when accumulating).  accumulate != 0
+ *      (FP32 only): D_e += A_e * B_e^T.
+ *   mode: FGB_GEMM_EXACT or FGB_GEMM_FAST as for fp8_block_gemm.
+ * K_cap % 128 == 0, 256 * K_cap below 2^32, 1 <= G <= 1024; a and b 16-byte
+ * aligned.  One kernel on `stream`.
+ */
+int fp8_kgrouped_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t *b, const uint8_t *sb,
+                      const int32_t *k_offsets, int G, int64_t M, int64_t N, int64_t K_cap, void *d,
+                      int d_dtype, int accumulate, int mode, void *stream);
+
+/*
  * permute_pad -- fused permute + pad ([FLOW] "Core method": expert reordering
  * fused with 16-aligned padding, on row-wise FP8 with its scales).
  *   xq [T, H] codes, xs [T, H/128] scales, topk_idx [T, topk] int32 (device)

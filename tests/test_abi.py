@@ -79,6 +79,16 @@ def test_gemm_validation():
     assert call(ag=1, bg=1, sa=_fake(0x1001)) == 1  # 1x32 scales need 4-byte alignment
     assert L.fp8_grouped_gemm(f, f, f, f, f, 0, 100, 256, 512, f, 1, 0, None) == 1
     assert L.fp8_grouped_gemm(f, f, f, f, f, 4, 100, 256, 512, f, 1, 5, None) == 2
+    kg = lambda G=4, M=256, N=256, Kc=1024, dt=0, acc=0, mode=0, a=f: L.fp8_kgrouped_gemm(
+        a, f, f, f, f, G, M, N, Kc, f, dt, acc, mode, None)
+    assert kg(G=0) == 1 and kg(G=1025) == 1
+    assert kg(Kc=1000) == 1          # K capacity must be a multiple of 128
+    assert kg(M=0) == 1
+    assert kg(Kc=1 << 24) == 1       # 256 * K_cap must stay below 2^32
+    assert kg(a=_fake(0x1008)) == 1  # codes 16-byte aligned
+    assert kg(dt=1, acc=1) == 2      # accumulate needs FP32 output
+    assert kg(mode=3) == 2
+    assert kg(a=None) == 1
 
 
 def test_transpose_and_moe_validation():

@@ -233,12 +233,12 @@ def test_grouped_direct_transpose(fgb, T, C):
     topk, G = 8, 32
     idx, _ = synth.routing(T=T, E=G, topk=topk, seed=T + 7)
     xq, xs = synth.wgrad_codes(T, C, seed=T + 8)
-    M_cap = T * topk + 15 * G
-    ws = torch.empty(fgb.permute_pad_workspace_size(T, topk, G), dtype=torch.uint8, device=DEV)
-    pq, ps, rmap, offs = fgb.permute_pad(xq.to(DEV), xs.to(DEV), torch.from_numpy(idx).to(DEV), G, 16, M_cap, ws)
-    qt, st, koff = fgb.fp8_grouped_direct_transpose(pq, ps, offs)
+    # the permuted, padded layout both sides start from (rows past off[G] stay 0xCD)
+    pq, ps, _, offs, _ = O.permute_pad(xq.numpy(), xs.numpy(), idx, G, 16)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    qt, st, koff = fgb.fp8_grouped_direct_transpose(t(pq), t(ps), t(offs))
     K_cap = qt.shape[1]
-    oqt, ost, okoff = O.grouped_direct_transpose(np_(pq), np_(ps), np_(offs), K_cap)
+    oqt, ost, okoff = O.grouped_direct_transpose(pq, ps, offs, K_cap)
     k = int(okoff[-1])
     assert np.array_equal(np_(koff), okoff)
     assert np.array_equal(np_(st)[:, :k // 128], ost[:, :k // 128])
@@ -507,16 +507,15 @@ def test_unpermute_backward(fgb, T, H, weighted):
     say("unpermute_backward", T, H, weighted)
     topk, G = 8, 32
     idx, probs = synth.routing(T=T, E=G, topk=topk, seed=T)
-    xq = torch.zeros((T, H), dtype=torch.uint8, device=DEV)
-    xs = torch.zeros((T, H // 128), dtype=torch.uint8, device=DEV)
     M_cap = T * topk + 15 * G
-    ws = torch.empty(fgb.permute_pad_workspace_size(T, topk, G), dtype=torch.uint8, device=DEV)
-    _, _, rmap, offs = fgb.permute_pad(xq, xs, torch.from_numpy(idx).to(DEV), G, 16, M_cap, ws)
+    # the row map of the forward permute (codes irrelevant here: one 128-column block)
+    z = np.zeros((T, 128), np.uint8)
+    _, _, rmap, _, _ = O.permute_pad(z, z[:, :1], idx, G, 16, M_cap)
     g = torch.Generator().manual_seed(T + H)
     dout = torch.randn((T, H), generator=g).to(torch.bfloat16)
     pr = torch.from_numpy(probs).to(DEV) if weighted else None
-    dy = fgb.unpermute_backward(dout.to(DEV), rmap, pr, M_cap)
-    ref = O.unpermute_backward(bits(dout), np_(rmap), probs if weighted else None, M_cap)
+    dy = fgb.unpermute_backward(dout.to(DEV), torch.from_numpy(rmap).to(DEV), pr, M_cap)
+    ref = O.unpermute_backward(bits(dout), rmap, probs if weighted else None, M_cap)
     assert np.array_equal(np_(dy), ref)
 
 
@@ -615,6 +614,84 @@ def test_grouped_gemm_moe_fc1_sampled(fgb, mode):
                                                                mi[sel], ni[sel])
         bounds = (rm, asum)
     check_gemm(d[mi, ni], ref, mode, True, bounds, K)
+
+
+def _kgrouped_bounds(a, sa, b, sb, koff, ei, mi, ni):
+    """FP8-unit error bounds of the sampled K-grouped products, expert by expert."""
+    rm = np.zeros(mi.size)
+    asum = np.zeros(mi.size)
+    for e in range(len(koff) - 1):
+        sel = ei == e
+        k0, k1 = int(koff[e]), int(koff[e + 1])
+        if sel.any() and k1 > k0:
+            rm[sel], asum[sel] = O.gemm_run_bounds_sampled(
+                a[:, k0:k1], sa[:, k0 // 128:k1 // 128], O.ROW1x128, b[:, k0:k1], sb[:, k0 // 128:k1 // 128],
+                O.ROW1x128, mi[sel], ni[sel])
+    return rm, asum
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_kgrouped_gemm_small(fgb, mode, accumulate):
+    say("k-grouped gemm small: ragged M and N, one empty expert", mode, accumulate)
+    M, N, K_cap = 300, 320, 1024
+    koff = np.array([0, 128, 128, 512, 896], np.int32)  # columns past 896 are never read
+    G = len(koff) - 1
+    a = rand_codes((M, K_cap), 61)
+    sa = rand_scales((M, K_cap // 128), -6, 6, 62)
+    b = rand_codes((N, K_cap), 63)
+    sb = rand_scales((N, K_cap // 128), -6, 6, 64)
+    init = torch.randn((G, M, N), generator=torch.Generator().manual_seed(65))
+    d = init.clone().to(DEV)
+    fgb.fp8_kgrouped_gemm(a.to(DEV), sa.to(DEV), b.to(DEV), sb.to(DEV), torch.from_numpy(koff).to(DEV), d=d,
+                          accumulate=accumulate, mode=_mode(fgb, mode))
+    got = np_(d).astype(np.float64).ravel()
+    if accumulate:
+        got = got - init.numpy().astype(np.float64).ravel()  # exact: |d| is far above the product's rounding
+    ei = np.repeat(np.arange(G), M * N)
+    mi = np.tile(np.repeat(np.arange(M), N), G)
+    ni = np.tile(np.arange(N), G * M)
+    ref = O.kgrouped_gemm_sampled(a.numpy(), sa.numpy(), b.numpy(), sb.numpy(), koff, ei, mi, ni)
+    assert np.all(got.reshape(G, M, N)[1] == 0.0)  # the empty expert
+    bounds = None
+    if mode == "fast":
+        bounds = _kgrouped_bounds(a.numpy(), sa.numpy(), b.numpy(), sb.numpy(), koff, ei, mi, ni)
+    if accumulate:
+        # D += P rounds once more in FP32: allow one FP32 ulp of |init + P| on top
+        tol = np.abs(init.numpy().ravel().astype(np.float64)) * 2.0 ** -23 + np.abs(ref) * 2.0 ** -23
+        if mode == "exact":
+            assert np.all(np.abs(got - ref) <= tol + 1e-5 * np.max(np.abs(ref)))
+        else:
+            rm, asum = bounds
+            assert np.all(np.abs(got - ref) <= tol + 2.0 ** -10 * rm + (K_cap / 8 + 4) * 2.0 ** -24 * asum)
+    else:
+        check_gemm(got, ref, mode, False, bounds, K_cap)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_kgrouped_gemm_moe_wgrad_sampled(fgb, mode):
+    say("k-grouped gemm: Wgrad of fc1 of the 32-expert layer (M=4096, N=7168), sampled", mode)
+    T, G, topk, M, N = 16384, 32, 8, 4096, 7168
+    idx, _ = synth.routing(T, G, topk, 1.1, 0)
+    seg = (np.bincount(idx.ravel(), minlength=G) + 15) // 16 * 16  # padded expert segments
+    koff = np.concatenate([[0], np.cumsum((seg + 127) // 128 * 128)]).astype(np.int32)
+    K_cap = fgb.grouped_k_cap(T * topk + 15 * G, G)
+    assert koff[-1] <= K_cap
+    a = rand_codes((M, K_cap), 71)
+    sa = rand_scales((M, K_cap // 128), -20, 4, 72)
+    b = rand_codes((N, K_cap), 73)
+    sb = rand_scales((N, K_cap // 128), -8, 2, 74)
+    d = np_(fgb.fp8_kgrouped_gemm(a.to(DEV), sa.to(DEV), b.to(DEV), sb.to(DEV), torch.from_numpy(koff).to(DEV),
+                                  out_dtype=torch.bfloat16, mode=_mode(fgb, mode)))
+    rng = np.random.default_rng(5)
+    ei = np.concatenate([rng.integers(0, G, 1500), np.arange(G), np.arange(G)])
+    mi = np.concatenate([rng.integers(0, M, 1500), np.zeros(G, np.int64), np.full(G, M - 1)])
+    ni = np.concatenate([rng.integers(0, N, 1500), np.full(G, N - 1), np.zeros(G, np.int64)])
+    ref = O.kgrouped_gemm_sampled(a.numpy(), sa.numpy(), b.numpy(), sb.numpy(), koff, ei, mi, ni)
+    bounds = None
+    if mode == "fast":
+        bounds = _kgrouped_bounds(a.numpy(), sa.numpy(), b.numpy(), sb.numpy(), koff, ei, mi, ni)
+    check_gemm(d[ei, mi, ni], ref, mode, True, bounds, int(np.max(np.diff(koff))))
 
 
 # ---------------------------------------------------------------------------
