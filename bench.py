@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--gemm-mode", choices=["exact", "fast"], default="exact")
-    ap.add_argument("--parts", default="linear,moe,wgrad,moss")
+    ap.add_argument("--parts", default="linear,moe,moe_bwd,wgrad,moss")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-study", action="store_true", help="skip the untimed transpose comparison")
     ap.add_argument("--seed", type=int, default=0)
@@ -104,6 +104,12 @@ def build(fgb, torch, synth, dev, seed, parts):
                         ws=torch.empty(fgb.permute_pad_workspace_size(T, topk, G), dtype=torch.uint8,
                                        device=dev),
                         counts=torch.from_numpy(__import__("numpy").bincount(idx.ravel(), minlength=G)))
+    if "moe_bwd" in parts:
+        if "moe" not in W:
+            raise SystemExit("--parts: moe_bwd needs moe (the backward reads the forward's tensors)")
+        E = W["moe"]
+        E["dO"] = synth.moe_grad(seed, device=dev)
+        E["ws_bwd"] = torch.empty(fgb.unpermute_backward_workspace_size(E["M_cap"]), dtype=torch.uint8, device=dev)
     if "wgrad" in parts:
         xq, xs = synth.wgrad_codes(32768, 7168, seed, 41, device=dev)
         gq, gs = synth.wgrad_codes(32768, 2048, seed, 42, device=dev)
@@ -157,13 +163,51 @@ def step(fgb, torch, W, rec, mode):
                                  fgb.permute_pad, xq, xs, E["idx"], G, 16, M_cap, E["ws"])
         h = rec("moe.grouped_gemm fc1", "mfma", 2 * rows * N1 * H, fgb.fp8_grouped_gemm, pq, ps,
                 w1q.view(G, N1, H), w1s.view(G, N1 // 128, H // 128), offs, mode=gm)
-        aq, as_ = rec("moe.swiglu_quant", "hbm", pad_rows * (2 * F * 2 + F * (1 + 1 / 128)), fgb.swiglu_quant,
-                      h, offs)
+        bwd = "dO" in E
+        if bwd:  # the backward recomputes SwiGLU from an FP8 copy of h written by the same pass
+            aq, as_, hq, hs = rec("moe.swiglu_quant+cache", "hbm",
+                                  pad_rows * (2 * F * 2 + F * (1 + 1 / 128) + 2 * F * (1 + 1 / 128)),
+                                  fgb.swiglu_quant_cache, h, offs)
+        else:
+            aq, as_ = rec("moe.swiglu_quant", "hbm", pad_rows * (2 * F * 2 + F * (1 + 1 / 128)),
+                          fgb.swiglu_quant, h, offs)
         y = rec("moe.grouped_gemm fc2", "mfma", 2 * rows * N2 * F, fgb.fp8_grouped_gemm, aq, as_,
                 w2q.view(G, N2, F), w2s.view(G, N2 // 128, F // 128), offs, mode=gm)
         o = rec("moe.unpermute_unpad", "hbm", T * topk * H * 2 + T * H * 2 + 8 * T * topk, fgb.unpermute_unpad,
                 y, rmap, E["probs"])
         out["moe"] = (o, offs)
+        if bwd:
+            # expert backward: Dgrad and K-grouped Wgrad of both expert linears, all operands FP8
+            dyq, dys = rec("moe_bwd.unpermute_backward_quant dO", "hbm",
+                           T * H * 2 + M_cap * H * (1 + 1 / 128) + 8 * T * topk,
+                           fgb.unpermute_backward_quant, E["dO"], rmap, E["probs"], M_cap, workspace=E["ws_bwd"])
+            w2t, w2ts = rec("moe_bwd.transpose W2 (batched blocks)", "hbm",
+                            2 * E["W2"].numel() + 2 * E["W2"].numel() // 16384, fgb.fp8_block_transpose_batched,
+                            w2q.view(G, N2, F), w2s.view(G, N2 // 128, F // 128))
+            da = rec("moe_bwd.grouped_gemm fc2 dgrad", "mfma", 2 * rows * F * N2, fgb.fp8_grouped_gemm, dyq, dys,
+                     w2t, w2ts, offs, mode=gm)
+            dyt, dyts, koff = rec("moe_bwd.grouped_direct_transpose dY", "hbm", 2 * pad_rows * H * (1 + 1 / 128),
+                                  fgb.fp8_grouped_direct_transpose, dyq, dys, offs)
+            at, ats, _ = rec("moe_bwd.grouped_direct_transpose A", "hbm", 2 * pad_rows * F * (1 + 1 / 128),
+                             fgb.fp8_grouped_direct_transpose, aq, as_, offs)
+            dw2 = rec("moe_bwd.kgrouped_gemm fc2 wgrad", "mfma", 2 * rows * N2 * F, fgb.fp8_kgrouped_gemm, dyt, dyts,
+                      at, ats, koff, mode=gm)
+            dhq, dhs = rec("moe_bwd.dswiglu_quant", "hbm", pad_rows * (6 * F + 4 * F / 128), fgb.dswiglu_quant,
+                           hq, hs, da, offs)
+            w1t, w1ts = rec("moe_bwd.transpose W1 (batched blocks)", "hbm",
+                            2 * E["W1"].numel() + 2 * E["W1"].numel() // 16384, fgb.fp8_block_transpose_batched,
+                            w1q.view(G, N1, H), w1s.view(G, N1 // 128, H // 128))
+            dxp = rec("moe_bwd.grouped_gemm fc1 dgrad", "mfma", 2 * rows * H * N1, fgb.fp8_grouped_gemm, dhq, dhs,
+                      w1t, w1ts, offs, mode=gm)
+            dht, dhts, _ = rec("moe_bwd.grouped_direct_transpose dH", "hbm", 2 * pad_rows * N1 * (1 + 1 / 128),
+                               fgb.fp8_grouped_direct_transpose, dhq, dhs, offs)
+            xt, xts, _ = rec("moe_bwd.grouped_direct_transpose X", "hbm", 2 * pad_rows * H * (1 + 1 / 128),
+                             fgb.fp8_grouped_direct_transpose, pq, ps, offs)
+            dw1 = rec("moe_bwd.kgrouped_gemm fc1 wgrad", "mfma", 2 * rows * N1 * H, fgb.fp8_kgrouped_gemm, dht, dhts,
+                      xt, xts, koff, mode=gm)
+            dx = rec("moe_bwd.unpermute_unpad dX (permute backward)", "hbm",
+                     T * topk * H * 2 + T * H * 2 + 4 * T * topk, fgb.unpermute_unpad, dxp, rmap, None)
+            out["moe_bwd"] = (dx, dw1, dw2)
     if "wg" in W:
         Wg = W["wg"]
         T, Cin = Wg["xq"].shape
@@ -245,6 +289,13 @@ def cpu_baseline(torch, synth, seed, kernel_results, step_floor_s):
     t = time.perf_counter(); O.unpermute_unpad(y, rm, probs); rates["unpermute"] = (2048 * 8 * 7168 * 2) / (time.perf_counter() - t)
     h = synth.bf16_bits(torch.randn(512, 4096).to(torch.bfloat16))
     t = time.perf_counter(); O.swiglu_quant(h); rates["swiglu"] = h.size * 2 * 1.25 / (time.perf_counter() - t)
+    hq, hs = O.quant_rowwise(h, 128)
+    da = synth.bf16_bits(torch.randn(512, 2048).to(torch.bfloat16))
+    t = time.perf_counter(); O.dswiglu_quant(hq, hs, da, None)
+    rates["dswiglu"] = 512 * (6 * 2048 + 4 * 2048 / 128) / (time.perf_counter() - t)
+    M_cap = 2048 * 8 + 15 * 32
+    t = time.perf_counter(); O.quant_rowwise(O.unpermute_backward(y[:2048], rm, probs, M_cap), 128)
+    rates["unpermute_bwd"] = (2048 * 7168 * 2 + M_cap * 7168 * (1 + 1 / 128)) / (time.perf_counter() - t)
     Wm, _ = synth.moss(seed, R=64, C=8192, M=1)
     wmb = synth.bf16_bits(Wm)
     t = time.perf_counter(); q, s2, s1 = O.mx2_quant(wmb, 10240); rates["mx2"] = wmb.size * 3 / (time.perf_counter() - t)
@@ -252,7 +303,8 @@ def cpu_baseline(torch, synth, seed, kernel_results, step_floor_s):
 
     def fam(name):
         for key, f in [("gemm", "gemm"), ("transpose", "transpose"), ("quant_blockwise", "quant_blockwise"),
-                       ("quant_rowwise", "quant_rowwise"), ("permute_pad", "permute"), ("unpermute", "unpermute"),
+                       ("quant_rowwise", "quant_rowwise"), ("permute_pad", "permute"),
+                       ("unpermute_backward", "unpermute_bwd"), ("unpermute", "unpermute"), ("dswiglu", "dswiglu"),
                        ("swiglu", "swiglu"), ("mx2", "mx2")]:
             if key in name:
                 return f
@@ -268,10 +320,12 @@ def cpu_baseline(torch, synth, seed, kernel_results, step_floor_s):
             "rates": {"quant_rowwise_GBps": rates["quant_rowwise"] / 1e9, "transpose_GBps": rates["transpose"] / 1e9,
                       "gemm_GFLOPs": rates["gemm"] / 1e9, "permute_GBps": rates["permute"] / 1e9,
                       "unpermute_GBps": rates["unpermute"] / 1e9, "swiglu_GBps": rates["swiglu"] / 1e9,
-                      "mx2_GBps": rates["mx2"] / 1e9, "quant_blockwise_GBps": rates["quant_blockwise"] / 1e9},
+                      "mx2_GBps": rates["mx2"] / 1e9, "quant_blockwise_GBps": rates["quant_blockwise"] / 1e9,
+                      "dswiglu_GBps": rates["dswiglu"] / 1e9, "unpermute_backward_quant_GBps": rates["unpermute_bwd"] / 1e9},
             "sample": ("single-threaded oracle on: 256x7168 bf16 quant (row and block) and direct transpose, "
                        "2000 sampled outputs of the 7168-deep Fprop, permute_pad of 2048 tokens top-8, "
-                       "unpermute of 2048 tokens, SwiGLU+quant of 512x4096, MOSS quant of 64x8192; "
+                       "unpermute of 2048 tokens, SwiGLU+quant of 512x4096, SwiGLU backward of 512x4096, "
+                       "unpermute backward + quant of 2048 tokens, MOSS quant of 64x8192; "
                        f"{sample_s:.1f} s; step time extrapolated from the per-op rates")}
 
 
@@ -421,7 +475,7 @@ def main():
         "dtype": "e4m3",
         "data": "synthetic (seeded; shapes and distributions of the DeepSeek-V3 / MoE / MOSS layers)",
         "config": {"workload": ("dsv3-linear T8192 Cin7168 Cout2048 (fwd+bwd) + moe 16384 tok top-8 of 32 "
-                                "experts H7168 F2048 (fwd) + wgrad T32768 Cin7168 Cout2048 + moss W^T 28672x8192 "
+                                "experts H7168 F2048 (fwd" + ("+bwd" if "moe_bwd" in parts else "") + ") + wgrad T32768 Cin7168 Cout2048 + moss W^T 28672x8192 "
                                 "A 4096x8192"),
                    "parts": sorted(parts), "gemm_mode": args.gemm_mode,
                    "gemm_contraction": "bf16 MFMA on exact scaled fp8->bf16 operands" if args.gemm_mode == "exact"

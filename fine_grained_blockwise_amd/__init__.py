@@ -19,7 +19,8 @@ __all__ = [
     "fp8_block_gemm", "fp8_grouped_gemm", "permute_pad",
     "permute_pad_workspace_size", "unpermute_unpad", "swiglu_quant", "dswiglu_quant", "mx2_quant",
     "mx2_dequant", "unpermute_backward", "unpermute_backward_workspace_size",
-    "fp8_block_transpose_batched", "fp8_grouped_direct_transpose", "fp8_kgrouped_gemm", "F32", "BF16", "ROW1x128", "ROW1x32", "BLOCK128", "GEMM_EXACT", "GEMM_FAST",
+    "fp8_block_transpose_batched", "fp8_grouped_direct_transpose", "fp8_kgrouped_gemm", "swiglu_quant_cache",
+    "unpermute_backward_quant", "F32", "BF16", "ROW1x128", "ROW1x32", "BLOCK128", "GEMM_EXACT", "GEMM_FAST",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,7 +36,7 @@ SYMBOLS = [
     "permute_pad", "permute_pad_workspace_size", "unpermute_unpad", "swiglu_quant", "mx2_quant",
     "mx2_dequant", "fp8_naive_transpose", "fp8_naive_transpose_workspace_size", "dswiglu_quant",
     "unpermute_backward", "unpermute_backward_workspace_size", "fp8_block_transpose_batched",
-    "fp8_grouped_direct_transpose", "fp8_kgrouped_gemm",
+    "fp8_grouped_direct_transpose", "fp8_kgrouped_gemm", "swiglu_quant_cache", "unpermute_backward_quant",
 ]
 
 
@@ -75,6 +76,8 @@ _SIG = {
     "unpermute_backward": (_i32, [_p, _p, _p, _i64, _i32, _i64, _i64, _p, _p, _sz, _p]),
     "unpermute_backward_workspace_size": (_sz, [_i64]),
     "swiglu_quant": (_i32, [_p, _i64, _i64, _i64, _p, _i32, _p, _p, _p]),
+    "swiglu_quant_cache": (_i32, [_p, _i64, _i64, _i64, _p, _i32, _p, _p, _p, _p, _p]),
+    "unpermute_backward_quant": (_i32, [_p, _p, _p, _i64, _i32, _i64, _i64, _p, _p, _p, _sz, _p]),
     "dswiglu_quant": (_i32, [_p, _p, _p, _i64, _i64, _p, _i32, _p, _p, _p]),
     "mx2_quant": (_i32, [_p, _i64, _i64, _i64, _p, _p, _p, _p]),
     "mx2_dequant": (_i32, [_p, _p, _p, _i64, _i64, _i64, _p, _p]),
@@ -352,6 +355,45 @@ def unpermute_backward(dout, row_map, probs, M_cap, dy=None, workspace=None):
           _ptr(None if probs is None else probs.contiguous()), T, topk, H, M_cap, _ptr(dy), _ptr(workspace),
           workspace.numel(), _stream(dout))
     return dy
+
+
+def unpermute_backward_quant(dout, row_map, probs, M_cap, q=None, s=None, workspace=None):
+    """unpermute_backward + 1x128 quant in one pass: dout bf16 [T, H] -> (q [M_cap, H], s [M_cap, H/128])."""
+    _check_dev(dout, row_map, probs, q, s)
+    for t in (dout, row_map, probs):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("unpermute_backward_quant: inputs must be contiguous")
+    T, H = dout.shape
+    topk = row_map.shape[1]
+    if q is None:
+        q = torch.empty((M_cap, H), dtype=torch.uint8, device=dout.device)
+    if s is None:
+        s = torch.empty((M_cap, H // 128), dtype=torch.uint8, device=dout.device)
+    if workspace is None:
+        workspace = torch.empty(max(unpermute_backward_workspace_size(M_cap), 1), dtype=torch.uint8,
+                                device=dout.device)
+    _call("unpermute_backward_quant", _ptr(dout), _ptr(row_map), _ptr(probs), T, topk, H, M_cap, _ptr(q),
+          _ptr(s), _ptr(workspace), workspace.numel(), _stream(dout))
+    return q, s
+
+
+def swiglu_quant_cache(h, group_offsets=None, q=None, s=None, hq=None, hs=None):
+    """swiglu_quant that also returns the FP8 cache of h: -> (q [M, F], s, hq [M, 2F], hs [M, 2F/128])."""
+    _check_dev(h, group_offsets, q, s, hq, hs)
+    M, F2 = h.shape
+    F = F2 // 2
+    if q is None:
+        q = torch.empty((M, F), dtype=torch.uint8, device=h.device)
+    if s is None:
+        s = torch.empty((M, F // 128), dtype=torch.uint8, device=h.device)
+    if hq is None:
+        hq = torch.empty((M, F2), dtype=torch.uint8, device=h.device)
+    if hs is None:
+        hs = torch.empty((M, F2 // 128), dtype=torch.uint8, device=h.device)
+    G = 0 if group_offsets is None else group_offsets.numel() - 1
+    _call("swiglu_quant_cache", _ptr(h), M, F, _row_ld(h), _ptr(group_offsets), G, _ptr(q), _ptr(s), _ptr(hq),
+          _ptr(hs), _stream(h))
+    return q, s, hq, hs
 
 
 def swiglu_quant(h, group_offsets=None, q=None, s=None):

@@ -148,13 +148,16 @@ gemm_fp8_kernel(GemmArgs p)
     // Within an XCD's contiguous range, tiles run in bands of GM m-tiles:
     // consecutive tiles walk down a band first, so the ~32 tiles an XCD runs
     // at once form a GM x 8 block sharing A rows and B columns in L2.
-    int64_t tile = xcd_remap(blockIdx.x, gridDim.x);
+    // K-grouped: workgroups run expert by expert, and the remap applies inside
+    // each expert's range, so every expert's tiles spread over all XCDs
+    // (expert K ranges differ widely; whole experts per XCD would unbalance them).
     int64_t tiles_here = gridDim.x;
     int ke = 0; // K-grouped: this workgroup's expert, whose K range is [koffs[ke], koffs[ke+1])
-    if constexpr (GK == GK_K) {
+    if constexpr (GK == GK_K)
         tiles_here = gridDim.x / p.G;
-        ke = (int)(tile / tiles_here);
-        tile %= tiles_here;
+    int64_t tile = xcd_remap(blockIdx.x % tiles_here, tiles_here);
+    if constexpr (GK == GK_K) {
+        ke = (int)(blockIdx.x / tiles_here);
         kbeg = p.koffs[ke];
         nk = (p.koffs[ke + 1] - kbeg) / BK;
     }

@@ -325,14 +325,34 @@ __device__ __forceinline__ float silu_mul(float g, float u)
     return s * u;
 }
 
+// 1x128 quantization of the 8 values a lane holds, 16 lanes forming one
+// group: returns the codes and the group's scale exponent.
+__device__ __forceinline__ uint2 quant8_group16(const float (&v)[8], int &e)
+{
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < 8; k++)
+        m = max(m, __float_as_uint(v[k]) & 0x7FFFFFFFu);
+    m = group_max_u32<16>(m);
+    e = scale_exp_from_bits(m, -22);
+    const float sc = pow2f(-e);
+    return make_uint2(cvt4_e4m3(v[0] * sc, v[1] * sc, v[2] * sc, v[3] * sc),
+                      cvt4_e4m3(v[4] * sc, v[5] * sc, v[6] * sc, v[7] * sc));
+}
+
 // One wave per row; lane owns 8 gate and the matching 8 up values (16-byte
-// loads); 16 lanes form one 128-element output group.
+// loads); 16 lanes form one 128-element output group.  CACHE: the same pass
+// also writes the 1x128 quantization of the input row [g | u] (the FP8 copy
+// the backward recomputes the activation from).
 constexpr int SW_U = 4; // 16-byte chunks of gate and of up in flight per lane
+template <bool CACHE>
 __global__ __launch_bounds__(256) void swiglu_quant_kernel(const uint8_t *__restrict__ h, int64_t M,
                                                            int64_t F, int64_t ldh_bytes,
                                                            const int32_t *__restrict__ offs, int G,
                                                            uint8_t *__restrict__ q,
-                                                           uint8_t *__restrict__ s)
+                                                           uint8_t *__restrict__ s,
+                                                           uint8_t *__restrict__ hq,
+                                                           uint8_t *__restrict__ hs)
 {
     const int lane = lane_id();
     const int64_t rows = offs ? (int64_t)offs[G] : M;
@@ -373,6 +393,26 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(const uint8_t *__rest
                     st_stream8(q + r * F + c * 8, o);
                     if ((lane & 15) == 0)
                         s[r * (F / 128) + c / 16] = (uint8_t)(e + 127);
+                }
+                if constexpr (CACHE) {
+                    float gf[8], uf[8];
+#pragma unroll
+                    for (int x = 0; x < 4; x++) {
+                        gf[2 * x] = bf16lo(gw[x]);
+                        gf[2 * x + 1] = bf16hi(gw[x]);
+                        uf[2 * x] = bf16lo(uw[x]);
+                        uf[2 * x + 1] = bf16hi(uw[x]);
+                    }
+                    int eg, eu;
+                    const uint2 og = quant8_group16(gf, eg), ou = quant8_group16(uf, eu);
+                    if (c < F8) {
+                        st_stream8(hq + r * 2 * F + c * 8, og);
+                        st_stream8(hq + r * 2 * F + F + c * 8, ou);
+                        if ((lane & 15) == 0) {
+                            hs[r * (F / 64) + c / 16] = (uint8_t)(eg + 127);
+                            hs[r * (F / 64) + F / 128 + c / 16] = (uint8_t)(eu + 127);
+                        }
+                    }
                 }
             }
         }
@@ -534,6 +574,62 @@ __global__ __launch_bounds__(256) void ub_gather_kernel(const uint16_t *__restri
     }
 }
 
+// As ub_gather_kernel, then 1x128 quantization of each bf16 row: padding
+// rows become code 0 with scale byte 105, as a zero row quantizes.
+constexpr int UBQ_U = 2;
+__global__ __launch_bounds__(256) void ub_gather_quant_kernel(const uint16_t *__restrict__ dout,
+                                                              const int32_t *__restrict__ inv,
+                                                              const float *__restrict__ probs, int topk, int64_t H,
+                                                              int64_t M_cap, uint8_t *__restrict__ q,
+                                                              uint8_t *__restrict__ s)
+{
+    const int lane = lane_id();
+    const int64_t H8 = H / 8;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    for (int64_t r = wave; r < M_cap; r += nwaves) {
+        const int32_t si = inv[r];
+        uint8_t *dq = q + r * H;
+        uint8_t *dsc = s + r * (H / 128);
+        if (si < 0) {
+            for (int64_t c = lane; c < H / 16; c += 64)
+                st_stream16(dq + c * 16, make_uint4(0, 0, 0, 0));
+            for (int64_t c = lane; c < H / 128; c += 64)
+                dsc[c] = 105;
+            continue;
+        }
+        const float w = probs ? probs[si] : 1.0f;
+        const uint16_t *src = dout + (int64_t)(si / topk) * H;
+        for (int64_t c0 = 0; c0 < H8; c0 += 64 * UBQ_U) {
+            uint4 v[UBQ_U];
+#pragma unroll
+            for (int u = 0; u < UBQ_U; u++) {
+                const int64_t c = c0 + u * 64 + lane;
+                v[u] = c < H8 ? *reinterpret_cast<const uint4 *>(src + c * 8) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < UBQ_U; u++) {
+                const int64_t c = c0 + u * 64 + lane;
+                const uint32_t x4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+                float y[8];
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    // the bf16 value of the unfused gradient, then its quantization
+                    y[2 * k] = bf16lo(bf16_rne(w * bf16lo(x4[k])));
+                    y[2 * k + 1] = bf16lo(bf16_rne(w * bf16hi(x4[k])));
+                }
+                int e;
+                const uint2 o = quant8_group16(y, e);
+                if (c < H8) {
+                    st_stream8(dq + c * 8, o);
+                    if ((lane & 15) == 0)
+                        dsc[c / 16] = (uint8_t)(e + 127);
+                }
+            }
+        }
+    }
+}
+
 } // namespace fgb
 
 using namespace fgb;
@@ -625,9 +721,33 @@ extern "C" int swiglu_quant(const void *h, int64_t M, int64_t F, int64_t ldh,
         return FGB_OK;
     int64_t grid = (M + 3) / 4;
     grid = grid < 16384 ? grid : 16384;
-    swiglu_quant_kernel<<<(unsigned)grid, 256, 0, (hipStream_t)stream>>>((const uint8_t *)h, M, F, ldh * 2,
-                                                                         group_offsets, G, q, s);
+    swiglu_quant_kernel<false><<<(unsigned)grid, 256, 0, (hipStream_t)stream>>>((const uint8_t *)h, M, F, ldh * 2,
+                                                                                group_offsets, G, q, s, nullptr,
+                                                                                nullptr);
     FGB_LAUNCHED("swiglu_quant");
+    return FGB_OK;
+}
+
+extern "C" int swiglu_quant_cache(const void *h, int64_t M, int64_t F, int64_t ldh,
+                                  const int32_t *group_offsets, int G, uint8_t *q, uint8_t *s,
+                                  uint8_t *hq, uint8_t *hs, void *stream)
+{
+    clear_error();
+    FGB_REQUIRE(h && q && s && hq && hs, FGB_EINVAL, "swiglu_quant_cache: null pointer");
+    FGB_REQUIRE(M >= 0 && F > 0 && F % 128 == 0, FGB_EINVAL,
+                "swiglu_quant_cache: F must be a positive multiple of 128");
+    FGB_REQUIRE(ldh >= 2 * F && ldh % 8 == 0, FGB_EINVAL,
+                "swiglu_quant_cache: ldh must be >= 2F and a multiple of 8");
+    FGB_REQUIRE(!group_offsets || G >= 1, FGB_EINVAL, "swiglu_quant_cache: G must be >= 1 with group_offsets");
+    FGB_REQUIRE(aligned16(h) && aligned16(q) && aligned16(hq), FGB_EINVAL,
+                "swiglu_quant_cache: h, q and hq must be 16-byte aligned");
+    if (M == 0)
+        return FGB_OK;
+    int64_t grid = (M + 3) / 4;
+    grid = grid < 16384 ? grid : 16384;
+    swiglu_quant_kernel<true><<<(unsigned)grid, 256, 0, (hipStream_t)stream>>>((const uint8_t *)h, M, F, ldh * 2,
+                                                                               group_offsets, G, q, s, hq, hs);
+    FGB_LAUNCHED("swiglu_quant_cache");
     return FGB_OK;
 }
 
@@ -683,5 +803,39 @@ extern "C" int unpermute_backward(const void *dout, const int32_t *row_map, cons
     ub_gather_kernel<<<(unsigned)(g3 < 16384 ? g3 : 16384), 256, 0, st>>>((const uint16_t *)dout, inv, probs, topk,
                                                                            H, M_cap, (uint16_t *)dy);
     FGB_LAUNCHED("unpermute_backward");
+    return FGB_OK;
+}
+
+extern "C" int unpermute_backward_quant(const void *dout, const int32_t *row_map, const float *probs, int64_t T,
+                                        int topk, int64_t H, int64_t M_cap, uint8_t *q, uint8_t *s,
+                                        void *workspace, size_t ws_bytes, void *stream)
+{
+    clear_error();
+    FGB_REQUIRE(dout && row_map && q && s, FGB_EINVAL, "unpermute_backward_quant: null pointer");
+    FGB_REQUIRE(T >= 0 && topk >= 1 && topk <= 64 && H > 0 && H % 128 == 0 && M_cap >= 0, FGB_EINVAL,
+                "unpermute_backward_quant: need topk in [1, 64] and H a positive multiple of 128");
+    FGB_REQUIRE(T * topk < (1ll << 31) && M_cap < (1ll << 31), FGB_EINVAL,
+                "unpermute_backward_quant: too many rows");
+    FGB_REQUIRE(aligned16(dout) && aligned16(q), FGB_EINVAL,
+                "unpermute_backward_quant: dout and q must be 16-byte aligned");
+    if (M_cap == 0)
+        return FGB_OK;
+    FGB_REQUIRE(workspace && ws_bytes >= unpermute_backward_workspace_size(M_cap), FGB_EWORKSPACE,
+                "unpermute_backward_quant: workspace must hold %zu bytes",
+                unpermute_backward_workspace_size(M_cap));
+    hipStream_t st = (hipStream_t)stream;
+    int32_t *inv = (int32_t *)workspace;
+    int64_t g1 = (M_cap + 255) / 256;
+    ub_fill_kernel<<<(unsigned)(g1 < 4096 ? g1 : 4096), 256, 0, st>>>(inv, M_cap);
+    FGB_LAUNCHED("unpermute_backward_quant");
+    if (T > 0) {
+        int64_t g2 = (T * topk + 255) / 256;
+        ub_scatter_kernel<<<(unsigned)(g2 < 4096 ? g2 : 4096), 256, 0, st>>>(row_map, T * topk, M_cap, inv);
+        FGB_LAUNCHED("unpermute_backward_quant");
+    }
+    int64_t g3 = (M_cap + 3) / 4;
+    ub_gather_quant_kernel<<<(unsigned)(g3 < 16384 ? g3 : 16384), 256, 0, st>>>(
+        (const uint16_t *)dout, inv, probs, topk, H, M_cap, q, s);
+    FGB_LAUNCHED("unpermute_backward_quant");
     return FGB_OK;
 }

@@ -307,6 +307,19 @@ int unpermute_backward(const void *dout, const int32_t *row_map, const float *pr
 size_t unpermute_backward_workspace_size(int64_t M_cap);
 
 /*
+ * unpermute_backward_quant -- unpermute_backward followed by 1x128
+ * quantization of its bf16 rows, in one pass ([FLOW] "Core method": the
+ * expert path stays in FP8 from the boundary on; the expert backward's two
+ * GEMMs read dy only as 1x128 FP8).  Bit for bit fp8_quant_rowwise of the dy
+ * unpermute_backward writes: padding and unreferenced rows become code 0x00
+ * with scale byte 105.  q [M_cap, H], s [M_cap, H/128] dense; H % 128 == 0;
+ * workspace as for unpermute_backward; dout and q 16-byte aligned.
+ */
+int unpermute_backward_quant(const void *dout, const int32_t *row_map, const float *probs, int64_t T, int topk,
+                             int64_t H, int64_t M_cap, uint8_t *q, uint8_t *s, void *workspace, size_t ws_bytes,
+                             void *stream);
+
+/*
  * swiglu_quant -- fused SwiGLU + 1x128 quantization ([FLOW] "Core method":
  * the activation emits FP8 directly; assumption 2: the first linear's
  * output is BF16).
@@ -322,6 +335,18 @@ size_t unpermute_backward_workspace_size(int64_t M_cap);
  */
 int swiglu_quant(const void *h, int64_t M, int64_t F, int64_t ldh, const int32_t *group_offsets,
                  int G, uint8_t *q, uint8_t *s, void *stream);
+
+/*
+ * swiglu_quant_cache -- swiglu_quant that also writes, from the same read of
+ * h, the FP8 copy of its input the backward recomputes the activation from
+ * ([DSV3] §3, low-precision activations: the SwiGLU input is cached in FP8).
+ * q, s as in swiglu_quant; hq [M, 2F] and hs [M, 2F/128] (dense) are the
+ * 1x128 quantization of the row [g | u] by the rule of fp8_quant_rowwise,
+ * bit for bit (the hq, hs that dswiglu_quant reads).  Rows >= off[G] are
+ * not written.  h, q and hq 16-byte aligned; F % 128 == 0.
+ */
+int swiglu_quant_cache(const void *h, int64_t M, int64_t F, int64_t ldh, const int32_t *group_offsets,
+                       int G, uint8_t *q, uint8_t *s, uint8_t *hq, uint8_t *hs, void *stream);
 
 /*
  * dswiglu_quant -- SwiGLU backward from the FP8-cached input, emitting FP8

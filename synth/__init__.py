@@ -20,6 +20,8 @@ Recipes (the readings are listed in the design notes):
                 Gumbel-top-k on weights (rank)^-1.1; probs = normalised
                 weights of the chosen experts; W1 bf16 [32, 4096, 7168],
                 W2 bf16 [32, 7168, 2048] N(0, 0.02).
+  moe_grad      dO bf16 [16384, 7168] N(0, 1e-3): the gradient of the MoE
+                layer's output, for the expert backward.
   wgrad_codes   row-wise E4M3 codes [T, C] drawn directly (sign uniform,
                 exponent field 15 - floor(3|z|) clipped at 0, mantissa
                 uniform, NaN pattern excluded) with per-1x128-tile scale bytes
@@ -105,6 +107,11 @@ def moe(seed=0, device="cpu", T=16384, H=7168, F=2048, E=32, topk=8, weights=Tru
         W1 = normal((E, 2 * F, H), 0.02, seed, 32, device, torch.bfloat16)
         W2 = normal((E, H, F), 0.02, seed, 33, device, torch.bfloat16)
     return X, idx, probs, W1, W2
+
+
+def moe_grad(seed=0, device="cpu", T=16384, H=7168):
+    """Gradient of the MoE layer output: dO bf16 [T, H] N(0, 1e-3)."""
+    return normal((T, H), 1e-3, seed, 34, device, torch.bfloat16)
 
 
 def wgrad_codes(T, C, seed=0, stream=41, device="cpu"):

@@ -101,6 +101,12 @@ def test_transpose_and_moe_validation():
     assert L.fp8_block_transpose_batched(f, f, 4, 200, 256, f, f, None) == 1
     assert L.fp8_grouped_direct_transpose(f, f, 1000, 256, f, 8, f, f, 1024, f, None) == 1  # K_cap too small
     assert L.fp8_grouped_direct_transpose(f, f, 1000, 200, f, 8, f, f, 4096, f, None) == 1  # cols % 128
+    assert L.swiglu_quant_cache(f, 64, 256, 512, None, 0, f, f, None, f, None) == 1  # null cache
+    assert L.swiglu_quant_cache(f, 64, 200, 512, None, 0, f, f, f, f, None) == 1    # F % 128
+    assert L.swiglu_quant_cache(f, 64, 256, 512, None, 0, f, f, _fake(0x1008), f, None) == 1  # alignment
+    assert L.unpermute_backward_quant(f, f, None, 64, 8, 200, 1000, f, f, f, 1 << 20, None) == 1  # H % 128
+    assert L.unpermute_backward_quant(f, f, None, 64, 8, 256, 1000, f, f, f, 100, None) == 3  # workspace
+    assert L.unpermute_backward_quant(f, f, None, 64, 0, 256, 1000, f, f, f, 1 << 20, None) == 1  # topk
     # three-pass baseline: shape and workspace checks
     assert fgb.fp8_naive_transpose_workspace_size(256, 384) == 4 * 256 * 384
     assert L.fp8_naive_transpose(f, f, 200, 256, f, f, f, 1 << 20, None) == 1

@@ -535,6 +535,48 @@ def test_swiglu_quant(fgb):
         assert np.array_equal(np_(q), oq)
 
 
+@pytest.mark.parametrize("M,F,use_off", [(70, 256, True), (1000, 2048, False)])
+def test_swiglu_quant_cache(fgb, M, F, use_off):
+    say("swiglu_quant_cache", M, F, use_off)
+    g = torch.Generator().manual_seed(M + 3)
+    h = (torch.randn(M, 2 * F, generator=g) * 4).to(torch.bfloat16)
+    h[0] = 0.0                      # all-zero groups: scale byte 105
+    h[1, :F] = -100.0               # exp(-g) overflows
+    h[2, F:] = 1e-38                # tiny up values
+    h[3, :128] = -448.0 * 2.0 ** 40  # a large group
+    off = np.array([0, 16, 16, 48, 64], np.int32) if use_off else None
+    t_off = None if off is None else torch.from_numpy(off).to(DEV)
+    q, s, hq, hs = fgb.swiglu_quant_cache(h.to(DEV), t_off)
+    oq, os_ = O.swiglu_quant(bits(h), off)
+    ohq, ohs = O.quant_rowwise(bits(h), 128)
+    rows = M if off is None else int(off[-1])
+    assert np.array_equal(np_(s)[:rows], os_[:rows]) and np.array_equal(np_(q)[:rows], oq[:rows])
+    assert np.array_equal(np_(hs)[:rows], ohs[:rows]) and np.array_equal(np_(hq)[:rows], ohq[:rows])
+    # the plain entry point on the same input gives the same activation codes
+    q2, s2 = fgb.swiglu_quant(h.to(DEV), t_off)
+    assert np.array_equal(np_(q2)[:rows], np_(q)[:rows]) and np.array_equal(np_(s2)[:rows], np_(s)[:rows])
+
+
+@pytest.mark.parametrize("T,H,weighted", [(64, 256, True), (2048, 7168, True), (300, 512, False)])
+def test_unpermute_backward_quant(fgb, T, H, weighted):
+    say("unpermute_backward_quant", T, H, weighted)
+    topk, G = 8, 32
+    idx, probs = synth.routing(T=T, E=G, topk=topk, seed=T + 1)
+    M_cap = T * topk + 15 * G
+    z = np.zeros((T, 128), np.uint8)
+    _, _, rmap, _, _ = O.permute_pad(z, z[:, :1], idx, G, 16, M_cap)
+    rmap[0, 1] = -1  # a dropped slot: its row is never referenced
+    g = torch.Generator().manual_seed(T + H + 1)
+    dout = torch.randn((T, H), generator=g).to(torch.bfloat16)
+    dout[1] = 0.0
+    pr = torch.from_numpy(probs).to(DEV) if weighted else None
+    q, s = fgb.unpermute_backward_quant(dout.to(DEV), torch.from_numpy(rmap).to(DEV), pr, M_cap)
+    dy = O.unpermute_backward(bits(dout), rmap, probs if weighted else None, M_cap)
+    oq, os_ = O.quant_rowwise(dy, 128)
+    assert np.array_equal(np_(s), os_)
+    assert np.array_equal(np_(q), oq)
+
+
 @pytest.mark.parametrize("M,F,use_off", [(37, 256, True), (4096, 2048, False)])
 def test_dswiglu_quant(fgb, M, F, use_off):
     say("dswiglu_quant", M, F, use_off)
