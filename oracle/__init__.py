@@ -43,6 +43,21 @@ def lib():
         L.orc_naive_transpose.argtypes = [p, p, i64, i64, p, p]
         L.orc_grouped_direct_transpose.argtypes = [p, p, i64, p, i32, p, p, i64, p]
         L.orc_kgrouped_gemm_sampled.argtypes = [p, p, p, p, p, i64, p, p, p, i64, p]
+        L.orc_e5m2_decode.restype = C.c_double
+        L.orc_e5m2_decode.argtypes = [C.c_uint8]
+        L.orc_e5m2_encode.restype = C.c_uint8
+        L.orc_e5m2_encode.argtypes = [C.c_double]
+        L.orc_fp8_encode_f32.argtypes = [p, i64, i32, p]
+        L.orc_fp8_decode_all.argtypes = [i32, p]
+        L.orc_scale_exp_fmt.restype = C.c_int
+        L.orc_scale_exp_fmt.argtypes = [C.c_double, i32, i32, i32]
+        L.orc_scale_exp_fmt_f32.argtypes = [p, i64, i32, i32, i32, p]
+        L.orc_quant_rowwise_fmt.argtypes = [p, i32, i64, i64, i64, i32, i32, i32, i32, p, i64, p, i64]
+        L.orc_dequant_fmt.argtypes = [p, p, i32, i32, i64, i64, p]
+        L.orc_direct_transpose_fmt.argtypes = [p, p, i64, i64, i32, p, p]
+        L.orc_block_gemm_fmt_sampled.argtypes = [p, p, i32, i32, p, p, i32, i32, i64, i64, p, p, i64, p]
+        L.orc_gemm_run_bounds_fmt_sampled.argtypes = [p, p, i32, i32, p, p, i32, i32, i64, i64, p, p, i64,
+                                                      i32, p, p]
         L.orc_quant_rowwise_sf.argtypes = [p, i64, i64, p, p]
         L.orc_dequant_sf.argtypes = [p, p, i64, i64, p]
         L.orc_naive_transpose_sf.argtypes = [p, p, i64, i64, p, p]
@@ -72,6 +87,16 @@ def lib():
 
 F32, BF16 = 0, 1
 ROW1x128, ROW1x32, BLOCK128 = 0, 1, 2
+E4M3, E5M2 = 0, 1
+SCALE_CEIL, SCALE_OCP_FLOOR = 0, 1
+
+
+def emin_for(group, fmt=0):
+    """Scale floor: the 1e-4 amax clamp for 128-element groups (-22 for E4M3,
+    -29 for E5M2), the E8M0 range (-127) for 32-element groups."""
+    if group == 32:
+        return -127
+    return -29 if fmt == E5M2 else -22
 
 
 def _p(a):
@@ -114,6 +139,83 @@ def scale_exp(amax, emin=-22):
     e = np.empty(a.shape, np.int32)
     lib().orc_scale_exp_f32(_p(a), a.size, emin, _p(e))
     return e
+
+
+def fp8_encode(x, fmt):
+    """orc_fp8_encode applied to float32 values (E4M3 or E5M2)."""
+    x = _c(x, np.float32)
+    q = np.empty(x.shape, np.uint8)
+    lib().orc_fp8_encode_f32(_p(x), x.size, fmt, _p(q))
+    return q
+
+
+def fp8_decode_all(fmt):
+    """orc_fp8_decode_all: the values of all 256 codes of a format."""
+    out = np.empty(256, np.float64)
+    lib().orc_fp8_decode_all(fmt, _p(out))
+    return out
+
+
+def scale_exp_fmt(amax, fmt, rule, emin):
+    """orc_scale_exp_fmt applied to float32 amax values."""
+    a = _c(amax, np.float32)
+    e = np.empty(a.shape, np.int32)
+    lib().orc_scale_exp_fmt_f32(_p(a), a.size, fmt, rule, emin, _p(e))
+    return e
+
+
+def quant_rowwise_fmt(x, group=128, fmt=0, rule=0):
+    """orc_quant_rowwise_fmt: x [rows, cols] fp32 or bf16 bits -> (q, s)."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty((rows, cols // group), np.uint8)
+    lib().orc_quant_rowwise_fmt(_p(x), _xdtype(x), rows, cols, cols, group, fmt, rule, emin_for(group, fmt), _p(q),
+                                cols, _p(s), cols // group)
+    return q, s
+
+
+def dequant_fmt(q, s, group, fmt):
+    """orc_dequant_fmt -> fp64 [rows, cols] (row-wise 1 x group scales)."""
+    q = _c(q, np.uint8)
+    s = _c(s, np.uint8)
+    out = np.empty(q.shape, np.float64)
+    lib().orc_dequant_fmt(_p(q), _p(s), group, fmt, q.shape[0], q.shape[1], _p(out))
+    return out
+
+
+def direct_transpose_fmt(q, s, fmt):
+    """orc_direct_transpose_fmt: as direct_transpose for codes of format fmt."""
+    q = _c(q, np.uint8)
+    s = _c(s, np.uint8)
+    T, Cc = q.shape
+    qt = np.empty((Cc, T), np.uint8)
+    st = np.empty((Cc, T // 128), np.uint8)
+    lib().orc_direct_transpose_fmt(_p(q), _p(s), T, Cc, fmt, _p(qt), _p(st))
+    return qt, st
+
+
+def block_gemm_fmt_sampled(a, sa, a_gran, a_fmt, b, sb, b_gran, b_fmt, mi, ni):
+    """orc_block_gemm_fmt_sampled: D = A B^T at (mi, ni), operand formats chosen."""
+    a, b, sa, sb = (_c(v, np.uint8) for v in (a, b, sa, sb))
+    mi = _c(np.asarray(mi, np.int64), np.int64)
+    ni = _c(np.asarray(ni, np.int64), np.int64)
+    out = np.empty(mi.shape, np.float64)
+    lib().orc_block_gemm_fmt_sampled(_p(a), _p(sa), a_gran, a_fmt, _p(b), _p(sb), b_gran, b_fmt, b.shape[0],
+                                     a.shape[1], _p(mi), _p(ni), mi.size, _p(out))
+    return out
+
+
+def gemm_run_bounds_fmt_sampled(a, sa, a_gran, a_fmt, b, sb, b_gran, b_fmt, mi, ni, run=8):
+    """orc_gemm_run_bounds_fmt_sampled -> (runmax, abssum) at (mi, ni)."""
+    a, b, sa, sb = (_c(v, np.uint8) for v in (a, b, sa, sb))
+    mi = _c(np.asarray(mi, np.int64), np.int64)
+    ni = _c(np.asarray(ni, np.int64), np.int64)
+    rm = np.empty(mi.shape, np.float64)
+    asum = np.empty(mi.shape, np.float64)
+    lib().orc_gemm_run_bounds_fmt_sampled(_p(a), _p(sa), a_gran, a_fmt, _p(b), _p(sb), b_gran, b_fmt, b.shape[0],
+                                          a.shape[1], _p(mi), _p(ni), mi.size, run, _p(rm), _p(asum))
+    return rm, asum
 
 
 def expf(x):

@@ -148,6 +148,163 @@ void orc_scale_exp_f32(const float *amax, int64_t n, int emin, int32_t *e)
 }
 
 /* ------------------------------------------------------------------------ */
+/* Format variants.  [LP] §2 format table: E5M2 is 1 sign / 5 exponent /    */
+/* 2 mantissa bits, largest finite magnitude 57344, with infinity; [MOSS]   */
+/* §3 uses it for backward-pass gradients.  Bias 15 and the Inf/NaN codes   */
+/* (exponent field 31) follow from "57344, has Inf" (OCP E5M2).             */
+/* ------------------------------------------------------------------------ */
+#define ORC_E4M3 0
+#define ORC_E5M2 1
+#define ORC_SCALE_CEIL 0
+#define ORC_SCALE_OCP_FLOOR 1
+
+/* Value of an E5M2 code, exactly, in double. */
+double orc_e5m2_decode(uint8_t c)
+{
+    int s = c >> 7, E = (c >> 2) & 31, m = c & 3;
+    double mag;
+    if (E == 31)
+        mag = m ? NAN : INFINITY;
+    else
+        mag = (E == 0) ? ldexp((double)m, -16) : ldexp((double)(4 + m), E - 17);
+    return s ? -mag : mag;
+}
+
+/* Round a real value to E5M2: nearest representable value, ties to the even
+ * mantissa, magnitudes at or above 57344 clipped to 57344 (the pages'
+ * quantize clips to the format's largest value), sign kept. */
+uint8_t orc_e5m2_encode(double v)
+{
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs(v);
+    if (a >= 57344.0)
+        return sign | 0x7B;
+    /* spacing: 2^(x-2) in the normal binade [2^x, 2^(x+1)), x >= -14;
+     * 2^-16 below 2^-14 (subnormals) */
+    int fx;
+    frexp(a, &fx);
+    int x = fx - 1;
+    double quantum = (a >= ldexp(1.0, -14)) ? ldexp(1.0, x - 2) : ldexp(1.0, -16);
+    double r = nearbyint(a / quantum) * quantum;
+    if (r == 0.0)
+        return sign;
+    if (r < ldexp(1.0, -14))
+        return sign | (uint8_t)(r / ldexp(1.0, -16));
+    int rx;
+    frexp(r, &rx);
+    int e = rx - 1;
+    if (e > 15)
+        return sign | 0x7B;
+    int m = (int)(r / ldexp(1.0, e - 2)) - 4; /* 4..7 -> 0..3 */
+    return sign | (uint8_t)(((e + 15) << 2) | m);
+}
+
+double orc_fp8_decode(uint8_t c, int fmt) { return fmt == ORC_E5M2 ? orc_e5m2_decode(c) : orc_e4m3_decode(c); }
+uint8_t orc_fp8_encode(double v, int fmt) { return fmt == ORC_E5M2 ? orc_e5m2_encode(v) : orc_e4m3_encode(v); }
+
+void orc_fp8_encode_f32(const float *x, int64_t n, int fmt, uint8_t *q)
+{
+    for (int64_t i = 0; i < n; i++)
+        q[i] = orc_fp8_encode((double)x[i], fmt);
+}
+
+void orc_fp8_decode_all(int fmt, double *out256)
+{
+    for (int c = 0; c < 256; c++)
+        out256[c] = orc_fp8_decode((uint8_t)c, fmt);
+}
+
+/* Scale exponent of an amax for an element format and a rule.
+ *   ORC_SCALE_CEIL: the rule used everywhere else in this path, with the
+ *     element format's largest value: the smallest e with amax <= max * 2^e
+ *     ([DSV3] §3 and §8 with max = 448, or 57344 for E5M2).
+ *   ORC_SCALE_OCP_FLOOR: the rule of the MX standard that [MOSS] §3 names for
+ *     its 32-element level: e = floor(log2 amax) - emax, emax the exponent of
+ *     the format's largest normal (8 for E4M3, 15 for E5M2); scaled values
+ *     above the largest finite value then clip in the encoder.
+ * Both are floored at emin; an all-zero group gets emin. */
+int orc_scale_exp_fmt(double amax, int fmt, int rule, int emin)
+{
+    if (!(amax > 0.0))
+        return emin;
+    int e;
+    if (rule == ORC_SCALE_OCP_FLOOR) {
+        int fx;
+        frexp(amax, &fx); /* amax in [2^(fx-1), 2^fx) */
+        e = (fx - 1) - (fmt == ORC_E5M2 ? 15 : 8);
+    } else {
+        double mx = fmt == ORC_E5M2 ? 57344.0 : 448.0;
+        e = (int)ceil(log2(amax / mx));
+        while (ldexp(mx, e) < amax)
+            e++;
+        while (ldexp(mx, e - 1) >= amax)
+            e--;
+    }
+    return e < emin ? emin : e;
+}
+
+void orc_scale_exp_fmt_f32(const float *amax, int64_t n, int fmt, int rule, int emin, int32_t *e)
+{
+    for (int64_t i = 0; i < n; i++)
+        e[i] = orc_scale_exp_fmt((double)amax[i], fmt, rule, emin);
+}
+
+/* 1 x g quantization in a chosen element format and scale rule (the
+ * gradient form of [MOSS] §3 uses E5M2; the 1e-4 amax clamp of [DSV3] §3
+ * becomes the floor emin = -22 for E4M3 and -29 for E5M2 with 128-element
+ * groups, -127 (E8M0) with 32-element groups). */
+void orc_quant_rowwise_fmt(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int group,
+                           int fmt, int rule, int emin, uint8_t *q, int64_t ldq, uint8_t *s, int64_t lds)
+{
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t j = 0; j < cols / group; j++) {
+            double amax = 0.0;
+            for (int64_t k = 0; k < group; k++) {
+                double v = fabs(load_elem(x, dtype, r * ldx + j * group + k));
+                if (v > amax)
+                    amax = v;
+            }
+            int e = orc_scale_exp_fmt(amax, fmt, rule, emin);
+            for (int64_t k = 0; k < group; k++)
+                q[r * ldq + j * group + k] = orc_fp8_encode(ldexp(load_elem(x, dtype, r * ldx + j * group + k), -e), fmt);
+            s[r * lds + j] = (uint8_t)(e + 127);
+        }
+    }
+}
+
+/* decode(q) * 2^(s - 127) in the given format (row-wise 1 x g scales). */
+void orc_dequant_fmt(const uint8_t *q, const uint8_t *s, int group, int fmt, int64_t rows, int64_t cols,
+                     double *out)
+{
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t c = 0; c < cols; c++)
+            out[r * cols + c] = ldexp(orc_fp8_decode(q[r * cols + c], fmt), (int)s[r * (cols / group) + c / group] - 127);
+}
+
+/* The direct transpose of orc_direct_transpose for codes of format fmt:
+ * dequantize, requantize at the 128x128 block's largest scale. */
+void orc_direct_transpose_fmt(const uint8_t *q, const uint8_t *s, int64_t T, int64_t C, int fmt,
+                              uint8_t *qt, uint8_t *st)
+{
+    for (int64_t tb = 0; tb < T / 128; tb++)
+        for (int64_t cb = 0; cb < C / 128; cb++) {
+            int emax = 0;
+            for (int64_t t = tb * 128; t < tb * 128 + 128; t++) {
+                int e = (int)s[t * (C / 128) + cb] - 127;
+                if (t == tb * 128 || e > emax)
+                    emax = e;
+            }
+            for (int64_t t = tb * 128; t < tb * 128 + 128; t++) {
+                int e = (int)s[t * (C / 128) + cb] - 127;
+                for (int64_t c = cb * 128; c < cb * 128 + 128; c++)
+                    qt[c * T + t] = orc_fp8_encode(ldexp(orc_fp8_decode(q[t * C + c], fmt), e - emax), fmt);
+            }
+            for (int64_t c = cb * 128; c < cb * 128 + 128; c++)
+                st[c * (T / 128) + tb] = (uint8_t)(emax + 127);
+        }
+}
+
+/* ------------------------------------------------------------------------ */
 /* 1 x g activation quantization.  [DSV3] §2 (online quantization: amax per */
 /* 1x128 activation tile, computed at run time) and §3 (1x128 tiles = per   */
 /* token per 128 channels; scale tensor [T, C/128]).  g = 32 is the MX      */
@@ -399,18 +556,22 @@ void orc_block_transpose(const uint8_t *q, const uint8_t *s, int64_t rows, int64
 /* Optional level-1 factor ([MOSS] §3): b_l1[n, ceil(K/g1)] multiplies the  */
 /* contribution of K range [g*g1, (g+1)*g1).                                */
 /* ------------------------------------------------------------------------ */
-static double g_dec[256];
+static double g_dec[256], g_dec5[256];
 static int g_dec_ready = 0;
 static void dec_table(void)
 {
     if (!g_dec_ready) {
-        for (int c = 0; c < 256; c++)
+        for (int c = 0; c < 256; c++) {
             g_dec[c] = orc_e4m3_decode((uint8_t)c);
+            g_dec5[c] = orc_e5m2_decode((uint8_t)c);
+        }
         g_dec_ready = 1;
     }
 }
 
 static int gran_size(int gran) { return gran == ORC_ROW1x32 ? 32 : 128; }
+
+static const double *g_deca = g_dec, *g_decb = g_dec; /* element decoders of A and B */
 
 static double gemm_one(const uint8_t *a, const uint8_t *sa, int a_gran, const uint8_t *b,
                        const uint8_t *sb, int b_gran, const float *b_l1, int64_t g1, int64_t N,
@@ -426,7 +587,7 @@ static double gemm_one(const uint8_t *a, const uint8_t *sa, int a_gran, const ui
         for (int64_t kb = k0; kb < k1; kb += gk) {
             double part = 0.0; /* exact */
             for (int64_t k = kb; k < kb + gk; k++)
-                part += g_dec[a[m * lda + k]] * g_dec[b[n * ldb + k]];
+                part += g_deca[a[m * lda + k]] * g_decb[b[n * ldb + k]];
             int ea = (int)sa[m * (K / ga) + kb / ga] - 127;
             int eb = (b_gran == ORC_BLOCK128) ? (int)sb[(n / 128) * (K / 128) + kb / 128] - 127
                                               : (int)sb[n * (K / gb) + kb / gb] - 127;
@@ -457,6 +618,21 @@ void orc_block_gemm_sampled(const uint8_t *a, const uint8_t *sa, int a_gran, con
     dec_table();
     for (int64_t i = 0; i < ns; i++)
         out[i] = gemm_one(a, sa, a_gran, b, sb, b_gran, b_l1, g1, N, K, lda, ldb, mi[i], ni[i]);
+}
+
+/* The same GEMM with the element format of each operand chosen (E4M3 or
+ * E5M2: [MOSS] §3 gradients in E5M2 meet E4M3 weights and activations in
+ * Dgrad and Wgrad).  Sampled outputs. */
+void orc_block_gemm_fmt_sampled(const uint8_t *a, const uint8_t *sa, int a_gran, int a_fmt, const uint8_t *b,
+                                const uint8_t *sb, int b_gran, int b_fmt, int64_t N, int64_t K,
+                                const int64_t *mi, const int64_t *ni, int64_t ns, double *out)
+{
+    dec_table();
+    g_deca = a_fmt == ORC_E5M2 ? g_dec5 : g_dec;
+    g_decb = b_fmt == ORC_E5M2 ? g_dec5 : g_dec;
+    for (int64_t i = 0; i < ns; i++)
+        out[i] = gemm_one(a, sa, a_gran, b, sb, b_gran, NULL, 0, N, K, K, K, mi[i], ni[i]);
+    g_deca = g_decb = g_dec;
 }
 
 /* K-grouped GEMM for the expert Wgrad ([DSV3] §5.6 grouped GEMMs; each    */
@@ -506,7 +682,7 @@ void orc_gemm_run_bounds_sampled(const uint8_t *a, const uint8_t *sa, int a_gran
                 int ea = (int)sa[m * (K / ga) + k / ga] - 127;
                 int eb = (b_gran == ORC_BLOCK128) ? (int)sb[(n / 128) * (K / 128) + k / 128] - 127
                                                   : (int)sb[n * (K / gb) + k / gb] - 127;
-                double pr = fabs(ldexp(g_dec[a[m * lda + k]] * g_dec[b[n * ldb + k]], ea + eb));
+                double pr = fabs(ldexp(g_deca[a[m * lda + k]] * g_decb[b[n * ldb + k]], ea + eb));
                 as += pr;
                 if (pr > mx)
                     mx = pr;
@@ -518,6 +694,19 @@ void orc_gemm_run_bounds_sampled(const uint8_t *a, const uint8_t *sa, int a_gran
         abssum[i] = as * f;
     }
     (void)N;
+}
+
+/* orc_gemm_run_bounds_sampled with the operands' element formats chosen. */
+void orc_gemm_run_bounds_fmt_sampled(const uint8_t *a, const uint8_t *sa, int a_gran, int a_fmt,
+                                     const uint8_t *b, const uint8_t *sb, int b_gran, int b_fmt, int64_t N,
+                                     int64_t K, const int64_t *mi, const int64_t *ni, int64_t ns, int run,
+                                     double *runmax, double *abssum)
+{
+    dec_table();
+    g_deca = a_fmt == ORC_E5M2 ? g_dec5 : g_dec;
+    g_decb = b_fmt == ORC_E5M2 ? g_dec5 : g_dec;
+    orc_gemm_run_bounds_sampled(a, sa, a_gran, b, sb, b_gran, NULL, N, K, K, K, mi, ni, ns, run, runmax, abssum);
+    g_deca = g_decb = g_dec;
 }
 
 /* M-grouped contiguous GEMM ([DSV3] §5.6): rows [off[g], off[g+1]) of A are */
