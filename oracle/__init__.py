@@ -77,6 +77,7 @@ def lib():
         L.orc_swiglu_quant.argtypes = [p, i64, i64, i64, p, i32, p, p]
         L.orc_dswiglu_quant.argtypes = [p, p, p, i64, i64, p, i32, p, p]
         L.orc_mx2_quant.argtypes = [p, i64, i64, i64, p, p, p]
+        L.orc_mx2_quant_rule.argtypes = [p, i64, i64, i64, i32, p, p, p]
         L.orc_mx2_dequant.argtypes = [p, p, p, i64, i64, i64, p]
         L.orc_snr_db.restype = C.c_double
         L.orc_snr_db.argtypes = [p, p, i64]
@@ -522,15 +523,19 @@ def dswiglu_quant(hq, hs, da, off=None):
     return dq, ds
 
 
-def mx2_quant(x, g1=10240):
-    """orc_mx2_quant: x bf16 bits [R, C] -> (q, s2 [R, C/32], s1 [R, ceil(C/g1)])."""
+def mx2_quant(x, g1=10240, rule=0):
+    """orc_mx2_quant_rule: x bf16 bits [R, C] -> (q, s2 [R, C/32], s1 [R, ceil(C/g1)]).
+    rule: SCALE_CEIL (orc_mx2_quant) or SCALE_OCP_FLOOR for the level-2 exponent."""
     x = _c(x, np.uint16)
     R, Cc = x.shape
     ng = (Cc + g1 - 1) // g1
     q = np.empty((R, Cc), np.uint8)
     s2 = np.empty((R, Cc // 32), np.uint8)
     s1 = np.empty((R, ng), np.float32)
-    lib().orc_mx2_quant(_p(x), R, Cc, g1, _p(q), _p(s2), _p(s1))
+    if rule == SCALE_CEIL:
+        lib().orc_mx2_quant(_p(x), R, Cc, g1, _p(q), _p(s2), _p(s1))
+    else:
+        lib().orc_mx2_quant_rule(_p(x), R, Cc, g1, rule, _p(q), _p(s2), _p(s1))
     return q, s2, s1
 
 

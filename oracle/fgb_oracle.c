@@ -963,8 +963,11 @@ void orc_dswiglu_quant(const uint8_t *hq, const uint8_t *hs, const uint16_t *da,
 /* scale rule above with floor -127.                                        */
 /*   x: bf16 [R, C]; q [R, C]; s2 [R, C/32]; s1 [R, ceil(C/g1)].            */
 /* ------------------------------------------------------------------------ */
-void orc_mx2_quant(const uint16_t *x, int64_t R, int64_t C, int64_t g1, uint8_t *q, uint8_t *s2,
-                   float *s1)
+/* rule: the level-2 exponent rule (ORC_SCALE_CEIL as everywhere, or the
+ * MX standard's ORC_SCALE_OCP_FLOOR that [MOSS] §3 points to for k2 = 32);
+ * codes clip at 448 (the encoder's saturation). */
+void orc_mx2_quant_rule(const uint16_t *x, int64_t R, int64_t C, int64_t g1, int rule, uint8_t *q, uint8_t *s2,
+                        float *s1)
 {
     int64_t ng = (C + g1 - 1) / g1;
     float *y = malloc((size_t)g1 * sizeof(float));
@@ -986,13 +989,18 @@ void orc_mx2_quant(const uint16_t *x, int64_t R, int64_t C, int64_t g1, uint8_t 
                 for (int64_t c = b; c < b + 32; c++)
                     if (fabs((double)y[c - c0]) > amax2)
                         amax2 = fabs((double)y[c - c0]);
-                int e = orc_scale_exp(amax2, -127);
+                int e = orc_scale_exp_fmt(amax2, ORC_E4M3, rule, -127);
                 for (int64_t c = b; c < b + 32; c++)
                     q[r * C + c] = orc_e4m3_encode(ldexp((double)y[c - c0], -e));
                 s2[r * (C / 32) + b / 32] = (uint8_t)(e + 127);
             }
         }
     free(y);
+}
+
+void orc_mx2_quant(const uint16_t *x, int64_t R, int64_t C, int64_t g1, uint8_t *q, uint8_t *s2, float *s1)
+{
+    orc_mx2_quant_rule(x, R, C, g1, ORC_SCALE_CEIL, q, s2, s1);
 }
 
 /* x_hat = fp32( fp32(decode(q) * 2^e2) * alpha1 ); the first product is    */

@@ -250,3 +250,31 @@ def test_gemm_fmt_exact_rationals():
     ref = O.block_gemm(a4, sa, O.ROW1x128, b, sb, O.ROW1x128)
     assert np.array_equal(O.block_gemm_fmt_sampled(a4, sa, O.ROW1x128, O.E4M3, b, sb, O.ROW1x128, O.E4M3, mi, ni),
                           ref[mi, ni])
+
+
+def test_mx2_floor_rule_is_level1_then_floor_rule_quant():
+    """Two-level quantization with the MX standard's level-2 rule: level 1 is
+    the pinned fp32 alpha1 = amax/448 and y = fp32(x / alpha1) (numpy fp32
+    division here), level 2 the floor-rule quantization of y in 32-groups
+    (the pinned quantizer above); the ceil variant is the pinned orc_mx2_quant."""
+    g = torch.Generator().manual_seed(9)
+    R, Cc, g1 = 5, 1024 + 96, 512
+    w = (torch.randn(R, Cc, generator=g) * 0.02 * torch.exp2(torch.randint(-6, 6, (R, 1), generator=g).float()))
+    w = w.to(torch.bfloat16)
+    wb = w.view(torch.int16).numpy().view(np.uint16)
+    wf = w.float().numpy()
+    q, s2, s1 = O.mx2_quant(wb, g1, O.SCALE_OCP_FLOOR)
+    q0, s20, s10 = O.mx2_quant(wb, g1)
+    assert np.array_equal(s1, s10)
+    ng = s1.shape[1]
+    for r in range(R):
+        for gi in range(ng):
+            c0, c1 = gi * g1, min((gi + 1) * g1, Cc)
+            amax = np.float32(np.abs(wf[r, c0:c1]).max())
+            alpha = np.float32(amax / np.float32(448)) if amax > 0 else np.float32(1)
+            assert s1[r, gi] == alpha
+            y = (wf[r, c0:c1] / alpha).astype(np.float32)[None, :]
+            qy, sy = O.quant_rowwise_fmt(y, 32, O.E4M3, O.SCALE_OCP_FLOOR)
+            assert np.array_equal(q[r, c0:c1], qy[0]) and np.array_equal(s2[r, c0 // 32:c1 // 32], sy[0])
+            qc, sc = O.quant_rowwise_fmt(y, 32, O.E4M3, O.SCALE_CEIL)
+            assert np.array_equal(q0[r, c0:c1], qc[0]) and np.array_equal(s20[r, c0 // 32:c1 // 32], sc[0])
