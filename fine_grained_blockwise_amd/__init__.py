@@ -20,7 +20,9 @@ __all__ = [
     "permute_pad_workspace_size", "unpermute_unpad", "swiglu_quant", "dswiglu_quant", "mx2_quant",
     "mx2_dequant", "unpermute_backward", "unpermute_backward_workspace_size",
     "fp8_block_transpose_batched", "fp8_grouped_direct_transpose", "fp8_kgrouped_gemm", "swiglu_quant_cache",
-    "unpermute_backward_quant", "F32", "BF16", "ROW1x128", "ROW1x32", "BLOCK128", "GEMM_EXACT", "GEMM_FAST",
+    "unpermute_backward_quant", "fp8_quant_rowwise_fmt", "fp8_dequant_fmt", "fgb_fp8_encode",
+    "fp8_direct_transpose_fmt", "mx2_quant_rule", "fp8_block_gemm_fmt", "fp8_grouped_gemm_masked",
+    "E4M3", "E5M2", "SCALE_CEIL", "SCALE_OCP_FLOOR", "F32", "BF16", "ROW1x128", "ROW1x32", "BLOCK128", "GEMM_EXACT", "GEMM_FAST",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -29,6 +31,8 @@ LIB_PATH = os.path.join(HERE, "libfgb.so")
 F32, BF16 = 0, 1
 ROW1x128, ROW1x32, BLOCK128 = 0, 1, 2
 GEMM_EXACT, GEMM_FAST = 0, 1
+E4M3, E5M2 = 0, 1
+SCALE_CEIL, SCALE_OCP_FLOOR = 0, 1
 
 SYMBOLS = [
     "fgb_last_error", "fgb_version", "fp8_quant_rowwise", "fp8_quant_blockwise", "fp8_dequant",
@@ -37,6 +41,8 @@ SYMBOLS = [
     "mx2_dequant", "fp8_naive_transpose", "fp8_naive_transpose_workspace_size", "dswiglu_quant",
     "unpermute_backward", "unpermute_backward_workspace_size", "fp8_block_transpose_batched",
     "fp8_grouped_direct_transpose", "fp8_kgrouped_gemm", "swiglu_quant_cache", "unpermute_backward_quant",
+    "fp8_quant_rowwise_fmt", "fp8_dequant_fmt", "fgb_fp8_encode", "fp8_direct_transpose_fmt", "mx2_quant_rule",
+    "fp8_block_gemm_fmt", "fp8_grouped_gemm_masked",
 ]
 
 
@@ -80,6 +86,14 @@ _SIG = {
     "unpermute_backward_quant": (_i32, [_p, _p, _p, _i64, _i32, _i64, _i64, _p, _p, _p, _sz, _p]),
     "dswiglu_quant": (_i32, [_p, _p, _p, _i64, _i64, _p, _i32, _p, _p, _p]),
     "mx2_quant": (_i32, [_p, _i64, _i64, _i64, _p, _p, _p, _p]),
+    "mx2_quant_rule": (_i32, [_p, _i64, _i64, _i64, _i32, _p, _p, _p, _p]),
+    "fp8_quant_rowwise_fmt": (_i32, [_p, _i32, _i64, _i64, _i64, _i32, _i32, _i32, _p, _i64, _p, _i64, _p]),
+    "fp8_dequant_fmt": (_i32, [_p, _p, _i32, _i32, _i64, _i64, _p, _i32, _p]),
+    "fgb_fp8_encode": (_i32, [_p, _i64, _i32, _p, _p]),
+    "fp8_direct_transpose_fmt": (_i32, [_p, _p, _i32, _i64, _i64, _p, _p, _p]),
+    "fp8_block_gemm_fmt": (_i32, [_p, _p, _i32, _i32, _p, _p, _i32, _i32, _p, _i64, _i64, _i64, _i64, _i64, _i64,
+                                  _p, _i32, _i64, _i32, _i32, _p]),
+    "fp8_grouped_gemm_masked": (_i32, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, _i32, _i32, _p]),
     "mx2_dequant": (_i32, [_p, _p, _p, _i64, _i64, _i64, _p, _p]),
 }
 for _name, (_res, _args) in _SIG.items():
@@ -153,6 +167,19 @@ def fp8_quant_rowwise(x, group=128, q=None, s=None):
     return q, s
 
 
+def fp8_quant_rowwise_fmt(x, group=128, fmt=E4M3, rule=SCALE_CEIL, q=None, s=None):
+    """fp8_quant_rowwise in element format fmt (E4M3/E5M2) with scale rule (SCALE_CEIL/SCALE_OCP_FLOOR)."""
+    _check_dev(x, q, s)
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((rows, cols // group), dtype=torch.uint8, device=x.device)
+    _call("fp8_quant_rowwise_fmt", _ptr(x), _dtype_code(x), rows, cols, _row_ld(x), group, fmt, rule, _ptr(q),
+          _row_ld(q), _ptr(s), _row_ld(s), _stream(x))
+    return q, s
+
+
 def fp8_quant_blockwise(w, q=None, s=None):
     """128 x 128 quantization of w [rows, cols] -> (q, s [ceil(rows/128), cols/128])."""
     _check_dev(w, q, s)
@@ -176,6 +203,28 @@ def fp8_dequant(q, s, gran, out_dtype=torch.float32):
     return out
 
 
+def fp8_dequant_fmt(q, s, gran, fmt, out_dtype=torch.float32):
+    """fp8_dequant for codes of format fmt."""
+    _check_dev(q, s)
+    for t in (q, s):
+        if not t.is_contiguous():
+            raise ValueError("fp8_dequant_fmt: q and s must be contiguous")
+    rows, cols = q.shape
+    out = torch.empty((rows, cols), dtype=out_dtype, device=q.device)
+    _call("fp8_dequant_fmt", _ptr(q), _ptr(s), gran, fmt, rows, cols, _ptr(out), _dtype_code(out), _stream(q))
+    return out
+
+
+def fgb_fp8_encode(x, fmt):
+    """Device encoding of a contiguous float32 tensor in format fmt (nearest even, clipped)."""
+    _check_dev(x)
+    if not x.is_contiguous():
+        raise ValueError("fgb_fp8_encode: x must be contiguous")
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _call("fgb_fp8_encode", _ptr(x), x.numel(), fmt, _ptr(q), _stream(x))
+    return q
+
+
 def fgb_e4m3_encode(x):
     """Device E4M3 encoding of a float32 tensor (nearest even, saturating)."""
     _check_dev(x)
@@ -196,6 +245,19 @@ def fp8_direct_transpose(q, s, s_gran=ROW1x128):
         st = torch.empty((Cc // 128, T // 128), dtype=torch.uint8, device=q.device)
     _call("fp8_direct_transpose", _ptr(q.contiguous()), _ptr(s.contiguous()), s_gran, T, Cc,
           _ptr(qt), _ptr(st), _stream(q))
+    return qt, st
+
+
+def fp8_direct_transpose_fmt(q, s, fmt):
+    """fp8_direct_transpose (1x128 scales) of codes in format fmt: (q [T, C], s) -> (qt [C, T], st)."""
+    _check_dev(q, s)
+    for t in (q, s):
+        if not t.is_contiguous():
+            raise ValueError("fp8_direct_transpose_fmt: q and s must be contiguous")
+    T, Cc = q.shape
+    qt = torch.empty((Cc, T), dtype=torch.uint8, device=q.device)
+    st = torch.empty((Cc, T // 128), dtype=torch.uint8, device=q.device)
+    _call("fp8_direct_transpose_fmt", _ptr(q), _ptr(s), fmt, T, Cc, _ptr(qt), _ptr(st), _stream(q))
     return qt, st
 
 
@@ -259,6 +321,40 @@ def fp8_block_gemm(a, sa, a_gran, b, sb, b_gran, b_l1=None, g1=0, out_dtype=torc
     _call("fp8_block_gemm", _ptr(a), _ptr(sa.contiguous()), a_gran, _ptr(b), _ptr(sb.contiguous()),
           b_gran, _ptr(b_l1), g1, M, N, K, _row_ld(a), _row_ld(b), _ptr(d), _dtype_code(d),
           _row_ld(d), int(bool(accumulate)), mode, None, 0, _stream(a))
+    return d
+
+
+def fp8_block_gemm_fmt(a, sa, a_gran, a_fmt, b, sb, b_gran, b_fmt=E4M3, out_dtype=torch.bfloat16, d=None,
+                       accumulate=False, mode=GEMM_EXACT):
+    """fp8_block_gemm with the operands' element formats (A: E4M3 or E5M2; B: E4M3)."""
+    _check_dev(a, sa, b, sb, d)
+    for t in (sa, sb):
+        if not t.is_contiguous():
+            raise ValueError("fp8_block_gemm_fmt: scale tensors must be contiguous")
+    M, K = a.shape
+    N = b.shape[0]
+    if d is None:
+        d = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _call("fp8_block_gemm_fmt", _ptr(a), _ptr(sa), a_gran, a_fmt, _ptr(b), _ptr(sb), b_gran, b_fmt, None, 0, M, N, K,
+          _row_ld(a), _row_ld(b), _ptr(d), _dtype_code(d), _row_ld(d), int(bool(accumulate)), mode, _stream(a))
+    return d
+
+
+def fp8_grouped_gemm_masked(a, sa, b, sb, masked_m, out_dtype=torch.bfloat16, d=None, mode=GEMM_EXACT):
+    """Masked grouped GEMM: a [G, M_max, K], b [G, N, K], masked_m int32 [G] (device) -> d [G, M_max, N];
+    rows m >= masked_m[g] of d are not written."""
+    _check_dev(a, sa, b, sb, masked_m, d)
+    for t in (a, sa, b, sb, masked_m):
+        if not t.is_contiguous():
+            raise ValueError("fp8_grouped_gemm_masked: operands must be contiguous")
+    G, M_max, K = a.shape
+    N = b.shape[1]
+    if d is None:
+        d = torch.empty((G, M_max, N), dtype=out_dtype, device=a.device)
+    elif not d.is_contiguous() or tuple(d.shape) != (G, M_max, N):
+        raise ValueError("fp8_grouped_gemm_masked: d must be a contiguous [G, M_max, N] tensor")
+    _call("fp8_grouped_gemm_masked", _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(masked_m), G, M_max, N, K, _ptr(d),
+          _dtype_code(d), mode, _stream(a))
     return d
 
 
@@ -434,6 +530,20 @@ def mx2_quant(x, g1=10240):
     s2 = torch.empty((R, Cc // 32), dtype=torch.uint8, device=x.device)
     s1 = torch.empty((R, ng), dtype=torch.float32, device=x.device)
     _call("mx2_quant", _ptr(x.contiguous()), R, Cc, g1, _ptr(q), _ptr(s2), _ptr(s1), _stream(x))
+    return q, s2, s1
+
+
+def mx2_quant_rule(x, g1=10240, rule=SCALE_CEIL):
+    """mx2_quant with the level-2 exponent rule chosen (SCALE_CEIL or SCALE_OCP_FLOOR)."""
+    _check_dev(x)
+    if not x.is_contiguous():
+        raise ValueError("mx2_quant_rule: x must be contiguous")
+    R, Cc = x.shape
+    ng = (Cc + g1 - 1) // g1
+    q = torch.empty((R, Cc), dtype=torch.uint8, device=x.device)
+    s2 = torch.empty((R, Cc // 32), dtype=torch.uint8, device=x.device)
+    s1 = torch.empty((R, ng), dtype=torch.float32, device=x.device)
+    _call("mx2_quant_rule", _ptr(x), R, Cc, g1, rule, _ptr(q), _ptr(s2), _ptr(s1), _stream(x))
     return q, s2, s1
 
 

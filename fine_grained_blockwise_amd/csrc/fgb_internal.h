@@ -48,6 +48,51 @@ __device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d
     return (uint32_t)w;
 }
 
+// Element formats and scale rules of the format-variant entry points.
+enum { FMT_E4M3 = 0, FMT_E5M2 = 1 };
+enum { RULE_CEIL = 0, RULE_OCP_FLOOR = 1 };
+
+// Scale exponent for an element format and rule.  CEIL: the smallest e with
+// amax <= max * 2^e (max = 1.75 * 2^EMAX, EMAX = 8 for E4M3, 15 for E5M2).
+// OCP_FLOOR: the MX standard's floor(log2 amax) - EMAX.  Floored at emin.
+template <int FMT, int RULE>
+__device__ __forceinline__ int scale_exp_fmt(uint32_t amax_bits, int emin)
+{
+    constexpr int EMAX = FMT == FMT_E5M2 ? 15 : 8;
+    int Ea = (int)(amax_bits >> 23) - 127;
+    int e = Ea - EMAX + ((RULE == RULE_CEIL && (amax_bits & 0x7FFFFFu) > 0x600000u) ? 1 : 0);
+    e = amax_bits < 0x00800000u ? emin : e;
+    return e < emin ? emin : e;
+}
+
+// Four fp32 values -> four E5M2 bytes (OCP E5M2, round to nearest even).
+// Callers keep |v| <= 57344.
+__device__ __forceinline__ uint32_t cvt4_e5m2(float a, float b, float c, float d)
+{
+    int w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+// Four fp32 values -> four codes of format FMT; CLIP first limits each value
+// to the format's largest finite magnitude (the floor rule can scale a
+// group's largest elements past it).
+template <int FMT, bool CLIP>
+__device__ __forceinline__ uint32_t cvt4_fmt(float a, float b, float c, float d)
+{
+    if constexpr (CLIP) {
+        constexpr float M = FMT == FMT_E5M2 ? 57344.0f : 448.0f;
+        a = __builtin_fminf(__builtin_fmaxf(a, -M), M);
+        b = __builtin_fminf(__builtin_fmaxf(b, -M), M);
+        c = __builtin_fminf(__builtin_fmaxf(c, -M), M);
+        d = __builtin_fminf(__builtin_fmaxf(d, -M), M);
+    }
+    if constexpr (FMT == FMT_E5M2)
+        return cvt4_e5m2(a, b, c, d);
+    else
+        return cvt4_e4m3(a, b, c, d);
+}
+
 // Decode bytes (0,1) or (2,3) of a word of E4M3 codes to fp32 (exact).
 __device__ __forceinline__ float2 dec2_lo(uint32_t w)
 {
@@ -57,6 +102,18 @@ __device__ __forceinline__ float2 dec2_lo(uint32_t w)
 __device__ __forceinline__ float2 dec2_hi(uint32_t w)
 {
     auto v = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    return make_float2(v[0], v[1]);
+}
+
+// The same for E5M2 codes.
+__device__ __forceinline__ float2 dec2_lo_e5m2(uint32_t w)
+{
+    auto v = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
+    return make_float2(v[0], v[1]);
+}
+__device__ __forceinline__ float2 dec2_hi_e5m2(uint32_t w)
+{
+    auto v = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true);
     return make_float2(v[0], v[1]);
 }
 

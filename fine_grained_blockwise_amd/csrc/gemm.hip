@@ -87,6 +87,8 @@ struct GemmArgs {
     int64_t b_stride, sb_stride; // M-grouped: per-expert B / SB strides
     const int32_t *koffs;        // K-grouped: per-expert K offsets [G+1] (multiples of 128)
     int64_t d_stride;            // K-grouped: per-expert output stride (elements)
+    const int32_t *masked_m;     // M-grouped, masked layout: valid rows per expert [G] (else NULL)
+    int64_t m_max;               // masked layout: rows reserved per expert
 };
 
 // Contiguous tile ranges per XCD: workgroup b runs on XCD b % 8.
@@ -115,6 +117,17 @@ __device__ __forceinline__ v8bf cvt8_bf16(uint32_t w0, uint32_t w1, float sc)
     return __builtin_bit_cast(v8bf, a);
 }
 
+// The same for 8 E5M2 codes (an E5M2 value times 2^e is exact in bf16 too).
+__device__ __forceinline__ v8bf cvt8_bf16_e5m2(uint32_t w0, uint32_t w1, float sc)
+{
+    uint4 a;
+    a.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, sc, false));
+    a.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, sc, true));
+    a.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, sc, false));
+    a.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, sc, true));
+    return __builtin_bit_cast(v8bf, a);
+}
+
 // Scale byte -> the fp32 whose exponent field it is (byte 0 is taken as 1).
 __device__ __forceinline__ float scale_f32(uint32_t byte) { return __uint_as_float(max(byte, 1u) << 23); }
 
@@ -123,13 +136,15 @@ __device__ __forceinline__ v8i cat(uint4 x, uint4 y)
     return (v8i){(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
 }
 
-template <int OPA, int OPB>
+// FA: A's element format for the matrix unit (0 = E4M3, 1 = E5M2); B is E4M3.
+template <int OPA, int OPB, int FA = 0>
 __device__ __forceinline__ v16f mfma_scaled(v8i a, v8i b, v16f c, uint32_t sa, uint32_t sb)
 {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OPA, (int)sa, OPB, (int)sb);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, 0, OPA, (int)sa, OPB, (int)sb);
 }
 
-template <int MODE, int AG, int BG, bool OUT_BF16, int GK>
+// AF: element format of A's codes (FMT_E4M3, or FMT_E5M2 for gradients).
+template <int MODE, int AG, int BG, bool OUT_BF16, int GK, int AF = FMT_E4M3>
 __global__ __launch_bounds__(Waves<MODE>::NW * 64) __attribute__((amdgpu_waves_per_eu(Waves<MODE>::NW / 4, Waves<MODE>::NW / 4))) void
 gemm_fp8_kernel(GemmArgs p)
 {
@@ -175,6 +190,20 @@ gemm_fp8_kernel(GemmArgs p)
     if constexpr (GK != GK_M) {
         m0 = tm * BM;
         m_end = p.M;
+    } else if (p.masked_m) {
+        // masked layout: expert e owns rows [e*m_max, (e+1)*m_max), of which
+        // the first masked_m[e] are valid; m-tiles past them exit
+        const int64_t tpe = (p.m_max + BM - 1) / BM;
+        const int e = (int)(tm / tpe);
+        const int64_t mt = tm % tpe;
+        int64_t valid = e < p.G ? (int64_t)p.masked_m[e] : 0;
+        valid = valid < 0 ? 0 : (valid > p.m_max ? p.m_max : valid);
+        if (mt * BM >= valid)
+            return; // uniform per workgroup
+        m0 = (int64_t)e * p.m_max + mt * BM;
+        m_end = (int64_t)e * p.m_max + valid;
+        B += (int64_t)e * p.b_stride;
+        SB += (int64_t)e * p.sb_stride;
     } else {
         int e = -1;
         int64_t base = 0;
@@ -451,7 +480,8 @@ gemm_fp8_kernel(GemmArgs p)
             const v8i av = cat(xa[i][0], xa[i][1]);
 #define FGB_J(I, J)                                                                                                    \
     if (i == I)                                                                                                        \
-        acc[I][J] = mfma_scaled<I, (BG == BG_BLOCK ? 0 : J)>(av, cat(xb[J][0], xb[J][1]), acc[I][J], wa, wb);
+        acc[I][J] = mfma_scaled<I, (BG == BG_BLOCK ? 0 : J), (AF == FMT_E5M2 ? 1 : 0)>(av, cat(xb[J][0], xb[J][1]),      \
+                                                                                       acc[I][J], wa, wb);
 #define FGB_I(I) FGB_J(I, 0) FGB_J(I, 1) FGB_J(I, 2) FGB_J(I, 3)
             FGB_I(0) FGB_I(1) FGB_I(2) FGB_I(3)
 #undef FGB_I
@@ -553,7 +583,10 @@ gemm_fp8_kernel(GemmArgs p)
         auto convert = [&](int sub, const uint4(&xa)[4], const uint4(&xb)[TJ]) {
 #pragma unroll
             for (int t = 0; t < 4; t++)
-                cA[t] = sub == 0 ? cvt8_bf16(xa[t].x, xa[t].y, sfA[t]) : cvt8_bf16(xa[t].z, xa[t].w, sfA[t]);
+                if constexpr (AF == FMT_E5M2)
+                    cA[t] = sub == 0 ? cvt8_bf16_e5m2(xa[t].x, xa[t].y, sfA[t]) : cvt8_bf16_e5m2(xa[t].z, xa[t].w, sfA[t]);
+                else
+                    cA[t] = sub == 0 ? cvt8_bf16(xa[t].x, xa[t].y, sfA[t]) : cvt8_bf16(xa[t].z, xa[t].w, sfA[t]);
 #pragma unroll
             for (int t = 0; t < TJ; t++)
                 cB[t] = sub == 0 ? cvt8_bf16(xb[t].x, xb[t].y, sfB[t]) : cvt8_bf16(xb[t].z, xb[t].w, sfB[t]);
@@ -693,10 +726,10 @@ gemm_fp8_kernel(GemmArgs p)
     }
 }
 
-template <int MODE, int AG, int BG, bool OUT_BF16, int GK>
+template <int MODE, int AG, int BG, bool OUT_BF16, int GK, int AF = FMT_E4M3>
 static int launch_one(const GemmArgs &p, int64_t grid, hipStream_t st)
 {
-    auto kern = gemm_fp8_kernel<MODE, AG, BG, OUT_BF16, GK>;
+    auto kern = gemm_fp8_kernel<MODE, AG, BG, OUT_BF16, GK, AF>;
     static bool attr_set = false; // per instantiation, set once per process
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
@@ -742,19 +775,32 @@ static int dispatch(int mode, int ag, int bg, bool bf16, const GemmArgs &p, int6
     return dispatch_mode<MODE_EXACT, GK>(ag, bg, bf16, p, grid, st);
 }
 
+// E5M2 A operand (gradients): dense, 1x128 A scales, 128x128 or 1x128 B scales.
+template <int MODE>
+static int dispatch_e5m2_mode(int bg, bool bf16, const GemmArgs &p, int64_t grid, hipStream_t st)
+{
+    if (bg == BG_BLOCK)
+        return bf16 ? launch_one<MODE, AG_ROW128, BG_BLOCK, true, GK_NONE, FMT_E5M2>(p, grid, st)
+                    : launch_one<MODE, AG_ROW128, BG_BLOCK, false, GK_NONE, FMT_E5M2>(p, grid, st);
+    return bf16 ? launch_one<MODE, AG_ROW128, BG_ROW128, true, GK_NONE, FMT_E5M2>(p, grid, st)
+                : launch_one<MODE, AG_ROW128, BG_ROW128, false, GK_NONE, FMT_E5M2>(p, grid, st);
+}
+
 } // namespace fgb
 
 using namespace fgb;
 
-extern "C" int fp8_block_gemm(const uint8_t *a, const uint8_t *sa, int a_gran, const uint8_t *b,
-                              const uint8_t *sb, int b_gran, const float *b_l1, int64_t g1,
-                              int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, void *d,
-                              int d_dtype, int64_t ldd, int accumulate, int mode, void *workspace,
-                              size_t ws_bytes, void *stream)
+extern "C" int fp8_block_gemm_fmt(const uint8_t *a, const uint8_t *sa, int a_gran, int a_fmt, const uint8_t *b,
+                                  const uint8_t *sb, int b_gran, int b_fmt, const float *b_l1, int64_t g1, int64_t M,
+                                  int64_t N, int64_t K, int64_t lda, int64_t ldb, void *d, int d_dtype, int64_t ldd,
+                                  int accumulate, int mode, void *stream)
 {
-    (void)workspace;
-    (void)ws_bytes;
     clear_error();
+    FGB_REQUIRE(a_fmt == FGB_E4M3 || a_fmt == FGB_E5M2, FGB_EUNSUPPORTED,
+                "fp8_block_gemm: a_fmt must be FGB_E4M3 or FGB_E5M2");
+    FGB_REQUIRE(b_fmt == FGB_E4M3, FGB_EUNSUPPORTED, "fp8_block_gemm: b_fmt must be FGB_E4M3");
+    FGB_REQUIRE(a_fmt == FGB_E4M3 || (a_gran == FGB_ROW1x128 && b_gran != FGB_ROW1x32 && !b_l1), FGB_EUNSUPPORTED,
+                "fp8_block_gemm: an E5M2 A needs 1x128 A scales, 128x128 or 1x128 B scales and no b_l1");
     FGB_REQUIRE(a && sa && b && sb && d, FGB_EINVAL, "fp8_block_gemm: null pointer");
     FGB_REQUIRE(M > 0 && N > 0 && K > 0 && K % 128 == 0, FGB_EINVAL,
                 "fp8_block_gemm: need M, N > 0 and K a positive multiple of 128 (M=%lld N=%lld K=%lld)",
@@ -800,7 +846,22 @@ extern "C" int fp8_block_gemm(const uint8_t *a, const uint8_t *sa, int a_gran, c
     p.tiles_n = (int)((N + BN - 1) / BN);
     int64_t tiles = ((M + BM - 1) / BM) * p.tiles_n;
     FGB_REQUIRE(tiles < (1ll << 31), FGB_EINVAL, "fp8_block_gemm: too many tiles");
+    if (a_fmt == FGB_E5M2)
+        return mode == FGB_GEMM_FAST
+                   ? dispatch_e5m2_mode<MODE_FAST>(bg, d_dtype == FGB_BF16, p, tiles, (hipStream_t)stream)
+                   : dispatch_e5m2_mode<MODE_EXACT>(bg, d_dtype == FGB_BF16, p, tiles, (hipStream_t)stream);
     return dispatch<GK_NONE>(mode, ag, bg, d_dtype == FGB_BF16, p, tiles, (hipStream_t)stream);
+}
+
+extern "C" int fp8_block_gemm(const uint8_t *a, const uint8_t *sa, int a_gran, const uint8_t *b, const uint8_t *sb,
+                              int b_gran, const float *b_l1, int64_t g1, int64_t M, int64_t N, int64_t K, int64_t lda,
+                              int64_t ldb, void *d, int d_dtype, int64_t ldd, int accumulate, int mode,
+                              void *workspace, size_t ws_bytes, void *stream)
+{
+    (void)workspace;
+    (void)ws_bytes;
+    return fp8_block_gemm_fmt(a, sa, a_gran, FGB_E4M3, b, sb, b_gran, FGB_E4M3, b_l1, g1, M, N, K, lda, ldb, d,
+                              d_dtype, ldd, accumulate, mode, stream);
 }
 
 extern "C" int fp8_grouped_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t *b,
@@ -833,6 +894,36 @@ extern "C" int fp8_grouped_gemm(const uint8_t *a, const uint8_t *sa, const uint8
     // sum over experts of ceil(rows_e / BM) <= ceil(M_cap / BM) + G
     int64_t tiles = ((M_cap + BM - 1) / BM + G) * p.tiles_n;
     FGB_REQUIRE(tiles < (1ll << 31), FGB_EINVAL, "fp8_grouped_gemm: too many tiles");
+    return dispatch<GK_M>(mode, AG_ROW128, BG_BLOCK, d_dtype == FGB_BF16, p, tiles, (hipStream_t)stream);
+}
+
+extern "C" int fp8_grouped_gemm_masked(const uint8_t *a, const uint8_t *sa, const uint8_t *b, const uint8_t *sb,
+                                       const int32_t *masked_m, int G, int64_t M_max, int64_t N, int64_t K, void *d,
+                                       int d_dtype, int mode, void *stream)
+{
+    clear_error();
+    FGB_REQUIRE(a && sa && b && sb && d && masked_m, FGB_EINVAL, "fp8_grouped_gemm_masked: null pointer");
+    FGB_REQUIRE(G >= 1 && G <= 1024, FGB_EINVAL, "fp8_grouped_gemm_masked: G must be in [1, 1024]");
+    FGB_REQUIRE(M_max > 0 && N > 0 && K > 0 && K % 128 == 0, FGB_EINVAL,
+                "fp8_grouped_gemm_masked: need M_max, N > 0 and K a positive multiple of 128");
+    FGB_REQUIRE(256 * K < (1ll << 32), FGB_EINVAL, "fp8_grouped_gemm_masked: K too large");
+    FGB_REQUIRE(aligned16(a) && aligned16(b), FGB_EINVAL, "fp8_grouped_gemm_masked: a and b must be 16-byte aligned");
+    FGB_REQUIRE(d_dtype == FGB_F32 || d_dtype == FGB_BF16, FGB_EUNSUPPORTED,
+                "fp8_grouped_gemm_masked: d_dtype must be FGB_F32 or FGB_BF16");
+    FGB_REQUIRE(mode == FGB_GEMM_EXACT || mode == FGB_GEMM_FAST, FGB_EUNSUPPORTED,
+                "fp8_grouped_gemm_masked: mode must be FGB_GEMM_EXACT or FGB_GEMM_FAST");
+    GemmArgs p{};
+    p.a = a; p.sa = sa; p.b = b; p.sb = sb; p.l1 = nullptr; p.d = d;
+    p.M = (int64_t)G * M_max; p.N = N; p.K = K; p.lda = K; p.ldb = K; p.ldd = N;
+    p.accumulate = 0;
+    p.tiles_n = (int)((N + BN - 1) / BN);
+    p.G = G;
+    p.b_stride = N * K;
+    p.sb_stride = ((N + 127) / 128) * (K / 128);
+    p.masked_m = masked_m;
+    p.m_max = M_max;
+    const int64_t tiles = (int64_t)G * ((M_max + BM - 1) / BM) * p.tiles_n;
+    FGB_REQUIRE(tiles < (1ll << 31), FGB_EINVAL, "fp8_grouped_gemm_masked: too many tiles");
     return dispatch<GK_M>(mode, AG_ROW128, BG_BLOCK, d_dtype == FGB_BF16, p, tiles, (hipStream_t)stream);
 }
 

@@ -18,6 +18,9 @@ namespace fgb {
 
 constexpr int MX_MAXCH = 8; // 16-byte chunks per thread: g1 <= 256 * 8 * 8
 
+// RULE: the level-2 exponent rule -- RULE_CEIL (above) or RULE_OCP_FLOOR, the
+// MX standard's floor(log2 amax32) - 8 with the elements clipped at 448.
+template <int RULE = RULE_CEIL>
 __global__ __launch_bounds__(256) void mx2_quant_kernel(const uint16_t *__restrict__ x, int64_t R,
                                                         int64_t C, int64_t g1, int64_t ng,
                                                         uint8_t *__restrict__ q,
@@ -73,12 +76,13 @@ __global__ __launch_bounds__(256) void mx2_quant_kernel(const uint16_t *__restri
             m2 = max(m2, __float_as_uint(y[2 * k + 1]) & 0x7FFFFFFFu);
         }
         m2 = group_max_u32<4>(m2); // 4 lanes = 32 elements
-        int e = scale_exp_from_bits(m2, -127);
+        int e = scale_exp_fmt<FMT_E4M3, RULE>(m2, -127);
         float sc = pow2f(-e);
         if (c < nch) {
+            constexpr bool CLIP = RULE == RULE_OCP_FLOOR;
             uint2 o;
-            o.x = cvt4_e4m3(y[0] * sc, y[1] * sc, y[2] * sc, y[3] * sc);
-            o.y = cvt4_e4m3(y[4] * sc, y[5] * sc, y[6] * sc, y[7] * sc);
+            o.x = cvt4_fmt<FMT_E4M3, CLIP>(y[0] * sc, y[1] * sc, y[2] * sc, y[3] * sc);
+            o.y = cvt4_fmt<FMT_E4M3, CLIP>(y[4] * sc, y[5] * sc, y[6] * sc, y[7] * sc);
             st_stream8(q + r * C + c0 + c * 8, o);
             if ((t & 3) == 0)
                 s2[r * (C / 32) + (c0 + c * 8) / 32] = (uint8_t)(e + 127);
@@ -128,10 +132,12 @@ __global__ __launch_bounds__(256) void mx2_dequant_kernel(const uint8_t *__restr
 
 using namespace fgb;
 
-extern "C" int mx2_quant(const void *x, int64_t R, int64_t C, int64_t g1, uint8_t *q, uint8_t *s2,
-                         float *s1, void *stream)
+extern "C" int mx2_quant_rule(const void *x, int64_t R, int64_t C, int64_t g1, int rule, uint8_t *q, uint8_t *s2,
+                              float *s1, void *stream)
 {
     clear_error();
+    FGB_REQUIRE(rule == FGB_SCALE_CEIL || rule == FGB_SCALE_OCP_FLOOR, FGB_EUNSUPPORTED,
+                "mx2_quant: rule must be FGB_SCALE_CEIL or FGB_SCALE_OCP_FLOOR");
     FGB_REQUIRE(x && q && s2 && s1, FGB_EINVAL, "mx2_quant: null pointer");
     FGB_REQUIRE(R >= 0 && C > 0 && C % 32 == 0, FGB_EINVAL, "mx2_quant: C must be a positive multiple of 32");
     FGB_REQUIRE(g1 > 0 && g1 % 32 == 0 && g1 <= 256 * 8 * MX_MAXCH, FGB_EUNSUPPORTED,
@@ -141,9 +147,20 @@ extern "C" int mx2_quant(const void *x, int64_t R, int64_t C, int64_t g1, uint8_
         return FGB_OK;
     int64_t ng = (C + g1 - 1) / g1;
     FGB_REQUIRE(R * ng < (1ll << 31), FGB_EINVAL, "mx2_quant: too many groups");
-    mx2_quant_kernel<<<(unsigned)(R * ng), 256, 0, (hipStream_t)stream>>>((const uint16_t *)x, R, C, g1, ng, q, s2, s1);
+    if (rule == FGB_SCALE_OCP_FLOOR)
+        mx2_quant_kernel<RULE_OCP_FLOOR><<<(unsigned)(R * ng), 256, 0, (hipStream_t)stream>>>((const uint16_t *)x, R, C, g1,
+                                                                                              ng, q, s2, s1);
+    else
+        mx2_quant_kernel<RULE_CEIL><<<(unsigned)(R * ng), 256, 0, (hipStream_t)stream>>>((const uint16_t *)x, R, C, g1, ng,
+                                                                                         q, s2, s1);
     FGB_LAUNCHED("mx2_quant");
     return FGB_OK;
+}
+
+extern "C" int mx2_quant(const void *x, int64_t R, int64_t C, int64_t g1, uint8_t *q, uint8_t *s2, float *s1,
+                         void *stream)
+{
+    return mx2_quant_rule(x, R, C, g1, FGB_SCALE_CEIL, q, s2, s1, stream);
 }
 
 extern "C" int mx2_dequant(const uint8_t *q, const uint8_t *s2, const float *s1, int64_t R,

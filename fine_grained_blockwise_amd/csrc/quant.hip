@@ -34,23 +34,28 @@ __device__ __forceinline__ uint32_t chunk_amax_bits(uint4 v)
     }
 }
 
-// Codes of a 16-byte chunk scaled by sc (= 2^-e, exact products).
+// Codes of a 16-byte chunk scaled by sc (= 2^-e, exact products), in
+// element format FMT; CLIP limits values to the format's maximum first.
+template <int FMT = FMT_E4M3, bool CLIP = false>
 __device__ __forceinline__ uint2 chunk_codes_bf16(uint4 v, float sc)
 {
     uint2 o;
-    o.x = cvt4_e4m3(bf16lo(v.x) * sc, bf16hi(v.x) * sc, bf16lo(v.y) * sc, bf16hi(v.y) * sc);
-    o.y = cvt4_e4m3(bf16lo(v.z) * sc, bf16hi(v.z) * sc, bf16lo(v.w) * sc, bf16hi(v.w) * sc);
+    o.x = cvt4_fmt<FMT, CLIP>(bf16lo(v.x) * sc, bf16hi(v.x) * sc, bf16lo(v.y) * sc, bf16hi(v.y) * sc);
+    o.y = cvt4_fmt<FMT, CLIP>(bf16lo(v.z) * sc, bf16hi(v.z) * sc, bf16lo(v.w) * sc, bf16hi(v.w) * sc);
     return o;
 }
+template <int FMT = FMT_E4M3, bool CLIP = false>
 __device__ __forceinline__ uint32_t chunk_codes_f32(uint4 v, float sc)
 {
-    return cvt4_e4m3(__uint_as_float(v.x) * sc, __uint_as_float(v.y) * sc,
-                     __uint_as_float(v.z) * sc, __uint_as_float(v.w) * sc);
+    return cvt4_fmt<FMT, CLIP>(__uint_as_float(v.x) * sc, __uint_as_float(v.y) * sc,
+                               __uint_as_float(v.z) * sc, __uint_as_float(v.w) * sc);
 }
 
 // One wave per row (grid-stride over rows); each lane owns a 16-byte chunk,
 // LPG consecutive lanes form one group; U chunks per lane are in flight.
-template <bool BF16, int GROUP>
+// FMT / RULE: element format and scale rule (E4M3 with the ceil rule is the
+// path's default; the floor rule clips the values it scales past the maximum).
+template <bool BF16, int GROUP, int FMT = FMT_E4M3, int RULE = RULE_CEIL>
 __global__ __launch_bounds__(256) void quant_rowwise_kernel(const uint8_t *__restrict__ x,
                                                             int64_t rows, int64_t cpr,
                                                             int64_t ldx_bytes,
@@ -79,13 +84,13 @@ __global__ __launch_bounds__(256) void quant_rowwise_kernel(const uint8_t *__res
             for (int u = 0; u < U; u++) {
                 int64_t c = c0 + u * 64 + lane;
                 uint32_t m = group_max_u32<LPG>(chunk_amax_bits<BF16>(v[u]));
-                int e = scale_exp_from_bits(m, emin);
+                int e = scale_exp_fmt<FMT, RULE>(m, emin);
                 float sc = pow2f(-e);
                 if (c < cpr) {
                     if constexpr (BF16)
-                        st_stream8(qr + c * 8, chunk_codes_bf16(v[u], sc));
+                        st_stream8(qr + c * 8, chunk_codes_bf16<FMT, RULE == RULE_OCP_FLOOR>(v[u], sc));
                     else
-                        st_stream4(qr + c * 4, chunk_codes_f32(v[u], sc));
+                        st_stream4(qr + c * 4, chunk_codes_f32<FMT, RULE == RULE_OCP_FLOOR>(v[u], sc));
                     if (lane % LPG == 0)
                         sr[c / LPG] = (uint8_t)(e + 127);
                 }
@@ -143,7 +148,7 @@ __global__ __launch_bounds__(256) void quant_blockwise_kernel(const uint8_t *__r
 }
 
 // Each thread decodes one 16-byte chunk of codes (16 codes of one scale group).
-template <bool OUT_BF16>
+template <bool OUT_BF16, int FMT = FMT_E4M3>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ q,
                                                       const uint8_t *__restrict__ s, int gran,
                                                       int64_t rows, int64_t cols,
@@ -166,7 +171,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
         float f[16];
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            float2 a = dec2_lo(w[j]), b = dec2_hi(w[j]);
+            float2 a = FMT == FMT_E5M2 ? dec2_lo_e5m2(w[j]) : dec2_lo(w[j]);
+            float2 b = FMT == FMT_E5M2 ? dec2_hi_e5m2(w[j]) : dec2_hi(w[j]);
             f[4 * j + 0] = ldexpf(a.x, e);
             f[4 * j + 1] = ldexpf(a.y, e);
             f[4 * j + 2] = ldexpf(b.x, e);
@@ -189,6 +195,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
     }
 }
 
+template <int FMT>
 __global__ __launch_bounds__(256) void encode_kernel(const float *__restrict__ x, int64_t n,
                                                      uint8_t *__restrict__ q)
 {
@@ -197,10 +204,9 @@ __global__ __launch_bounds__(256) void encode_kernel(const float *__restrict__ x
         float v[4];
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            float f = i * 4 + j < n ? x[i * 4 + j] : 0.0f;
-            v[j] = fminf(fmaxf(f, -448.0f), 448.0f);
+            v[j] = i * 4 + j < n ? x[i * 4 + j] : 0.0f;
         }
-        uint32_t w = cvt4_e4m3(v[0], v[1], v[2], v[3]);
+        uint32_t w = cvt4_fmt<FMT, true>(v[0], v[1], v[2], v[3]);
         if (i * 4 + 3 < n) {
             *reinterpret_cast<uint32_t *>(q + i * 4) = w;
         } else {
@@ -222,9 +228,23 @@ static int grid_for(int64_t work, int64_t per_block, int64_t cap)
 
 using namespace fgb;
 
-extern "C" int fp8_quant_rowwise(const void *x, int x_dtype, int64_t rows, int64_t cols,
-                                 int64_t ldx, int group, uint8_t *q, int64_t ldq, uint8_t *s,
-                                 int64_t lds, void *stream)
+template <int FMT, int RULE>
+static void launch_rowwise(const void *x, bool bf16, int group, int64_t rows, int64_t cpr, int64_t ldx_bytes, uint8_t *q,
+                           int64_t ldq, uint8_t *s, int64_t lds, int emin, int grid, hipStream_t st)
+{
+    const uint8_t *xb = (const uint8_t *)x;
+    if (bf16 && group == 128)
+        quant_rowwise_kernel<true, 128, FMT, RULE><<<grid, 256, 0, st>>>(xb, rows, cpr, ldx_bytes, q, ldq, s, lds, emin);
+    else if (bf16)
+        quant_rowwise_kernel<true, 32, FMT, RULE><<<grid, 256, 0, st>>>(xb, rows, cpr, ldx_bytes, q, ldq, s, lds, emin);
+    else if (group == 128)
+        quant_rowwise_kernel<false, 128, FMT, RULE><<<grid, 256, 0, st>>>(xb, rows, cpr, ldx_bytes, q, ldq, s, lds, emin);
+    else
+        quant_rowwise_kernel<false, 32, FMT, RULE><<<grid, 256, 0, st>>>(xb, rows, cpr, ldx_bytes, q, ldq, s, lds, emin);
+}
+
+extern "C" int fp8_quant_rowwise_fmt(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, int group,
+                                     int fmt, int rule, uint8_t *q, int64_t ldq, uint8_t *s, int64_t lds, void *stream)
 {
     clear_error();
     FGB_REQUIRE(x && q && s, FGB_EINVAL, "fp8_quant_rowwise: null pointer");
@@ -232,6 +252,10 @@ extern "C" int fp8_quant_rowwise(const void *x, int x_dtype, int64_t rows, int64
                 "fp8_quant_rowwise: x_dtype must be FGB_F32 or FGB_BF16");
     FGB_REQUIRE(group == 128 || group == 32, FGB_EUNSUPPORTED,
                 "fp8_quant_rowwise: group must be 128 or 32");
+    FGB_REQUIRE(fmt == FGB_E4M3 || fmt == FGB_E5M2, FGB_EUNSUPPORTED,
+                "fp8_quant_rowwise: fmt must be FGB_E4M3 or FGB_E5M2");
+    FGB_REQUIRE(rule == FGB_SCALE_CEIL || rule == FGB_SCALE_OCP_FLOOR, FGB_EUNSUPPORTED,
+                "fp8_quant_rowwise: rule must be FGB_SCALE_CEIL or FGB_SCALE_OCP_FLOOR");
     FGB_REQUIRE(rows >= 0 && cols > 0 && cols % group == 0, FGB_EINVAL,
                 "fp8_quant_rowwise: cols must be a positive multiple of group (rows=%lld cols=%lld)",
                 (long long)rows, (long long)cols);
@@ -247,18 +271,27 @@ extern "C" int fp8_quant_rowwise(const void *x, int x_dtype, int64_t rows, int64
         return FGB_OK;
     hipStream_t st = (hipStream_t)stream;
     int64_t cpr = cols * esz / 16;
-    int emin = group == 128 ? -22 : -127;
+    // the 1e-4 amax clamp for 128-element groups, the E8M0 range for 32
+    int emin = group == 128 ? (fmt == FGB_E5M2 ? -29 : -22) : -127;
     int grid = grid_for(rows, 4, 16384);
-    if (x_dtype == FGB_BF16 && group == 128)
-        quant_rowwise_kernel<true, 128><<<grid, 256, 0, st>>>((const uint8_t *)x, rows, cpr, ldx * esz, q, ldq, s, lds, emin);
-    else if (x_dtype == FGB_BF16)
-        quant_rowwise_kernel<true, 32><<<grid, 256, 0, st>>>((const uint8_t *)x, rows, cpr, ldx * esz, q, ldq, s, lds, emin);
-    else if (group == 128)
-        quant_rowwise_kernel<false, 128><<<grid, 256, 0, st>>>((const uint8_t *)x, rows, cpr, ldx * esz, q, ldq, s, lds, emin);
+    const bool bf16 = x_dtype == FGB_BF16;
+    if (fmt == FGB_E4M3 && rule == FGB_SCALE_CEIL)
+        launch_rowwise<FMT_E4M3, RULE_CEIL>(x, bf16, group, rows, cpr, ldx * esz, q, ldq, s, lds, emin, grid, st);
+    else if (fmt == FGB_E4M3)
+        launch_rowwise<FMT_E4M3, RULE_OCP_FLOOR>(x, bf16, group, rows, cpr, ldx * esz, q, ldq, s, lds, emin, grid, st);
+    else if (rule == FGB_SCALE_CEIL)
+        launch_rowwise<FMT_E5M2, RULE_CEIL>(x, bf16, group, rows, cpr, ldx * esz, q, ldq, s, lds, emin, grid, st);
     else
-        quant_rowwise_kernel<false, 32><<<grid, 256, 0, st>>>((const uint8_t *)x, rows, cpr, ldx * esz, q, ldq, s, lds, emin);
+        launch_rowwise<FMT_E5M2, RULE_OCP_FLOOR>(x, bf16, group, rows, cpr, ldx * esz, q, ldq, s, lds, emin, grid, st);
     FGB_LAUNCHED("fp8_quant_rowwise");
     return FGB_OK;
+}
+
+extern "C" int fp8_quant_rowwise(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, int group,
+                                 uint8_t *q, int64_t ldq, uint8_t *s, int64_t lds, void *stream)
+{
+    return fp8_quant_rowwise_fmt(x, x_dtype, rows, cols, ldx, group, FGB_E4M3, FGB_SCALE_CEIL, q, ldq, s, lds,
+                                 stream);
 }
 
 extern "C" int fp8_quant_blockwise(const void *w, int w_dtype, int64_t rows, int64_t cols,
@@ -293,10 +326,11 @@ extern "C" int fp8_quant_blockwise(const void *w, int w_dtype, int64_t rows, int
     return FGB_OK;
 }
 
-extern "C" int fp8_dequant(const uint8_t *q, const uint8_t *s, int gran, int64_t rows,
-                           int64_t cols, void *out, int out_dtype, void *stream)
+extern "C" int fp8_dequant_fmt(const uint8_t *q, const uint8_t *s, int gran, int fmt, int64_t rows, int64_t cols,
+                               void *out, int out_dtype, void *stream)
 {
     clear_error();
+    FGB_REQUIRE(fmt == FGB_E4M3 || fmt == FGB_E5M2, FGB_EUNSUPPORTED, "fp8_dequant: fmt must be FGB_E4M3 or FGB_E5M2");
     FGB_REQUIRE(q && s && out, FGB_EINVAL, "fp8_dequant: null pointer");
     FGB_REQUIRE(gran == FGB_ROW1x128 || gran == FGB_ROW1x32 || gran == FGB_BLOCK128,
                 FGB_EUNSUPPORTED, "fp8_dequant: unknown granularity");
@@ -310,25 +344,44 @@ extern "C" int fp8_dequant(const uint8_t *q, const uint8_t *s, int gran, int64_t
         return FGB_OK;
     hipStream_t st = (hipStream_t)stream;
     int grid = grid_for(rows * (cols / 16), 256, 1 << 16);
-    if (out_dtype == FGB_BF16)
+    if (out_dtype == FGB_BF16 && fmt == FGB_E5M2)
+        dequant_kernel<true, FMT_E5M2><<<grid, 256, 0, st>>>(q, s, gran, rows, cols, out);
+    else if (out_dtype == FGB_BF16)
         dequant_kernel<true><<<grid, 256, 0, st>>>(q, s, gran, rows, cols, out);
+    else if (fmt == FGB_E5M2)
+        dequant_kernel<false, FMT_E5M2><<<grid, 256, 0, st>>>(q, s, gran, rows, cols, out);
     else
         dequant_kernel<false><<<grid, 256, 0, st>>>(q, s, gran, rows, cols, out);
     FGB_LAUNCHED("fp8_dequant");
     return FGB_OK;
 }
 
-extern "C" int fgb_e4m3_encode(const float *x, int64_t n, uint8_t *q, void *stream)
+extern "C" int fp8_dequant(const uint8_t *q, const uint8_t *s, int gran, int64_t rows, int64_t cols, void *out,
+                           int out_dtype, void *stream)
+{
+    return fp8_dequant_fmt(q, s, gran, FGB_E4M3, rows, cols, out, out_dtype, stream);
+}
+
+extern "C" int fgb_fp8_encode(const float *x, int64_t n, int fmt, uint8_t *q, void *stream)
 {
     clear_error();
-    FGB_REQUIRE(x && q, FGB_EINVAL, "fgb_e4m3_encode: null pointer");
-    FGB_REQUIRE(n >= 0, FGB_EINVAL, "fgb_e4m3_encode: negative n");
+    FGB_REQUIRE(x && q, FGB_EINVAL, "fgb_fp8_encode: null pointer");
+    FGB_REQUIRE(n >= 0, FGB_EINVAL, "fgb_fp8_encode: negative n");
+    FGB_REQUIRE(fmt == FGB_E4M3 || fmt == FGB_E5M2, FGB_EUNSUPPORTED, "fgb_fp8_encode: fmt must be FGB_E4M3 or FGB_E5M2");
     FGB_REQUIRE(((uintptr_t)x & 15) == 0 && ((uintptr_t)q & 3) == 0, FGB_EINVAL,
-                "fgb_e4m3_encode: x must be 16-byte and q 4-byte aligned");
+                "fgb_fp8_encode: x must be 16-byte and q 4-byte aligned");
     if (n == 0)
         return FGB_OK;
     int grid = grid_for((n + 3) / 4, 256, 1 << 16);
-    encode_kernel<<<grid, 256, 0, (hipStream_t)stream>>>(x, n, q);
-    FGB_LAUNCHED("fgb_e4m3_encode");
+    if (fmt == FGB_E5M2)
+        encode_kernel<FMT_E5M2><<<grid, 256, 0, (hipStream_t)stream>>>(x, n, q);
+    else
+        encode_kernel<FMT_E4M3><<<grid, 256, 0, (hipStream_t)stream>>>(x, n, q);
+    FGB_LAUNCHED("fgb_fp8_encode");
     return FGB_OK;
+}
+
+extern "C" int fgb_e4m3_encode(const float *x, int64_t n, uint8_t *q, void *stream)
+{
+    return fgb_fp8_encode(x, n, FGB_E4M3, q, stream);
 }

@@ -38,13 +38,20 @@ __device__ __forceinline__ void tr4x4(uint32_t a, uint32_t b, uint32_t c, uint32
     o3 = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u);     // a3 b3 c3 d3
 }
 
+template <int FMT = FMT_E4M3>
 __device__ __forceinline__ uint32_t shift_word(uint32_t w, float f)
 {
-    float2 a = dec2_lo(w), b = dec2_hi(w);
-    return cvt4_e4m3(a.x * f, a.y * f, b.x * f, b.y * f);
+    if constexpr (FMT == FMT_E5M2) {
+        float2 a = dec2_lo_e5m2(w), b = dec2_hi_e5m2(w);
+        return cvt4_e5m2(a.x * f, a.y * f, b.x * f, b.y * f);
+    } else {
+        float2 a = dec2_lo(w), b = dec2_hi(w);
+        return cvt4_e4m3(a.x * f, a.y * f, b.x * f, b.y * f);
+    }
 }
 
-template <bool ROWSCALE>
+// FMT: element format of the codes (the shift is the same exponent move).
+template <bool ROWSCALE, int FMT = FMT_E4M3>
 __global__ __launch_bounds__(256) void direct_transpose_kernel(const uint8_t *__restrict__ q,
                                                                const uint8_t *__restrict__ s,
                                                                int64_t T, int64_t C,
@@ -90,11 +97,11 @@ __global__ __launch_bounds__(256) void direct_transpose_kernel(const uint8_t *__
         emax = (int)group_max_u32<8>(m); // lanes with equal csub hold all 128 rows
 #pragma unroll
         for (int j = 0; j < 16; j++) {
-            int k = min(emax - e[j], 31);
+            int k = min(emax - e[j], 64); // E5M2 codes survive shifts up to 32, E4M3 up to 17
             float f = pow2f(-k);
 #pragma unroll
             for (int x = 0; x < 4; x++)
-                w[j][x] = shift_word(w[j][x], f);
+                w[j][x] = shift_word<FMT>(w[j][x], f);
         }
     }
     uint32_t o[16][4]; // o[c][i]: column c0+c, rows t0+4i .. t0+4i+3
@@ -259,6 +266,30 @@ extern "C" int fp8_direct_transpose(const uint8_t *q, const uint8_t *s, int s_gr
     else
         direct_transpose_kernel<false><<<(int)grid, 256, 0, stm>>>(q, s, rows, cols, qt, st, nb);
     FGB_LAUNCHED("fp8_direct_transpose");
+    return FGB_OK;
+}
+
+extern "C" int fp8_direct_transpose_fmt(const uint8_t *q, const uint8_t *s, int fmt, int64_t rows, int64_t cols,
+                                        uint8_t *qt, uint8_t *st, void *stream)
+{
+    clear_error();
+    FGB_REQUIRE(fmt == FGB_E4M3 || fmt == FGB_E5M2, FGB_EUNSUPPORTED,
+                "fp8_direct_transpose_fmt: fmt must be FGB_E4M3 or FGB_E5M2");
+    if (fmt == FGB_E4M3)
+        return fp8_direct_transpose(q, s, FGB_ROW1x128, rows, cols, qt, st, stream);
+    FGB_REQUIRE(q && s && qt && st, FGB_EINVAL, "fp8_direct_transpose_fmt: null pointer");
+    FGB_REQUIRE(rows >= 0 && cols >= 0 && rows % 128 == 0 && cols % 128 == 0, FGB_EINVAL,
+                "fp8_direct_transpose_fmt: rows and cols must be multiples of 128 (rows=%lld cols=%lld)",
+                (long long)rows, (long long)cols);
+    FGB_REQUIRE(aligned16(q) && aligned16(qt), FGB_EINVAL,
+                "fp8_direct_transpose_fmt: q and qt must be 16-byte aligned");
+    int64_t nb = (rows / 128) * (cols / 128);
+    if (nb == 0)
+        return FGB_OK;
+    int64_t grid = (nb + 3) / 4;
+    FGB_REQUIRE(grid < (1ll << 31), FGB_EINVAL, "fp8_direct_transpose_fmt: too many blocks");
+    direct_transpose_kernel<true, FMT_E5M2><<<(int)grid, 256, 0, (hipStream_t)stream>>>(q, s, rows, cols, qt, st, nb);
+    FGB_LAUNCHED("fp8_direct_transpose_fmt");
     return FGB_OK;
 }
 

@@ -59,6 +59,15 @@ extern "C" {
 #define FGB_GEMM_EXACT 0 /* FP32 accumulation of exact products (bf16 matrix unit) */
 #define FGB_GEMM_FAST 1  /* FP8 matrix unit with its own product-sum precision */
 
+/* element formats of the format-variant entry points ([LP] §2 format table) */
+#define FGB_E4M3 0 /* OCP E4M3FN: bias 7, max 448, no Inf (the path's default) */
+#define FGB_E5M2 1 /* OCP E5M2: bias 15, max 57344, Inf/NaN at exponent field 31 */
+
+/* scale rules of the format-variant entry points */
+#define FGB_SCALE_CEIL 0      /* smallest e with amax <= max * 2^e (the rule everywhere else) */
+#define FGB_SCALE_OCP_FLOOR 1 /* MX standard: e = floor(log2 amax) - emax (8 for E4M3, 15 for E5M2);
+                                 scaled values above the format's maximum clip to it */
+
 /* scale granularities */
 #define FGB_ROW1x128 0 /* one scale per row per 128 columns: s[rows, cols/128] */
 #define FGB_ROW1x32 1  /* one scale per row per 32 columns:  s[rows, cols/32] */
@@ -86,6 +95,21 @@ int fp8_quant_rowwise(const void *x, int x_dtype, int64_t rows, int64_t cols, in
                       int group, uint8_t *q, int64_t ldq, uint8_t *s, int64_t lds, void *stream);
 
 /*
+ * fp8_quant_rowwise_fmt -- fp8_quant_rowwise with the element format and the
+ * scale rule chosen ([MOSS] §3: E5M2 for backward-pass gradients; its
+ * two-level section names the MX standard for the 32-element level, whose
+ * shared exponent is floor(log2 amax) - emax).  fmt = FGB_E4M3 or FGB_E5M2;
+ * rule = FGB_SCALE_CEIL or FGB_SCALE_OCP_FLOOR.  The floor is the 1e-4 amax
+ * clamp for 128-element groups (e >= -22 for E4M3, e >= -29 for E5M2) and
+ * e >= -127 for 32-element groups.  Codes: the format's code of x * 2^-e,
+ * round to nearest even, clipped at the format's maximum (only the floor
+ * rule reaches it).  Other arguments as fp8_quant_rowwise, which equals
+ * fmt = FGB_E4M3, rule = FGB_SCALE_CEIL.
+ */
+int fp8_quant_rowwise_fmt(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, int group, int fmt,
+                          int rule, uint8_t *q, int64_t ldq, uint8_t *s, int64_t lds, void *stream);
+
+/*
  * fp8_quant_blockwise -- 128 x 128 weight-block quantization.
  * [DSV3] §3: per 128 input channels x 128 output channels; scale tensor
  * [Cout/128, Cin/128].  The last row block may be partial (rows % 128 != 0,
@@ -103,6 +127,20 @@ int fp8_quant_blockwise(const void *w, int w_dtype, int64_t rows, int64_t cols, 
  */
 int fp8_dequant(const uint8_t *q, const uint8_t *s, int gran, int64_t rows, int64_t cols,
                 void *out, int out_dtype, void *stream);
+
+/*
+ * fp8_dequant_fmt -- fp8_dequant for codes of format fmt (FGB_E4M3 or
+ * FGB_E5M2); fp8_dequant is fmt = FGB_E4M3.
+ */
+int fp8_dequant_fmt(const uint8_t *q, const uint8_t *s, int gran, int fmt, int64_t rows, int64_t cols, void *out,
+                    int out_dtype, void *stream);
+
+/*
+ * fgb_fp8_encode -- the device conversion of fmt (FGB_E4M3 or FGB_E5M2) for
+ * each fp32 value: round to nearest even, clipped at +-448 or +-57344, sign
+ * kept; exposed for exhaustive checks.  x 16-byte, q 4-byte aligned.
+ */
+int fgb_fp8_encode(const float *x, int64_t n, int fmt, uint8_t *q, void *stream);
 
 /*
  * fgb_e4m3_encode -- E4M3 of each fp32 value (round to nearest even,
@@ -126,6 +164,15 @@ int fgb_e4m3_encode(const float *x, int64_t n, uint8_t *q, void *stream);
  */
 int fp8_direct_transpose(const uint8_t *q, const uint8_t *s, int s_gran, int64_t rows,
                          int64_t cols, uint8_t *qt, uint8_t *st, void *stream);
+
+/*
+ * fp8_direct_transpose_fmt -- fp8_direct_transpose with s_gran =
+ * FGB_ROW1x128 for codes of format fmt (FGB_E4M3 or FGB_E5M2): E5M2
+ * gradients ([MOSS] §3) take the same block-max exponent shift ([FLOW]
+ * "Core method"), re-rounded with round-to-nearest-even in E5M2.
+ */
+int fp8_direct_transpose_fmt(const uint8_t *q, const uint8_t *s, int fmt, int64_t rows, int64_t cols, uint8_t *qt,
+                             uint8_t *st, void *stream);
 
 /*
  * fp8_block_transpose_batched -- fp8_direct_transpose with s_gran =
@@ -209,6 +256,37 @@ int fp8_block_gemm(const uint8_t *a, const uint8_t *sa, int a_gran, const uint8_
                    int64_t N, int64_t K, int64_t lda, int64_t ldb, void *d, int d_dtype,
                    int64_t ldd, int accumulate, int mode, void *workspace, size_t ws_bytes,
                    void *stream);
+
+/*
+ * fp8_block_gemm_fmt -- fp8_block_gemm with each operand's element format
+ * chosen: a_fmt = FGB_E4M3 or FGB_E5M2 (a gradient in E5M2, [MOSS] §3, as A
+ * of Dgrad dY x W or Wgrad dY^T x X), b_fmt = FGB_E4M3.  An E5M2 A needs
+ * a_gran = FGB_ROW1x128, b_gran = FGB_BLOCK128 or FGB_ROW1x128 and no b_l1.
+ * In FGB_GEMM_EXACT mode E5M2 values times their power-of-two scale are
+ * exact in bf16 as E4M3 ones are, so the result is again the FP32
+ * accumulation of exact products; FGB_GEMM_FAST feeds the codes to the
+ * matrix unit as E5M2.  Other arguments as fp8_block_gemm (no workspace).
+ */
+int fp8_block_gemm_fmt(const uint8_t *a, const uint8_t *sa, int a_gran, int a_fmt, const uint8_t *b,
+                       const uint8_t *sb, int b_gran, int b_fmt, const float *b_l1, int64_t g1, int64_t M,
+                       int64_t N, int64_t K, int64_t lda, int64_t ldb, void *d, int d_dtype, int64_t ldd,
+                       int accumulate, int mode, void *stream);
+
+/*
+ * fp8_grouped_gemm_masked -- the masked grouped layout of [DSV3] §5.6: each
+ * expert owns a fixed block of M_max rows of which only the first
+ * masked_m[e] are valid (the count is known on the device only, as after a
+ * low-latency dispatch for decode).
+ *   a  [G, M_max, K] codes, sa [G, M_max, K/128] (1x128 scales), dense
+ *   b  [G, N, K] codes, sb [G, ceil(N/128), K/128] (128x128 scales), dense
+ *   masked_m : device int32 [G]; values are clamped to [0, M_max]
+ *   d  [G, M_max, N] dense, FGB_BF16 or FGB_F32; for each expert e only rows
+ *      [0, masked_m[e]) are computed and written.
+ *   mode as for fp8_block_gemm.  K % 128 == 0.
+ */
+int fp8_grouped_gemm_masked(const uint8_t *a, const uint8_t *sa, const uint8_t *b, const uint8_t *sb,
+                            const int32_t *masked_m, int G, int64_t M_max, int64_t N, int64_t K, void *d,
+                            int d_dtype, int mode, void *stream);
 
 /*
  * fp8_grouped_gemm -- M-grouped contiguous FP8 GEMM for MoE experts ([DSV3]
@@ -378,6 +456,15 @@ int dswiglu_quant(const uint8_t *hq, const uint8_t *hs, const void *da, int64_t 
  */
 int mx2_quant(const void *x, int64_t R, int64_t C, int64_t g1, uint8_t *q, uint8_t *s2, float *s1,
               void *stream);
+
+/*
+ * mx2_quant_rule -- mx2_quant with the level-2 exponent rule chosen: rule =
+ * FGB_SCALE_CEIL (mx2_quant) or FGB_SCALE_OCP_FLOOR, the MX standard's
+ * floor(log2 amax32) - 8 ([MOSS] §3 names the MX standard for k2 = 32),
+ * codes clipped at 448.
+ */
+int mx2_quant_rule(const void *x, int64_t R, int64_t C, int64_t g1, int rule, uint8_t *q, uint8_t *s2, float *s1,
+                   void *stream);
 
 /*
  * mx2_dequant -- x_hat = fp32( fp32(decode(q) * 2^(s2 - 127)) * alpha1 ).

@@ -107,6 +107,22 @@ def test_transpose_and_moe_validation():
     assert L.unpermute_backward_quant(f, f, None, 64, 8, 200, 1000, f, f, f, 1 << 20, None) == 1  # H % 128
     assert L.unpermute_backward_quant(f, f, None, 64, 8, 256, 1000, f, f, f, 100, None) == 3  # workspace
     assert L.unpermute_backward_quant(f, f, None, 64, 0, 256, 1000, f, f, f, 1 << 20, None) == 1  # topk
+    # format variants
+    assert L.fp8_quant_rowwise_fmt(f, 1, 4, 256, 256, 128, 2, 0, f, 256, f, 2, None) == 2  # unknown format
+    assert L.fp8_quant_rowwise_fmt(f, 1, 4, 256, 256, 128, 1, 2, f, 256, f, 2, None) == 2  # unknown rule
+    assert L.fp8_quant_rowwise_fmt(f, 1, 4, 200, 256, 128, 1, 1, f, 256, f, 2, None) == 1  # cols % group
+    assert L.fp8_dequant_fmt(f, f, 0, 3, 4, 256, f, 0, None) == 2
+    assert L.fgb_fp8_encode(f, 16, 5, f, None) == 2
+    assert L.fp8_direct_transpose_fmt(f, f, 1, 200, 256, f, f, None) == 1
+    assert L.fp8_direct_transpose_fmt(f, f, 4, 256, 256, f, f, None) == 2
+    assert L.mx2_quant_rule(f, 4, 1024, 512, 3, f, f, f, None) == 2
+    gf = lambda af=1, bf=0, ag=0, bg=2, l1=None: L.fp8_block_gemm_fmt(f, f, ag, af, f, f, bg, bf, l1, 0, 256, 256,
+                                                                     512, 512, 512, f, 1, 256, 0, 0, None)
+    assert gf(af=2) == 2 and gf(bf=1) == 2   # A E4M3/E5M2 only, B E4M3 only
+    assert gf(ag=1, bg=1) == 2               # E5M2 A needs 1x128 scales
+    assert gf(l1=f) == 2                     # no level-1 factor with E5M2
+    gm = lambda G=4, Mm=256, K=512, m=f: L.fp8_grouped_gemm_masked(f, f, f, f, m, G, Mm, 256, K, f, 1, 0, None)
+    assert gm(G=0) == 1 and gm(Mm=0) == 1 and gm(K=500) == 1 and gm(m=None) == 1
     # three-pass baseline: shape and workspace checks
     assert fgb.fp8_naive_transpose_workspace_size(256, 384) == 4 * 256 * 384
     assert L.fp8_naive_transpose(f, f, 200, 256, f, f, f, 1 << 20, None) == 1
