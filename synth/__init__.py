@@ -26,6 +26,9 @@ Recipes (the readings are listed in the design notes):
                 exponent field 15 - floor(3|z|) clipped at 0, mantissa
                 uniform, NaN pattern excluded) with per-1x128-tile scale bytes
                 127 + U{-20..4}.
+  token_scaled  bf16 [T, C] N(0,1) times 2^u per row, u ~ U{lo..hi} (tokens whose
+                magnitudes differ by up to 2^24, the range of the Wgrad workload's
+                tile scales).
   moss          W bf16 [8192, 28672] N(0, 0.02) times a per-row factor
                 10^U(-2, 1); A bf16 [4096, 8192] N(0, 1).
 """
@@ -126,6 +129,14 @@ def wgrad_codes(T, C, seed=0, stream=41, device="cpu"):
     s = (torch.randint(-20, 5, (T, C // 128), generator=g, device=device, dtype=torch.int32)
          + 127).to(torch.uint8)
     return q, s
+
+
+def token_scaled(T, C, lo=-20, hi=4, seed=0, stream=51, device="cpu"):
+    """bf16 [T, C]: N(0, 1) rows, row t times 2^u_t with u_t ~ U{lo..hi}."""
+    g = _gen(seed, stream, device)
+    x = torch.randn((T, C), generator=g, device=device)
+    u = torch.randint(lo, hi + 1, (T, 1), generator=g, device=device).float()
+    return (x * torch.exp2(u)).to(torch.bfloat16)
 
 
 def moss(seed=0, device="cpu", R=8192, C=28672, M=4096):
