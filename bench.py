@@ -329,6 +329,87 @@ def cpu_baseline(torch, synth, seed, kernel_results, step_floor_s):
                        f"{sample_s:.1f} s; step time extrapolated from the per-op rates")}
 
 
+def _time_us(torch, fn, reps=10):
+    for _ in range(2):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
+def format_variants(fgb, torch, W, dev, args):
+    """Outside the step: the format variants on the step's tensors -- E5M2
+    gradient quantization and transpose of the MoE dO, the Dgrad GEMM with an
+    E5M2 gradient, the MX floor rule in the MOSS quantizer, and the masked
+    grouped GEMM at a decode shape."""
+    gm = fgb.GEMM_EXACT if args.gemm_mode == "exact" else fgb.GEMM_FAST
+    peak = MFMA_PEAK_TFLOPS[args.gemm_mode]
+    out = {}
+    dO = W["moe"]["dO"]
+    T, H = dO.shape
+    gq, gs = fgb.fp8_quant_rowwise_fmt(dO, 128, fgb.E5M2, fgb.SCALE_CEIL)
+    us = _time_us(torch, lambda: fgb.fp8_quant_rowwise_fmt(dO, 128, fgb.E5M2, fgb.SCALE_CEIL, gq, gs))
+    nb = T * H * 3 + T * H // 128
+    out["quant_rowwise E5M2 dO [16384, 7168]"] = {"us": round(us, 1), "GB/s": round(nb / us / 1e3, 1),
+                                                   "frac": round(nb / us / 1e3 / HBM_PEAK_GBS, 4)}
+    us = _time_us(torch, lambda: fgb.fp8_direct_transpose_fmt(gq, gs, fgb.E5M2))
+    nb = 2 * (T * H + T * H // 128)
+    out["direct_transpose E5M2 dO"] = {"us": round(us, 1), "GB/s": round(nb / us / 1e3, 1),
+                                       "frac": round(nb / us / 1e3 / HBM_PEAK_GBS, 4)}
+    del gq, gs
+    L = W["lin"]
+    Tl, Cin = L["X"].shape
+    Cout = L["W"].shape[0]
+    wq, ws = fgb.fp8_quant_blockwise(L["W"])
+    wqt, wst = fgb.fp8_direct_transpose(wq, ws, fgb.BLOCK128)
+    lq, ls = fgb.fp8_quant_rowwise_fmt(L["dY"], 128, fgb.E5M2, fgb.SCALE_CEIL)
+    d = torch.empty((Tl, Cin), dtype=torch.bfloat16, device=dev)
+    us = _time_us(torch, lambda: fgb.fp8_block_gemm_fmt(lq, ls, fgb.ROW1x128, fgb.E5M2, wqt, wst, fgb.BLOCK128,
+                                                        fgb.E4M3, d=d, mode=gm))
+    fl = 2 * Tl * Cin * Cout
+    out["gemm dgrad, dY E5M2 (8192x7168x2048)"] = {"us": round(us, 1), "TFLOP/s": round(fl / us / 1e6, 1),
+                                                   "frac": round(fl / us / 1e6 / peak, 4)}
+    del wq, ws, wqt, wst, lq, ls, d
+    if "moss" in W:
+        Wt = W["moss"]["Wt"]
+        R, Cc = Wt.shape
+        g1 = 10240
+        us = _time_us(torch, lambda: fgb.mx2_quant_rule(Wt, g1, fgb.SCALE_OCP_FLOOR))
+        nb = R * Cc * (3 + 1 / 32) + 4 * R * ((Cc + g1 - 1) // g1)
+        out["mx2_quant floor rule W^T [28672, 8192]"] = {"us": round(us, 1), "GB/s": round(nb / us / 1e3, 1),
+                                                         "frac": round(nb / us / 1e3 / HBM_PEAK_GBS, 4)}
+    # masked grouped GEMM, decode: 512 tokens top-8 over the 32 experts' fc1 (N 4096, K 7168)
+    import numpy as np
+
+    import synth
+
+    E = W["moe"]
+    G, N1 = E["G"], E["N1"]
+    w1q, w1s = fgb.fp8_quant_blockwise(E["W1"])
+    idx, _ = synth.routing(512, G, 8, 1.1, args.seed)
+    counts = np.bincount(idx.ravel(), minlength=G)
+    M_max = 512
+    xa = torch.randn((G * M_max, H), device=dev).to(torch.bfloat16)
+    aq, as_ = fgb.fp8_quant_rowwise(xa)
+    del xa
+    mm = torch.from_numpy(counts.astype(np.int32)).to(dev)
+    d = torch.empty((G, M_max, N1), dtype=torch.bfloat16, device=dev)
+    us = _time_us(torch, lambda: fgb.fp8_grouped_gemm_masked(aq.view(G, M_max, H), as_.view(G, M_max, H // 128),
+                                                             w1q.view(G, N1, H), w1s.view(G, N1 // 128, H // 128), mm,
+                                                             d=d, mode=gm))
+    fl = 2 * int(counts.sum()) * N1 * H
+    wb = G * N1 * H  # the expert weights are read at least once: decode is weight-bandwidth bound
+    out["masked grouped gemm, decode 512 tok top-8 (fc1)"] = {
+        "us": round(us, 1), "TFLOP/s": round(fl / us / 1e6, 1), "weight GB/s": round(wb / us / 1e3, 1),
+        "frac_of_hbm": round(wb / us / 1e3 / HBM_PEAK_GBS, 4)}
+    del w1q, w1s, aq, as_, d
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -454,6 +535,10 @@ def main():
                                   "rows": rows, "F": F}
         del hq, hs, da, dq, ds
         log(f"dswiglu study: {extra['dswiglu_quant']}")
+
+    if "moe" in W and "dO" in W["moe"] and "lin" in W and not args.no_study:
+        extra["format_variants"] = format_variants(fgb, torch, W, dev, args)
+        log(f"format variants: {extra['format_variants']}")
 
     log(f"timed: {ms_step:.3f} ms/step")
     cpu = None
