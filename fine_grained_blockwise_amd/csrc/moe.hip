@@ -574,56 +574,87 @@ __global__ __launch_bounds__(256) void ub_gather_kernel(const uint16_t *__restri
     }
 }
 
-// As ub_gather_kernel, then 1x128 quantization of each bf16 row: padding
-// rows become code 0 with scale byte 105, as a zero row quantizes.
-constexpr int UBQ_U = 2;
-__global__ __launch_bounds__(256) void ub_gather_quant_kernel(const uint16_t *__restrict__ dout,
-                                                              const int32_t *__restrict__ inv,
-                                                              const float *__restrict__ probs, int topk, int64_t H,
-                                                              int64_t M_cap, uint8_t *__restrict__ q,
-                                                              uint8_t *__restrict__ s)
+// unpermute_backward fused with 1x128 quantization, token-major: a wave takes token t, keeps its dO row
+// chunks in registers (the row is read once, not once per slot) and, for
+// each of the token's slots, writes the probs-weighted, bf16-rounded,
+// 1x128-quantized copy into the slot's row of the padded layout.  Work
+// items past the T tokens are rows; those no slot references (inv < 0) get
+// code 0 / scale 105, as a zero row quantizes.  Per slot: the product w * x
+// rounded to bf16 (v_cvt_pk_bf16_f32, round to nearest even: the value the
+// unfused unpermute_backward writes), then quantized.
+typedef __bf16 fgb_bf2 __attribute__((ext_vector_type(2)));
+typedef float fgb_f2 __attribute__((ext_vector_type(2)));
+constexpr int UBT_U = 2;
+__global__ __launch_bounds__(256) void ub_token_quant_kernel(const uint16_t *__restrict__ dout,
+                                                             const int32_t *__restrict__ row_map,
+                                                             const float *__restrict__ probs,
+                                                             const int32_t *__restrict__ inv, int64_t T, int topk,
+                                                             int64_t H, int64_t M_cap, uint8_t *__restrict__ q,
+                                                             uint8_t *__restrict__ s)
 {
     const int lane = lane_id();
     const int64_t H8 = H / 8;
     const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
-    for (int64_t r = wave; r < M_cap; r += nwaves) {
-        const int32_t si = inv[r];
-        uint8_t *dq = q + r * H;
-        uint8_t *dsc = s + r * (H / 128);
-        if (si < 0) {
+    for (int64_t it = wave; it < T + M_cap; it += nwaves) {
+        if (it >= T) {
+            const int64_t r = it - T;
+            if (inv[r] >= 0)
+                continue;
+            uint8_t *dq = q + r * H;
             for (int64_t c = lane; c < H / 16; c += 64)
                 st_stream16(dq + c * 16, make_uint4(0, 0, 0, 0));
             for (int64_t c = lane; c < H / 128; c += 64)
-                dsc[c] = 105;
+                s[r * (H / 128) + c] = 105;
             continue;
         }
-        const float w = probs ? probs[si] : 1.0f;
-        const uint16_t *src = dout + (int64_t)(si / topk) * H;
-        for (int64_t c0 = 0; c0 < H8; c0 += 64 * UBQ_U) {
-            uint4 v[UBQ_U];
+        const int64_t t = it;
+        // lane k < topk holds slot k's row and weight
+        int32_t rv = -1;
+        float wv = 0.0f;
+        if (lane < topk) {
+            rv = row_map[t * topk + lane];
+            wv = probs ? probs[t * topk + lane] : 1.0f;
+        }
+        const uint16_t *src = dout + t * H;
+        for (int64_t c0 = 0; c0 < H8; c0 += 64 * UBT_U) {
+            float x[UBT_U][8];
 #pragma unroll
-            for (int u = 0; u < UBQ_U; u++) {
+            for (int u = 0; u < UBT_U; u++) {
                 const int64_t c = c0 + u * 64 + lane;
-                v[u] = c < H8 ? *reinterpret_cast<const uint4 *>(src + c * 8) : make_uint4(0, 0, 0, 0);
-            }
-#pragma unroll
-            for (int u = 0; u < UBQ_U; u++) {
-                const int64_t c = c0 + u * 64 + lane;
-                const uint32_t x4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-                float y[8];
+                const uint4 v = c < H8 ? ld_stream16(src + c * 8) : make_uint4(0, 0, 0, 0);
+                const uint32_t x4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int k = 0; k < 4; k++) {
-                    // the bf16 value of the unfused gradient, then its quantization
-                    y[2 * k] = bf16lo(bf16_rne(w * bf16lo(x4[k])));
-                    y[2 * k + 1] = bf16lo(bf16_rne(w * bf16hi(x4[k])));
+                    x[u][2 * k] = bf16lo(x4[k]);
+                    x[u][2 * k + 1] = bf16hi(x4[k]);
                 }
-                int e;
-                const uint2 o = quant8_group16(y, e);
-                if (c < H8) {
-                    st_stream8(dq + c * 8, o);
-                    if ((lane & 15) == 0)
-                        dsc[c / 16] = (uint8_t)(e + 127);
+            }
+            for (int k = 0; k < topk; k++) {
+                const int32_t r = __builtin_amdgcn_readlane(rv, k);
+                if (r < 0 || r >= M_cap)
+                    continue; // dropped slot (uniform)
+                const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wv), k));
+                uint8_t *dq = q + (int64_t)r * H;
+                uint8_t *dsc = s + (int64_t)r * (H / 128);
+#pragma unroll
+                for (int u = 0; u < UBT_U; u++) {
+                    const int64_t c = c0 + u * 64 + lane;
+                    float y[8];
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        const fgb_f2 pr = {w * x[u][2 * j], w * x[u][2 * j + 1]};
+                        const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, fgb_bf2));
+                        y[2 * j] = bf16lo(b);
+                        y[2 * j + 1] = bf16hi(b);
+                    }
+                    int e;
+                    const uint2 o = quant8_group16(y, e);
+                    if (c < H8) {
+                        st_stream8(dq + c * 8, o);
+                        if ((lane & 15) == 0)
+                            dsc[c / 16] = (uint8_t)(e + 127);
+                    }
                 }
             }
         }
@@ -833,9 +864,9 @@ extern "C" int unpermute_backward_quant(const void *dout, const int32_t *row_map
         ub_scatter_kernel<<<(unsigned)(g2 < 4096 ? g2 : 4096), 256, 0, st>>>(row_map, T * topk, M_cap, inv);
         FGB_LAUNCHED("unpermute_backward_quant");
     }
-    int64_t g3 = (M_cap + 3) / 4;
-    ub_gather_quant_kernel<<<(unsigned)(g3 < 16384 ? g3 : 16384), 256, 0, st>>>(
-        (const uint16_t *)dout, inv, probs, topk, H, M_cap, q, s);
+    int64_t g3 = (T + M_cap + 3) / 4;
+    ub_token_quant_kernel<<<(unsigned)(g3 < 16384 ? g3 : 16384), 256, 0, st>>>(
+        (const uint16_t *)dout, row_map, probs, inv, T, topk, H, M_cap, q, s);
     FGB_LAUNCHED("unpermute_backward_quant");
     return FGB_OK;
 }
