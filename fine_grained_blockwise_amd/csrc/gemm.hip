@@ -58,9 +58,9 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int NBUF = 4;                              // ring of half-step (K = 64) buffers
-constexpr int HALF_BYTES = BM * 64;                  // one operand tile of a half-step: 16 KB
-constexpr int BUF_BYTES = 2 * HALF_BYTES;            // A and B: 32 KB
+constexpr int NBUF = 2;                              // ring of K-step (K = 128) buffers
+constexpr int STEP_BYTES = BM * BK;                  // one operand tile of a K step: 32 KB
+constexpr int BUF_BYTES = 2 * STEP_BYTES;            // A and B: 64 KB
 constexpr int EPI_BYTES = 4 * 128 * (128 * 2 + 16); // epilogue staging, 4 waves (bf16; fp32 halves fit too)
 constexpr int MAIN_BYTES = NBUF * BUF_BYTES + 2 * 2 * 256 * 4; // ring + two K steps of scale tables
 constexpr int LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES; // 136 KB
@@ -99,12 +99,12 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t nb)
 }
 
 
-// LDS chunk swizzle of a 64-byte tile row: chunk c of row r sits at position
-// c ^ swz(r & 15).  Bit 0 = r bit 2, bit 1 = r bit 1 ^ r bit 3: for 16
-// consecutive rows the pairs (r % 4, position) are all distinct, and so are
-// the pairs (r % 2, position) within each 8 consecutive rows, so 16-byte
-// reads of one chunk over 8 or 16 consecutive rows touch every bank once.
-__device__ __forceinline__ int swz(int r) { return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1); }
+// LDS chunk swizzle of a 128-byte tile row: chunk c of row r sits at
+// position c ^ (r % 8).  For 8 consecutive rows reading one chunk the
+// positions are all distinct (every bank once), and 16 consecutive rows touch
+// every bank exactly twice, so 16-byte reads of a chunk column are free of
+// conflicts whether the LDS serves 8 or 16 lanes per pass.
+__device__ __forceinline__ int swz(int r) { return r & 7; }
 
 // 8 E4M3 codes (two words) -> one 8-element bf16 operand, each value times 2^e (sc = 2^e).
 __device__ __forceinline__ v8bf cvt8_bf16(uint32_t w0, uint32_t w1, float sc)
@@ -151,7 +151,7 @@ gemm_fp8_kernel(GemmArgs p)
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     // NW waves: a 2 x NW/2 grid of 128 x WNC sub-tiles (TJ column tiles of 32)
     constexpr int NW = Waves<MODE>::NW, WNC = 256 / (NW / 2), TJ = WNC / 32;
-    constexpr int RPW = 256 / NW, IPO = RPW / 16; // copy rows and instructions per wave and operand
+    constexpr int RPW = 256 / NW, IPO = RPW / 8; // copy rows and instructions per wave and operand
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / (NW / 2), wn = wave % (NW / 2);
     const int l32 = lane & 31, hk = lane >> 5;
@@ -225,33 +225,32 @@ gemm_fp8_kernel(GemmArgs p)
     const int64_t n0 = tn * BN;
 
     // ---- LDS layout ----------------------------------------------------------
-    // Ring of 4 half-step buffers (K = 64 each): buffer b holds the A tile
-    // (256 rows x 64 bytes) at b*32K and the B tile at b*32K + 16K.  Row r's
-    // 16-byte chunk c sits at r*64 + 16*(c ^ swz(r & 15)).  Scale
-    // tables (one dword per tile row of A and per tile column of B, the scale
-    // byte zero-extended, or the 4 bytes of the step's 32-element blocks) for
-    // two K steps follow the ring.
-    // Half-step h uses buffer h % 4 and is copied with the 8 copy
-    // instructions of each wave (4 for A, 4 for B), plus, for the first half
-    // of K step j, one scale copy per operand into scale slot j % 2.  The
-    // copy of half-step h+4 is issued over the slots of half-step h, after
-    // the barrier that follows the last read of buffer h % 4; it must land by
-    // the barrier before half-step h+3 is read, three half-steps later.
+    // Ring of 2 K-step buffers (K = 128 each): buffer b holds the A tile
+    // (256 rows x 128 bytes) at b*64K and the B tile at b*64K + 32K.  Row r's
+    // 16-byte chunk c sits at r*128 + 16*(c ^ swz(r)).  Scale tables (one
+    // dword per tile row of A and per tile column of B, the scale byte
+    // zero-extended, or the 4 bytes of the step's 32-element blocks) for two
+    // K steps follow the ring.  Step k uses buffer k % 2 and scale slot k % 2;
+    // each wave copies it with 2*IPO tile instructions and one scale
+    // instruction, issued over the slots after the barrier that frees buffer
+    // k % 2 (every wave has read step k-2).
     constexpr int RING_BYTES = NBUF * BUF_BYTES;
     constexpr int SC_SLOT = 2 * 256 * 4; // A and B tables of one K step
 
     // ---- copy plan ---------------------------------------------------------
-    // Instruction g (0..IPO-1) of wave w copies tile rows w*RPW + g*16 .. +15:
-    // lane l lands at LDS (w*RPW + g*16)*64 + 16*l, i.e. row +l/4, position
-    // l%4, which holds chunk (l%4) ^ swz(l/4) of that row.  Rows past the end
+    // Instruction g (0..IPO-1) of wave w copies tile rows w*RPW + g*8 .. +7,
+    // 128 bytes (one K step) of each: lane l lands at LDS
+    // (w*RPW + g*8)*128 + 16*l, i.e. row +l/8, position l%8, which holds chunk
+    // (l%8) ^ swz(l/8) of that row (the first row is a multiple of 8).  Each
+    // instruction thus reads 8 whole 128-byte lines.  Rows past the end
     // re-read the last valid row (those outputs are never stored).
     const uint8_t *a_base = p.a + m0 * p.lda + kbeg;
     const uint8_t *b_base = B + n0 * p.ldb + kbeg;
     uint32_t a_off[IPO], b_off[IPO];
 #pragma unroll
     for (int g = 0; g < IPO; g++) {
-        const int r = wave * RPW + g * 16 + (lane >> 2);
-        const int chunk = (lane & 3) ^ swz(lane >> 2);
+        const int r = wave * RPW + g * 8 + (lane >> 3);
+        const int chunk = (lane & 7) ^ swz(lane >> 3);
         const int64_t ar = m0 + r < m_end ? r : m_end - 1 - m0;
         const int64_t br = n0 + r < N ? r : N - 1 - n0;
         a_off[g] = (uint32_t)(ar * p.lda + chunk * 16);
@@ -313,18 +312,18 @@ gemm_fp8_kernel(GemmArgs p)
     const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
     const uint8_t *a_base_u = uniform(a_base), *b_base_u = uniform(b_base);
     const uint8_t *sa_base_u = uniform(sa_base), *sb_base_u = uniform(sb_base);
-    const int nk32 = (int)nk, nh = 2 * nk32; // K steps, half-steps (K < 2^24)
-    // Copy instruction i (0..2*IPO-1: A g=0..IPO-1, then B) of half-step h
-    // (clamped to the last one: copies past the end refill a free buffer
-    // with data nothing reads).
-    auto dma_tile = [&](int h, int i) {
-        const int hc = h < nh ? h : nh - 1;
-        const uint32_t dst = lds_base + (uint32_t)(hc & 3) * BUF_BYTES + (i >= IPO ? HALF_BYTES : 0) +
-                             (wave_u * RPW + (i % IPO) * 16) * 64;
+    const int nk32 = (int)nk; // K steps (K < 2^24)
+    // Copy instruction i (0..2*IPO-1: A g=0..IPO-1, then B) of K step k
+    // (clamped to the last one: copies past the end rewrite the last step's
+    // buffer with the bytes it already holds).
+    auto dma_tile = [&](int k, int i) {
+        const int kc = k < nk32 ? k : nk32 - 1;
+        const uint32_t dst = lds_base + (uint32_t)(kc & 1) * BUF_BYTES + (i >= IPO ? STEP_BYTES : 0) +
+                             (wave_u * RPW + (i % IPO) * 8) * 128;
         if (i < IPO)
-            dma16(a_base_u + (uint32_t)hc * 64u, a_off[i % IPO], dst);
+            dma16(a_base_u + (uint32_t)kc * 128u, a_off[i % IPO], dst);
         else
-            dma16(b_base_u + (uint32_t)hc * 64u, b_off[i % IPO], dst);
+            dma16(b_base_u + (uint32_t)kc * 128u, b_off[i % IPO], dst);
     };
     // The scale copies of K step ks (clamped likewise).  Both operands use
     // the same copy size (1x32 scales come on both sides or on neither).
@@ -352,12 +351,13 @@ gemm_fp8_kernel(GemmArgs p)
                 dma1(g, off, dst + (is_a ? 0u : 1024u));
         }
     };
-    // All copies of half-step h (the prologue's batches).
-    auto dma_half = [&](int h, int first, int last) { // instructions first..last
-        if (first == 0 && (h & 1) == 0)
-            dma_scales(h >> 1);
+    // Copies of step k: its scale instruction when first == 0, then tile
+    // instructions first..last.
+    auto dma_step = [&](int k, int first, int last) {
+        if (first == 0)
+            dma_scales(k);
         for (int i = first; i <= last; i++)
-            dma_tile(h, i);
+            dma_tile(k, i);
     };
     // Wait until at most n copy instructions are outstanding, then sync.
 #define FGB_WAIT_SYNC(n)                                                                                               \
@@ -403,15 +403,15 @@ gemm_fp8_kernel(GemmArgs p)
     };
 
     // ---- fragment addressing ---------------------------------------------------
-    // The wave's row t*32 + l32 of an operand tile (offset wm*128 or wn*128
-    // rows); chunk c of it at qoff[c] + t*2048 (the swizzle depends on
-    // l32 % 16 only).
-    int qoff[4];
+    // The wave's row t*32 + l32 of an operand tile (offset wm*128 or wn*WNC
+    // rows); chunk c of it at qoff[c] + t*4096 (the swizzle depends on
+    // l32 % 8 only).
+    int qoff[8];
 #pragma unroll
-    for (int c = 0; c < 4; c++)
-        qoff[c] = l32 * 64 + ((c ^ swz(l32 & 15)) * 16);
-    auto lds_a = [&](int h) { return smem + (h & 3) * BUF_BYTES + wm * 128 * 64; };
-    auto lds_b = [&](int h) { return smem + (h & 3) * BUF_BYTES + HALF_BYTES + wn * WNC * 64; };
+    for (int c = 0; c < 8; c++)
+        qoff[c] = l32 * 128 + ((c ^ swz(l32)) * 16);
+    auto lds_a = [&](int k) { return smem + (k & 1) * BUF_BYTES + wm * 128 * 128; };
+    auto lds_b = [&](int k) { return smem + (k & 1) * BUF_BYTES + STEP_BYTES + wn * WNC * 128; };
 
     v16f acc[4][TJ];
 #pragma unroll
@@ -422,40 +422,40 @@ gemm_fp8_kernel(GemmArgs p)
 
     if (nk32 > 0) { // an expert of the K-grouped form may have no rows: the tile is zero
     // ---- prologue ----------------------------------------------------------------
-    // Half-steps 0..2 and part of half-step 3 in flight (the rest is issued in
-    // the first slots of the main loop); wait for half-step 0 and sync.
-    dma_half(0, 0, 2 * IPO - 1);
-    dma_half(1, 0, 2 * IPO - 1);
-    dma_half(2, 0, 2 * IPO - 1);
+    // Step 0 and the first part of step 1 in flight (the rest of step 1 is
+    // issued in the first slots of the main loop); wait for step 0 and sync.
     if constexpr (NW == 4) {
-        dma_half(3, 0, 5);
-        FGB_WAIT_SYNC(24); // 8 + 10 + 6 instructions issued after half-step 0
+        dma_step(0, 0, 2 * IPO - 1);
+        dma_step(1, 0, 11);
+        FGB_WAIT_SYNC(13); // step 1's scale and 12 tile instructions
     } else {
-        dma_half(3, 0, 1);
-        FGB_WAIT_SYNC(11); // 4 + 5 + 2
+        dma_step(0, 0, 2 * IPO - 1);
+        dma_step(1, 0, 2);
+        FGB_WAIT_SYNC(4); // step 1's scale and 3 tile instructions
     }
     uint32_t ca[NA], cb[NB], sva[4], svb[4];
     read_scales(0, sva, svb);
     pack_scales(sva, svb, ca, cb);
 
     // ---- main loop ----------------------------------------------------------------
-    // A K step is 8 slots; slot s of step j issues 2 copy instructions
-    // (half-step 2j+3's last two in slot 0, 2j+4's in slots 1-4 with step
-    // j+2's scale copies, 2j+5's first six in slots 5-7).  The barriers
-    // before slots 1 and 5 wait for half-steps 2j+1 and 2j+2 (18 copy
-    // instructions issued after them in either case).
+    // A K step is 8 slots.  One barrier per step waits for step ks+1's copies
+    // (all issued at least four slots earlier) before its first reads and
+    // frees buffer ks % 2 (every wave has issued its last read of step ks);
+    // step ks+2's copies go out right after the barrier that frees its buffer.
     if constexpr (MODE == MODE_FAST) {
-        // A half-step is one 64-deep MFMA sub-step: 16 scaled MFMAs, 4 per
-        // slot; its fragments (chunks hk and 2+hk of each tile row: hardware
-        // K blocks 0 and 1) are read in the first two slots after the barrier
-        // that precedes it.
-        uint4 f[2][2][4][2]; // [half-step parity][A/B][tile][chunk]
-        auto read_frag = [&](int h, int op, uint4(&x)[4][2]) {
-            const uint8_t *base = op == 0 ? lds_a(h) : lds_b(h);
+        // A half-step (64 of the step's 128 K) is one MFMA sub-step: 16 scaled
+        // MFMAs, 4 per slot.  Lane half hk reads chunks 4hs+hk and 4hs+2+hk of
+        // each tile row for half hs (hardware K blocks 0 and 1).  Half 1 of
+        // step ks is read in slot 1; the barrier in slot 3 then frees buffer
+        // ks % 2 and step ks+2's copies go out over slots 3-7 and 0-1; the
+        // barrier in slot 5 waits for step ks+1, whose half 0 is read there.
+        uint4 f[2][2][4][2]; // [half][A/B][tile][chunk]
+        auto read_frag = [&](int k, int hs, int op, uint4(&x)[4][2]) {
+            const uint8_t *base = op == 0 ? lds_a(k) : lds_b(k);
 #pragma unroll
             for (int t = 0; t < 4; t++) {
-                x[t][0] = *reinterpret_cast<const uint4 *>(base + qoff[hk] + t * 2048);
-                x[t][1] = *reinterpret_cast<const uint4 *>(base + qoff[2 + hk] + t * 2048);
+                x[t][0] = *reinterpret_cast<const uint4 *>(base + qoff[4 * hs + hk] + t * 4096);
+                x[t][1] = *reinterpret_cast<const uint4 *>(base + qoff[4 * hs + 2 + hk] + t * 4096);
             }
         };
         // MFMAs of row tile i for half-step parity hs (32-blocks 2hs, 2hs+1 of the step)
@@ -487,57 +487,54 @@ gemm_fp8_kernel(GemmArgs p)
 #undef FGB_I
 #undef FGB_J
         };
-        read_frag(0, 0, f[0][0]);
-        read_frag(0, 1, f[0][1]);
+        read_frag(0, 0, 0, f[0][0]);
+        read_frag(0, 0, 1, f[0][1]);
         for (int ks = 0; ks < nk32; ks++) {
-            const int h0 = 2 * ks;
             // slot 0
-            dma_tile(h0 + 3, 6);
-            dma_tile(h0 + 3, 7);
+            dma_tile(ks + 1, 12);
+            dma_tile(ks + 1, 13);
             mfma_row(0, 0, f[0][0], f[0][1]);
             __builtin_amdgcn_sched_barrier(0);
             // slot 1
-            FGB_WAIT_SYNC(18);
-            dma_scales(ks + 2);
-            dma_tile(h0 + 4, 0);
-            dma_tile(h0 + 4, 1);
-            read_frag(h0 + 1, 0, f[1][0]);
-            read_frag(h0 + 1, 1, f[1][1]);
+            dma_tile(ks + 1, 14);
+            dma_tile(ks + 1, 15);
+            read_frag(ks, 1, 0, f[1][0]);
+            read_frag(ks, 1, 1, f[1][1]);
             mfma_row(0, 1, f[0][0], f[0][1]);
             __builtin_amdgcn_sched_barrier(0);
             // slot 2
-            dma_tile(h0 + 4, 2);
-            dma_tile(h0 + 4, 3);
             mfma_row(0, 2, f[0][0], f[0][1]);
             __builtin_amdgcn_sched_barrier(0);
-            // slot 3
-            dma_tile(h0 + 4, 4);
-            dma_tile(h0 + 4, 5);
+            // slot 3: every wave's reads of step ks are done -> buffer ks % 2 is free
+            __syncthreads();
+            dma_step(ks + 2, 0, 1);
             mfma_row(0, 3, f[0][0], f[0][1]);
             __builtin_amdgcn_sched_barrier(0);
             // slot 4
-            dma_tile(h0 + 4, 6);
-            dma_tile(h0 + 4, 7);
+            dma_tile(ks + 2, 2);
+            dma_tile(ks + 2, 3);
+            dma_tile(ks + 2, 4);
             mfma_row(1, 0, f[1][0], f[1][1]);
             __builtin_amdgcn_sched_barrier(0);
-            // slot 5
-            FGB_WAIT_SYNC(18);
+            // slot 5: step ks+1 has landed (6 instructions of step ks+2 were issued after it)
+            FGB_WAIT_SYNC(6);
             read_scales(ks + 1, sva, svb);
-            dma_tile(h0 + 5, 0);
-            dma_tile(h0 + 5, 1);
-            read_frag(h0 + 2, 0, f[0][0]);
-            read_frag(h0 + 2, 1, f[0][1]);
+            dma_tile(ks + 2, 5);
+            dma_tile(ks + 2, 6);
+            dma_tile(ks + 2, 7);
+            read_frag(ks + 1, 0, 0, f[0][0]);
+            read_frag(ks + 1, 0, 1, f[0][1]);
             mfma_row(1, 1, f[1][0], f[1][1]);
             __builtin_amdgcn_sched_barrier(0);
             // slot 6
-            dma_tile(h0 + 5, 2);
-            dma_tile(h0 + 5, 3);
+            dma_tile(ks + 2, 8);
+            dma_tile(ks + 2, 9);
             mfma_row(1, 2, f[1][0], f[1][1]);
             __builtin_amdgcn_sched_barrier(0);
             // slot 7: the next step's scales replace the current ones after
             // this slot's MFMAs
-            dma_tile(h0 + 5, 4);
-            dma_tile(h0 + 5, 5);
+            dma_tile(ks + 2, 10);
+            dma_tile(ks + 2, 11);
             mfma_row(1, 3, f[1][0], f[1][1]);
             pack_scales(sva, svb, ca, cb);
             __builtin_amdgcn_sched_barrier(0);
@@ -548,26 +545,23 @@ gemm_fp8_kernel(GemmArgs p)
         // tiles, 2 B tiles; the scale folded in) and its 8 bf16 MFMAs; while
         // one wave of a SIMD converts, the other keeps the matrix unit busy.
         // Sub-step s of a step takes bytes 0-7 (s even) or 8-15 (s odd) of
-        // chunk 2q' + hk of its half-step, q = s/2 the 32-wide pair, q' = q%2.
-        // Pair q+1's LDS reads are issued two slots before its first
-        // conversion.  Each slot issues one copy instruction: half-step
-        // 2j+3's last two in slots 0-1, 2j+4's (with step j+2's scale copy)
-        // in slots 2-5, 2j+5's first two in slots 6-7.  The barriers before
-        // slots 2 and 6 wait for half-steps 2j+1 and 2j+2 (9 copy
-        // instructions issued after them in either case).
+        // chunk 2q + hk, q = s/2 the 32-wide pair.  Pair q+1's LDS reads are
+        // issued two slots before its first conversion.  The barrier before
+        // slot 6 (after the reads of pair 3) waits for step ks+1 and frees
+        // buffer ks % 2; step ks+2's copies go out in slots 6-7 and 0-2.
         static_assert(NW == 8, "exact mode runs 8 waves");
         uint4 rA[2][4], rB[2][TJ]; // FP8 fragments of two pairs
         v8bf cA[4], cB[TJ];        // bf16 operands of the current sub-step
         float sfA[4], sfB[TJ];     // scale factors of the pair being converted
-        auto read_pair = [&](int h, int qq, uint4(&xa)[4], uint4(&xb)[TJ]) {
-            const uint8_t *la = lds_a(h), *lb = lds_b(h);
-            const int c = 2 * qq + hk;
+        auto read_pair = [&](int k, int q, uint4(&xa)[4], uint4(&xb)[TJ]) {
+            const uint8_t *la = lds_a(k), *lb = lds_b(k);
+            const int c = 2 * q + hk;
 #pragma unroll
             for (int t = 0; t < 4; t++)
-                xa[t] = *reinterpret_cast<const uint4 *>(la + qoff[c] + t * 2048);
+                xa[t] = *reinterpret_cast<const uint4 *>(la + qoff[c] + t * 4096);
 #pragma unroll
             for (int t = 0; t < TJ; t++)
-                xb[t] = *reinterpret_cast<const uint4 *>(lb + qoff[c] + t * 2048);
+                xb[t] = *reinterpret_cast<const uint4 *>(lb + qoff[c] + t * 4096);
         };
         auto factors = [&](int q) {
 #pragma unroll
@@ -610,32 +604,30 @@ gemm_fp8_kernel(GemmArgs p)
         read_pair(0, 0, rA[0], rB[0]);
         factors(0);
         for (int ks = 0; ks < nk32; ks++) {
-            const int h0 = 2 * ks;
             // slots 0-1: read pair 1; sub-steps 0, 1 (pair 0)
-            read_pair(h0, 1, rA[1], rB[1]);
-            FGB_SLOT(0, 0, dma_tile(h0 + 3, 2));
-            FGB_SLOT(1, 0, dma_tile(h0 + 3, 3));
-            // slots 2-3: half-step h0+1 landed; read pair 2; sub-steps 2, 3 (pair 1)
-            FGB_WAIT_SYNC(9);
-            dma_scales(ks + 2);
-            read_pair(h0 + 1, 0, rA[0], rB[0]);
+            read_pair(ks, 1, rA[1], rB[1]);
+            FGB_SLOT(0, 0, (dma_tile(ks + 1, 3), dma_tile(ks + 1, 4)));
+            FGB_SLOT(1, 0, (dma_tile(ks + 1, 5), dma_tile(ks + 1, 6)));
+            // slots 2-3: read pair 2; sub-steps 2, 3 (pair 1)
+            read_pair(ks, 2, rA[0], rB[0]);
             factors(1);
-            FGB_SLOT(0, 1, dma_tile(h0 + 4, 0));
-            FGB_SLOT(1, 1, dma_tile(h0 + 4, 1));
+            FGB_SLOT(0, 1, dma_tile(ks + 1, 7));
+            FGB_SLOT(1, 1, (void)0);
             // slots 4-5: read pair 3; sub-steps 4, 5 (pair 2)
-            read_pair(h0 + 1, 1, rA[1], rB[1]);
+            read_pair(ks, 3, rA[1], rB[1]);
             factors(2);
-            FGB_SLOT(0, 0, dma_tile(h0 + 4, 2));
-            FGB_SLOT(1, 0, dma_tile(h0 + 4, 3));
-            // slots 6-7: half-step h0+2 landed; the next step's scales and pair 0;
-            // sub-steps 6, 7 (pair 3).  After the last step these reads touch
-            // only LDS and are discarded.
-            FGB_WAIT_SYNC(9);
+            FGB_SLOT(0, 0, (void)0);
+            FGB_SLOT(1, 0, (void)0);
+            // slots 6-7: step ks+1 has landed (nothing issued after it) and
+            // buffer ks % 2 is free; the next step's scales and pair 0; sub-steps
+            // 6, 7 (pair 3).  After the last step these reads touch only LDS
+            // and are discarded.
+            FGB_WAIT_SYNC(0);
             read_scales(ks + 1, sva, svb);
-            read_pair(h0 + 2, 0, rA[0], rB[0]);
+            read_pair(ks + 1, 0, rA[0], rB[0]);
             factors(3);
-            FGB_SLOT(0, 1, dma_tile(h0 + 5, 0));
-            FGB_SLOT(1, 1, dma_tile(h0 + 5, 1));
+            FGB_SLOT(0, 1, (dma_step(ks + 2, 0, 0)));
+            FGB_SLOT(1, 1, (dma_tile(ks + 2, 1), dma_tile(ks + 2, 2)));
             pack_scales(sva, svb, ca, cb);
             factors(0);
         }
