@@ -14,8 +14,12 @@
 // csub*16..: 16 row loads of 16 bytes (8 lanes cover one 128-byte row
 // segment), the shift applied in the row domain where k is uniform per row,
 // a 16x16 byte transpose in registers with v_perm_b32, and 16 column stores of
-// 16 bytes (8 lanes cover one 128-byte output row segment).  No LDS, no bank
-// conflicts; HBM-bound.
+// 16 bytes (8 lanes cover one 128-byte output row segment).  The four waves
+// of a workgroup take four consecutive row blocks of one column block, so
+// each output row gets 512 contiguous bytes at once (measured: 5.0 TB/s on
+// [131584, 7168] against 3.5-4.0 TB/s with four column blocks per
+// workgroup, whose writes land in four separate 128-byte pieces per row).
+// No LDS, no bank conflicts; HBM-bound.
 //
 // The shift decodes two codes to fp32 (exact), multiplies by 2^-k (exact) and
 // converts back with round-to-nearest-even; for E - k >= 1 that is the plain
@@ -63,8 +67,10 @@ __global__ __launch_bounds__(256) void direct_transpose_kernel(const uint8_t *__
     const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (blk >= nblocks)
         return;
+    // consecutive waves take consecutive row blocks of one column block, so
+    // each output row receives long runs from one workgroup
     const int64_t ncb = C / 128, ntb = T / 128;
-    const int64_t tb = blk / ncb, cb = blk % ncb;
+    const int64_t tb = blk % ntb, cb = blk / ntb;
     { // matrix blockIdx.y of a dense batch
         const int64_t e = blockIdx.y;
         q += e * T * C;
@@ -152,7 +158,7 @@ __global__ __launch_bounds__(256) void grouped_direct_transpose_kernel(
     if (slot >= nslots)
         return;
     const int64_t ncb = C / 128, nkb = Kc / 128;
-    const int64_t kb = slot / ncb, cb = slot % ncb;
+    const int64_t kb = slot / ncb, cb = slot % ncb; // (K-block-major measured faster here)
     int ex = -1;
     for (int g = 0; g < G; g++)
         if (kb * 128 >= koff[g] && kb * 128 < koff[g + 1])
