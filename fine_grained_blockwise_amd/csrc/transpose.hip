@@ -174,15 +174,19 @@ __global__ __launch_bounds__(256) void grouped_direct_transpose_kernel(
     uint32_t w[16][4];
     int e[16];
     uint32_t m = 0;
+    // absent rows (past a short last block) re-read the block's first row
+    // and are zeroed after the load: no branches around the loads
 #pragma unroll
     for (int j = 0; j < 16; j++) {
         const bool present = tl + j < n;
-        const uint4 v = present ? ld_stream16(q + (r0 + tl + j) * C + c0) : make_uint4(0, 0, 0, 0);
-        w[j][0] = v.x;
-        w[j][1] = v.y;
-        w[j][2] = v.z;
-        w[j][3] = v.w;
-        e[j] = present ? s[(r0 + tl + j) * ncb + cb] : 0;
+        const int64_t row = r0 + (present ? tl + j : 0);
+        const uint4 v = ld_stream16(q + row * C + c0);
+        const int ej = s[row * ncb + cb];
+        w[j][0] = present ? v.x : 0u;
+        w[j][1] = present ? v.y : 0u;
+        w[j][2] = present ? v.z : 0u;
+        w[j][3] = present ? v.w : 0u;
+        e[j] = present ? ej : 0;
         m = max(m, (uint32_t)e[j]);
     }
     const int emax = (int)group_max_u32<8>(m);
