@@ -154,16 +154,24 @@ def step(fgb, torch, W, rec, mode):
         rows = int(E["counts"].sum())
         pad_rows = int(((E["counts"] + 15) // 16 * 16).sum())
         xq, xs = rec("moe.quant_rowwise X", "hbm", T * H * 3 + T * H // 128, fgb.fp8_quant_rowwise, E["X"])
-        w1q, w1s = rec("moe.quant_blockwise W1", "hbm", E["W1"].numel() * 3 + E["W1"].numel() // 16384,
-                       fgb.fp8_quant_blockwise, E["W1"])
-        w2q, w2s = rec("moe.quant_blockwise W2", "hbm", E["W2"].numel() * 3 + E["W2"].numel() // 16384,
-                       fgb.fp8_quant_blockwise, E["W2"])
+        bwd = "dO" in E
+        if bwd:  # the expert backward's Dgrad reads W^T: the quantizer writes both copies in one pass
+            w1q, w1s, w1t, w1ts = rec("moe.quant_blockwise+transpose W1", "hbm",
+                                      E["W1"].numel() * 4 + 2 * (E["W1"].numel() // 16384),
+                                      fgb.fp8_quant_blockwise_t, E["W1"].view(G, N1, H))
+            w2q, w2s, w2t, w2ts = rec("moe.quant_blockwise+transpose W2", "hbm",
+                                      E["W2"].numel() * 4 + 2 * (E["W2"].numel() // 16384),
+                                      fgb.fp8_quant_blockwise_t, E["W2"].view(G, N2, F))
+        else:
+            w1q, w1s = rec("moe.quant_blockwise W1", "hbm", E["W1"].numel() * 3 + E["W1"].numel() // 16384,
+                           fgb.fp8_quant_blockwise, E["W1"])
+            w2q, w2s = rec("moe.quant_blockwise W2", "hbm", E["W2"].numel() * 3 + E["W2"].numel() // 16384,
+                           fgb.fp8_quant_blockwise, E["W2"])
         pq, ps, rmap, offs = rec("moe.permute_pad", "hbm",
                                  T * H * (1 + 1 / 128) + pad_rows * H * (1 + 1 / 128) + 8 * T * topk,
                                  fgb.permute_pad, xq, xs, E["idx"], G, 16, M_cap, E["ws"])
         h = rec("moe.grouped_gemm fc1", "mfma", 2 * rows * N1 * H, fgb.fp8_grouped_gemm, pq, ps,
                 w1q.view(G, N1, H), w1s.view(G, N1 // 128, H // 128), offs, mode=gm)
-        bwd = "dO" in E
         if bwd:  # the backward recomputes SwiGLU from an FP8 copy of h written by the same pass
             aq, as_, hq, hs = rec("moe.swiglu_quant+cache", "hbm",
                                   pad_rows * (2 * F * 2 + F * (1 + 1 / 128) + 2 * F * (1 + 1 / 128)),
@@ -181,9 +189,6 @@ def step(fgb, torch, W, rec, mode):
             dyq, dys = rec("moe_bwd.unpermute_backward_quant dO", "hbm",
                            T * H * 2 + M_cap * H * (1 + 1 / 128) + 8 * T * topk,
                            fgb.unpermute_backward_quant, E["dO"], rmap, E["probs"], M_cap, workspace=E["ws_bwd"])
-            w2t, w2ts = rec("moe_bwd.transpose W2 (batched blocks)", "hbm",
-                            2 * E["W2"].numel() + 2 * E["W2"].numel() // 16384, fgb.fp8_block_transpose_batched,
-                            w2q.view(G, N2, F), w2s.view(G, N2 // 128, F // 128))
             da = rec("moe_bwd.grouped_gemm fc2 dgrad", "mfma", 2 * rows * F * N2, fgb.fp8_grouped_gemm, dyq, dys,
                      w2t, w2ts, offs, mode=gm)
             dyt, dyts, koff = rec("moe_bwd.grouped_direct_transpose dY", "hbm", 2 * pad_rows * H * (1 + 1 / 128),
@@ -194,9 +199,6 @@ def step(fgb, torch, W, rec, mode):
                       at, ats, koff, mode=gm)
             dhq, dhs = rec("moe_bwd.dswiglu_quant", "hbm", pad_rows * (6 * F + 4 * F / 128), fgb.dswiglu_quant,
                            hq, hs, da, offs)
-            w1t, w1ts = rec("moe_bwd.transpose W1 (batched blocks)", "hbm",
-                            2 * E["W1"].numel() + 2 * E["W1"].numel() // 16384, fgb.fp8_block_transpose_batched,
-                            w1q.view(G, N1, H), w1s.view(G, N1 // 128, H // 128))
             dxp = rec("moe_bwd.grouped_gemm fc1 dgrad", "mfma", 2 * rows * H * N1, fgb.fp8_grouped_gemm, dhq, dhs,
                       w1t, w1ts, offs, mode=gm)
             dht, dhts, _ = rec("moe_bwd.grouped_direct_transpose dH", "hbm", 2 * pad_rows * N1 * (1 + 1 / 128),

@@ -42,7 +42,7 @@ SYMBOLS = [
     "unpermute_backward", "unpermute_backward_workspace_size", "fp8_block_transpose_batched",
     "fp8_grouped_direct_transpose", "fp8_kgrouped_gemm", "swiglu_quant_cache", "unpermute_backward_quant",
     "fp8_quant_rowwise_fmt", "fp8_dequant_fmt", "fgb_fp8_encode", "fp8_direct_transpose_fmt", "mx2_quant_rule",
-    "fp8_block_gemm_fmt", "fp8_grouped_gemm_masked",
+    "fp8_block_gemm_fmt", "fp8_grouped_gemm_masked", "fp8_quant_blockwise_t",
 ]
 
 
@@ -94,6 +94,7 @@ _SIG = {
     "fp8_block_gemm_fmt": (_i32, [_p, _p, _i32, _i32, _p, _p, _i32, _i32, _p, _i64, _i64, _i64, _i64, _i64, _i64,
                                   _p, _i32, _i64, _i32, _i32, _p]),
     "fp8_grouped_gemm_masked": (_i32, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, _i32, _i32, _p]),
+    "fp8_quant_blockwise_t": (_i32, [_p, _i32, _i32, _i64, _i64, _p, _p, _p, _p, _p]),
     "mx2_dequant": (_i32, [_p, _p, _p, _i64, _i64, _i64, _p, _p]),
 }
 for _name, (_res, _args) in _SIG.items():
@@ -191,6 +192,26 @@ def fp8_quant_blockwise(w, q=None, s=None):
     _call("fp8_quant_blockwise", _ptr(w), _dtype_code(w), rows, cols, _row_ld(w), _ptr(q),
           _row_ld(q), _ptr(s), _row_ld(s), _stream(w))
     return q, s
+
+
+def fp8_quant_blockwise_t(w):
+    """128x128 quantization of bf16 w [G, rows, cols] (or [rows, cols]) with the transposed copy:
+    -> (q, s [G, rows/128, cols/128], qt [G, cols, rows], st [G, cols/128, rows/128])."""
+    _check_dev(w)
+    if not w.is_contiguous():
+        raise ValueError("fp8_quant_blockwise_t: w must be contiguous")
+    w3 = w if w.dim() == 3 else w.unsqueeze(0)
+    G, rows, cols = w3.shape
+    dev = w.device
+    q = torch.empty((G, rows, cols), dtype=torch.uint8, device=dev)
+    s = torch.empty((G, rows // 128, cols // 128), dtype=torch.uint8, device=dev)
+    qt = torch.empty((G, cols, rows), dtype=torch.uint8, device=dev)
+    st = torch.empty((G, cols // 128, rows // 128), dtype=torch.uint8, device=dev)
+    _call("fp8_quant_blockwise_t", _ptr(w3), _dtype_code(w3), G, rows, cols, _ptr(q), _ptr(s), _ptr(qt), _ptr(st),
+          _stream(w))
+    if w.dim() == 2:
+        return q[0], s[0], qt[0], st[0]
+    return q, s, qt, st
 
 
 def fp8_dequant(q, s, gran, out_dtype=torch.float32):

@@ -147,6 +147,88 @@ __global__ __launch_bounds__(256) void quant_blockwise_kernel(const uint8_t *__r
         s[rb * lds + cb] = (uint8_t)(e + 127);
 }
 
+// 128x128 quantization of bf16 weights that also writes the transposed
+// codes (the exact k = 0 byte transpose of each block, whose scale is
+// symmetric): one wave per block.  Lane (tsub = lane & 7, csub = lane >> 3)
+// owns the 16x16 sub-tile at rows tsub*16.., columns csub*16..: 16 rows of
+// 32 bytes in registers (8 lanes cover a 256-byte row segment), the block's
+// amax by a wave reduction, codes stored as 16-byte row pieces, then a 16x16
+// byte transpose in registers (v_perm_b32) stored as 16-byte column pieces
+// (8 lanes cover a 128-byte row of the transposed copy).  Blocks run
+// column-block-fastest within a matrix, so the four waves of a workgroup read
+// 1 KB of each bf16 row together (measured faster than row-block-fastest,
+// which groups the transposed copy's writes instead).
+__device__ __forceinline__ void tr4x4b(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t &o0, uint32_t &o1,
+                                       uint32_t &o2, uint32_t &o3)
+{
+    const uint32_t ab_lo = __builtin_amdgcn_perm(b, a, 0x05010400u);
+    const uint32_t ab_hi = __builtin_amdgcn_perm(b, a, 0x07030602u);
+    const uint32_t cd_lo = __builtin_amdgcn_perm(d, c, 0x05010400u);
+    const uint32_t cd_hi = __builtin_amdgcn_perm(d, c, 0x07030602u);
+    o0 = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u);
+    o1 = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u);
+    o2 = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u);
+    o3 = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u);
+}
+
+__global__ __launch_bounds__(256) void quant_blockwise_t_kernel(const uint16_t *__restrict__ w, int64_t rows,
+                                                                int64_t cols, int64_t nblocks,
+                                                                uint8_t *__restrict__ q, uint8_t *__restrict__ s,
+                                                                uint8_t *__restrict__ qt,
+                                                                uint8_t *__restrict__ st)
+{
+    const int lane = lane_id();
+    const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (blk >= nblocks)
+        return; // uniform per wave
+    const int64_t nrb = rows / 128, ncb = cols / 128, per = nrb * ncb;
+    const int64_t g = blk / per, bi = blk % per;
+    const int64_t rb = bi / ncb, cb = bi % ncb;
+    w += g * rows * cols;
+    q += g * rows * cols;
+    qt += g * rows * cols;
+    s += g * per;
+    st += g * per;
+    const int tsub = lane & 7, csub = lane >> 3;
+    const int64_t r0 = rb * 128 + tsub * 16, c0 = cb * 128 + csub * 16;
+    uint4 v[16][2];
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+        const uint16_t *src = w + (r0 + j) * cols + c0;
+        v[j][0] = ld_stream16(src);
+        v[j][1] = ld_stream16(src + 8);
+        m = max(m, max(chunk_amax_bits<true>(v[j][0]), chunk_amax_bits<true>(v[j][1])));
+    }
+    m = group_max_u32<64>(m);
+    const int e = scale_exp_from_bits(m, -22);
+    const float sc = pow2f(-e);
+    uint32_t c[16][4]; // c[j]: the 16 codes of row r0+j
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+        const uint2 lo = chunk_codes_bf16(v[j][0], sc), hi = chunk_codes_bf16(v[j][1], sc);
+        c[j][0] = lo.x;
+        c[j][1] = lo.y;
+        c[j][2] = hi.x;
+        c[j][3] = hi.y;
+        st_stream16(q + (r0 + j) * cols + c0, make_uint4(c[j][0], c[j][1], c[j][2], c[j][3]));
+    }
+    uint32_t o[16][4]; // o[k][i]: column c0+k, rows r0+4i .. r0+4i+3
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int x = 0; x < 4; x++)
+            tr4x4b(c[4 * i + 0][x], c[4 * i + 1][x], c[4 * i + 2][x], c[4 * i + 3][x], o[4 * x + 0][i],
+                   o[4 * x + 1][i], o[4 * x + 2][i], o[4 * x + 3][i]);
+#pragma unroll
+    for (int k = 0; k < 16; k++)
+        st_stream16(qt + (c0 + k) * rows + r0, make_uint4(o[k][0], o[k][1], o[k][2], o[k][3]));
+    if (lane == 0) {
+        s[rb * ncb + cb] = (uint8_t)(e + 127);
+        st[cb * nrb + rb] = (uint8_t)(e + 127);
+    }
+}
+
 // Each thread decodes one 16-byte chunk of codes (16 codes of one scale group).
 template <bool OUT_BF16, int FMT = FMT_E4M3>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ q,
@@ -323,6 +405,27 @@ extern "C" int fp8_quant_blockwise(const void *w, int w_dtype, int64_t rows, int
     else
         quant_blockwise_kernel<false><<<(int)nb, 256, 0, st>>>((const uint8_t *)w, rows, ldw * esz, q, ldq, s, lds, nbc);
     FGB_LAUNCHED("fp8_quant_blockwise");
+    return FGB_OK;
+}
+
+extern "C" int fp8_quant_blockwise_t(const void *w, int w_dtype, int G, int64_t rows, int64_t cols, uint8_t *q,
+                                     uint8_t *s, uint8_t *qt, uint8_t *st, void *stream)
+{
+    clear_error();
+    FGB_REQUIRE(w && q && s && qt && st, FGB_EINVAL, "fp8_quant_blockwise_t: null pointer");
+    FGB_REQUIRE(w_dtype == FGB_BF16, FGB_EUNSUPPORTED, "fp8_quant_blockwise_t: w_dtype must be FGB_BF16");
+    FGB_REQUIRE(G >= 1 && rows >= 0 && cols >= 0 && rows % 128 == 0 && cols % 128 == 0, FGB_EINVAL,
+                "fp8_quant_blockwise_t: need G >= 1 and rows, cols multiples of 128 (rows=%lld cols=%lld)",
+                (long long)rows, (long long)cols);
+    FGB_REQUIRE(aligned16(w) && aligned16(q) && aligned16(qt), FGB_EINVAL,
+                "fp8_quant_blockwise_t: w, q and qt must be 16-byte aligned");
+    const int64_t nb = (int64_t)G * (rows / 128) * (cols / 128);
+    if (nb == 0)
+        return FGB_OK;
+    FGB_REQUIRE((nb + 3) / 4 < (1ll << 31), FGB_EINVAL, "fp8_quant_blockwise_t: too many blocks");
+    quant_blockwise_t_kernel<<<(unsigned)((nb + 3) / 4), 256, 0, (hipStream_t)stream>>>((const uint16_t *)w, rows, cols,
+                                                                                      nb, q, s, qt, st);
+    FGB_LAUNCHED("fp8_quant_blockwise_t");
     return FGB_OK;
 }
 

@@ -121,6 +121,22 @@ int fp8_quant_blockwise(const void *w, int w_dtype, int64_t rows, int64_t cols, 
                         uint8_t *q, int64_t ldq, uint8_t *s, int64_t lds, void *stream);
 
 /*
+ * fp8_quant_blockwise_t -- fp8_quant_blockwise of G stacked bf16 matrices
+ * that also writes each matrix's transposed codes and scales, the copy the
+ * Dgrad GEMM reads ([DSV3] §1: Dgrad multiplies by W, so the NT GEMM needs
+ * W^T K-major; §3: 128x128 blocks, whose scale is the same for the
+ * transposed block).  One pass: the transposed copy is the exact byte
+ * transpose of each block (fp8_block_transpose_batched of the codes), so no
+ * code is read back ([FLOW] "Core method": the FP8 copies a recipe needs are
+ * produced where the data is quantized).
+ *   w  [G, rows, cols] bf16 dense; rows % 128 == 0, cols % 128 == 0
+ *   q  [G, rows, cols], s [G, rows/128, cols/128]  (as fp8_quant_blockwise)
+ *   qt [G, cols, rows], st [G, cols/128, rows/128]
+ */
+int fp8_quant_blockwise_t(const void *w, int w_dtype, int G, int64_t rows, int64_t cols, uint8_t *q, uint8_t *s,
+                          uint8_t *qt, uint8_t *st, void *stream);
+
+/*
  * fp8_dequant -- decode(q) * 2^(s - 127) into FP32 or BF16 (diagnostic helper).
  *   q [rows, cols] dense; s dense in the layout gran names; out [rows, cols]
  *   dense, dtype out_dtype.  BF16 output rounds to nearest even.

@@ -123,6 +123,9 @@ def test_transpose_and_moe_validation():
     assert gf(l1=f) == 2                     # no level-1 factor with E5M2
     gm = lambda G=4, Mm=256, K=512, m=f: L.fp8_grouped_gemm_masked(f, f, f, f, m, G, Mm, 256, K, f, 1, 0, None)
     assert gm(G=0) == 1 and gm(Mm=0) == 1 and gm(K=500) == 1 and gm(m=None) == 1
+    assert L.fp8_quant_blockwise_t(f, 0, 2, 256, 256, f, f, f, f, None) == 2   # bf16 only
+    assert L.fp8_quant_blockwise_t(f, 1, 2, 200, 256, f, f, f, f, None) == 1   # rows % 128
+    assert L.fp8_quant_blockwise_t(f, 1, 0, 256, 256, f, f, f, f, None) == 1   # G >= 1
     # three-pass baseline: shape and workspace checks
     assert fgb.fp8_naive_transpose_workspace_size(256, 384) == 4 * 256 * 384
     assert L.fp8_naive_transpose(f, f, 200, 256, f, f, f, 1 << 20, None) == 1

@@ -245,6 +245,22 @@ def test_grouped_direct_transpose(fgb, T, C):
     assert np.array_equal(np_(qt)[:, :k], oqt[:, :k])
 
 
+@pytest.mark.parametrize("G,rows,cols", [(1, 128, 128), (3, 256, 384), (32, 2048, 7168)])
+def test_quant_blockwise_t(fgb, G, rows, cols):
+    say("quant_blockwise with transposed copy", G, rows, cols)
+    g = torch.Generator().manual_seed(G + rows + cols)
+    w = (torch.randn(G, rows, cols, generator=g) * 0.02
+         * torch.exp2(torch.randint(-20, 8, (G, rows // 128, 1, cols // 128, 1), generator=g).float())
+         .expand(G, rows // 128, 128, cols // 128, 128).reshape(G, rows, cols)).to(torch.bfloat16)
+    w[0, :128, :128] = 0.0  # an all-zero block
+    q, s, qt, st = fgb.fp8_quant_blockwise_t(w.to(DEV))
+    for e in sorted({0, G - 1, G // 2}):
+        oq, os_ = O.quant_blockwise(bits(w[e]))
+        oqt, ost = O.block_transpose(oq, os_)
+        assert np.array_equal(np_(s[e]), os_) and np.array_equal(np_(q[e]), oq), e
+        assert np.array_equal(np_(st[e]), ost) and np.array_equal(np_(qt[e]), oqt), e
+
+
 def test_transpose_block_weights(fgb):
     say("transpose: 128x128-block weight transpose")
     q = rand_codes((2048, 1024), 5)
