@@ -119,6 +119,11 @@ def _call(name, *args):
 
 
 def _ptr(t):
+    # A temporary passed here (e.g. x.contiguous()) may be freed as soon as the
+    # call returns: every kernel is enqueued on torch's current stream, the
+    # stream the temporary was allocated on, and torch's caching allocator only
+    # hands a freed block to later work on that same stream, so the kernel
+    # always reads it before anything can overwrite it.
     return None if t is None else C.c_void_p(t.data_ptr())
 
 
