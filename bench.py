@@ -343,6 +343,69 @@ def _time_us(torch, fn, reps=10):
     return e0.elapsed_time(e1) / reps * 1e3
 
 
+def isolated_flushed(fgb, torch, W, dev):
+    """The bandwidth kernels of the step, each timed alone: before every one of
+    21 repetitions a 512 MB scratch buffer is written (twice the 256 MB
+    Infinity Cache), so the kernel's operands come from HBM; median of the
+    last 20 (the first warms up)."""
+    scratch = torch.empty(512 * 2 ** 20 // 4, dtype=torch.float32, device=dev)
+
+    def med_us(fn):
+        ts = []
+        for r in range(21):
+            scratch.fill_(float(r))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        ts = sorted(ts[1:])
+        return (ts[9] + ts[10]) / 2
+
+    out = {}
+
+    def rec(name, nbytes, fn):
+        us = med_us(fn)
+        out[name] = {"us": round(us, 1), "GB/s": round(nbytes / us / 1e3, 1),
+                     "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+    E = W["moe"]
+    T, H = E["X"].shape
+    G, M_cap, F = E["G"], E["M_cap"], E["F"]
+    topk = E["idx"].shape[1]
+    pad_rows = int(((E["counts"] + 15) // 16 * 16).sum())
+    xq, xs = fgb.fp8_quant_rowwise(E["X"])
+    rec("quant_rowwise X [16384, 7168]", T * H * 3 + T * H // 128, lambda: fgb.fp8_quant_rowwise(E["X"], 128, xq, xs))
+    L = W["lin"]
+    Tl, Cin = L["X"].shape
+    lq, ls = fgb.fp8_quant_rowwise(L["X"])
+    rec("quant_rowwise X [8192, 7168]", Tl * Cin * 3 + Tl * Cin // 128,
+        lambda: fgb.fp8_quant_rowwise(L["X"], 128, lq, ls))
+    rec("quant_blockwise W1 [131072, 7168]", E["W1"].numel() * 3 + E["W1"].numel() // 16384,
+        lambda: fgb.fp8_quant_blockwise(E["W1"]))
+    pq, ps, rmap, offs = fgb.permute_pad(xq, xs, E["idx"], G, 16, M_cap, E["ws"])
+    rec("permute_pad", T * H * (1 + 1 / 128) + pad_rows * H * (1 + 1 / 128) + 8 * T * topk,
+        lambda: fgb.permute_pad(xq, xs, E["idx"], G, 16, M_cap, E["ws"]))
+    h = torch.randn((M_cap, 2 * F), device=dev).to(torch.bfloat16)
+    rec("swiglu_quant", pad_rows * (2 * F * 2 + F * (1 + 1 / 128)), lambda: fgb.swiglu_quant(h, offs))
+    del h
+    y = torch.randn((M_cap, H), device=dev).to(torch.bfloat16)
+    rec("unpermute_unpad", T * topk * H * 2 + T * H * 2 + 8 * T * topk, lambda: fgb.unpermute_unpad(y, rmap, E["probs"]))
+    del y, pq, ps
+    Wg = W["wg"]
+    for key, qk, sk in (("direct_transpose X [32768, 7168]", "xq", "xs"), ("direct_transpose dY [32768, 2048]", "gq", "gs")):
+        q, sc = Wg[qk], Wg[sk]
+        rec(key, 2 * (q.numel() + q.numel() // 128), lambda: fgb.fp8_direct_transpose(q, sc))
+    if "moss" in W:
+        Wt = W["moss"]["Wt"]
+        R, Cc = Wt.shape
+        rec("mx2_quant W^T [28672, 8192]", R * Cc * (3 + 1 / 32) + 4 * R * ((Cc + 10239) // 10240),
+            lambda: fgb.mx2_quant(Wt, 10240))
+    del scratch
+    return out
+
+
 def format_variants(fgb, torch, W, dev, args):
     """Outside the step: the format variants on the step's tensors -- E5M2
     gradient quantization and transpose of the MoE dO, the Dgrad GEMM with an
@@ -538,6 +601,9 @@ def main():
         del hq, hs, da, dq, ds
         log(f"dswiglu study: {extra['dswiglu_quant']}")
 
+    if "moe" in W and "lin" in W and "wg" in W and not args.no_study:
+        extra["isolated_flushed"] = isolated_flushed(fgb, torch, W, dev)
+        log(f"isolated, Infinity Cache flushed: {extra['isolated_flushed']}")
     if "moe" in W and "dO" in W["moe"] and "lin" in W and not args.no_study:
         extra["format_variants"] = format_variants(fgb, torch, W, dev, args)
         log(f"format variants: {extra['format_variants']}")
