@@ -317,7 +317,16 @@ def cpu_baseline(torch, synth, seed, kernel_results, step_floor_s):
         f = fam(name)
         cpu_step_s += work / rates[f]
     value = 100.0 * step_floor_s / cpu_step_s
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": value, "unit": "% of MI355X roofline (step, extrapolated)", "cores": 1, "kind": "oracle",
+            "host_cpu": cpu_model, "host_nproc": os.cpu_count(),
             "step_seconds_extrapolated": cpu_step_s,
             "rates": {"quant_rowwise_GBps": rates["quant_rowwise"] / 1e9, "transpose_GBps": rates["transpose"] / 1e9,
                       "gemm_GFLOPs": rates["gemm"] / 1e9, "permute_GBps": rates["permute"] / 1e9,
