@@ -271,36 +271,47 @@ def cpu_baseline(torch, synth, seed, kernel_results, step_floor_s):
     import oracle as O
 
     rates = {}  # units of work per second, per op family
+    budget_s = 1.5  # per op family: the sample is repeated until this much CPU time is spent
+
+    def rate(key, work, fn):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            n += 1
+            dt = time.perf_counter() - t0
+            if dt >= budget_s:
+                break
+        rates[key] = n * work / dt
+
     t_all = time.perf_counter()
-    X, Wl, dY = synth.linear_dsv3(seed, T=256)
+    X, Wl, dY = synth.linear_dsv3(seed, T=1024)
     xb = synth.bf16_bits(X)
-    t = time.perf_counter(); xq, xs = O.quant_rowwise(xb); rates["quant_rowwise"] = xb.size * 3 / (time.perf_counter() - t)
-    wb = synth.bf16_bits(Wl[:256])
-    t = time.perf_counter(); O.quant_blockwise(wb); rates["quant_blockwise"] = wb.size * 3 / (time.perf_counter() - t)
-    t = time.perf_counter(); O.direct_transpose(xq, xs); rates["transpose"] = 2 * xq.size / (time.perf_counter() - t)
+    rate("quant_rowwise", xb.size * 3, lambda: O.quant_rowwise(xb))
+    xq, xs = O.quant_rowwise(xb)
+    wb = synth.bf16_bits(Wl[:1024])
+    rate("quant_blockwise", wb.size * 3, lambda: O.quant_blockwise(wb))
+    rate("transpose", 2 * xq.size, lambda: O.direct_transpose(xq, xs))
     wq, ws = O.quant_blockwise(synth.bf16_bits(Wl))
-    mi = np.arange(2000) % 256
-    ni = (np.arange(2000) * 7) % 2048
-    t = time.perf_counter(); O.block_gemm_sampled(xq, xs, O.ROW1x128, wq, ws, O.BLOCK128, mi, ni)
-    rates["gemm"] = 2 * 2000 * 7168 / (time.perf_counter() - t)
+    mi = np.arange(20000) % 1024
+    ni = (np.arange(20000) * 7) % 2048
+    rate("gemm", 2 * 20000 * 7168, lambda: O.block_gemm_sampled(xq, xs, O.ROW1x128, wq, ws, O.BLOCK128, mi, ni))
     Xm, idx, probs, _, _ = synth.moe(seed, T=2048, weights=False)
     xmq, xms = O.quant_rowwise(synth.bf16_bits(Xm))
-    t = time.perf_counter(); pq, ps, rm, off, used = O.permute_pad(xmq, xms, idx, 32, 16)
-    rates["permute"] = (xmq.size + used * 7168) / (time.perf_counter() - t)
+    pq, ps, rm, off, used = O.permute_pad(xmq, xms, idx, 32, 16)
+    rate("permute", xmq.size + used * 7168, lambda: O.permute_pad(xmq, xms, idx, 32, 16))
     y = synth.bf16_bits(torch.randn(used, 7168).to(torch.bfloat16))
-    t = time.perf_counter(); O.unpermute_unpad(y, rm, probs); rates["unpermute"] = (2048 * 8 * 7168 * 2) / (time.perf_counter() - t)
-    h = synth.bf16_bits(torch.randn(512, 4096).to(torch.bfloat16))
-    t = time.perf_counter(); O.swiglu_quant(h); rates["swiglu"] = h.size * 2 * 1.25 / (time.perf_counter() - t)
+    rate("unpermute", 2048 * 8 * 7168 * 2, lambda: O.unpermute_unpad(y, rm, probs))
+    h = synth.bf16_bits(torch.randn(1024, 4096).to(torch.bfloat16))
+    rate("swiglu", h.size * 2 * 1.25, lambda: O.swiglu_quant(h))
     hq, hs = O.quant_rowwise(h, 128)
-    da = synth.bf16_bits(torch.randn(512, 2048).to(torch.bfloat16))
-    t = time.perf_counter(); O.dswiglu_quant(hq, hs, da, None)
-    rates["dswiglu"] = 512 * (6 * 2048 + 4 * 2048 / 128) / (time.perf_counter() - t)
+    da = synth.bf16_bits(torch.randn(1024, 2048).to(torch.bfloat16))
+    rate("dswiglu", 1024 * (6 * 2048 + 4 * 2048 / 128), lambda: O.dswiglu_quant(hq, hs, da, None))
     M_cap = 2048 * 8 + 15 * 32
-    t = time.perf_counter(); O.quant_rowwise(O.unpermute_backward(y[:2048], rm, probs, M_cap), 128)
-    rates["unpermute_bwd"] = (2048 * 7168 * 2 + M_cap * 7168 * (1 + 1 / 128)) / (time.perf_counter() - t)
-    Wm, _ = synth.moss(seed, R=64, C=8192, M=1)
+    rate("unpermute_bwd", 2048 * 7168 * 2 + M_cap * 7168 * (1 + 1 / 128),
+         lambda: O.quant_rowwise(O.unpermute_backward(y[:2048], rm, probs, M_cap), 128))
+    Wm, _ = synth.moss(seed, R=256, C=8192, M=1)
     wmb = synth.bf16_bits(Wm)
-    t = time.perf_counter(); q, s2, s1 = O.mx2_quant(wmb, 10240); rates["mx2"] = wmb.size * 3 / (time.perf_counter() - t)
+    rate("mx2", wmb.size * 3, lambda: O.mx2_quant(wmb, 10240))
     sample_s = time.perf_counter() - t_all
 
     def fam(name):
@@ -333,11 +344,12 @@ def cpu_baseline(torch, synth, seed, kernel_results, step_floor_s):
                       "unpermute_GBps": rates["unpermute"] / 1e9, "swiglu_GBps": rates["swiglu"] / 1e9,
                       "mx2_GBps": rates["mx2"] / 1e9, "quant_blockwise_GBps": rates["quant_blockwise"] / 1e9,
                       "dswiglu_GBps": rates["dswiglu"] / 1e9, "unpermute_backward_quant_GBps": rates["unpermute_bwd"] / 1e9},
-            "sample": ("single-threaded oracle on: 256x7168 bf16 quant (row and block) and direct transpose, "
-                       "2000 sampled outputs of the 7168-deep Fprop, permute_pad of 2048 tokens top-8, "
-                       "unpermute of 2048 tokens, SwiGLU+quant of 512x4096, SwiGLU backward of 512x4096, "
-                       "unpermute backward + quant of 2048 tokens, MOSS quant of 64x8192; "
-                       f"{sample_s:.1f} s; step time extrapolated from the per-op rates")}
+            "sample": ("single-threaded oracle on: 1024x7168 bf16 quant (row and block) and direct transpose, "
+                       "20000 sampled outputs of the 7168-deep Fprop, permute_pad of 2048 tokens top-8, "
+                       "unpermute of 2048 tokens, SwiGLU+quant of 1024x4096, SwiGLU backward of 1024x4096, "
+                       "unpermute backward + quant of 2048 tokens, MOSS quant of 256x8192; each repeated "
+                       f"until {budget_s} s of CPU time; {sample_s:.1f} s in all; "
+                       "step time extrapolated from the per-op rates")}
 
 
 def _time_us(torch, fn, reps=10):
