@@ -91,6 +91,22 @@ struct GemmArgs {
     int64_t m_max;               // masked layout: rows reserved per expert
 };
 
+// Rows [lo, hi) of expert g in the M-grouped layouts: the group offsets, or
+// in the masked layout the first masked_m[g] (clamped to [0, m_max]) rows of
+// the expert's m_max-row slot.
+__device__ __forceinline__ void expert_rows(const GemmArgs &p, int g, int64_t &lo, int64_t &hi)
+{
+    if (p.masked_m) {
+        int64_t v = p.masked_m[g];
+        v = v < 0 ? 0 : (v > p.m_max ? p.m_max : v);
+        lo = (int64_t)g * p.m_max;
+        hi = lo + v;
+    } else {
+        lo = p.offs[g];
+        hi = p.offs[g + 1];
+    }
+}
+
 // Contiguous tile ranges per XCD: workgroup b runs on XCD b % 8.
 __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t nb)
 {
@@ -98,6 +114,19 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t nb)
     return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
+// Chunks of 32 tiles (one per CU of an XCD): XCD x runs chunk x of each group
+// of 8 chunks, so at any time the eight XCDs work on 8 neighbouring chunks,
+// i.e. on the same expert's weights; a last partial group falls back to
+// contiguous ranges.  Workgroup b runs on XCD b % 8.
+__device__ __forceinline__ int64_t xcd_chunked(int64_t b, int64_t nb)
+{
+    constexpr int64_t CH = 32;
+    const int64_t full = nb / (8 * CH) * (8 * CH);
+    if (b >= full)
+        return full + xcd_remap(b - full, nb - full);
+    const int64_t x = b & 7, i = b >> 3;
+    return (i / CH) * (8 * CH) + x * CH + (i % CH);
+}
 
 // LDS chunk swizzle of a 128-byte tile row: chunk c of row r sits at
 // position c ^ (r % 8).  For 8 consecutive rows reading one chunk the
@@ -160,9 +189,12 @@ gemm_fp8_kernel(GemmArgs p)
     const int64_t N = p.N;
 
     // ---- tile -> (m0, n0) ------------------------------------------------
-    // Within an XCD's contiguous range, tiles run in bands of GM m-tiles:
-    // consecutive tiles walk down a band first, so the ~32 tiles an XCD runs
-    // at once form a GM x 8 block sharing A rows and B columns in L2.
+    // Tiles run in bands of GM m-tiles: consecutive tiles walk down a band
+    // first, so the ~32 tiles an XCD runs at once form a GM x 8 block sharing
+    // A rows and B columns in L2.  Dense and K-grouped: each XCD takes a
+    // contiguous range of tiles.  M-grouped: chunks of 32 tiles interleave
+    // over the XCDs, so all of them work on one expert's weights at a time
+    // (with contiguous ranges each XCD held other experts' weights).
     // K-grouped: workgroups run expert by expert, and the remap applies inside
     // each expert's range, so every expert's tiles spread over all XCDs
     // (expert K ranges differ widely; whole experts per XCD would unbalance them).
@@ -170,7 +202,22 @@ gemm_fp8_kernel(GemmArgs p)
     int ke = 0; // K-grouped: this workgroup's expert, whose K range is [koffs[ke], koffs[ke+1])
     if constexpr (GK == GK_K)
         tiles_here = gridDim.x / p.G;
-    int64_t tile = xcd_remap(blockIdx.x % tiles_here, tiles_here);
+    if constexpr (GK == GK_M) {
+        // The grid is a host-side bound; the m-tiles that exist are counted
+        // from the expert row ranges and the surplus workgroups exit, so the
+        // XCD mapping spreads only real tiles.
+        int64_t mt = 0;
+        for (int g = 0; g < p.G; g++) {
+            int64_t lo, hi;
+            expert_rows(p, g, lo, hi);
+            mt += hi > lo ? (hi - lo + BM - 1) / BM : 0;
+        }
+        tiles_here = min(mt, (int64_t)gridDim.x / p.tiles_n) * p.tiles_n;
+        if ((int64_t)blockIdx.x >= tiles_here)
+            return; // uniform per workgroup
+    }
+    const int64_t tile = GK == GK_M ? xcd_chunked(blockIdx.x, tiles_here)
+                                    : xcd_remap(blockIdx.x % tiles_here, tiles_here);
     if constexpr (GK == GK_K) {
         ke = (int)(blockIdx.x / tiles_here);
         kbeg = p.koffs[ke];
@@ -190,26 +237,13 @@ gemm_fp8_kernel(GemmArgs p)
     if constexpr (GK != GK_M) {
         m0 = tm * BM;
         m_end = p.M;
-    } else if (p.masked_m) {
-        // masked layout: expert e owns rows [e*m_max, (e+1)*m_max), of which
-        // the first masked_m[e] are valid; m-tiles past them exit
-        const int64_t tpe = (p.m_max + BM - 1) / BM;
-        const int e = (int)(tm / tpe);
-        const int64_t mt = tm % tpe;
-        int64_t valid = e < p.G ? (int64_t)p.masked_m[e] : 0;
-        valid = valid < 0 ? 0 : (valid > p.m_max ? p.m_max : valid);
-        if (mt * BM >= valid)
-            return; // uniform per workgroup
-        m0 = (int64_t)e * p.m_max + mt * BM;
-        m_end = (int64_t)e * p.m_max + valid;
-        B += (int64_t)e * p.b_stride;
-        SB += (int64_t)e * p.sb_stride;
     } else {
         int e = -1;
         int64_t base = 0;
         for (int g = 0; g < p.G; g++) {
-            int64_t lo = p.offs[g], hi = p.offs[g + 1];
-            int64_t nt = (hi - lo + BM - 1) / BM;
+            int64_t lo, hi;
+            expert_rows(p, g, lo, hi);
+            const int64_t nt = hi > lo ? (hi - lo + BM - 1) / BM : 0;
             if (tm >= base && tm < base + nt) {
                 e = g;
                 m0 = lo + (tm - base) * BM;
@@ -218,7 +252,7 @@ gemm_fp8_kernel(GemmArgs p)
             base += nt;
         }
         if (e < 0)
-            return; // past the last expert tile (uniform per workgroup)
+            return; // not reached: tm < the counted m-tiles (uniform per workgroup)
         B += (int64_t)e * p.b_stride;
         SB += (int64_t)e * p.sb_stride;
     }
