@@ -55,6 +55,10 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB read + 1 GiB write elementwise kernel 3 times (the reference "
                          "point for scaling HBM byte counters), then exit")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="only time this library's blockwise GEMM (both modes) beside the vendor library's plain "
+                         "bf16 GEMM and row-wise-scaled FP8 GEMM (torch.matmul, torch._scaled_mm) at three shapes "
+                         "of the step, then exit: context for the GEMM rates, not part of the path")
     return ap.parse_args()
 
 
@@ -496,6 +500,40 @@ def format_variants(fgb, torch, W, dev, args):
     return out
 
 
+def vendor_gemm(fgb, torch, synth, dev, seed):
+    """Rates of the blockwise GEMM (A 1x128, B 128x128 scales; exact and fast
+    modes) and, on the same N(0,1) data, of the vendor library's bf16 GEMM
+    (no scaling) and FP8 GEMM with one scale per row of A and per row of B:
+    simpler computations than the blockwise one, timed as a point of
+    comparison for what the chip sustains at these shapes."""
+    out = {}
+    for (M, N, K) in [(16384, 4096, 7168), (8192, 2048, 7168), (8192, 7168, 2048)]:
+        fl = 2.0 * M * N * K
+        a = synth.normal((M, K), 1.0, seed, 61, dev, torch.bfloat16)
+        b = synth.normal((N, K), 1.0, seed, 62, dev, torch.bfloat16)
+        aq, as_ = fgb.fp8_quant_rowwise(a)
+        bq, bs = fgb.fp8_quant_blockwise(b)
+        a8, b8 = a.to(torch.float8_e4m3fn), b.to(torch.float8_e4m3fn)
+        sa = torch.ones(M, 1, device=dev)
+        sb = torch.ones(1, N, device=dev)
+        r = {}
+        for name, fn in [
+            ("blockwise exact", lambda: fgb.fp8_block_gemm(aq, as_, fgb.ROW1x128, bq, bs, fgb.BLOCK128,
+                                                            mode=fgb.GEMM_EXACT)),
+            ("blockwise fast", lambda: fgb.fp8_block_gemm(aq, as_, fgb.ROW1x128, bq, bs, fgb.BLOCK128,
+                                                           mode=fgb.GEMM_FAST)),
+            ("vendor bf16", lambda: torch.matmul(a, b.t())),
+            ("vendor fp8 row-wise scaled", lambda: torch._scaled_mm(a8, b8.t(), scale_a=sa, scale_b=sb,
+                                                                    out_dtype=torch.bfloat16)),
+        ]:
+            us = _time_us(torch, fn, reps=20)
+            r[name] = {"us": round(us, 1), "TFLOP/s": round(fl / us / 1e6, 1)}
+        out[f"{M}x{N}x{K}"] = r
+        log(f"vendor gemm {M}x{N}x{K}: {r}")
+        del a, b, aq, as_, bq, bs, a8, b8
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -516,6 +554,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration": {"launches": 3, "read_bytes_per_launch": 4 * n,
                                                "write_bytes_per_launch": 4 * n}}))
+        return
+    if args.vendor_gemm:
+        print(json.dumps({"vendor_gemm": vendor_gemm(fgb, torch, synth, dev, args.seed)}))
         return
     parts = set(args.parts.split(","))
     W = build(fgb, torch, synth, dev, args.seed, parts)
