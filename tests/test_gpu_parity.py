@@ -642,6 +642,57 @@ def test_grouped_gemm_small(fgb, mode):
 
 
 @pytest.mark.parametrize("mode", MODES)
+def test_grouped_gemm_all_experts_empty(fgb, mode):
+    say("grouped gemm: every expert empty (no tile exists, nothing written)", mode)
+    G, N, K, M_cap = 5, 256, 256, 300
+    off = np.zeros(G + 1, np.int32)
+    a = rand_codes((M_cap, K), 61)
+    sa = rand_scales((M_cap, K // 128), -4, 4, 62)
+    b = rand_codes((G, N, K), 63)
+    sb = rand_scales((G, N // 128, K // 128), -4, 4, 64)
+    d = torch.full((M_cap, N), 7.0, dtype=torch.bfloat16, device=DEV)
+    fgb.fp8_grouped_gemm(a.to(DEV), sa.to(DEV), b.to(DEV), sb.to(DEV), torch.from_numpy(off).to(DEV), d=d,
+                         mode=_mode(fgb, mode))
+    assert bool((d == 7.0).all())
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_grouped_gemm_past_one_chunk_group(fgb, mode):
+    """272 tiles: one full group of 8 x 32 tiles spread over the XCDs plus a
+    partial group of 16; every segment boundary row and sampled interior rows."""
+    say("grouped gemm: 3 experts, 17 m-tiles x 16 n-tiles, sampled + boundaries", mode)
+    G, N, K = 3, 4096, 256
+    off = np.array([0, 2000, 3504, 4208], np.int32)  # 2000, 1504, 704 rows: 8 + 6 + 3 m-tiles
+    M_cap = 4400
+    a = rand_codes((M_cap, K), 71)
+    sa = rand_scales((M_cap, K // 128), -6, 6, 72)
+    b = rand_codes((G, N, K), 73)
+    sb = rand_scales((G, N // 128, K // 128), -6, 6, 74)
+    d = torch.full((M_cap, N), 7.0, dtype=torch.float32, device=DEV)
+    fgb.fp8_grouped_gemm(a.to(DEV), sa.to(DEV), b.to(DEV), sb.to(DEV), torch.from_numpy(off).to(DEV), d=d,
+                         mode=_mode(fgb, mode))
+    got = np_(d)
+    assert np.all(got[off[G]:] == 7.0)
+    rng = np.random.default_rng(7)
+    edge = np.concatenate([off[:G], off[1:] - 1, off[:G] + 255, off[:G] + 256])
+    mi = np.concatenate([rng.integers(0, off[G], 6000), edge[edge < off[G]]])
+    mi = np.repeat(mi, 4)
+    ni = np.concatenate([rng.integers(0, N, mi.size - 8), [0, 255, 256, 2047, 2048, 3839, 3840, N - 1]])
+    ref = O.grouped_gemm_sampled(a.numpy(), sa.numpy(), b.numpy(), sb.numpy(), off, mi, ni)
+    bounds = None
+    if mode == "fast":
+        rm = np.zeros(mi.size)
+        asum = np.zeros(mi.size)
+        for g in range(G):
+            sel = (mi >= off[g]) & (mi < off[g + 1])
+            if sel.any():
+                rm[sel], asum[sel] = O.gemm_run_bounds_sampled(a.numpy(), sa.numpy(), O.ROW1x128, b.numpy()[g],
+                                                               sb.numpy()[g], O.BLOCK128, mi[sel], ni[sel])
+        bounds = (rm, asum)
+    check_gemm(got[mi, ni], ref, mode, False, bounds, K)
+
+
+@pytest.mark.parametrize("mode", MODES)
 def test_grouped_gemm_moe_fc1_sampled(fgb, mode):
     say("grouped gemm: fc1 of the 32-expert layer (N=4096, K=7168), sampled", mode)
     T, G, N, K = 16384, 32, 4096, 7168
