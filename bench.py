@@ -579,7 +579,7 @@ def vendor_gemm(fgb, torch, synth, dev, seed):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (sharding is a design note only)"}))
+        print(json.dumps({"error": "this library runs on one GPU; --gpus must be 1 (multi-GPU sharding is described, not implemented)"}))
         sys.exit(2)
     import torch
 
