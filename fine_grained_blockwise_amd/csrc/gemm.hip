@@ -72,7 +72,8 @@ template <int MODE> struct Waves {
     static constexpr int NW = MODE == MODE_EXACT ? 8 : 4;
 };
 enum { AG_ROW128 = 0, AG_ROW32 = 1 };
-enum { GK_NONE = 0, GK_M = 1, GK_K = 2 }; // dense, M-grouped (experts' rows), K-grouped (experts' K ranges)
+// dense, M-grouped (experts' rows: contiguous segments, or the masked layout), K-grouped (experts' K ranges)
+enum { GK_NONE = 0, GK_M = 1, GK_K = 2, GK_MM = 3 };
 enum { BG_ROW128 = 0, BG_ROW32 = 1, BG_BLOCK = 2 };
 
 struct GemmArgs {
@@ -202,7 +203,8 @@ gemm_fp8_kernel(GemmArgs p)
     int ke = 0; // K-grouped: this workgroup's expert, whose K range is [koffs[ke], koffs[ke+1])
     if constexpr (GK == GK_K)
         tiles_here = gridDim.x / p.G;
-    if constexpr (GK == GK_M) {
+    constexpr bool MG = GK == GK_M || GK == GK_MM; // M-grouped (GK_MM: the masked layout)
+    if constexpr (MG) {
         // The grid is a host-side bound; the m-tiles that exist are counted
         // from the expert row ranges and the surplus workgroups exit, so the
         // XCD mapping spreads only real tiles.
@@ -216,7 +218,7 @@ gemm_fp8_kernel(GemmArgs p)
         if ((int64_t)blockIdx.x >= tiles_here)
             return; // uniform per workgroup
     }
-    const int64_t tile = GK == GK_M ? xcd_chunked(blockIdx.x, tiles_here)
+    const int64_t tile = MG ? xcd_chunked(blockIdx.x, tiles_here)
                                     : xcd_remap(blockIdx.x % tiles_here, tiles_here);
     if constexpr (GK == GK_K) {
         ke = (int)(blockIdx.x / tiles_here);
@@ -234,7 +236,7 @@ gemm_fp8_kernel(GemmArgs p)
     }
     int64_t m0 = 0, m_end = 0;
     const uint8_t *B = p.b, *SB = p.sb;
-    if constexpr (GK != GK_M) {
+    if constexpr (!MG) {
         m0 = tm * BM;
         m_end = p.M;
     } else {
@@ -619,17 +621,29 @@ gemm_fp8_kernel(GemmArgs p)
             for (int t = 0; t < TJ; t++)
                 cB[t] = sub == 0 ? cvt8_bf16(xb[t].x, xb[t].y, sfB[t]) : cvt8_bf16(xb[t].z, xb[t].w, sfB[t]);
         };
+        // Masked layout (decode: experts with few valid rows): the wave's 32-row
+        // tiles past the expert's valid rows take no MFMAs, and a wave with no
+        // valid row skips its conversions too (rows_here below); it still makes
+        // its copies and meets every barrier.  Both conditions are uniform over
+        // the wave.  Only this form takes the branches: where full tiles
+        // dominate they cost ~5%.
+        const int nv = GK != GK_MM ? 4
+                                   : (int)min((int64_t)4, max((int64_t)0, (m_end - m0 - (int64_t)(wave_u / (NW / 2)) * 128 + 31) / 32));
         auto mfmas = [&]() {
 #pragma unroll
             for (int i = 0; i < 4; i++)
+                if (GK != GK_MM || i == 0 || i < nv)
 #pragma unroll
                 for (int j = 0; j < TJ; j++)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cA[i], cB[j], acc[i][j], 0, 0, 0);
         };
+        const bool rows_here = GK != GK_MM || m0 + (int64_t)(wave_u / (NW / 2)) * 128 < m_end;
 #define FGB_SLOT(SUB, RX, DMA)                                                                                         \
     do {                                                                                                               \
-        convert(SUB, rA[RX], rB[RX]);                                                                                  \
-        mfmas();                                                                                                       \
+        if (rows_here) {                                                                                               \
+            convert(SUB, rA[RX], rB[RX]);                                                                              \
+            mfmas();                                                                                                   \
+        }                                                                                                              \
         __builtin_amdgcn_sched_barrier(0);                                                                             \
         DMA;                                                                                                           \
         __builtin_amdgcn_sched_barrier(0);                                                                             \
@@ -771,10 +785,10 @@ static int launch_one(const GemmArgs &p, int64_t grid, hipStream_t st)
 template <int MODE, int GK>
 static int dispatch_mode(int ag, int bg, bool bf16, const GemmArgs &p, int64_t grid, hipStream_t st)
 {
-    if constexpr (GK == GK_M) {
+    if constexpr (GK == GK_M || GK == GK_MM) {
         if (ag == AG_ROW128 && bg == BG_BLOCK)
-            return bf16 ? launch_one<MODE, AG_ROW128, BG_BLOCK, true, GK_M>(p, grid, st)
-                        : launch_one<MODE, AG_ROW128, BG_BLOCK, false, GK_M>(p, grid, st);
+            return bf16 ? launch_one<MODE, AG_ROW128, BG_BLOCK, true, GK>(p, grid, st)
+                        : launch_one<MODE, AG_ROW128, BG_BLOCK, false, GK>(p, grid, st);
     } else if constexpr (GK == GK_K) {
         if (ag == AG_ROW128 && bg == BG_ROW128)
             return bf16 ? launch_one<MODE, AG_ROW128, BG_ROW128, true, GK_K>(p, grid, st)
@@ -950,7 +964,7 @@ extern "C" int fp8_grouped_gemm_masked(const uint8_t *a, const uint8_t *sa, cons
     p.m_max = M_max;
     const int64_t tiles = (int64_t)G * ((M_max + BM - 1) / BM) * p.tiles_n;
     FGB_REQUIRE(tiles < (1ll << 31), FGB_EINVAL, "fp8_grouped_gemm_masked: too many tiles");
-    return dispatch<GK_M>(mode, AG_ROW128, BG_BLOCK, d_dtype == FGB_BF16, p, tiles, (hipStream_t)stream);
+    return dispatch<GK_MM>(mode, AG_ROW128, BG_BLOCK, d_dtype == FGB_BF16, p, tiles, (hipStream_t)stream);
 }
 
 extern "C" int fp8_kgrouped_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t *b, const uint8_t *sb,
