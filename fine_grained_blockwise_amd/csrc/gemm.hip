@@ -495,7 +495,13 @@ gemm_fp8_kernel(GemmArgs p)
             }
         };
         // MFMAs of row tile i for half-step parity hs (32-blocks 2hs, 2hs+1 of the step)
+        // Masked layout: row tiles past the expert's valid rows take no MFMAs
+        // (uniform over the wave; see the exact-mode loop).
+        const int nvf = GK != GK_MM ? 4
+                                    : (int)min((int64_t)4, max((int64_t)0, (m_end - m0 - (int64_t)(wave_u / (NW / 2)) * 128 + 31) / 32));
         auto mfma_row = [&](int hs, int i, const uint4(&xa)[4][2], const uint4(&xb)[4][2]) {
+            if (GK == GK_MM && i >= nvf)
+                return;
             uint32_t wa = 0, wb = 0;
             if constexpr (A32) {
                 const int sh = 8 * (2 * hs + hk);
