@@ -294,7 +294,10 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const uint16_t *__restri
 // The exponential is the library's own fp32 function: Cody-Waite reduction
 // x = n*ln2 + r with ln2 split in two (Cody & Waite 1980), the degree-7 Taylor
 // polynomial of e^r (coefficients 1/j! rounded to fp32) in Horner form with
-// fused multiply-adds, and scaling by 2^n in two exact power-of-two steps.
+// fused multiply-adds, and scaling by 2^n.  The definition scales in two
+// power-of-two steps, p * 2^(n/2) (exact: p is near 1 and |n/2| <= 75 keeps
+// it normal in the range that is not clamped) and then * 2^(n - n/2), which
+// rounds once; v_ldexp_f32 rounds p * 2^n once, so it gives the same value.
 // Every step rounds once in fp32, so the result is reproducible bit for bit.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float fgb_expf(float x)
@@ -310,9 +313,7 @@ __device__ __forceinline__ float fgb_expf(float x)
     p = __builtin_fmaf(p, r, 0x1p-1f);
     p = __builtin_fmaf(p, r, 1.0f);
     p = __builtin_fmaf(p, r, 1.0f);
-    int ni = (int)n;
-    int n1 = ni / 2, n2 = ni - n1;
-    float res = (p * pow2f(n1)) * pow2f(n2);
+    float res = __builtin_amdgcn_ldexpf(p, (int)n);
     res = x > 0x1.62e43p+6f ? __builtin_inff() : res;
     res = x < -0x1.9fe36ap+6f ? 0.0f : res;
     return res;
