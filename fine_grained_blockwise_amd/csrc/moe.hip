@@ -65,14 +65,37 @@ __global__ __launch_bounds__(256) void pp_scan_kernel(const int32_t *__restrict_
                                                       int32_t *__restrict__ total,
                                                       int32_t *__restrict__ offs)
 {
-    extern __shared__ int32_t sh[]; // [G] padded sizes, then [G+1] offsets
-    int32_t *padded = sh, *off = sh + G;
-    for (int e = threadIdx.x; e < G; e += blockDim.x) {
-        int32_t s = 0;
-        for (int c = 0; c < nchunks; c++)
-            s += cnt[(int64_t)c * G + e];
-        total[e] = s;
-        padded[e] = (s + pad - 1) / pad * pad;
+    extern __shared__ int32_t sh[]; // [G] padded sizes, [G+1] offsets, [256] slice sums
+    int32_t *padded = sh, *off = sh + G, *part = sh + 2 * G + 1;
+    // S threads per expert (G <= 128), each summing a slice of the chunks;
+    // with more experts one thread per expert walks all chunks.
+    const int S = G <= 128 ? 256 / G : 1;
+    const int per = (nchunks + S - 1) / S;
+    if (S > 1) {
+        const int e = threadIdx.x / S, j = threadIdx.x % S;
+        const bool act = e < G;
+        const int c0 = min(nchunks, j * per), c1 = min(nchunks, c0 + per);
+        int32_t sum = 0;
+        if (act)
+            for (int c = c0; c < c1; c++)
+                sum += cnt[(int64_t)c * G + e];
+        part[threadIdx.x] = sum;
+        __syncthreads();
+        if (act && j == 0) {
+            int32_t t = 0;
+            for (int k = 0; k < S; k++)
+                t += part[threadIdx.x + k];
+            total[e] = t;
+            padded[e] = (t + pad - 1) / pad * pad;
+        }
+    } else {
+        for (int e = threadIdx.x; e < G; e += blockDim.x) {
+            int32_t t = 0;
+            for (int c = 0; c < nchunks; c++)
+                t += cnt[(int64_t)c * G + e];
+            total[e] = t;
+            padded[e] = (t + pad - 1) / pad * pad;
+        }
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -86,11 +109,25 @@ __global__ __launch_bounds__(256) void pp_scan_kernel(const int32_t *__restrict_
     __syncthreads();
     for (int e = threadIdx.x; e <= G; e += blockDim.x)
         offs[e] = off[e];
-    for (int e = threadIdx.x; e < G; e += blockDim.x) {
-        int32_t run = off[e];
-        for (int c = 0; c < nchunks; c++) {
-            base[(int64_t)c * G + e] = run;
-            run += cnt[(int64_t)c * G + e];
+    if (S > 1) {
+        const int e = threadIdx.x / S, j = threadIdx.x % S;
+        if (e < G) {
+            int32_t run = off[e];
+            for (int k = 0; k < j; k++)
+                run += part[e * S + k]; // the expert's slots in earlier slices
+            const int c0 = min(nchunks, j * per), c1 = min(nchunks, c0 + per);
+            for (int c = c0; c < c1; c++) {
+                base[(int64_t)c * G + e] = run;
+                run += cnt[(int64_t)c * G + e];
+            }
+        }
+    } else {
+        for (int e = threadIdx.x; e < G; e += blockDim.x) {
+            int32_t run = off[e];
+            for (int c = 0; c < nchunks; c++) {
+                base[(int64_t)c * G + e] = run;
+                run += cnt[(int64_t)c * G + e];
+            }
         }
     }
 }
@@ -703,7 +740,7 @@ extern "C" int permute_pad(const uint8_t *xq, const uint8_t *xs, const int32_t *
         pp_count_kernel<<<nchunks, 256, G * sizeof(int32_t), st>>>(topk_idx, T, topk, G, w.cnt);
         FGB_LAUNCHED("permute_pad/count");
     }
-    pp_scan_kernel<<<1, 256, (2 * G + 1) * sizeof(int32_t), st>>>(w.cnt, nchunks, G, pad_multiple,
+    pp_scan_kernel<<<1, 256, (2 * G + 1 + 256) * sizeof(int32_t), st>>>(w.cnt, nchunks, G, pad_multiple,
                                                                  w.base, w.total, group_offsets);
     FGB_LAUNCHED("permute_pad/scan");
     if (nchunks > 0) {
