@@ -128,6 +128,14 @@ __device__ __forceinline__ uint32_t bf16_rne(float f)
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two fp32 values -> two bf16 (round to nearest even, v_cvt_pk_bf16_f32), lo in the low half.
+typedef __bf16 fgb_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float fgb_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((fgb_f32x2){lo, hi}, fgb_bf16x2));
+}
+
 // DPP lane moves (row = 16 lanes).
 #define FGB_DPP_QUAD_XOR1 0xB1 // quad_perm [1,0,3,2]
 #define FGB_DPP_QUAD_XOR2 0x4E // quad_perm [2,3,0,1]

@@ -714,19 +714,45 @@ gemm_fp8_kernel(GemmArgs p)
         for (int ii = 0; ii < EPI_ROWS / 32; ii++) {
             const int i = part * (EPI_ROWS / 32) + ii;
 #pragma unroll
-            for (int j = 0; j < TJ; j++)
+            for (int j = 0; j < TJ; j++) {
+                if constexpr (OUT_BF16) {
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    int row = ii * 32 + (r / 4) * 8 + hk * 4 + (r % 4);
-                    int col = j * 32 + l32;
-                    float v = acc[i][j][r];
-                    if (p.l1)
-                        v *= l1v[j];
-                    if constexpr (OUT_BF16)
-                        *reinterpret_cast<uint16_t *>(ep + row * ROWB + col * 2) = (uint16_t)bf16_rne(v);
-                    else
+                    for (int q = 0; q < 4; q++) {
+                        // Rows ii*32 + q*8 + hk*4 + 0..3 of column j*32 + l32.
+                        // Lanes l and l^1 hold neighbouring columns: one exchange
+                        // per row pair gives the even lane rows 0 and 2, the odd
+                        // lane rows 1 and 3, each as two neighbouring columns (one
+                        // 4-byte LDS write instead of two 2-byte ones).
+                        float v[4];
+#pragma unroll
+                        for (int t = 0; t < 4; t++) {
+                            v[t] = acc[i][j][4 * q + t];
+                            if (p.l1)
+                                v[t] *= l1v[j];
+                        }
+                        const bool odd = l32 & 1;
+                        const float y0 = __uint_as_float(dpp<FGB_DPP_QUAD_XOR1>(__float_as_uint(odd ? v[0] : v[1])));
+                        const float y1 = __uint_as_float(dpp<FGB_DPP_QUAD_XOR1>(__float_as_uint(odd ? v[2] : v[3])));
+                        const int row = ii * 32 + q * 8 + hk * 4 + (odd ? 1 : 0);
+                        const int col = j * 32 + (l32 & ~1);
+                        *reinterpret_cast<uint32_t *>(ep + row * ROWB + col * 2) =
+                            odd ? pack_bf16x2(y0, v[1]) : pack_bf16x2(v[0], y0);
+                        *reinterpret_cast<uint32_t *>(ep + (row + 2) * ROWB + col * 2) =
+                            odd ? pack_bf16x2(y1, v[3]) : pack_bf16x2(v[2], y1);
+                    }
+                } else {
+                    // FP32 out: one 4-byte write per value (8-byte pairs measured slower)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        const int row = ii * 32 + (r / 4) * 8 + hk * 4 + (r % 4);
+                        const int col = j * 32 + l32;
+                        float v = acc[i][j][r];
+                        if (p.l1)
+                            v *= l1v[j];
                         *reinterpret_cast<float *>(ep + row * ROWB + col * 4) = v;
+                    }
                 }
+            }
         }
         __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0): this wave's LDS writes done
         __builtin_amdgcn_wave_barrier();
