@@ -61,9 +61,13 @@ constexpr int BM = 256, BN = 256, BK = 128;
 constexpr int NBUF = 2;                              // ring of K-step (K = 128) buffers
 constexpr int STEP_BYTES = BM * BK;                  // one operand tile of a K step: 32 KB
 constexpr int BUF_BYTES = 2 * STEP_BYTES;            // A and B: 64 KB
-constexpr int EPI_BYTES = 4 * 128 * (128 * 2 + 16); // epilogue staging, 4 waves (bf16; fp32 halves fit too)
-constexpr int MAIN_BYTES = NBUF * BUF_BYTES + 2 * 2 * 256 * 4; // ring + two K steps of scale tables
-constexpr int LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES; // 136 KB
+constexpr int SC_SLOT = 2 * 256 * 4;                 // A and B scale tables of one K step: 2 KB
+constexpr int SC_OFF = 0;                             // LDS: scale tables of two K steps,
+constexpr int RING_OFF = 2 * SC_SLOT;                 // then the ring of K-step buffers,
+constexpr int EPI_OFF = RING_OFF + BUF_BYTES;         // the epilogue staging from buffer 1 on
+constexpr int EPI_CAP = 8 * 64 * (64 * 2 + 16);       // largest staging (8 waves x 64 rows of 64 bf16): 72 KB
+constexpr int LDS_BYTES = EPI_OFF + EPI_CAP;          // 140 KB
+static_assert(LDS_BYTES >= RING_OFF + NBUF * BUF_BYTES, "the ring fits");
 
 enum { MODE_EXACT = 0, MODE_FAST = 1 };
 // Waves per workgroup: exact mode runs two waves per SIMD (its conversion
@@ -261,17 +265,15 @@ gemm_fp8_kernel(GemmArgs p)
     const int64_t n0 = tn * BN;
 
     // ---- LDS layout ----------------------------------------------------------
-    // Ring of 2 K-step buffers (K = 128 each): buffer b holds the A tile
-    // (256 rows x 128 bytes) at b*64K and the B tile at b*64K + 32K.  Row r's
-    // 16-byte chunk c sits at r*128 + 16*(c ^ swz(r)).  Scale tables (one
-    // dword per tile row of A and per tile column of B, the scale byte
-    // zero-extended, or the 4 bytes of the step's 32-element blocks) for two
-    // K steps follow the ring.  Step k uses buffer k % 2 and scale slot k % 2;
+    // Scale tables (one dword per tile row of A and per tile column of B, the
+    // scale byte zero-extended, or the 4 bytes of the step's 32-element
+    // blocks) for two K steps at SC_OFF, then a ring of 2 K-step buffers
+    // (K = 128 each) at RING_OFF: buffer b holds the A tile (256 rows x 128
+    // bytes) at b*64K and the B tile at b*64K + 32K.  Row r's 16-byte chunk c
+    // sits at r*128 + 16*(c ^ swz(r)).  Step k uses buffer k % 2 and scale slot k % 2;
     // each wave copies it with 2*IPO tile instructions and one scale
     // instruction, issued over the slots after the barrier that frees buffer
     // k % 2 (every wave has read step k-2).
-    constexpr int RING_BYTES = NBUF * BUF_BYTES;
-    constexpr int SC_SLOT = 2 * 256 * 4; // A and B tables of one K step
 
     // ---- copy plan ---------------------------------------------------------
     // Instruction g (0..IPO-1) of wave w copies tile rows w*RPW + g*8 .. +7,
@@ -354,7 +356,7 @@ gemm_fp8_kernel(GemmArgs p)
     // buffer with the bytes it already holds).
     auto dma_tile = [&](int k, int i) {
         const int kc = k < nk32 ? k : nk32 - 1;
-        const uint32_t dst = lds_base + (uint32_t)(kc & 1) * BUF_BYTES + (i >= IPO ? STEP_BYTES : 0) +
+        const uint32_t dst = lds_base + RING_OFF + (uint32_t)(kc & 1) * BUF_BYTES + (i >= IPO ? STEP_BYTES : 0) +
                              (wave_u * RPW + (i % IPO) * 8) * 128;
         if (i < IPO)
             dma16(a_base_u + (uint32_t)kc * 128u, a_off[i % IPO], dst);
@@ -365,7 +367,7 @@ gemm_fp8_kernel(GemmArgs p)
     // the same copy size (1x32 scales come on both sides or on neither).
     auto dma_scales = [&](int ks) {
         const int kc = ks < nk32 ? ks : nk32 - 1;
-        const uint32_t dst = lds_base + RING_BYTES + (uint32_t)(kc & 1) * SC_SLOT + (wave_u & 3) * 256;
+        const uint32_t dst = lds_base + SC_OFF + (uint32_t)(kc & 1) * SC_SLOT + (wave_u & 3) * 256;
         const uint32_t ka = A32 ? (uint32_t)kc * 4u : (uint32_t)kc, kb = B32 ? (uint32_t)kc * 4u : (uint32_t)kc;
         if constexpr (NW == 4) {
             if constexpr (A32)
@@ -411,7 +413,7 @@ gemm_fp8_kernel(GemmArgs p)
     // read_scales issues the LDS reads (raw dwords); pack_scales combines them
     // and is placed a few slots later so the reads have landed by then.
     auto read_scales = [&](int ks, uint32_t(&va)[4], uint32_t(&vb)[4]) {
-        const uint32_t *ta = reinterpret_cast<const uint32_t *>(smem + RING_BYTES + (ks & 1) * SC_SLOT);
+        const uint32_t *ta = reinterpret_cast<const uint32_t *>(smem + SC_OFF + (ks & 1) * SC_SLOT);
         const uint32_t *tb = ta + 256;
 #pragma unroll
         for (int t = 0; t < 4; t++) {
@@ -446,8 +448,8 @@ gemm_fp8_kernel(GemmArgs p)
 #pragma unroll
     for (int c = 0; c < 8; c++)
         qoff[c] = l32 * 128 + ((c ^ swz(l32)) * 16);
-    auto lds_a = [&](int k) { return smem + (k & 1) * BUF_BYTES + wm * 128 * 128; };
-    auto lds_b = [&](int k) { return smem + (k & 1) * BUF_BYTES + STEP_BYTES + wn * WNC * 128; };
+    auto lds_a = [&](int k) { return smem + RING_OFF + (k & 1) * BUF_BYTES + wm * 128 * 128; };
+    auto lds_b = [&](int k) { return smem + RING_OFF + (k & 1) * BUF_BYTES + STEP_BYTES + wn * WNC * 128; };
 
     v16f acc[4][TJ];
 #pragma unroll
@@ -693,15 +695,16 @@ gemm_fp8_kernel(GemmArgs p)
 
     // ---- epilogue --------------------------------------------------------------
     // 32x32 accumulator layout: lane l, register r -> row (r/4)*8 + (l/32)*4 + r%4,
-    // column l%32.  The tile is staged through LDS (free after the last
-    // barrier) so that global stores are 16 bytes per lane along rows: each
+    // column l%32.  The tile is staged through LDS (free after the barrier
+    // below; from buffer 1 on) so that global stores are 16 bytes per lane along rows: each
     // wave writes its 128 x WNC block, EPI_ROWS rows at a time, as
     // [row][WNC + pad] and reads it back row-contiguous.
     __syncthreads();
     constexpr int ESZ = OUT_BF16 ? 2 : 4;
     constexpr int ROWB = WNC * ESZ + 16; // padded LDS row (bytes)
-    constexpr int EPI_ROWS = NW * 128 * ROWB <= LDS_BYTES ? 128 : NW * 64 * ROWB <= LDS_BYTES ? 64 : 32;
-    uint8_t *ep = smem + wave * (EPI_ROWS * ROWB);
+    constexpr int EPI_ROWS = NW * 128 * ROWB <= EPI_CAP ? 128 : NW * 64 * ROWB <= EPI_CAP ? 64 : 32;
+    static_assert(NW * EPI_ROWS * ROWB <= EPI_CAP, "the staging fits");
+    uint8_t *ep = smem + EPI_OFF + wave * (EPI_ROWS * ROWB);
     float l1v[TJ];
 #pragma unroll
     for (int j = 0; j < TJ; j++) {
