@@ -42,7 +42,7 @@ SYMBOLS = [
     "unpermute_backward", "unpermute_backward_workspace_size", "fp8_block_transpose_batched",
     "fp8_grouped_direct_transpose", "fp8_kgrouped_gemm", "swiglu_quant_cache", "unpermute_backward_quant",
     "fp8_quant_rowwise_fmt", "fp8_dequant_fmt", "fgb_fp8_encode", "fp8_direct_transpose_fmt", "mx2_quant_rule",
-    "fp8_block_gemm_fmt", "fp8_grouped_gemm_masked", "fp8_quant_blockwise_t",
+    "fp8_block_gemm_fmt", "fp8_grouped_gemm_masked", "fp8_quant_blockwise_t", "swiglu_f32", "dswiglu_f32",
 ]
 
 
@@ -96,6 +96,8 @@ _SIG = {
     "fp8_grouped_gemm_masked": (_i32, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _p, _i32, _i32, _p]),
     "fp8_quant_blockwise_t": (_i32, [_p, _i32, _i32, _i64, _i64, _p, _p, _p, _p, _p]),
     "mx2_dequant": (_i32, [_p, _p, _p, _i64, _i64, _i64, _p, _p]),
+    "swiglu_f32": (_i32, [_p, _p, _i64, _p, _p]),
+    "dswiglu_f32": (_i32, [_p, _p, _p, _i64, _p, _p, _p]),
 }
 for _name, (_res, _args) in _SIG.items():
     _f = getattr(_lib, _name)
@@ -531,6 +533,30 @@ def swiglu_quant(h, group_offsets=None, q=None, s=None):
     _call("swiglu_quant", _ptr(h), M, F, _row_ld(h), _ptr(group_offsets), G, _ptr(q), _ptr(s),
           _stream(h))
     return q, s
+
+
+def swiglu_f32(g, u):
+    """Diagnostic: a = silu(g) * u in fp32, elementwise, the arithmetic of swiglu_quant."""
+    _check_dev(g, u)
+    g = g.contiguous().float()
+    u = u.contiguous().float()
+    if g.shape != u.shape:
+        raise ValueError("swiglu_f32: g and u must have the same shape")
+    a = torch.empty_like(g)
+    _call("swiglu_f32", _ptr(g), _ptr(u), g.numel(), _ptr(a), _stream(g))
+    return a
+
+
+def dswiglu_f32(g, u, da):
+    """Diagnostic: (du, dg) of the SwiGLU backward in fp32, elementwise, the arithmetic of dswiglu_quant."""
+    _check_dev(g, u, da)
+    g, u, da = (t.contiguous().float() for t in (g, u, da))
+    if g.shape != u.shape or g.shape != da.shape:
+        raise ValueError("dswiglu_f32: g, u and da must have the same shape")
+    du = torch.empty_like(g)
+    dg = torch.empty_like(g)
+    _call("dswiglu_f32", _ptr(g), _ptr(u), _ptr(da), g.numel(), _ptr(du), _ptr(dg), _stream(g))
+    return du, dg
 
 
 def dswiglu_quant(hq, hs, da, group_offsets=None, dq=None, ds=None):

@@ -356,11 +356,25 @@ __device__ __forceinline__ float fgb_expf(float x)
     return res;
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u)
+// The SwiGLU forward and backward values of one element in fp32, each
+// operation one rounding, in the order the C ABI declares; shared by the
+// quantizing kernels and the fp32 diagnostic entry points.
+__device__ __forceinline__ float swiglu_elem(float g, float u)
 {
     float e = fgb_expf(-g);
     float s = g / (1.0f + e);
     return s * u;
+}
+
+__device__ __forceinline__ void dswiglu_elem(float g, float u, float a, float &du, float &dg)
+{
+    const float e = fgb_expf(-g);
+    const float d = 1.0f + e;
+    const float sg = 1.0f / d;
+    const float silu = g / d;
+    du = a * silu;
+    const float dsilu = sg * (1.0f + g * (1.0f - sg));
+    dg = (a * u) * dsilu;
 }
 
 // 1x128 quantization of the 8 values a lane holds, 16 lanes forming one
@@ -416,8 +430,8 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(const uint8_t *__rest
                 uint32_t m = 0;
 #pragma unroll
                 for (int x = 0; x < 4; x++) {
-                    a[2 * x] = silu_mul(bf16lo(gw[x]), bf16lo(uw[x]));
-                    a[2 * x + 1] = silu_mul(bf16hi(gw[x]), bf16hi(uw[x]));
+                    a[2 * x] = swiglu_elem(bf16lo(gw[x]), bf16lo(uw[x]));
+                    a[2 * x + 1] = swiglu_elem(bf16hi(gw[x]), bf16hi(uw[x]));
                     m = max(m, __float_as_uint(a[2 * x]) & 0x7FFFFFFFu);
                     m = max(m, __float_as_uint(a[2 * x + 1]) & 0x7FFFFFFFu);
                 }
@@ -519,13 +533,7 @@ __global__ __launch_bounds__(256) void dswiglu_quant_kernel(const uint8_t *__res
                 uint32_t mg = 0, mu = 0;
 #pragma unroll
                 for (int k = 0; k < 8; k++) {
-                    const float e = fgb_expf(-g[k]);
-                    const float d = 1.0f + e;
-                    const float sg = 1.0f / d;
-                    const float silu = g[k] / d;
-                    du[k] = a[k] * silu;
-                    const float dsilu = sg * (1.0f + g[k] * (1.0f - sg));
-                    dg[k] = (a[k] * uu[k]) * dsilu;
+                    dswiglu_elem(g[k], uu[k], a[k], du[k], dg[k]);
                     mg = max(mg, __float_as_uint(dg[k]) & 0x7FFFFFFFu);
                     mu = max(mu, __float_as_uint(du[k]) & 0x7FFFFFFFu);
                 }
@@ -547,6 +555,26 @@ __global__ __launch_bounds__(256) void dswiglu_quant_kernel(const uint8_t *__res
                 }
             }
         }
+    }
+}
+
+// fp32 diagnostic forms: the element functions alone, one thread per element.
+__global__ __launch_bounds__(256) void swiglu_f32_kernel(const float *__restrict__ g, const float *__restrict__ u,
+                                                         int64_t n, float *__restrict__ a)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        a[i] = swiglu_elem(g[i], u[i]);
+}
+
+__global__ __launch_bounds__(256) void dswiglu_f32_kernel(const float *__restrict__ g, const float *__restrict__ u,
+                                                          const float *__restrict__ da, int64_t n,
+                                                          float *__restrict__ du, float *__restrict__ dg)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        float x, y;
+        dswiglu_elem(g[i], u[i], da[i], x, y);
+        du[i] = x;
+        dg[i] = y;
     }
 }
 
@@ -906,5 +934,32 @@ extern "C" int unpermute_backward_quant(const void *dout, const int32_t *row_map
     ub_token_quant_kernel<<<(unsigned)(g3 < 16384 ? g3 : 16384), 256, 0, st>>>(
         (const uint16_t *)dout, row_map, probs, inv, T, topk, H, M_cap, q, s);
     FGB_LAUNCHED("unpermute_backward_quant");
+    return FGB_OK;
+}
+
+extern "C" int swiglu_f32(const float *g, const float *u, int64_t n, float *a, void *stream)
+{
+    clear_error();
+    FGB_REQUIRE(n >= 0, FGB_EINVAL, "swiglu_f32: n must be >= 0");
+    if (n == 0)
+        return FGB_OK;
+    FGB_REQUIRE(g && u && a, FGB_EINVAL, "swiglu_f32: null pointer");
+    const int64_t grid = min((n + 255) / 256, (int64_t)65536);
+    swiglu_f32_kernel<<<(unsigned)grid, 256, 0, (hipStream_t)stream>>>(g, u, n, a);
+    FGB_LAUNCHED("swiglu_f32");
+    return FGB_OK;
+}
+
+extern "C" int dswiglu_f32(const float *g, const float *u, const float *da, int64_t n, float *du, float *dg,
+                           void *stream)
+{
+    clear_error();
+    FGB_REQUIRE(n >= 0, FGB_EINVAL, "dswiglu_f32: n must be >= 0");
+    if (n == 0)
+        return FGB_OK;
+    FGB_REQUIRE(g && u && da && du && dg, FGB_EINVAL, "dswiglu_f32: null pointer");
+    const int64_t grid = min((n + 255) / 256, (int64_t)65536);
+    dswiglu_f32_kernel<<<(unsigned)grid, 256, 0, (hipStream_t)stream>>>(g, u, da, n, du, dg);
+    FGB_LAUNCHED("dswiglu_f32");
     return FGB_OK;
 }

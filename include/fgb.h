@@ -462,6 +462,21 @@ int dswiglu_quant(const uint8_t *hq, const uint8_t *hs, const void *da, int64_t 
                   const int32_t *group_offsets, int G, uint8_t *dq, uint8_t *ds, void *stream);
 
 /*
+ * swiglu_f32, dswiglu_f32 -- diagnostic forms of swiglu_quant and
+ * dswiglu_quant: the same per-element fp32 arithmetic (the operations and
+ * order declared above), on fp32 inputs given directly and without the
+ * quantization, so that the values before rounding to FP8 can be compared
+ * bit for bit.
+ *   swiglu_f32:  a[i] = (g[i] / (1 + exp(-g[i]))) * u[i].
+ *   dswiglu_f32: du[i], dg[i] of dswiglu_quant for g[i], u[i] and the
+ *                gradient da[i].
+ *   All arrays are device fp32 [n], dense; outputs may not alias inputs.
+ *   Errors: FGB_EINVAL for n < 0 or a null pointer (n > 0).
+ */
+int swiglu_f32(const float *g, const float *u, int64_t n, float *a, void *stream);
+int dswiglu_f32(const float *g, const float *u, const float *da, int64_t n, float *du, float *dg, void *stream);
+
+/*
  * mx2_quant -- MOSS two-level microscaling ([MOSS] §3 two-level
  * microscaling, Fig. 2): level 1 is an FP32 factor alpha1 per g1 contiguous
  * elements of a row (last group partial), alpha1 = fp32(amax / 448), or 1

@@ -76,6 +76,8 @@ def lib():
         L.orc_expf_bulk.argtypes = [p, i64, p]
         L.orc_swiglu_quant.argtypes = [p, i64, i64, i64, p, i32, p, p]
         L.orc_dswiglu_quant.argtypes = [p, p, p, i64, i64, p, i32, p, p]
+        L.orc_swiglu_f32.argtypes = [p, p, i64, p]
+        L.orc_dswiglu_f32.argtypes = [p, p, p, i64, p, p]
         L.orc_mx2_quant.argtypes = [p, i64, i64, i64, p, p, p]
         L.orc_mx2_quant_rule.argtypes = [p, i64, i64, i64, i32, p, p, p]
         L.orc_mx2_dequant.argtypes = [p, p, p, i64, i64, i64, p]
@@ -483,6 +485,26 @@ def unpermute_backward(dout, row_map, probs, M_cap):
         pp = _p(probs)
     lib().orc_unpermute_backward(_p(dout), _p(row_map), pp, T, topk, H, M_cap, _p(dy))
     return dy
+
+
+def swiglu_f32(g, u):
+    """orc_swiglu_f32: a = silu(g) * u in fp32, elementwise (no quantization)."""
+    g = _c(g, np.float32)
+    u = _c(u, np.float32)
+    a = np.empty_like(g)
+    lib().orc_swiglu_f32(_p(g), _p(u), g.size, _p(a))
+    return a
+
+
+def dswiglu_f32(g, u, da):
+    """orc_dswiglu_f32: (du, dg) of the SwiGLU backward in fp32, elementwise (no quantization)."""
+    g = _c(g, np.float32)
+    u = _c(u, np.float32)
+    da = _c(da, np.float32)
+    du = np.empty_like(g)
+    dg = np.empty_like(g)
+    lib().orc_dswiglu_f32(_p(g), _p(u), _p(da), g.size, _p(du), _p(dg))
+    return du, dg
 
 
 def swiglu_quant(h, off=None):

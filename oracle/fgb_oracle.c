@@ -954,6 +954,34 @@ void orc_dswiglu_quant(const uint8_t *hq, const uint8_t *hs, const uint16_t *da,
 }
 
 /* ------------------------------------------------------------------------ */
+/* The SwiGLU forward and backward values in fp32, element by element,      */
+/* before any quantization: the same operations, in the same order, as     */
+/* orc_swiglu_quant and orc_dswiglu_quant above ([FLOW] "Core method";      */
+/* [DSV3] §3), for inputs given directly as fp32 (g, u; the gradient a).    */
+/* ------------------------------------------------------------------------ */
+void orc_swiglu_f32(const float *g, const float *u, int64_t n, float *a)
+{
+    for (int64_t i = 0; i < n; i++) {
+        float e = orc_expf(-g[i]);
+        float silu = g[i] / (1.0f + e);
+        a[i] = silu * u[i];
+    }
+}
+
+void orc_dswiglu_f32(const float *g, const float *u, const float *da, int64_t n, float *du, float *dg)
+{
+    for (int64_t i = 0; i < n; i++) {
+        float e = orc_expf(-g[i]);
+        float d = 1.0f + e;
+        float sg = 1.0f / d;
+        float silu = g[i] / d;
+        du[i] = da[i] * silu;
+        float dsilu = sg * (1.0f + g[i] * (1.0f - sg));
+        dg[i] = (da[i] * u[i]) * dsilu;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* MOSS two-level microscaling ([MOSS] §3 "two-level microscaling" and Fig. */
 /* 2): level 1 is an FP32 factor alpha1 = max|X| / 448 over a group of about */
 /* 10K elements; level 2 is an E8M0 power-of-two scale per 32 elements of   */

@@ -147,6 +147,10 @@ def test_transpose_and_moe_validation():
     assert L.dswiglu_quant(f, f, f, 10, 128, f, 0, f, f, None) == 1  # offsets without G
     assert L.mx2_quant(f, 4, 64, 48, f, f, f, None) == 2
     assert L.mx2_quant(f, 4, 48, 64, f, f, f, None) == 1
+    assert L.swiglu_f32(f, f, -1, f, None) == 1
+    assert L.swiglu_f32(f, None, 5, f, None) == 1
+    assert L.swiglu_f32(None, None, 0, None, None) == 0  # nothing to do
+    assert L.dswiglu_f32(f, f, f, 5, f, None, None) == 1
 
 
 def test_oracle_and_library_share_nothing():

@@ -609,6 +609,43 @@ def test_dswiglu_quant(fgb, M, F, use_off):
     assert np.array_equal(np_(dq)[:rows], oq[:rows])
 
 
+def _every_swiglu_input():
+    """Every g the SwiGLU kernels can see: all finite bf16 values (the forward's
+    input) and every finite E4M3 code times every 1x128 scale 2^-22..2^127
+    (the backward's dequantized cache)."""
+    b = np.arange(65536, dtype=np.uint32)
+    gb = (b << 16).view(np.float32)
+    gb = gb[np.isfinite(gb)]
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    dec = O.fp8_decode_all(O.E4M3)[codes].astype(np.float64)
+    g8 = dec[None, :] * np.ldexp(1.0, np.arange(-22, 128))[:, None]
+    g8 = g8[np.abs(g8) <= np.finfo(np.float32).max].astype(np.float32)  # finite in fp32
+    return np.concatenate([gb, g8])
+
+
+def test_swiglu_elementwise_exhaustive(fgb):
+    """The fp32 values swiglu_quant and dswiglu_quant quantize, for every input
+    g they can see, bit for bit against the oracle (random bf16 u and da, and
+    u = da = 1)."""
+    say("swiglu / dswiglu fp32 element values, every possible g")
+    g = _every_swiglu_input()
+    rng = np.random.default_rng(9)
+    for kind in ("random", "ones"):
+        if kind == "random":
+            u = torch.from_numpy(rng.standard_normal(g.size).astype(np.float32)).to(torch.bfloat16).float().numpy()
+            da = torch.from_numpy((rng.standard_normal(g.size) * 0.1).astype(np.float32)).to(torch.bfloat16).float().numpy()
+        else:
+            u = np.ones_like(g)
+            da = np.ones_like(g)
+        gd, ud, dad = (torch.from_numpy(np.ascontiguousarray(x)).to(DEV) for x in (g, u, da))
+        a = np_(fgb.swiglu_f32(gd, ud))
+        assert np.array_equal(a.view(np.uint32), O.swiglu_f32(g, u).view(np.uint32))
+        du, dg = fgb.dswiglu_f32(gd, ud, dad)
+        rdu, rdg = O.dswiglu_f32(g, u, da)
+        assert np.array_equal(np_(du).view(np.uint32), rdu.view(np.uint32))
+        assert np.array_equal(np_(dg).view(np.uint32), rdg.view(np.uint32))
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_grouped_gemm_small(fgb, mode):
     say("grouped gemm small, one empty expert, ragged segments", mode)

@@ -857,6 +857,34 @@ def test_dswiglu_quant_composition_and_special_cases():
     assert np.array_equal(dq2[:12], dq[:12]) and np.all(dq2[12:] == 0)
 
 
+def test_swiglu_f32_forms_are_the_quantized_paths_values():
+    """orc_swiglu_f32 and orc_dswiglu_f32 give exactly the fp32 values that
+    orc_swiglu_quant and orc_dswiglu_quant quantize: their 1x128 quantization
+    reproduces those outputs bit for bit."""
+    rng = np.random.default_rng(53)
+    M, F = 32, 256
+    h = torch.from_numpy((rng.standard_normal((M, 2 * F)) * 3).astype(np.float32)).to(torch.bfloat16)
+    hb = h.view(torch.int16).numpy().view(np.uint16)
+    g = h[:, :F].float().numpy()
+    u = h[:, F:].float().numpy()
+    a = O.swiglu_f32(g, u)
+    q_ref, s_ref = O.swiglu_quant(hb)
+    q, s = O.quant_rowwise(a, 128)
+    assert np.array_equal(q, q_ref) and np.array_equal(s, s_ref)
+    hq, hs, da = _dswiglu_inputs(63, M, F)
+    dab = da.view(torch.int16).numpy().view(np.uint16)
+    hd = O.dequant(hq, hs, O.ROW1x128).astype(np.float32)
+    du, dg = O.dswiglu_f32(hd[:, :F], hd[:, F:], da.float().numpy())
+    dq_ref, ds_ref = O.dswiglu_quant(hq, hs, dab)
+    dq, ds = O.quant_rowwise(np.concatenate([dg, du], axis=1), 128)
+    assert np.array_equal(dq, dq_ref) and np.array_equal(ds, ds_ref)
+    # special values: silu(0) = 0 with the sign of 0 * u, the clamps of exp
+    gz = np.array([0.0, -0.0, 100.0, -100.0, 89.0, -89.0, 1e-30, -1e-30], np.float32)
+    az = O.swiglu_f32(gz, np.ones_like(gz))
+    assert az[0] == 0 and az[2] == 100.0 and az[3] == 0.0 and az[4] == 89.0
+    assert np.signbit(az[1]) and np.signbit(az[3])  # -0/(1+e) and -100/inf are -0
+
+
 # --------------------------------------------------------------------------
 # MOSS two-level
 # --------------------------------------------------------------------------
