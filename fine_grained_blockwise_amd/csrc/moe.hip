@@ -356,13 +356,45 @@ __device__ __forceinline__ float fgb_expf(float x)
     return res;
 }
 
+// Correctly rounded 1/d for d in [1, 2^126): the hardware reciprocal
+// (within 1 ulp) refined by two Newton steps with fused multiply-adds, whose
+// remainders 1 - d*y are exact.
+__device__ __forceinline__ float recip_rn(float d)
+{
+    float y = __builtin_amdgcn_rcpf(d);
+    float r = __builtin_fmaf(-d, y, 1.0f);
+    y = __builtin_fmaf(r, y, y);
+    r = __builtin_fmaf(-d, y, 1.0f);
+    return __builtin_fmaf(r, y, y);
+}
+
+// Correctly rounded g/d from y = RN(1/d): q = g*y is within an ulp of the
+// quotient, its remainder g - q*d is exact, and one correction q + r*y rounds
+// to RN(g/d) (Markstein's theorem); an exact q (r = 0, also a signed zero) is
+// kept as it is.
+__device__ __forceinline__ float div_rn(float g, float d, float y)
+{
+    const float q = g * y;
+    const float r = __builtin_fmaf(-q, d, g);
+    return r == 0.0f ? q : __builtin_fmaf(r, y, q);
+}
+
 // The SwiGLU forward and backward values of one element in fp32, each
 // operation one rounding, in the order the C ABI declares; shared by the
-// quantizing kernels and the fp32 diagnostic entry points.
+// quantizing kernels and the fp32 diagnostic entry points.  The divisions
+// by d = 1 + e are IEEE-exact: recip_rn / div_rn where d < 2^126 (1/d normal),
+// the compiler's division otherwise (g < -87, rare; the branch is skipped
+// when no lane of the wave needs it).  Both sides are checked bit for bit
+// against the oracle's divisions for every input the kernels can see.
 __device__ __forceinline__ float swiglu_elem(float g, float u)
 {
-    float e = fgb_expf(-g);
-    float s = g / (1.0f + e);
+    const float e = fgb_expf(-g);
+    const float d = 1.0f + e;
+    float s;
+    if (d < 0x1p126f)
+        s = div_rn(g, d, recip_rn(d));
+    else
+        s = g / d;
     return s * u;
 }
 
@@ -370,8 +402,14 @@ __device__ __forceinline__ void dswiglu_elem(float g, float u, float a, float &d
 {
     const float e = fgb_expf(-g);
     const float d = 1.0f + e;
-    const float sg = 1.0f / d;
-    const float silu = g / d;
+    float sg, silu;
+    if (d < 0x1p126f) {
+        sg = recip_rn(d);
+        silu = div_rn(g, d, sg);
+    } else {
+        sg = 1.0f / d;
+        silu = g / d;
+    }
     du = a * silu;
     const float dsilu = sg * (1.0f + g * (1.0f - sg));
     dg = (a * u) * dsilu;
