@@ -140,7 +140,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 #define FGB_DPP_QUAD_XOR1 0xB1 // quad_perm [1,0,3,2]
 #define FGB_DPP_QUAD_XOR2 0x4E // quad_perm [2,3,0,1]
 #define FGB_DPP_HALF_MIRROR 0x141
-#define FGB_DPP_ROW_ROR4 0x124
 #define FGB_DPP_ROW_ROR8 0x128
 
 template <int CTRL>
