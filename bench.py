@@ -267,6 +267,20 @@ def traffic_for(kernel_name, mode):
         return None
 
 
+# Which sampled oracle rate prices each recorded operation of the step (first
+# match wins: the fused weight quantizer is a quantizer, not a transpose).
+ORACLE_FAMILIES = [("gemm", "gemm"), ("quant_blockwise", "quant_blockwise"), ("quant_rowwise", "quant_rowwise"),
+                   ("transpose", "transpose"), ("permute_pad", "permute"), ("unpermute_backward", "unpermute_bwd"),
+                   ("unpermute", "unpermute"), ("dswiglu", "dswiglu"), ("swiglu", "swiglu"), ("mx2", "mx2")]
+
+
+def oracle_family(name):
+    for key, fam in ORACLE_FAMILIES:
+        if key in name:
+            return fam
+    return None
+
+
 INPUT_KEYS = {"lin": ["X", "W", "dY"], "moe": ["X", "idx", "probs", "W1", "W2", "dO"],
               "wg": ["xq", "xs", "gq", "gs"], "moss": ["Wt", "A"]}
 
@@ -356,18 +370,9 @@ def cpu_baseline(torch, synth, seed, kernel_results, step_floor_s):
     rate("mx2", wmb.size * 3, lambda: O.mx2_quant(wmb, 10240))
     sample_s = time.perf_counter() - t_all
 
-    def fam(name):
-        for key, f in [("gemm", "gemm"), ("transpose", "transpose"), ("quant_blockwise", "quant_blockwise"),
-                       ("quant_rowwise", "quant_rowwise"), ("permute_pad", "permute"),
-                       ("unpermute_backward", "unpermute_bwd"), ("unpermute", "unpermute"), ("dswiglu", "dswiglu"),
-                       ("swiglu", "swiglu"), ("mx2", "mx2")]:
-            if key in name:
-                return f
-        return None
-
     cpu_step_s = cpu_step_all_s = 0.0
     for name, (ms, kind, work) in kernel_results.items():
-        f = fam(name)
+        f = oracle_family(name)
         cpu_step_s += work / rates[f]
         cpu_step_all_s += work / rates_all[f]
     value = 100.0 * step_floor_s / cpu_step_s
