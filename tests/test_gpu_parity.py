@@ -854,3 +854,55 @@ def test_mx2_small_and_rows_of_full(fgb):
         assert np.array_equal(np_(q), oq)
         xh = np_(fgb.mx2_dequant(q, s2, s1, g1))
         assert np.array_equal(xh, O.mx2_dequant(oq, os2, os1, g1))
+
+
+def test_determinism_every_kernel_family(fgb):
+    """Each kernel family twice on the same device inputs: identical bytes (no
+    float atomics, no order-dependent reductions anywhere)."""
+    say("determinism: every kernel family run twice")
+    torch.manual_seed(11)
+    T, H, F, G, topk = 1024, 1024, 512, 8, 4
+    x = torch.randn(T, H, device=DEV).to(torch.bfloat16)
+    w = (torch.randn(G, 2 * F, H, device=DEV) * 0.02).to(torch.bfloat16)
+    idx = torch.stack([torch.randperm(G)[:topk] for _ in range(T)]).to(torch.int32).to(DEV)
+    probs = torch.rand(T, topk, device=DEV)
+    h = (torch.randn(T * topk + 15 * G, 2 * F, device=DEV) * 3).to(torch.bfloat16)
+    yb = torch.randn(T * topk + 15 * G, H, device=DEV).to(torch.bfloat16)
+
+    def run():
+        out = []
+        xq, xs = fgb.fp8_quant_rowwise(x)
+        wq, ws, wqt, wst = fgb.fp8_quant_blockwise_t(w)
+        xt, xts = fgb.fp8_direct_transpose(xq, xs)
+        out += [xq, xs, wq, ws, wqt, wst, xt, xts]
+        for mode in (fgb.GEMM_EXACT, fgb.GEMM_FAST):
+            for od in (torch.bfloat16, torch.float32):
+                out.append(fgb.fp8_block_gemm(xq, xs, fgb.ROW1x128, wq[0], ws[0], fgb.BLOCK128, out_dtype=od,
+                                              mode=mode))
+        pq, ps, rmap, offs = fgb.permute_pad(xq, xs, idx, G, 16)
+        n = int(offs[-1])  # rows at or past off[G] are not written
+        out += [pq[:n], ps[:n], rmap, offs]
+        for mode in (fgb.GEMM_EXACT, fgb.GEMM_FAST):
+            y = fgb.fp8_grouped_gemm(pq, ps, wq, ws, offs, mode=mode)
+            out.append(y[:int(offs[-1])])
+        q, s, hq, hs = fgb.swiglu_quant_cache(h[:pq.shape[0]], offs)
+        out += [q[:n], s[:n], hq[:n], hs[:n]]
+        dq, ds = fgb.dswiglu_quant(hq, hs, h[:pq.shape[0], :F].contiguous(), offs)
+        out += [dq[:n], ds[:n]]
+        out.append(fgb.unpermute_unpad(yb, rmap, probs))
+        uq, us = fgb.unpermute_backward_quant(x, rmap, probs, pq.shape[0])
+        out += [uq, us]
+        qt, st, koff = fgb.fp8_grouped_direct_transpose(uq, us, offs)
+        kend = int(koff[-1])
+        out += [qt[:, :kend], st[:, :kend // 128], koff]
+        for mode in (fgb.GEMM_EXACT, fgb.GEMM_FAST):
+            out.append(fgb.fp8_kgrouped_gemm(qt[:256], st[:256], qt, st, koff, mode=mode))
+        mq, m2, m1 = fgb.mx2_quant(x, 640)
+        out += [mq, m2, m1]
+        torch.cuda.synchronize()
+        return [t.clone() for t in out]
+
+    a, b = run(), run()
+    for i, (u, v) in enumerate(zip(a, b)):
+        assert u.shape == v.shape and torch.equal(u.view(torch.uint8) if u.dtype.is_floating_point else u,
+                                                  v.view(torch.uint8) if v.dtype.is_floating_point else v), i
