@@ -805,12 +805,19 @@ template <int MODE, int AG, int BG, bool OUT_BF16, int GK, int AF = FMT_E4M3>
 static int launch_one(const GemmArgs &p, int64_t grid, hipStream_t st)
 {
     auto kern = gemm_fp8_kernel<MODE, AG, BG, OUT_BF16, GK, AF>;
-    static bool attr_set = false; // per instantiation, set once per process
-    if (!attr_set) {
+    // The LDS limit is raised once per instantiation and device (a process may
+    // use several devices); devices beyond the table set it on every call.
+    static bool attr_set[64] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
+        dev = -1;
+    const bool cached = dev >= 0 && dev < 64;
+    if (!cached || !attr_set[dev]) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
         if (e != hipSuccess)
             return set_error(FGB_EHIP, "gemm: hipFuncSetAttribute failed: %s", hipGetErrorString(e));
-        attr_set = true;
+        if (cached)
+            attr_set[dev] = true;
     }
     kern<<<(unsigned)grid, Waves<MODE>::NW * 64, LDS_BYTES, st>>>(p);
     FGB_LAUNCHED("gemm_fp8_kernel");
