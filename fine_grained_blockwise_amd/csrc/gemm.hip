@@ -26,29 +26,26 @@
 //   are).  Twice the MFMA rate, with the matrix unit's own product-sum
 //   precision (see above); accumulation across K groups is FP32.
 //
-// Tiling: 256x256 output tile per workgroup of 4 waves (each wave 128x128 =
-// 4x4 tiles of 32x32), K step 128 split into two 64-deep half-steps.  A and
-// B tiles go HBM -> LDS with global_load_lds (16 bytes per lane) through a
-// ring of 4 half-step buffers; each wave issues two copy instructions per
-// 16 (exact) or 4 (fast) MFMAs, so the copies of half-step h+4 trickle out
-// during half-step h and have three half-steps to land, and a barrier comes
-// once per half-step.  The scale bytes travel the same way (one dword per
-// tile row or column, in two K-step tables).  LDS rows are 64 bytes with
-// the 16-byte chunk index XOR-swizzled by a function of row % 16, so the
-// operand reads of 8 or 16 consecutive rows hit distinct banks and each copy
-// instruction has per-lane offsets that do not depend on which 16 rows it
-// moves.  Tiles
-// are mapped to XCDs in contiguous ranges, in bands of 4 m-tiles, so
-// neighbouring tiles share an XCD's L2.
+// Tiling: a 256x256 output tile per workgroup, K steps of 128.  Four waves,
+// one per SIMD, each own a 128x128 quarter (4x4 tiles of 32x32); the exact
+// mode's masked layout runs eight waves of 128x64 instead (two per SIMD).  A
+// and B tiles go HBM -> LDS with global_load_lds (16 bytes per lane) through
+// a ring of two K-step buffers (64 KB each, A then B); one barrier per K step
+// waits for step k+1 and frees the buffer of step k, and step k+2's copies
+// trickle out over the slots that follow it, between the MFMAs.  The scale
+// bytes travel the same way into two K-step tables.  A tile row (128 bytes
+// of one K step) keeps its 16-byte chunk c at position c ^ (row % 8), so the
+// reads of one chunk by 8 or 16 consecutive rows are free of bank conflicts.
+// Tiles run in bands of 4 m-tiles; dense and K-grouped launches give each XCD
+// a contiguous range of tiles, M-grouped ones interleave chunks of 32 tiles
+// over the XCDs.
 //
 // Fragment layout, per lane (row r = lane%32 of a 32-row tile, half h =
-// lane/32), per 64-byte half-step: chunks h and 2+h.
-//   FAST : one 64-wide MFMA step per half-step: chunk h is bytes 0-15
-//          (hardware K block 0), chunk 2+h bytes 16-31 (block 1); the
-//          hardware takes block b's scale from lane r + 32b, so lane half h
-//          supplies the scale of the half-step's 32-block h.
-//   EXACT: 32-wide pair p' (0, 1) of the half-step uses chunk 2p'+h; its
-//          bytes 0-7 feed one bf16 MFMA sub-step and bytes 8-15 the next.
+// lane/32), per K step (chunks 0-7 of each tile row):
+//   FAST : half-step hs (64 K) is one 32x32x64 scaled MFMA; lane half h
+//          supplies chunks 4hs+h and 4hs+2+h.
+//   EXACT: 16-deep sub-step s uses bytes 0-7 (s even) or 8-15 (s odd) of
+//          chunk 2(s/2)+h, converted to 8 bf16 values.
 #include "fgb_internal.h"
 
 namespace fgb {
@@ -70,14 +67,16 @@ constexpr int LDS_BYTES = EPI_OFF + EPI_CAP;          // 140 KB
 static_assert(LDS_BYTES >= RING_OFF + NBUF * BUF_BYTES, "the ring fits");
 
 enum { MODE_EXACT = 0, MODE_FAST = 1 };
-// Waves per workgroup: exact mode runs two waves per SIMD (its conversion
-// work hides behind the other wave's MFMAs), fast mode one.
-template <int MODE> struct Waves {
-    static constexpr int NW = MODE == MODE_EXACT ? 8 : 4;
-};
 enum { AG_ROW128 = 0, AG_ROW32 = 1 };
 // dense, M-grouped (experts' rows: contiguous segments, or the masked layout), K-grouped (experts' K ranges)
 enum { GK_NONE = 0, GK_M = 1, GK_K = 2, GK_MM = 3 };
+// Waves per workgroup: one per SIMD (each 128 x 128 of the tile), except the
+// exact mode's masked layout, which runs two per SIMD (each 128 x 64): there
+// most tiles have valid rows only in their upper half, and with 128 x 128
+// waves the lower half's SIMDs would idle.
+template <int MODE, int GK> struct Waves {
+    static constexpr int NW = MODE == MODE_EXACT && GK == GK_MM ? 8 : 4;
+};
 enum { BG_ROW128 = 0, BG_ROW32 = 1, BG_BLOCK = 2 };
 
 struct GemmArgs {
@@ -179,12 +178,12 @@ __device__ __forceinline__ v16f mfma_scaled(v8i a, v8i b, v16f c, uint32_t sa, u
 
 // AF: element format of A's codes (FMT_E4M3, or FMT_E5M2 for gradients).
 template <int MODE, int AG, int BG, bool OUT_BF16, int GK, int AF = FMT_E4M3>
-__global__ __launch_bounds__(Waves<MODE>::NW * 64) __attribute__((amdgpu_waves_per_eu(Waves<MODE>::NW / 4, Waves<MODE>::NW / 4))) void
+__global__ __launch_bounds__((Waves<MODE, GK>::NW * 64)) __attribute__((amdgpu_waves_per_eu(Waves<MODE, GK>::NW / 4, Waves<MODE, GK>::NW / 4))) void
 gemm_fp8_kernel(GemmArgs p)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     // NW waves: a 2 x NW/2 grid of 128 x WNC sub-tiles (TJ column tiles of 32)
-    constexpr int NW = Waves<MODE>::NW, WNC = 256 / (NW / 2), TJ = WNC / 32;
+    constexpr int NW = Waves<MODE, GK>::NW, WNC = 256 / (NW / 2), TJ = WNC / 32;
     constexpr int RPW = 256 / NW, IPO = RPW / 8; // copy rows and instructions per wave and operand
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / (NW / 2), wn = wave % (NW / 2);
@@ -462,10 +461,14 @@ gemm_fp8_kernel(GemmArgs p)
     // ---- prologue ----------------------------------------------------------------
     // Step 0 and the first part of step 1 in flight (the rest of step 1 is
     // issued in the first slots of the main loop); wait for step 0 and sync.
-    if constexpr (NW == 4) {
+    if constexpr (MODE == MODE_FAST) {
         dma_step(0, 0, 2 * IPO - 1);
         dma_step(1, 0, 11);
-        FGB_WAIT_SYNC(13); // step 1's scale and 12 tile instructions
+        FGB_WAIT_SYNC(14); // step 1's two scale and 12 tile instructions
+    } else if constexpr (NW == 4) {
+        dma_step(0, 0, 2 * IPO - 1);
+        dma_step(1, 0, 7);
+        FGB_WAIT_SYNC(10); // step 1's two scale and 8 tile instructions
     } else {
         dma_step(0, 0, 2 * IPO - 1);
         dma_step(1, 0, 2);
@@ -583,8 +586,145 @@ gemm_fp8_kernel(GemmArgs p)
             pack_scales(sva, svb, ca, cb);
             __builtin_amdgcn_sched_barrier(0);
         }
+    } else if constexpr (NW == 4) {
+        // Exact mode, 4 waves (one per SIMD, each 128 x 128).  A slot is one
+        // 16-deep sub-step s: its 16 bf16 MFMAs, with the 32 conversions of
+        // sub-step s+1 into the other operand buffer issued between them, so
+        // the single wave keeps the matrix unit fed while it converts.  Sub-step
+        // s takes bytes 0-7 (s even) or 8-15 (s odd) of chunk 2q + hk of each
+        // tile row, q = s/2 the 32-wide pair.  A slot is cut into quarters of
+        // 4 MFMAs (row tile t) and 8 conversions (A and B tile t), each quarter
+        // carrying its share of the slot's LDS reads and copies, so that no
+        // run of memory instructions leaves the matrix unit idle.  Pair q's
+        // reads are issued one slot before its first conversion; the barrier
+        // before slot 6 waits for step ks+1 and frees buffer ks % 2 (pair 3
+        // was converted in slot 5); step ks+2's copies go out in slots 6-7 and
+        // 0-2.
+        static_assert(GK != GK_MM, "the masked layout runs 8 waves");
+        uint4 rA[2][4], rB[2][4]; // FP8 fragments of two pairs
+        v8bf cA[2][4], cB[2][4];  // bf16 operands of two sub-steps
+        float sfA[4], sfB[4];     // scale factors of the pair being converted
+        auto factors = [&](int q) {
+#pragma unroll
+            for (int t = 0; t < 4; t++)
+                if (A32 || q == 0)
+                    sfA[t] = scale_f32(A32 ? (ca[t] >> (8 * q)) & 0xFFu : (ca[0] >> (8 * t)) & 0xFFu);
+#pragma unroll
+            for (int t = 0; t < 4; t++)
+                if (B32 || q == 0)
+                    sfB[t] = scale_f32(B32 ? (cb[t] >> (8 * q)) & 0xFFu
+                                           : (BG == BG_BLOCK ? cb[0] : (cb[0] >> (8 * t)) & 0xFFu));
+        };
+        // Tile t of pair q of step k (A and B), its conversion for sub-step
+        // half `half` into buffer `half`, and the MFMAs of row tile i.
+        auto read_piece = [&](int k, int q, int t, uint4(&xa)[4], uint4(&xb)[4]) {
+            const int c = 2 * q + hk;
+            xa[t] = *reinterpret_cast<const uint4 *>(lds_a(k) + qoff[c] + t * 4096);
+            xb[t] = *reinterpret_cast<const uint4 *>(lds_b(k) + qoff[c] + t * 4096);
+        };
+        auto cvt_piece = [&](int half, int t, const uint4(&xa)[4], const uint4(&xb)[4]) {
+            if constexpr (AF == FMT_E5M2)
+                cA[half][t] = half == 0 ? cvt8_bf16_e5m2(xa[t].x, xa[t].y, sfA[t]) : cvt8_bf16_e5m2(xa[t].z, xa[t].w, sfA[t]);
+            else
+                cA[half][t] = half == 0 ? cvt8_bf16(xa[t].x, xa[t].y, sfA[t]) : cvt8_bf16(xa[t].z, xa[t].w, sfA[t]);
+            cB[half][t] = half == 0 ? cvt8_bf16(xb[t].x, xb[t].y, sfB[t]) : cvt8_bf16(xb[t].z, xb[t].w, sfB[t]);
+        };
+        auto mfma_row = [&](int buf, int i) {
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cA[buf][i], cB[buf][j], acc[i][j], 0, 0, 0);
+        };
+        // Quarter T of a slot: the statements written before it (copies,
+        // reads), then row tile T's 4 MFMAs on buffer 1 - HALF, each followed
+        // by 2 of the 8 conversions of piece T of the next sub-step (from
+        // fragments RX) into buffer HALF.
+#define FGB_Q(HALF, RX, T)                                                                                             \
+    do {                                                                                                               \
+        cvt_piece(HALF, T, rA[RX], rB[RX]);                                                                            \
+        mfma_row(1 - (HALF), T);                                                                                       \
+        for (int k_ = 0; k_ < 4; k_++) {                                                                               \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); /* 1 MFMA */                                            \
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0); /* 2 VALU */                                            \
+        }                                                                                                              \
+        __builtin_amdgcn_sched_barrier(0);                                                                             \
+    } while (0)
+
+        // sub-step 0 of step 0 into buffer 0
+        factors(0);
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+            read_piece(0, 0, t, rA[0], rB[0]);
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+            cvt_piece(0, t, rA[0], rB[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        for (int ks = 0; ks < nk32; ks++) {
+            // slot s: MFMAs of sub-step s (buffer s % 2); conversions of
+            // sub-step s+1 (pair (s+1)/2, half (s+1) % 2) into buffer (s+1) % 2
+            // slot 0: pair 1's reads; step ks+1's copies 8-11
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                read_piece(ks, 1, t, rA[1], rB[1]);
+                dma_tile(ks + 1, 8 + t);
+                FGB_Q(1, 0, t);
+            }
+            // slot 1: copies 12-13
+            factors(1);
+            dma_tile(ks + 1, 12);
+            FGB_Q(0, 1, 0);
+            dma_tile(ks + 1, 13);
+            FGB_Q(0, 1, 1);
+            FGB_Q(0, 1, 2);
+            FGB_Q(0, 1, 3);
+            // slot 2: pair 2's reads; copies 14-15
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                read_piece(ks, 2, t, rA[0], rB[0]);
+                if (t < 2)
+                    dma_tile(ks + 1, 14 + t);
+                FGB_Q(1, 1, t);
+            }
+            // slot 3
+            factors(2);
+#pragma unroll
+            for (int t = 0; t < 4; t++)
+                FGB_Q(0, 0, t);
+            // slot 4: pair 3's reads
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                read_piece(ks, 3, t, rA[1], rB[1]);
+                FGB_Q(1, 0, t);
+            }
+            // slot 5
+            factors(3);
+#pragma unroll
+            for (int t = 0; t < 4; t++)
+                FGB_Q(0, 1, t);
+            // slot 6: step ks+1 has landed (nothing issued after it) and buffer
+            // ks % 2 is free; step ks+1's scales and pair 0, step ks+2's scales
+            // and copies 0-3.  After the last step these reads touch only LDS
+            // and are discarded.
+            FGB_WAIT_SYNC(0);
+            read_scales(ks + 1, sva, svb);
+            dma_scales(ks + 2);
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                read_piece(ks + 1, 0, t, rA[0], rB[0]);
+                dma_tile(ks + 2, t);
+                FGB_Q(1, 1, t);
+            }
+            // slot 7: step ks+1's scales replace the current ones; copies 4-7
+            pack_scales(sva, svb, ca, cb);
+            factors(0);
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                dma_tile(ks + 2, 4 + t);
+                FGB_Q(0, 0, t);
+            }
+        }
+#undef FGB_Q
     } else {
-        // Exact mode, 8 waves (two per SIMD, each 128 x 64): a slot is one
+        // Exact mode, 8 waves (the masked layout; two per SIMD, each 128 x 64): a slot is one
         // 16-deep sub-step -- the 24 conversions of its FP8 fragments (4 A
         // tiles, 2 B tiles; the scale folded in) and its 8 bf16 MFMAs; while
         // one wave of a SIMD converts, the other keeps the matrix unit busy.
@@ -819,7 +959,7 @@ static int launch_one(const GemmArgs &p, int64_t grid, hipStream_t st)
         if (cached)
             attr_set[dev] = true;
     }
-    kern<<<(unsigned)grid, Waves<MODE>::NW * 64, LDS_BYTES, st>>>(p);
+    kern<<<(unsigned)grid, Waves<MODE, GK>::NW * 64, LDS_BYTES, st>>>(p);
     FGB_LAUNCHED("gemm_fp8_kernel");
     return FGB_OK;
 }
