@@ -848,9 +848,21 @@ gemm_fp8_kernel(GemmArgs p)
     float l1v[TJ];
 #pragma unroll
     for (int j = 0; j < TJ; j++) {
-        int64_t col = n0 + wn * WNC + j * 32 + l32;
+        const int64_t col = n0 + wn * WNC + j * 32 + l32;
         l1v[j] = (p.l1 && col < N) ? p.l1[col] : 1.0f;
     }
+    // read-back geometry: one row segment of 16 bytes per lane
+    constexpr int LPR = WNC * ESZ / 16; // lanes per row
+    constexpr int RPI = 64 / LPR;       // rows per instruction
+    const int lr = lane / LPR, lc = lane % LPR;
+    const int64_t col0 = n0 + wn * WNC + lc * (16 / ESZ);
+    const int64_t row_w = m0 + wm * 128; // the wave's first row
+    const int64_t ld_bytes = p.ldd * ESZ;
+    uint8_t *const dwave = (uint8_t *)p.d + (ke * p.d_stride + row_w * p.ldd + col0) * ESZ;
+    // rows of the wave below m_end (0..128) and whether this lane's 16 bytes are a whole aligned segment
+    const int rows_ok = (int)min((int64_t)128, max((int64_t)0, m_end - row_w));
+    const bool col_ok = col0 < N;
+    const bool full = col0 + 16 / ESZ <= N && (((uintptr_t)dwave & 15) == 0) && ((ld_bytes & 15) == 0);
 #pragma unroll
     for (int part = 0; part < 128 / EPI_ROWS; part++) {
 #pragma unroll
@@ -899,20 +911,13 @@ gemm_fp8_kernel(GemmArgs p)
         }
         __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0): this wave's LDS writes done
         __builtin_amdgcn_wave_barrier();
-        // read back: one row segment of 16 bytes per lane
-        constexpr int LPR = WNC * ESZ / 16; // lanes per row
-        constexpr int RPI = 64 / LPR;       // rows per instruction
-        const int lr = lane / LPR, lc = lane % LPR;
 #pragma unroll
         for (int rr = 0; rr < EPI_ROWS; rr += RPI) {
-            const int row_l = rr + lr;
-            const int64_t row = m0 + wm * 128 + part * EPI_ROWS + row_l;
-            const int64_t col0 = n0 + wn * WNC + lc * (16 / ESZ);
-            uint4 v = *reinterpret_cast<const uint4 *>(ep + row_l * ROWB + lc * 16);
-            if (row >= m_end || col0 >= N)
+            const int row_l = part * EPI_ROWS + rr + lr; // row within the wave's 128
+            uint4 v = *reinterpret_cast<const uint4 *>(ep + (rr + lr) * ROWB + lc * 16);
+            if (row_l >= rows_ok || !col_ok)
                 continue;
-            uint8_t *dst = (uint8_t *)p.d + (ke * p.d_stride + row * p.ldd + col0) * ESZ;
-            const bool full = col0 + 16 / ESZ <= N && (((uintptr_t)dst & 15) == 0);
+            uint8_t *dst = dwave + row_l * ld_bytes;
             if constexpr (OUT_BF16) {
                 if (full) {
                     *reinterpret_cast<uint4 *>(dst) = v;
