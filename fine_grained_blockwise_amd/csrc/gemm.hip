@@ -837,14 +837,22 @@ gemm_fp8_kernel(GemmArgs p)
     // 32x32 accumulator layout: lane l, register r -> row (r/4)*8 + (l/32)*4 + r%4,
     // column l%32.  The tile is staged through LDS (free after the barrier
     // below; from buffer 1 on) so that global stores are 16 bytes per lane along rows: each
-    // wave writes its 128 x WNC block, EPI_ROWS rows at a time, as
-    // [row][WNC + pad] and reads it back row-contiguous.
+    // wave writes its 128 x WNC block, EPI_ROWS rows at a time, and reads it back
+    // row-contiguous.  FP32 out stages [row][WNC + pad] floats.  BF16 out stages
+    // row pairs: a lane's registers 4q..4q+3 are rows 2p..2p+3 of one column, so
+    // one conversion packs rows (2p, 2p+1) into a dword at [pair][column]; the
+    // read-back takes 32 bytes of one pair (8 columns) and splits them into the
+    // two rows' 16 bytes, with no exchange between lanes.
     __syncthreads();
     constexpr int ESZ = OUT_BF16 ? 2 : 4;
     constexpr int ROWB = WNC * ESZ + 16; // padded LDS row (bytes)
+    constexpr int RPB = 2 * WNC * 2 + 16; // BF16 out: padded LDS row pair (bytes; 2 * ROWB - 16)
     constexpr int EPI_ROWS = NW * 128 * ROWB <= EPI_CAP ? 128 : NW * 64 * ROWB <= EPI_CAP ? 64 : 32;
     static_assert(NW * EPI_ROWS * ROWB <= EPI_CAP, "the staging fits");
+    static_assert(!OUT_BF16 || (EPI_ROWS / 2) * RPB <= EPI_ROWS * ROWB, "the row-pair staging fits the wave's share");
     uint8_t *ep = smem + EPI_OFF + wave * (EPI_ROWS * ROWB);
+    // level-1 factor of each column (MOSS); 1.0 without them, which leaves
+    // every value as it is
     float l1v[TJ];
 #pragma unroll
     for (int j = 0; j < TJ; j++) {
@@ -873,27 +881,17 @@ gemm_fp8_kernel(GemmArgs p)
                 if constexpr (OUT_BF16) {
 #pragma unroll
                     for (int q = 0; q < 4; q++) {
-                        // Rows ii*32 + q*8 + hk*4 + 0..3 of column j*32 + l32.
-                        // Lanes l and l^1 hold neighbouring columns: one exchange
-                        // per row pair gives the even lane rows 0 and 2, the odd
-                        // lane rows 1 and 3, each as two neighbouring columns (one
-                        // 4-byte LDS write instead of two 2-byte ones).
+                        // Rows ii*32 + q*8 + hk*4 + 0..3 of column j*32 + l32, as
+                        // two row pairs: one dword per pair (low half the even row).
                         float v[4];
 #pragma unroll
                         for (int t = 0; t < 4; t++) {
-                            v[t] = acc[i][j][4 * q + t];
-                            if (p.l1)
-                                v[t] *= l1v[j];
+                            v[t] = acc[i][j][4 * q + t] * l1v[j];
                         }
-                        const bool odd = l32 & 1;
-                        const float y0 = __uint_as_float(dpp<FGB_DPP_QUAD_XOR1>(__float_as_uint(odd ? v[0] : v[1])));
-                        const float y1 = __uint_as_float(dpp<FGB_DPP_QUAD_XOR1>(__float_as_uint(odd ? v[2] : v[3])));
-                        const int row = ii * 32 + q * 8 + hk * 4 + (odd ? 1 : 0);
-                        const int col = j * 32 + (l32 & ~1);
-                        *reinterpret_cast<uint32_t *>(ep + row * ROWB + col * 2) =
-                            odd ? pack_bf16x2(y0, v[1]) : pack_bf16x2(v[0], y0);
-                        *reinterpret_cast<uint32_t *>(ep + (row + 2) * ROWB + col * 2) =
-                            odd ? pack_bf16x2(y1, v[3]) : pack_bf16x2(v[2], y1);
+                        const int rp = ii * 16 + q * 4 + hk * 2;
+                        const int col = j * 32 + l32;
+                        *reinterpret_cast<uint32_t *>(ep + rp * RPB + col * 4) = pack_bf16x2(v[0], v[1]);
+                        *reinterpret_cast<uint32_t *>(ep + (rp + 1) * RPB + col * 4) = pack_bf16x2(v[2], v[3]);
                     }
                 } else {
                     // FP32 out: one 4-byte write per value (8-byte pairs measured slower)
@@ -901,9 +899,7 @@ gemm_fp8_kernel(GemmArgs p)
                     for (int r = 0; r < 16; r++) {
                         const int row = ii * 32 + (r / 4) * 8 + hk * 4 + (r % 4);
                         const int col = j * 32 + l32;
-                        float v = acc[i][j][r];
-                        if (p.l1)
-                            v *= l1v[j];
+                        const float v = acc[i][j][r] * l1v[j];
                         *reinterpret_cast<float *>(ep + row * ROWB + col * 4) = v;
                     }
                 }
@@ -911,33 +907,58 @@ gemm_fp8_kernel(GemmArgs p)
         }
         __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0): this wave's LDS writes done
         __builtin_amdgcn_wave_barrier();
+        if constexpr (OUT_BF16) {
+            // a lane takes 8 columns of one row pair: 32 bytes of pairs -> 16 bytes of each row
 #pragma unroll
-        for (int rr = 0; rr < EPI_ROWS; rr += RPI) {
-            const int row_l = part * EPI_ROWS + rr + lr; // row within the wave's 128
-            uint4 v = *reinterpret_cast<const uint4 *>(ep + (rr + lr) * ROWB + lc * 16);
-            if (row_l >= rows_ok || !col_ok)
-                continue;
-            uint8_t *dst = dwave + row_l * ld_bytes;
-            if constexpr (OUT_BF16) {
-                if (full) {
-                    *reinterpret_cast<uint4 *>(dst) = v;
-                } else {
-                    uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-                    for (int e = 0; e < 8 && col0 + e < N; e++)
-                        reinterpret_cast<uint16_t *>(dst)[e] = (uint16_t)(w4[e / 2] >> (16 * (e & 1)));
+            for (int rr = 0; rr < EPI_ROWS / 2; rr += RPI) {
+                const int rp = rr + lr;
+                const uint4 x = *reinterpret_cast<const uint4 *>(ep + rp * RPB + lc * 32);
+                const uint4 y = *reinterpret_cast<const uint4 *>(ep + rp * RPB + lc * 32 + 16);
+                const uint32_t w[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+                uint4 ev, od;
+                uint32_t *e4 = &ev.x, *o4 = &od.x;
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    e4[k] = (w[2 * k] & 0xFFFFu) | (w[2 * k + 1] << 16);
+                    o4[k] = (w[2 * k] >> 16) | (w[2 * k + 1] & 0xFFFF0000u);
                 }
-            } else {
-                float f4[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
-                float *fd = reinterpret_cast<float *>(dst);
-                if (full) {
-                    if (p.accumulate) {
-                        float4 o = *reinterpret_cast<const float4 *>(fd);
-                        f4[0] += o.x; f4[1] += o.y; f4[2] += o.z; f4[3] += o.w;
+#pragma unroll
+                for (int s = 0; s < 2; s++) {
+                    const int row_l = part * EPI_ROWS + 2 * rp + s; // row within the wave's 128
+                    if (row_l >= rows_ok || !col_ok)
+                        continue;
+                    const uint4 v = s ? od : ev;
+                    uint8_t *dst = dwave + row_l * ld_bytes;
+                    if (full) {
+                        *reinterpret_cast<uint4 *>(dst) = v;
+                    } else {
+                        uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+                        for (int e = 0; e < 8 && col0 + e < N; e++)
+                            reinterpret_cast<uint16_t *>(dst)[e] = (uint16_t)(w4[e / 2] >> (16 * (e & 1)));
                     }
-                    *reinterpret_cast<float4 *>(fd) = make_float4(f4[0], f4[1], f4[2], f4[3]);
-                } else {
-                    for (int e = 0; e < 4 && col0 + e < N; e++)
-                        fd[e] = p.accumulate ? fd[e] + f4[e] : f4[e];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int rr = 0; rr < EPI_ROWS; rr += RPI) {
+                const int row_l = part * EPI_ROWS + rr + lr; // row within the wave's 128
+                uint4 v = *reinterpret_cast<const uint4 *>(ep + (rr + lr) * ROWB + lc * 16);
+                if (row_l >= rows_ok || !col_ok)
+                    continue;
+                uint8_t *dst = dwave + row_l * ld_bytes;
+                {
+                    float f4[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+                    float *fd = reinterpret_cast<float *>(dst);
+                    if (full) {
+                        if (p.accumulate) {
+                            float4 o = *reinterpret_cast<const float4 *>(fd);
+                            f4[0] += o.x; f4[1] += o.y; f4[2] += o.z; f4[3] += o.w;
+                        }
+                        *reinterpret_cast<float4 *>(fd) = make_float4(f4[0], f4[1], f4[2], f4[3]);
+                    } else {
+                        for (int e = 0; e < 4 && col0 + e < N; e++)
+                            fd[e] = p.accumulate ? fd[e] + f4[e] : f4[e];
+                    }
                 }
             }
         }
