@@ -409,15 +409,17 @@ def test_gemm_mx_per32_with_level1(fgb, mode):
     l1 = torch.rand(N, generator=torch.Generator().manual_seed(15)) * 2 + 0.1
     l1n = l1.numpy().reshape(N, 1)
     ref = O.block_gemm(a.numpy(), sa.numpy(), O.ROW1x32, b.numpy(), sb.numpy(), O.ROW1x32, l1n, 10240)
-    d = fgb.fp8_block_gemm(a.to(DEV), sa.to(DEV), fgb.ROW1x32, b.to(DEV), sb.to(DEV), fgb.ROW1x32,
-                           b_l1=l1.to(DEV), g1=10240, out_dtype=torch.float32, mode=_mode(fgb, mode))
     bounds = None
     if mode == "fast":
         mi, ni = _all_pairs(M, N)
         bounds = [x.reshape(ref.shape) for x in
                   O.gemm_run_bounds_sampled(a.numpy(), sa.numpy(), O.ROW1x32, b.numpy(), sb.numpy(), O.ROW1x32, mi, ni,
                                             b_l1=l1.numpy())]
-    check_gemm(np_(d), ref, mode, False, bounds, K)
+    for bf16 in (False, True):  # the level-1 factor is applied in both epilogues
+        d = fgb.fp8_block_gemm(a.to(DEV), sa.to(DEV), fgb.ROW1x32, b.to(DEV), sb.to(DEV), fgb.ROW1x32,
+                               b_l1=l1.to(DEV), g1=10240, out_dtype=torch.bfloat16 if bf16 else torch.float32,
+                               mode=_mode(fgb, mode))
+        check_gemm(np_(d), ref, mode, bf16, bounds, K)
 
 
 def _sample(M, N, n, seed):
