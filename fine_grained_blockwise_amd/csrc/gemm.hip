@@ -487,9 +487,11 @@ gemm_fp8_kernel(GemmArgs p)
         // A half-step (64 of the step's 128 K) is one MFMA sub-step: 16 scaled
         // MFMAs, 4 per slot.  Lane half hk reads chunks 4hs+hk and 4hs+2+hk of
         // each tile row for half hs (hardware K blocks 0 and 1).  Half 1 of
-        // step ks is read in slot 1; the barrier in slot 3 then frees buffer
-        // ks % 2 and step ks+2's copies go out over slots 3-7 and 0-1; the
-        // barrier in slot 5 waits for step ks+1, whose half 0 is read there.
+        // step ks is read in slots 1 (A) and 2 (B); the barrier in slot 3 then
+        // frees buffer ks % 2 and step ks+2's copies go out over slots 3-7 and
+        // 0-1; the barrier in slot 5 waits for step ks+1, whose half 0 is read
+        // in slots 5 (A) and 6 (B).  Each slot's 8 reads go out two after each
+        // of its MFMAs: 16 reads in a row starved the matrix unit.
         uint4 f[2][2][4][2]; // [half][A/B][tile][chunk]
         auto read_frag = [&](int k, int hs, int op, uint4(&x)[4][2]) {
             const uint8_t *base = op == 0 ? lds_a(k) : lds_b(k);
@@ -546,11 +548,19 @@ gemm_fp8_kernel(GemmArgs p)
             dma_tile(ks + 1, 14);
             dma_tile(ks + 1, 15);
             read_frag(ks, 1, 0, f[1][0]);
-            read_frag(ks, 1, 1, f[1][1]);
             mfma_row(0, 1, f[0][0], f[0][1]);
+            for (int k_ = 0; k_ < 4; k_++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // 1 MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); // 2 LDS reads
+            }
             __builtin_amdgcn_sched_barrier(0);
             // slot 2
+            read_frag(ks, 1, 1, f[1][1]);
             mfma_row(0, 2, f[0][0], f[0][1]);
+            for (int k_ = 0; k_ < 4; k_++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // 1 MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); // 2 LDS reads
+            }
             __builtin_amdgcn_sched_barrier(0);
             // slot 3: every wave's reads of step ks are done -> buffer ks % 2 is free
             __syncthreads();
@@ -570,13 +580,21 @@ gemm_fp8_kernel(GemmArgs p)
             dma_tile(ks + 2, 6);
             dma_tile(ks + 2, 7);
             read_frag(ks + 1, 0, 0, f[0][0]);
-            read_frag(ks + 1, 0, 1, f[0][1]);
             mfma_row(1, 1, f[1][0], f[1][1]);
+            for (int k_ = 0; k_ < 4; k_++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // 1 MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); // 2 LDS reads
+            }
             __builtin_amdgcn_sched_barrier(0);
             // slot 6
             dma_tile(ks + 2, 8);
             dma_tile(ks + 2, 9);
+            read_frag(ks + 1, 0, 1, f[0][1]);
             mfma_row(1, 2, f[1][0], f[1][1]);
+            for (int k_ = 0; k_ < 4; k_++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // 1 MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); // 2 LDS reads
+            }
             __builtin_amdgcn_sched_barrier(0);
             // slot 7: the next step's scales replace the current ones after
             // this slot's MFMAs
