@@ -161,11 +161,76 @@ def _row_ld(t):
     return t.stride(0)
 
 
+def _need(t, name, shape=None, dtype=None, contiguous=False):
+    """Raise ValueError unless t has the given shape, dtype and layout."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(int(v) for v in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(v) for v in shape)}, got {tuple(t.shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _scale_shape(rows, K, gran):
+    """Shape of the scale tensor of a [rows, K] code tensor with granularity gran."""
+    if gran == ROW1x128:
+        return (rows, K // 128)
+    if gran == ROW1x32:
+        return (rows, K // 32)
+    if gran == BLOCK128:
+        return ((rows + 127) // 128, K // 128)
+    raise ValueError(f"unknown scale granularity {gran}")
+
+
+def _out_dtype(dtype, name):
+    if dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"{name}: the output dtype must be float32 or bfloat16, got {dtype}")
+    return dtype
+
+
+def _check_2d_codes(t, name):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    return _need(t, name, dtype=torch.uint8)
+
+
+def _gemm_out(d, M, N, out_dtype, name, contiguous=False):
+    """The output tensor of a GEMM: validated when given (shape [M, N], float32 or bfloat16, unit column
+    stride or contiguous), else None (the caller allocates)."""
+    if d is None:
+        _out_dtype(out_dtype, name)
+        return None
+    _out_dtype(d.dtype, name)
+    _need(d, f"{name}: d", shape=(M, N), contiguous=contiguous)
+    if d.dim() == 2 and d.stride(1) != 1:
+        raise ValueError(f"{name}: d must have unit column stride")
+    return d
+
+
+def _quant_io_check(name, x, group, q, s, block=False):
+    """Shape checks of a quantizer's input and optional outputs; returns (rows, cols)."""
+    if x.dim() != 2:
+        raise ValueError(f"{name}: the input must be 2-D")
+    _dtype_code(x)
+    rows, cols = x.shape
+    if group not in (32, 128) or cols % group:
+        raise ValueError(f"{name}: cols ({cols}) must be a multiple of the group (32 or 128, got {group})")
+    if q is not None:
+        _need(q, f"{name}: q", shape=(rows, cols), dtype=torch.uint8)
+    if s is not None:
+        shp = ((rows + 127) // 128, cols // 128) if block else (rows, cols // group)
+        _need(s, f"{name}: s", shape=shp, dtype=torch.uint8)
+    return rows, cols
+
+
 # ---------------------------------------------------------------------------
 def fp8_quant_rowwise(x, group=128, q=None, s=None):
     """1 x group quantization of x [rows, cols] (fp32/bf16) -> (q uint8, s uint8 [rows, cols/group])."""
+    rows, cols = _quant_io_check("fp8_quant_rowwise", x, group, q, s)
     _check_dev(x, q, s)
-    rows, cols = x.shape
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     if s is None:
@@ -177,8 +242,8 @@ def fp8_quant_rowwise(x, group=128, q=None, s=None):
 
 def fp8_quant_rowwise_fmt(x, group=128, fmt=E4M3, rule=SCALE_CEIL, q=None, s=None):
     """fp8_quant_rowwise in element format fmt (E4M3/E5M2) with scale rule (SCALE_CEIL/SCALE_OCP_FLOOR)."""
+    rows, cols = _quant_io_check("fp8_quant_rowwise_fmt", x, group, q, s)
     _check_dev(x, q, s)
-    rows, cols = x.shape
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     if s is None:
@@ -190,8 +255,8 @@ def fp8_quant_rowwise_fmt(x, group=128, fmt=E4M3, rule=SCALE_CEIL, q=None, s=Non
 
 def fp8_quant_blockwise(w, q=None, s=None):
     """128 x 128 quantization of w [rows, cols] -> (q, s [ceil(rows/128), cols/128])."""
+    rows, cols = _quant_io_check("fp8_quant_blockwise", w, 128, q, s, block=True)
     _check_dev(w, q, s)
-    rows, cols = w.shape
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=w.device)
     if s is None:
@@ -204,9 +269,10 @@ def fp8_quant_blockwise(w, q=None, s=None):
 def fp8_quant_blockwise_t(w):
     """128x128 quantization of bf16 w [G, rows, cols] (or [rows, cols]) with the transposed copy:
     -> (q, s [G, rows/128, cols/128], qt [G, cols, rows], st [G, cols/128, rows/128])."""
+    if w.dim() not in (2, 3):
+        raise ValueError("fp8_quant_blockwise_t: w must be [rows, cols] or [G, rows, cols]")
+    _need(w, "fp8_quant_blockwise_t: w", dtype=torch.bfloat16, contiguous=True)
     _check_dev(w)
-    if not w.is_contiguous():
-        raise ValueError("fp8_quant_blockwise_t: w must be contiguous")
     w3 = w if w.dim() == 3 else w.unsqueeze(0)
     G, rows, cols = w3.shape
     dev = w.device
@@ -223,8 +289,11 @@ def fp8_quant_blockwise_t(w):
 
 def fp8_dequant(q, s, gran, out_dtype=torch.float32):
     """decode(q) * 2^(s-127) -> out [rows, cols] (fp32 or bf16); q, s dense."""
-    _check_dev(q, s)
+    _check_2d_codes(q, "fp8_dequant: q")
     rows, cols = q.shape
+    _need(s, "fp8_dequant: s", shape=_scale_shape(rows, cols, gran), dtype=torch.uint8)
+    _out_dtype(out_dtype, "fp8_dequant")
+    _check_dev(q, s)
     out = torch.empty((rows, cols), dtype=out_dtype, device=q.device)
     _call("fp8_dequant", _ptr(q.contiguous()), _ptr(s.contiguous()), gran, rows, cols, _ptr(out),
           _dtype_code(out), _stream(q))
@@ -233,11 +302,12 @@ def fp8_dequant(q, s, gran, out_dtype=torch.float32):
 
 def fp8_dequant_fmt(q, s, gran, fmt, out_dtype=torch.float32):
     """fp8_dequant for codes of format fmt."""
-    _check_dev(q, s)
-    for t in (q, s):
-        if not t.is_contiguous():
-            raise ValueError("fp8_dequant_fmt: q and s must be contiguous")
+    _check_2d_codes(q, "fp8_dequant_fmt: q")
     rows, cols = q.shape
+    _need(q, "fp8_dequant_fmt: q", contiguous=True)
+    _need(s, "fp8_dequant_fmt: s", shape=_scale_shape(rows, cols, gran), dtype=torch.uint8, contiguous=True)
+    _out_dtype(out_dtype, "fp8_dequant_fmt")
+    _check_dev(q, s)
     out = torch.empty((rows, cols), dtype=out_dtype, device=q.device)
     _call("fp8_dequant_fmt", _ptr(q), _ptr(s), gran, fmt, rows, cols, _ptr(out), _dtype_code(out), _stream(q))
     return out
@@ -264,8 +334,12 @@ def fgb_e4m3_encode(x):
 
 def fp8_direct_transpose(q, s, s_gran=ROW1x128):
     """Scaling-aware transpose: (q [T, C], s) -> (qt [C, T], st)."""
-    _check_dev(q, s)
+    _check_2d_codes(q, "fp8_direct_transpose: q")
     T, Cc = q.shape
+    if s_gran not in (ROW1x128, BLOCK128):
+        raise ValueError("fp8_direct_transpose: s_gran must be ROW1x128 or BLOCK128")
+    _need(s, "fp8_direct_transpose: s", shape=_scale_shape(T, Cc, s_gran), dtype=torch.uint8)
+    _check_dev(q, s)
     qt = torch.empty((Cc, T), dtype=torch.uint8, device=q.device)
     if s_gran == ROW1x128:
         st = torch.empty((Cc, T // 128), dtype=torch.uint8, device=q.device)
@@ -278,11 +352,11 @@ def fp8_direct_transpose(q, s, s_gran=ROW1x128):
 
 def fp8_direct_transpose_fmt(q, s, fmt):
     """fp8_direct_transpose (1x128 scales) of codes in format fmt: (q [T, C], s) -> (qt [C, T], st)."""
-    _check_dev(q, s)
-    for t in (q, s):
-        if not t.is_contiguous():
-            raise ValueError("fp8_direct_transpose_fmt: q and s must be contiguous")
+    _check_2d_codes(q, "fp8_direct_transpose_fmt: q")
     T, Cc = q.shape
+    _need(q, "fp8_direct_transpose_fmt: q", contiguous=True)
+    _need(s, "fp8_direct_transpose_fmt: s", shape=(T, Cc // 128), dtype=torch.uint8, contiguous=True)
+    _check_dev(q, s)
     qt = torch.empty((Cc, T), dtype=torch.uint8, device=q.device)
     st = torch.empty((Cc, T // 128), dtype=torch.uint8, device=q.device)
     _call("fp8_direct_transpose_fmt", _ptr(q), _ptr(s), fmt, T, Cc, _ptr(qt), _ptr(st), _stream(q))
@@ -291,8 +365,12 @@ def fp8_direct_transpose_fmt(q, s, fmt):
 
 def fp8_block_transpose_batched(q, s):
     """Per-matrix 128x128-block transposes: q [G, rows, cols] -> qt [G, cols, rows]."""
-    _check_dev(q, s)
+    if q.dim() != 3:
+        raise ValueError("fp8_block_transpose_batched: q must be [G, rows, cols]")
     G, rows, cols = q.shape
+    _need(q, "fp8_block_transpose_batched: q", dtype=torch.uint8)
+    _need(s, "fp8_block_transpose_batched: s", shape=(G, rows // 128, cols // 128), dtype=torch.uint8)
+    _check_dev(q, s)
     qt = torch.empty((G, cols, rows), dtype=torch.uint8, device=q.device)
     st = torch.empty((G, cols // 128, rows // 128), dtype=torch.uint8, device=q.device)
     _call("fp8_block_transpose_batched", _ptr(q.contiguous()), _ptr(s.contiguous()), G, rows, cols, _ptr(qt),
@@ -307,8 +385,13 @@ def grouped_k_cap(M_cap, G):
 
 def fp8_grouped_direct_transpose(q, s, group_offsets, K_cap=None):
     """Direct transpose of expert segments: q [M_cap, C] -> (qt [C, K_cap], st, k_offsets [G+1])."""
-    _check_dev(q, s, group_offsets)
+    _check_2d_codes(q, "fp8_grouped_direct_transpose: q")
     M_cap, Cc = q.shape
+    _need(s, "fp8_grouped_direct_transpose: s", shape=(M_cap, Cc // 128), dtype=torch.uint8)
+    if group_offsets.dim() != 1 or group_offsets.numel() < 2:
+        raise ValueError("fp8_grouped_direct_transpose: group_offsets must be [G+1] with G >= 1")
+    _need(group_offsets, "fp8_grouped_direct_transpose: group_offsets", dtype=torch.int32, contiguous=True)
+    _check_dev(q, s, group_offsets)
     G = group_offsets.numel() - 1
     if K_cap is None:
         K_cap = grouped_k_cap(M_cap, G)
@@ -326,8 +409,12 @@ def fp8_naive_transpose_workspace_size(rows, cols):
 
 def fp8_naive_transpose(q, s, workspace=None):
     """Three-pass baseline (dequantize, transpose, requantize): (q [T, C], s) -> (qt [C, T], st)."""
-    _check_dev(q, s)
+    _check_2d_codes(q, "fp8_naive_transpose: q")
     T, Cc = q.shape
+    _need(s, "fp8_naive_transpose: s", shape=(T, Cc // 128), dtype=torch.uint8)
+    if workspace is not None:
+        _need(workspace, "fp8_naive_transpose: workspace", dtype=torch.uint8, contiguous=True)
+    _check_dev(q, s, workspace)
     qt = torch.empty((Cc, T), dtype=torch.uint8, device=q.device)
     st = torch.empty((Cc, T // 128), dtype=torch.uint8, device=q.device)
     if workspace is None:
@@ -341,9 +428,18 @@ def fp8_naive_transpose(q, s, workspace=None):
 def fp8_block_gemm(a, sa, a_gran, b, sb, b_gran, b_l1=None, g1=0, out_dtype=torch.bfloat16,
                    d=None, accumulate=False, mode=GEMM_EXACT):
     """D = A * B^T with blockwise scales (A [M,K], B [N,K] codes) -> D [M, N]."""
-    _check_dev(a, sa, b, sb, b_l1, d)
+    _check_2d_codes(a, "fp8_block_gemm: a")
+    _check_2d_codes(b, "fp8_block_gemm: b")
     M, K = a.shape
     N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("fp8_block_gemm: a and b must have the same K")
+    _need(sa, "fp8_block_gemm: sa", shape=_scale_shape(M, K, a_gran), dtype=torch.uint8)
+    _need(sb, "fp8_block_gemm: sb", shape=_scale_shape(N, K, b_gran), dtype=torch.uint8)
+    if b_l1 is not None:
+        _need(b_l1, "fp8_block_gemm: b_l1", shape=(N,), dtype=torch.float32, contiguous=True)
+    d = _gemm_out(d, M, N, out_dtype, "fp8_block_gemm")
+    _check_dev(a, sa, b, sb, b_l1, d)
     if d is None:
         d = torch.empty((M, N), dtype=out_dtype, device=a.device)
     _call("fp8_block_gemm", _ptr(a), _ptr(sa.contiguous()), a_gran, _ptr(b), _ptr(sb.contiguous()),
@@ -355,12 +451,16 @@ def fp8_block_gemm(a, sa, a_gran, b, sb, b_gran, b_l1=None, g1=0, out_dtype=torc
 def fp8_block_gemm_fmt(a, sa, a_gran, a_fmt, b, sb, b_gran, b_fmt=E4M3, out_dtype=torch.bfloat16, d=None,
                        accumulate=False, mode=GEMM_EXACT):
     """fp8_block_gemm with the operands' element formats (A: E4M3 or E5M2; B: E4M3)."""
-    _check_dev(a, sa, b, sb, d)
-    for t in (sa, sb):
-        if not t.is_contiguous():
-            raise ValueError("fp8_block_gemm_fmt: scale tensors must be contiguous")
+    _check_2d_codes(a, "fp8_block_gemm_fmt: a")
+    _check_2d_codes(b, "fp8_block_gemm_fmt: b")
     M, K = a.shape
     N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("fp8_block_gemm_fmt: a and b must have the same K")
+    _need(sa, "fp8_block_gemm_fmt: sa", shape=_scale_shape(M, K, a_gran), dtype=torch.uint8, contiguous=True)
+    _need(sb, "fp8_block_gemm_fmt: sb", shape=_scale_shape(N, K, b_gran), dtype=torch.uint8, contiguous=True)
+    d = _gemm_out(d, M, N, out_dtype, "fp8_block_gemm_fmt")
+    _check_dev(a, sa, b, sb, d)
     if d is None:
         d = torch.empty((M, N), dtype=out_dtype, device=a.device)
     _call("fp8_block_gemm_fmt", _ptr(a), _ptr(sa), a_gran, a_fmt, _ptr(b), _ptr(sb), b_gran, b_fmt, None, 0, M, N, K,
@@ -371,16 +471,24 @@ def fp8_block_gemm_fmt(a, sa, a_gran, a_fmt, b, sb, b_gran, b_fmt=E4M3, out_dtyp
 def fp8_grouped_gemm_masked(a, sa, b, sb, masked_m, out_dtype=torch.bfloat16, d=None, mode=GEMM_EXACT):
     """Masked grouped GEMM: a [G, M_max, K], b [G, N, K], masked_m int32 [G] (device) -> d [G, M_max, N];
     rows m >= masked_m[g] of d are not written."""
-    _check_dev(a, sa, b, sb, masked_m, d)
-    for t in (a, sa, b, sb, masked_m):
-        if not t.is_contiguous():
-            raise ValueError("fp8_grouped_gemm_masked: operands must be contiguous")
+    name = "fp8_grouped_gemm_masked"
+    if a.dim() != 3 or b.dim() != 3:
+        raise ValueError(f"{name}: a must be [G, M_max, K] and b [G, N, K]")
     G, M_max, K = a.shape
     N = b.shape[1]
+    _need(a, f"{name}: a", dtype=torch.uint8, contiguous=True)
+    _need(b, f"{name}: b", shape=(G, N, K), dtype=torch.uint8, contiguous=True)
+    _need(sa, f"{name}: sa", shape=(G, M_max, K // 128), dtype=torch.uint8, contiguous=True)
+    _need(sb, f"{name}: sb", shape=(G, (N + 127) // 128, K // 128), dtype=torch.uint8, contiguous=True)
+    _need(masked_m, f"{name}: masked_m", shape=(G,), dtype=torch.int32, contiguous=True)
+    if d is None:
+        _out_dtype(out_dtype, name)
+    else:
+        _out_dtype(d.dtype, name)
+        _need(d, f"{name}: d", shape=(G, M_max, N), contiguous=True)
+    _check_dev(a, sa, b, sb, masked_m, d)
     if d is None:
         d = torch.empty((G, M_max, N), dtype=out_dtype, device=a.device)
-    elif not d.is_contiguous() or tuple(d.shape) != (G, M_max, N):
-        raise ValueError("fp8_grouped_gemm_masked: d must be a contiguous [G, M_max, N] tensor")
     _call("fp8_grouped_gemm_masked", _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(masked_m), G, M_max, N, K, _ptr(d),
           _dtype_code(d), mode, _stream(a))
     return d
@@ -389,9 +497,18 @@ def fp8_grouped_gemm_masked(a, sa, b, sb, masked_m, out_dtype=torch.bfloat16, d=
 def fp8_grouped_gemm(a, sa, b, sb, group_offsets, out_dtype=torch.bfloat16, d=None,
                      mode=GEMM_EXACT):
     """M-grouped contiguous GEMM: a [M_cap, K], b [G, N, K], offsets [G+1] (device) -> d [M_cap, N]."""
-    _check_dev(a, sa, b, sb, group_offsets, d)
+    name = "fp8_grouped_gemm"
+    _check_2d_codes(a, f"{name}: a")
     M_cap, K = a.shape
-    G, N, _ = b.shape
+    if b.dim() != 3:
+        raise ValueError(f"{name}: b must be [G, N, K]")
+    G, N = b.shape[0], b.shape[1]
+    _need(b, f"{name}: b", shape=(G, N, K), dtype=torch.uint8)
+    _need(sa, f"{name}: sa", shape=(M_cap, K // 128), dtype=torch.uint8)
+    _need(sb, f"{name}: sb", shape=(G, (N + 127) // 128, K // 128), dtype=torch.uint8)
+    _need(group_offsets, f"{name}: group_offsets", shape=(G + 1,), dtype=torch.int32, contiguous=True)
+    d = _gemm_out(d, M_cap, N, out_dtype, name, contiguous=True)
+    _check_dev(a, sa, b, sb, group_offsets, d)
     if d is None:
         d = torch.empty((M_cap, N), dtype=out_dtype, device=a.device)
     _call("fp8_grouped_gemm", _ptr(a.contiguous()), _ptr(sa.contiguous()), _ptr(b.contiguous()),
@@ -403,19 +520,29 @@ def fp8_grouped_gemm(a, sa, b, sb, group_offsets, out_dtype=torch.bfloat16, d=No
 def fp8_kgrouped_gemm(a, sa, b, sb, k_offsets, out_dtype=torch.float32, d=None, accumulate=False,
                       mode=GEMM_EXACT):
     """K-grouped GEMM (expert Wgrad): a [M, K_cap], b [N, K_cap], k_offsets [G+1] (device) -> d [G, M, N]."""
-    _check_dev(a, sa, b, sb, k_offsets, d)
-    for t in (a, sa, b, sb, k_offsets):
-        if not t.is_contiguous():
-            raise ValueError("fp8_kgrouped_gemm: operands must be contiguous")
+    name = "fp8_kgrouped_gemm"
+    _check_2d_codes(a, f"{name}: a")
+    _check_2d_codes(b, f"{name}: b")
     M, K_cap = a.shape
     N = b.shape[0]
-    G = k_offsets.numel() - 1
     if b.shape[1] != K_cap:
         raise ValueError("fp8_kgrouped_gemm: a and b must have the same K capacity")
+    if k_offsets.dim() != 1 or k_offsets.numel() < 2:
+        raise ValueError(f"{name}: k_offsets must be [G+1] with G >= 1")
+    G = k_offsets.numel() - 1
+    for t, nm in ((a, "a"), (b, "b")):
+        _need(t, f"{name}: {nm}", contiguous=True)
+    _need(sa, f"{name}: sa", shape=(M, K_cap // 128), dtype=torch.uint8, contiguous=True)
+    _need(sb, f"{name}: sb", shape=(N, K_cap // 128), dtype=torch.uint8, contiguous=True)
+    _need(k_offsets, f"{name}: k_offsets", dtype=torch.int32, contiguous=True)
+    if d is None:
+        _out_dtype(out_dtype, name)
+    else:
+        _out_dtype(d.dtype, name)
+        _need(d, f"{name}: d", shape=(G, M, N), contiguous=True)
+    _check_dev(a, sa, b, sb, k_offsets, d)
     if d is None:
         d = torch.empty((G, M, N), dtype=out_dtype, device=a.device)
-    elif not d.is_contiguous() or tuple(d.shape) != (G, M, N):
-        raise ValueError("fp8_kgrouped_gemm: d must be a contiguous [G, M, N] tensor")
     _call("fp8_kgrouped_gemm", _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(k_offsets), G, M, N, K_cap,
           _ptr(d), _dtype_code(d), int(bool(accumulate)), mode, _stream(a))
     return d
@@ -427,11 +554,25 @@ def permute_pad_workspace_size(T, topk, G):
 
 def permute_pad(xq, xs, topk_idx, G, pad_multiple=16, M_cap=None, workspace=None, out=None):
     """Fused permute + pad -> (out_q [M_cap, H], out_s, row_map [T, topk], group_offsets [G+1])."""
-    _check_dev(xq, xs, topk_idx)
+    name = "permute_pad"
+    _check_2d_codes(xq, f"{name}: xq")
     T, H = xq.shape
+    _need(xs, f"{name}: xs", shape=(T, H // 128), dtype=torch.uint8)
+    if topk_idx.dim() != 2 or topk_idx.shape[0] != T:
+        raise ValueError(f"{name}: topk_idx must be [T, topk]")
+    _need(topk_idx, f"{name}: topk_idx", dtype=torch.int32)
     topk = topk_idx.shape[1]
     if M_cap is None:
         M_cap = T * topk + (pad_multiple - 1) * G
+    if out is not None:
+        out_q, out_s, row_map, offs = out
+        _need(out_q, f"{name}: out_q", shape=(M_cap, H), dtype=torch.uint8, contiguous=True)
+        _need(out_s, f"{name}: out_s", shape=(M_cap, H // 128), dtype=torch.uint8, contiguous=True)
+        _need(row_map, f"{name}: row_map", shape=(T, topk), dtype=torch.int32, contiguous=True)
+        _need(offs, f"{name}: group_offsets", shape=(G + 1,), dtype=torch.int32, contiguous=True)
+    if workspace is not None:
+        _need(workspace, f"{name}: workspace", dtype=torch.uint8, contiguous=True)
+    _check_dev(xq, xs, topk_idx, workspace, *(out or ()))
     dev = xq.device
     if out is None:
         out_q = torch.empty((M_cap, H), dtype=torch.uint8, device=dev)
@@ -451,9 +592,18 @@ def permute_pad(xq, xs, topk_idx, G, pad_multiple=16, M_cap=None, workspace=None
 
 def unpermute_unpad(y, row_map, probs=None, out=None):
     """out [T, H] bf16 = sum over slots of probs * y[row_map] (fmaf fold, RNE to bf16)."""
-    _check_dev(y, row_map, probs)
+    name = "unpermute_unpad"
+    if y.dim() != 2 or row_map.dim() != 2:
+        raise ValueError(f"{name}: y must be [rows, H] and row_map [T, topk]")
+    _need(y, f"{name}: y", dtype=torch.bfloat16)
+    _need(row_map, f"{name}: row_map", dtype=torch.int32)
     T, topk = row_map.shape
     H = y.shape[1]
+    if probs is not None:
+        _need(probs, f"{name}: probs", shape=(T, topk), dtype=torch.float32)
+    if out is not None:
+        _need(out, f"{name}: out", shape=(T, H), dtype=torch.bfloat16, contiguous=True)
+    _check_dev(y, row_map, probs, out)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
     _call("unpermute_unpad", _ptr(y.contiguous()), _ptr(row_map.contiguous()),
@@ -467,9 +617,20 @@ def unpermute_backward_workspace_size(M_cap):
 
 def unpermute_backward(dout, row_map, probs, M_cap, dy=None, workspace=None):
     """Gradient of unpermute_unpad: dout bf16 [T, H] -> dy bf16 [M_cap, H] (padding rows zero)."""
-    _check_dev(dout, row_map, probs)
+    name = "unpermute_backward"
+    if dout.dim() != 2 or row_map.dim() != 2 or row_map.shape[0] != dout.shape[0]:
+        raise ValueError(f"{name}: dout must be [T, H] and row_map [T, topk]")
+    _need(dout, f"{name}: dout", dtype=torch.bfloat16)
+    _need(row_map, f"{name}: row_map", dtype=torch.int32)
     T, H = dout.shape
     topk = row_map.shape[1]
+    if probs is not None:
+        _need(probs, f"{name}: probs", shape=(T, topk), dtype=torch.float32)
+    if dy is not None:
+        _need(dy, f"{name}: dy", shape=(M_cap, H), dtype=torch.bfloat16, contiguous=True)
+    if workspace is not None:
+        _need(workspace, f"{name}: workspace", dtype=torch.uint8, contiguous=True)
+    _check_dev(dout, row_map, probs, dy, workspace)
     if dy is None:
         dy = torch.empty((M_cap, H), dtype=torch.bfloat16, device=dout.device)
     if workspace is None:
@@ -483,12 +644,22 @@ def unpermute_backward(dout, row_map, probs, M_cap, dy=None, workspace=None):
 
 def unpermute_backward_quant(dout, row_map, probs, M_cap, q=None, s=None, workspace=None):
     """unpermute_backward + 1x128 quant in one pass: dout bf16 [T, H] -> (q [M_cap, H], s [M_cap, H/128])."""
-    _check_dev(dout, row_map, probs, q, s)
-    for t in (dout, row_map, probs):
-        if t is not None and not t.is_contiguous():
-            raise ValueError("unpermute_backward_quant: inputs must be contiguous")
+    name = "unpermute_backward_quant"
+    if dout.dim() != 2 or row_map.dim() != 2 or row_map.shape[0] != dout.shape[0]:
+        raise ValueError(f"{name}: dout must be [T, H] and row_map [T, topk]")
     T, H = dout.shape
     topk = row_map.shape[1]
+    _need(dout, f"{name}: dout", dtype=torch.bfloat16, contiguous=True)
+    _need(row_map, f"{name}: row_map", dtype=torch.int32, contiguous=True)
+    if probs is not None:
+        _need(probs, f"{name}: probs", shape=(T, topk), dtype=torch.float32, contiguous=True)
+    if q is not None:
+        _need(q, f"{name}: q", shape=(M_cap, H), dtype=torch.uint8, contiguous=True)
+    if s is not None:
+        _need(s, f"{name}: s", shape=(M_cap, H // 128), dtype=torch.uint8, contiguous=True)
+    if workspace is not None:
+        _need(workspace, f"{name}: workspace", dtype=torch.uint8, contiguous=True)
+    _check_dev(dout, row_map, probs, q, s, workspace)
     if q is None:
         q = torch.empty((M_cap, H), dtype=torch.uint8, device=dout.device)
     if s is None:
@@ -503,9 +674,18 @@ def unpermute_backward_quant(dout, row_map, probs, M_cap, q=None, s=None, worksp
 
 def swiglu_quant_cache(h, group_offsets=None, q=None, s=None, hq=None, hs=None):
     """swiglu_quant that also returns the FP8 cache of h: -> (q [M, F], s, hq [M, 2F], hs [M, 2F/128])."""
-    _check_dev(h, group_offsets, q, s, hq, hs)
+    name = "swiglu_quant_cache"
+    if h.dim() != 2:
+        raise ValueError(f"{name}: h must be [M, 2F]")
+    _need(h, f"{name}: h", dtype=torch.bfloat16)
     M, F2 = h.shape
     F = F2 // 2
+    for t, nm, shp in ((q, "q", (M, F)), (s, "s", (M, F // 128)), (hq, "hq", (M, F2)), (hs, "hs", (M, F2 // 128))):
+        if t is not None:
+            _need(t, f"{name}: {nm}", shape=shp, dtype=torch.uint8, contiguous=True)
+    if group_offsets is not None:
+        _need(group_offsets, f"{name}: group_offsets", dtype=torch.int32, contiguous=True)
+    _check_dev(h, group_offsets, q, s, hq, hs)
     if q is None:
         q = torch.empty((M, F), dtype=torch.uint8, device=h.device)
     if s is None:
@@ -522,9 +702,18 @@ def swiglu_quant_cache(h, group_offsets=None, q=None, s=None, hq=None, hs=None):
 
 def swiglu_quant(h, group_offsets=None, q=None, s=None):
     """SwiGLU of h [M, 2F] (gate|up, bf16) + 1x128 quant -> (q [M, F], s [M, F/128])."""
-    _check_dev(h, group_offsets, q, s)
+    name = "swiglu_quant"
+    if h.dim() != 2:
+        raise ValueError(f"{name}: h must be [M, 2F]")
+    _need(h, f"{name}: h", dtype=torch.bfloat16)
     M, F2 = h.shape
     F = F2 // 2
+    for t, nm, shp in ((q, "q", (M, F)), (s, "s", (M, F // 128))):
+        if t is not None:
+            _need(t, f"{name}: {nm}", shape=shp, dtype=torch.uint8, contiguous=True)
+    if group_offsets is not None:
+        _need(group_offsets, f"{name}: group_offsets", dtype=torch.int32, contiguous=True)
+    _check_dev(h, group_offsets, q, s)
     if q is None:
         q = torch.empty((M, F), dtype=torch.uint8, device=h.device)
     if s is None:
@@ -561,8 +750,17 @@ def dswiglu_f32(g, u, da):
 
 def dswiglu_quant(hq, hs, da, group_offsets=None, dq=None, ds=None):
     """SwiGLU backward from the FP8-cached input: (hq [M,2F], hs, da bf16 [M,F]) -> (dq [M,2F], ds)."""
-    _check_dev(hq, hs, da, group_offsets)
+    name = "dswiglu_quant"
+    _check_2d_codes(hq, f"{name}: hq")
     M, F2 = hq.shape
+    _need(hs, f"{name}: hs", shape=(M, F2 // 128), dtype=torch.uint8)
+    _need(da, f"{name}: da", shape=(M, F2 // 2), dtype=torch.bfloat16)
+    for t, nm, shp in ((dq, "dq", (M, F2)), (ds, "ds", (M, F2 // 128))):
+        if t is not None:
+            _need(t, f"{name}: {nm}", shape=shp, dtype=torch.uint8, contiguous=True)
+    if group_offsets is not None:
+        _need(group_offsets, f"{name}: group_offsets", dtype=torch.int32, contiguous=True)
+    _check_dev(hq, hs, da, group_offsets, dq, ds)
     if dq is None:
         dq = torch.empty((M, F2), dtype=torch.uint8, device=hq.device)
     if ds is None:
@@ -575,6 +773,9 @@ def dswiglu_quant(hq, hs, da, group_offsets=None, dq=None, ds=None):
 
 def mx2_quant(x, g1=10240):
     """MOSS two-level quantization of x [R, C] bf16 -> (q, s2 [R, C/32], s1 fp32 [R, ceil(C/g1)])."""
+    if x.dim() != 2:
+        raise ValueError("mx2_quant: x must be 2-D")
+    _need(x, "mx2_quant: x", dtype=torch.bfloat16)
     _check_dev(x)
     R, Cc = x.shape
     ng = (Cc + g1 - 1) // g1
@@ -587,9 +788,10 @@ def mx2_quant(x, g1=10240):
 
 def mx2_quant_rule(x, g1=10240, rule=SCALE_CEIL):
     """mx2_quant with the level-2 exponent rule chosen (SCALE_CEIL or SCALE_OCP_FLOOR)."""
+    if x.dim() != 2:
+        raise ValueError("mx2_quant_rule: x must be 2-D")
+    _need(x, "mx2_quant_rule: x", dtype=torch.bfloat16, contiguous=True)
     _check_dev(x)
-    if not x.is_contiguous():
-        raise ValueError("mx2_quant_rule: x must be contiguous")
     R, Cc = x.shape
     ng = (Cc + g1 - 1) // g1
     q = torch.empty((R, Cc), dtype=torch.uint8, device=x.device)
@@ -601,8 +803,13 @@ def mx2_quant_rule(x, g1=10240, rule=SCALE_CEIL):
 
 def mx2_dequant(q, s2, s1, g1=10240):
     """x_hat = (decode(q) * 2^(s2-127)) * s1 -> fp32 [R, C]."""
-    _check_dev(q, s2, s1)
+    _check_2d_codes(q, "mx2_dequant: q")
     R, Cc = q.shape
+    _need(s2, "mx2_dequant: s2", shape=(R, Cc // 32), dtype=torch.uint8)
+    if g1 <= 0:
+        raise ValueError("mx2_dequant: g1 must be positive")
+    _need(s1, "mx2_dequant: s1", shape=(R, (Cc + g1 - 1) // g1), dtype=torch.float32)
+    _check_dev(q, s2, s1)
     out = torch.empty((R, Cc), dtype=torch.float32, device=q.device)
     _call("mx2_dequant", _ptr(q.contiguous()), _ptr(s2.contiguous()), _ptr(s1.contiguous()), R, Cc,
           g1, _ptr(out), _stream(q))

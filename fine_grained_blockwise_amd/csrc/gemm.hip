@@ -161,8 +161,13 @@ __device__ __forceinline__ v8bf cvt8_bf16_e5m2(uint32_t w0, uint32_t w1, float s
     return __builtin_bit_cast(v8bf, a);
 }
 
-// Scale byte -> the fp32 whose exponent field it is (byte 0 is taken as 1).
-__device__ __forceinline__ float scale_f32(uint32_t byte) { return __uint_as_float(max(byte, 1u) << 23); }
+// Scale byte -> the fp32 whose exponent field it is.  The scaled conversion
+// reads only the exponent field of its scale operand, as an E8M0 value, so
+// byte 0 (exponent field 0, the fp32 zero) multiplies by 2^-127 exactly like
+// every other byte multiplies by 2^(byte - 127) (measured on gfx950 for every
+// code at exponent fields 0, 1 and 127; the result is the nearest bf16, so it
+// is exact wherever code * 2^(byte - 127) has a bf16 representation).
+__device__ __forceinline__ float scale_f32(uint32_t byte) { return __uint_as_float(byte << 23); }
 
 __device__ __forceinline__ v8i cat(uint4 x, uint4 y)
 {
