@@ -422,6 +422,27 @@ def test_gemm_mx_per32_with_level1(fgb, mode):
         check_gemm(np_(d), ref, mode, bf16, bounds, K)
 
 
+def test_gemm_mx_scale_byte_zero_exact(fgb):
+    """E8M0 byte 0 means 2^-127 on the GPU as in the oracle: an A operand whose every 1x32 scale is byte 0
+    (the scale the 1x32 quantizer gives a group with amax <= 448 * 2^-127), with codes whose value times
+    2^-127 has a bf16 representation (exponent field >= 4), gives outputs near 2^-110 that the exact mode
+    must reproduce; reading byte 0 as 2^-126 would double them."""
+    say("gemm exact: 1x32 A scales all byte 0 (2^-127)")
+    M, N, K = 96, 160, 512
+    g = torch.Generator().manual_seed(21)
+    a = torch.randint(0, 256, (M, K), generator=g, dtype=torch.int32).to(torch.uint8)
+    a = (a & 0x87) | ((torch.randint(4, 16, (M, K), generator=g, dtype=torch.int32).to(torch.uint8)) << 3)
+    a[(a & 0x7F) == 0x7F] ^= 1
+    b = rand_codes((N, K), 22)
+    sa = torch.zeros((M, K // 32), dtype=torch.uint8)
+    sb = rand_scales((N, K // 32), -8, 8, 23)
+    ref = O.block_gemm(a.numpy(), sa.numpy(), O.ROW1x32, b.numpy(), sb.numpy(), O.ROW1x32)
+    assert 0 < np.max(np.abs(ref)) < 2.0 ** -90
+    d = fgb.fp8_block_gemm(a.to(DEV), sa.to(DEV), fgb.ROW1x32, b.to(DEV), sb.to(DEV), fgb.ROW1x32,
+                           out_dtype=torch.float32, mode=fgb.GEMM_EXACT)
+    check_gemm(np_(d), ref, "exact", False)
+
+
 def _sample(M, N, n, seed):
     rng = np.random.default_rng(seed)
     mi = np.concatenate([rng.integers(0, M, n), [0, M - 1, M - 1]])
