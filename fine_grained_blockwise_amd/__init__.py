@@ -22,6 +22,7 @@ __all__ = [
     "fp8_block_transpose_batched", "fp8_grouped_direct_transpose", "fp8_kgrouped_gemm", "swiglu_quant_cache",
     "unpermute_backward_quant", "fp8_quant_rowwise_fmt", "fp8_dequant_fmt", "fgb_fp8_encode",
     "fp8_direct_transpose_fmt", "mx2_quant_rule", "fp8_block_gemm_fmt", "fp8_grouped_gemm_masked",
+    "permute_pad_noalloc", "PERMUTE_PAD_NOALLOC_SCRATCH_BYTES",
     "E4M3", "E5M2", "SCALE_CEIL", "SCALE_OCP_FLOOR", "F32", "BF16", "ROW1x128", "ROW1x32", "BLOCK128", "GEMM_EXACT", "GEMM_FAST",
 ]
 
@@ -43,6 +44,7 @@ SYMBOLS = [
     "fp8_grouped_direct_transpose", "fp8_kgrouped_gemm", "swiglu_quant_cache", "unpermute_backward_quant",
     "fp8_quant_rowwise_fmt", "fp8_dequant_fmt", "fgb_fp8_encode", "fp8_direct_transpose_fmt", "mx2_quant_rule",
     "fp8_block_gemm_fmt", "fp8_grouped_gemm_masked", "fp8_quant_blockwise_t", "swiglu_f32", "dswiglu_f32",
+    "permute_pad_noalloc",
 ]
 
 
@@ -78,6 +80,7 @@ _SIG = {
     "permute_pad": (_i32, [_p, _p, _p, _i64, _i32, _i32, _i64, _i32, _p, _p, _p, _p, _i64, _p,
                            _sz, _p]),
     "permute_pad_workspace_size": (_sz, [_i64, _i32, _i32]),
+    "permute_pad_noalloc": (_i32, [_p, _p, _p, _i64, _i32, _i32, _i64, _i32, _p, _p, _p, _p, _i64, _p]),
     "unpermute_unpad": (_i32, [_p, _p, _p, _i64, _i32, _i64, _p, _p]),
     "unpermute_backward": (_i32, [_p, _p, _p, _i64, _i32, _i64, _i64, _p, _p, _sz, _p]),
     "unpermute_backward_workspace_size": (_sz, [_i64]),
@@ -587,6 +590,38 @@ def permute_pad(xq, xs, topk_idx, G, pad_multiple=16, M_cap=None, workspace=None
     _call("permute_pad", _ptr(xq.contiguous()), _ptr(xs.contiguous()), _ptr(topk_idx.contiguous()),
           T, topk, G, H, pad_multiple, _ptr(out_q), _ptr(out_s), _ptr(row_map), _ptr(offs), M_cap,
           _ptr(workspace), workspace.numel(), _stream(xq))
+    return out_q, out_s, row_map, offs
+
+
+PERMUTE_PAD_NOALLOC_SCRATCH_BYTES = 1 << 20
+
+
+def permute_pad_noalloc(xq, xs, topk_idx, G, out, pad_multiple=16):
+    """permute_pad without any allocation: the caller passes the outputs
+    out = (out_q [M_cap, H], out_s [M_cap, H/128], row_map [T, topk], group_offsets [G+1]); the workspace
+    is the library's per-GPU scratch array (see include/fgb.h for the size limit and the concurrency rule)."""
+    name = "permute_pad_noalloc"
+    _check_2d_codes(xq, f"{name}: xq")
+    T, H = xq.shape
+    _need(xs, f"{name}: xs", shape=(T, H // 128), dtype=torch.uint8, contiguous=True)
+    _need(xq, f"{name}: xq", contiguous=True)
+    if topk_idx.dim() != 2 or topk_idx.shape[0] != T:
+        raise ValueError(f"{name}: topk_idx must be [T, topk]")
+    _need(topk_idx, f"{name}: topk_idx", dtype=torch.int32, contiguous=True)
+    topk = topk_idx.shape[1]
+    if out is None or len(out) != 4:
+        raise ValueError(f"{name}: out must be (out_q, out_s, row_map, group_offsets)")
+    out_q, out_s, row_map, offs = out
+    if out_q.dim() != 2:
+        raise ValueError(f"{name}: out_q must be [M_cap, H]")
+    M_cap = out_q.shape[0]
+    _need(out_q, f"{name}: out_q", shape=(M_cap, H), dtype=torch.uint8, contiguous=True)
+    _need(out_s, f"{name}: out_s", shape=(M_cap, H // 128), dtype=torch.uint8, contiguous=True)
+    _need(row_map, f"{name}: row_map", shape=(T, topk), dtype=torch.int32, contiguous=True)
+    _need(offs, f"{name}: group_offsets", shape=(G + 1,), dtype=torch.int32, contiguous=True)
+    _check_dev(xq, xs, topk_idx, out_q, out_s, row_map, offs)
+    _call(name, _ptr(xq), _ptr(xs), _ptr(topk_idx), T, topk, G, H, pad_multiple, _ptr(out_q), _ptr(out_s),
+          _ptr(row_map), _ptr(offs), M_cap, _stream(xq))
     return out_q, out_s, row_map, offs
 
 

@@ -19,6 +19,8 @@
 //           the 1x128 rule gives an all-zero tile).
 #include "fgb_internal.h"
 
+#include <mutex>
+
 namespace fgb {
 
 constexpr int PP_CHUNK = 256; // tokens per histogram chunk
@@ -765,41 +767,30 @@ __global__ __launch_bounds__(256) void ub_token_quant_kernel(const uint16_t *__r
     }
 }
 
-} // namespace fgb
-
-using namespace fgb;
-
-extern "C" size_t permute_pad_workspace_size(int64_t T, int topk, int G)
+// Validation and launches of permute_pad, with the workspace already chosen
+// (the caller's, or the no-allocation variant's scratch array).
+static int permute_pad_check(const char *name, const uint8_t *xq, const uint8_t *xs, const int32_t *topk_idx,
+                             int64_t T, int topk, int G, int64_t H, int pad_multiple, const uint8_t *out_q,
+                             const uint8_t *out_s, const int32_t *row_map, const int32_t *group_offsets,
+                             int64_t M_cap)
 {
-    (void)topk;
-    if (T < 0 || G < 1)
-        return 0;
-    return (2 * pp_nchunks(T) * (size_t)G + (size_t)G) * sizeof(int32_t);
+    FGB_REQUIRE(xq && xs && topk_idx && out_q && out_s && row_map && group_offsets, FGB_EINVAL,
+                "%s: null pointer", name);
+    FGB_REQUIRE(T >= 0 && topk >= 1 && topk <= 64 && G >= 1 && G <= 1024, FGB_EINVAL,
+                "%s: need T >= 0, 1 <= topk <= 64, 1 <= G <= 1024", name);
+    FGB_REQUIRE(H > 0 && H % 128 == 0, FGB_EINVAL, "%s: H must be a positive multiple of 128", name);
+    FGB_REQUIRE(pad_multiple >= 1 && pad_multiple <= 256, FGB_EINVAL, "%s: pad_multiple must be in [1, 256]", name);
+    FGB_REQUIRE(M_cap >= T * topk + (int64_t)(pad_multiple - 1) * G, FGB_EINVAL,
+                "%s: M_cap must be >= T*topk + (pad_multiple-1)*G", name);
+    FGB_REQUIRE(M_cap < (1ll << 31), FGB_EINVAL, "%s: M_cap must fit in int32", name);
+    FGB_REQUIRE(aligned16(xq) && aligned16(out_q), FGB_EINVAL, "%s: xq and out_q must be 16-byte aligned", name);
+    return FGB_OK;
 }
 
-extern "C" int permute_pad(const uint8_t *xq, const uint8_t *xs, const int32_t *topk_idx,
-                           int64_t T, int topk, int G, int64_t H, int pad_multiple,
-                           uint8_t *out_q, uint8_t *out_s, int32_t *row_map,
-                           int32_t *group_offsets, int64_t M_cap, void *workspace,
-                           size_t ws_bytes, void *stream)
+static int permute_pad_launch(const uint8_t *xq, const uint8_t *xs, const int32_t *topk_idx, int64_t T, int topk,
+                              int G, int64_t H, int pad_multiple, uint8_t *out_q, uint8_t *out_s, int32_t *row_map,
+                              int32_t *group_offsets, int64_t M_cap, void *workspace, hipStream_t st)
 {
-    clear_error();
-    FGB_REQUIRE(xq && xs && topk_idx && out_q && out_s && row_map && group_offsets, FGB_EINVAL,
-                "permute_pad: null pointer");
-    FGB_REQUIRE(T >= 0 && topk >= 1 && topk <= 64 && G >= 1 && G <= 1024, FGB_EINVAL,
-                "permute_pad: need T >= 0, 1 <= topk <= 64, 1 <= G <= 1024");
-    FGB_REQUIRE(H > 0 && H % 128 == 0, FGB_EINVAL, "permute_pad: H must be a positive multiple of 128");
-    FGB_REQUIRE(pad_multiple >= 1 && pad_multiple <= 256, FGB_EINVAL,
-                "permute_pad: pad_multiple must be in [1, 256]");
-    FGB_REQUIRE(M_cap >= T * topk + (int64_t)(pad_multiple - 1) * G, FGB_EINVAL,
-                "permute_pad: M_cap must be >= T*topk + (pad_multiple-1)*G");
-    FGB_REQUIRE(M_cap < (1ll << 31), FGB_EINVAL, "permute_pad: M_cap must fit in int32");
-    FGB_REQUIRE(aligned16(xq) && aligned16(out_q), FGB_EINVAL,
-                "permute_pad: xq and out_q must be 16-byte aligned");
-    size_t need = permute_pad_workspace_size(T, topk, G);
-    FGB_REQUIRE(workspace && ws_bytes >= need, FGB_EWORKSPACE,
-                "permute_pad: workspace of %zu bytes required", need);
-    hipStream_t st = (hipStream_t)stream;
     PPWorkspace w = pp_carve(workspace, T, G);
     int nchunks = (int)pp_nchunks(T);
     if (nchunks > 0) {
@@ -822,6 +813,92 @@ extern "C" int permute_pad(const uint8_t *xq, const uint8_t *xs, const int32_t *
         FGB_LAUNCHED("permute_pad/copy");
     }
     return FGB_OK;
+}
+
+// ---- the no-allocation variant's scratch array ------------------------------
+// One copy per GPU, alive until the process ends.  The host never passes the
+// array's name to a kernel (in host code it is only a stand-in for the
+// symbol): the device address of each GPU's copy is looked up once per
+// device with hipGetSymbolAddress, with that device current, and kept here.
+static __device__ __align__(256) int32_t scratch[FGB_PERMUTE_PAD_NOALLOC_SCRATCH_BYTES / sizeof(int32_t)];
+
+constexpr int PP_MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[PP_MAX_DEVICES];
+
+// The current device's copy of `scratch` (looked up on the first call made
+// with that device current).
+static int scratch_for_current_device(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return set_error(FGB_EHIP, "permute_pad_noalloc: hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= PP_MAX_DEVICES)
+        return set_error(FGB_EUNSUPPORTED, "permute_pad_noalloc: device %d beyond the %d supported", dev,
+                         PP_MAX_DEVICES);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return set_error(FGB_EHIP, "permute_pad_noalloc: hipGetSymbolAddress failed: %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return FGB_OK;
+}
+
+} // namespace fgb
+
+using namespace fgb;
+
+extern "C" int permute_pad(const uint8_t *xq, const uint8_t *xs, const int32_t *topk_idx,
+                           int64_t T, int topk, int G, int64_t H, int pad_multiple,
+                           uint8_t *out_q, uint8_t *out_s, int32_t *row_map,
+                           int32_t *group_offsets, int64_t M_cap, void *workspace,
+                           size_t ws_bytes, void *stream)
+{
+    clear_error();
+    int rc = permute_pad_check("permute_pad", xq, xs, topk_idx, T, topk, G, H, pad_multiple, out_q, out_s, row_map,
+                               group_offsets, M_cap);
+    if (rc != FGB_OK)
+        return rc;
+    size_t need = permute_pad_workspace_size(T, topk, G);
+    FGB_REQUIRE(workspace && ws_bytes >= need, FGB_EWORKSPACE,
+                "permute_pad: workspace of %zu bytes required", need);
+    return permute_pad_launch(xq, xs, topk_idx, T, topk, G, H, pad_multiple, out_q, out_s, row_map, group_offsets,
+                              M_cap, workspace, (hipStream_t)stream);
+}
+
+extern "C" int permute_pad_noalloc(const uint8_t *xq, const uint8_t *xs, const int32_t *topk_idx, int64_t T,
+                                   int topk, int G, int64_t H, int pad_multiple, uint8_t *out_q, uint8_t *out_s,
+                                   int32_t *row_map, int32_t *group_offsets, int64_t M_cap, void *stream)
+{
+    clear_error();
+    int rc = permute_pad_check("permute_pad_noalloc", xq, xs, topk_idx, T, topk, G, H, pad_multiple, out_q, out_s,
+                               row_map, group_offsets, M_cap);
+    if (rc != FGB_OK)
+        return rc;
+    const size_t need = permute_pad_workspace_size(T, topk, G);
+    FGB_REQUIRE(need <= (size_t)FGB_PERMUTE_PAD_NOALLOC_SCRATCH_BYTES, FGB_EWORKSPACE,
+                "permute_pad_noalloc: these sizes need %zu bytes of scratch, more than the %d bytes it holds "
+                "(2*ceil(T/256)*G + G int32 words); call permute_pad with a workspace instead",
+                need, (int)FGB_PERMUTE_PAD_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    rc = scratch_for_current_device(&ws);
+    if (rc != FGB_OK)
+        return rc;
+    return permute_pad_launch(xq, xs, topk_idx, T, topk, G, H, pad_multiple, out_q, out_s, row_map, group_offsets,
+                              M_cap, ws, (hipStream_t)stream);
+}
+
+extern "C" size_t permute_pad_workspace_size(int64_t T, int topk, int G)
+{
+    (void)topk;
+    if (T < 0 || G < 1)
+        return 0;
+    return (2 * pp_nchunks(T) * (size_t)G + (size_t)G) * sizeof(int32_t);
 }
 
 extern "C" int unpermute_unpad(const void *y, const int32_t *row_map, const float *probs,

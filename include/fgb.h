@@ -378,6 +378,33 @@ int permute_pad(const uint8_t *xq, const uint8_t *xs, const int32_t *topk_idx, i
 /* Workspace bytes permute_pad needs for these sizes. */
 size_t permute_pad_workspace_size(int64_t T, int topk, int G);
 
+/* Size of the scratch array that permute_pad_noalloc uses on each GPU. */
+#define FGB_PERMUTE_PAD_NOALLOC_SCRATCH_BYTES (1 << 20)
+
+/*
+ * permute_pad_noalloc -- permute_pad for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels and the same outputs, bit for bit, with
+ * the workspace taken from a scratch array of FGB_PERMUTE_PAD_NOALLOC_SCRATCH_BYTES
+ * (1 MiB) that the library holds on each GPU it runs on, from the first call
+ * on that GPU until the process ends.  The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine); the caller passes every
+ * input and output, as for permute_pad.
+ *   Arguments: as permute_pad, without workspace and ws_bytes.
+ *   Limit: permute_pad_workspace_size(T, topk, G) <= 1 MiB, i.e.
+ *          2*ceil(T/256)*G + G <= 262144 (e.g. T <= 1,048,320 tokens at G = 32);
+ *          larger sizes return FGB_EWORKSPACE before anything is enqueued.
+ *   Concurrency: every call on one GPU shares that GPU's scratch array (its
+ *          contents on entry do not matter: every word is written before it is
+ *          read), so calls that overlap in time on one GPU -- on different
+ *          streams, or from different threads -- race; calls on one stream are
+ *          ordered and safe.
+ *   Errors: as permute_pad; FGB_EHIP if the scratch address cannot be looked up.
+ */
+int permute_pad_noalloc(const uint8_t *xq, const uint8_t *xs, const int32_t *topk_idx, int64_t T, int topk,
+                        int G, int64_t H, int pad_multiple, uint8_t *out_q, uint8_t *out_s, int32_t *row_map,
+                        int32_t *group_offsets, int64_t M_cap, void *stream);
+
 /*
  * unpermute_unpad -- inverse of permute_pad on the expert output ([FLOW]
  * "Core method": fused unpermute + unpadding).

@@ -169,3 +169,20 @@ def test_oracle_and_library_share_nothing():
             if fn.endswith((".py", ".hip", ".h")):
                 txt = open(os.path.join(dp, fn)).read()
                 assert not re.search(r"import\s+oracle|from\s+oracle|liboracle|fgb_oracle", txt), fn
+
+
+def test_permute_pad_noalloc_rejects_sizes_beyond_its_scratch():
+    import fine_grained_blockwise_amd as fgb
+    L = fgb.lib()
+    f = _fake()
+    T, topk, G = 1 << 20, 8, 1024
+    need = L.permute_pad_workspace_size(T, topk, G)
+    assert need > fgb.PERMUTE_PAD_NOALLOC_SCRATCH_BYTES
+    assert L.permute_pad_noalloc(f, f, f, T, topk, G, 7168, 16, f, f, f, f, T * topk + 15 * G, None) == 3
+    assert b"scratch" in L.fgb_last_error()
+    # the largest size it takes at G = 32: 2*ceil(T/256)*32 + 32 words fit in 1 MiB
+    T = 4095 * 256
+    assert L.permute_pad_workspace_size(T, topk, 32) <= fgb.PERMUTE_PAD_NOALLOC_SCRATCH_BYTES
+    assert L.permute_pad_workspace_size(T + 256, topk, 32) > fgb.PERMUTE_PAD_NOALLOC_SCRATCH_BYTES
+    # argument errors come first, as for permute_pad
+    assert L.permute_pad_noalloc(None, f, f, 16, topk, 32, 7168, 16, f, f, f, f, 16 * topk + 15 * 32, None) == 1
