@@ -31,3 +31,31 @@ def test_bench_line_contract():
     assert rf["bound"] in ("hbm", "mfma", "alu")
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
     assert len(line["kernels"]) == 9  # the Linear forward and backward: 3 quant, 2 transposes, W^T, 3 GEMMs
+    # every GEMM is priced at the dense FP8 peak in `value`; the mode's own instruction peak beside it
+    assert line["value_at_contraction_peak"] >= line["value"] > 0
+    for name, k in line["kernels"].items():
+        if k["unit"] == "TFLOP/s":
+            assert abs(k["frac_of_fp8_peak"] - k["achieved"] / 5000.0) < 1e-3, name
+    hist = line["scale_exponent_histograms"]
+    assert set(hist) >= {"lin.X 1x128", "lin.W 128x128", "lin.dY 1x128"}
+    for h in hist.values():
+        assert h["min_e"] <= h["max_e"] and sum(h["counts"].values()) > 0
+    assert sum(hist["lin.X 1x128"]["counts"].values()) == 8192 * 7168 // 128
+    und = line["transpose_underflow"]
+    assert set(und) == {"lin.direct_transpose Xq", "lin.direct_transpose dYq"}
+    for u in und.values():
+        assert 0 <= u["became_zero"] <= u["nonzero_in"]
+
+
+def test_bench_output_check_against_the_oracle():
+    print("bench: linear part with the CPU-baseline leg and its output check", flush=True)
+    r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--parts", "linear", "--steps", "1",
+                        "--warmup", "1", "--no-study"],
+                       capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    chk = line["cpu_baseline"]["output_check"]
+    for name in ("lin.gemm fprop", "lin.gemm dgrad", "lin.gemm wgrad"):
+        c = chk[name]
+        assert c["within_tolerance"] and c["beyond_one_bf16_ulp"] == 0, (name, c)
+        assert 0 <= c["calc_diff"] < 1e-4, (name, c)
