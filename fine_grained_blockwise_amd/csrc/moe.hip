@@ -14,7 +14,9 @@
 //   rowmap  per chunk, the rank of every (token, slot) among the chunk's slots
 //           of the same expert, in (token, slot) order -> row_map
 //   copy    one wave per token: the 16-byte chunks of the code row and the
-//           scale row are read once and written to each destination; extra
+//           scale row are read once (streaming loads) and written to each
+//           destination with ordinary stores (the kernel's traffic is ~90%
+//           writes; ordinary stores measured 3% faster here); extra
 //           waves fill the padding rows (code 0, scale byte 105 -- what
 //           the 1x128 rule gives an all-zero tile).
 #include "fgb_internal.h"
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(256) void pp_copy_kernel(const uint8_t *__restrict_
                 for (int u = 0; u < 8; u++) {
                     int64_t c = c0 + u * 64 + lane;
                     if (c < H16)
-                        st_stream16(dst + c * 16, v[u]);
+                        st_plain16(dst + c * 16, v[u]);
                 }
             }
         }
@@ -247,7 +249,7 @@ __global__ __launch_bounds__(256) void pp_copy_kernel(const uint8_t *__restrict_
             return;
         uint8_t *dst = out_q + r * H;
         for (int64_t c = lane; c < H16; c += 64)
-            st_stream16(dst + c * 16, make_uint4(0, 0, 0, 0));
+            st_plain16(dst + c * 16, make_uint4(0, 0, 0, 0));
         for (int64_t c = lane; c < H128; c += 64)
             out_s[r * H128 + c] = 105;
     }

@@ -13,13 +13,10 @@
 // csub = lane >> 3) owns the 16x16 byte sub-tile at rows tsub*16.., columns
 // csub*16..: 16 row loads of 16 bytes (8 lanes cover one 128-byte row
 // segment), the shift applied in the row domain where k is uniform per row,
-// a 16x16 byte transpose in registers with v_perm_b32, and 16 column stores of
-// 16 bytes (8 lanes cover one 128-byte output row segment).  The four waves
-// of a workgroup take four consecutive row blocks of one column block, so
-// each output row gets 512 contiguous bytes at once (measured: 5.0 TB/s on
-// [131584, 7168] against 3.5-4.0 TB/s with four column blocks per
-// workgroup, whose writes land in four separate 128-byte pieces per row).
-// No LDS, no bank conflicts; HBM-bound.
+// and a 16x16 byte transpose in registers with v_perm_b32.  A workgroup of
+// eight waves takes eight consecutive row blocks of one column block and
+// stages their transposed blocks in LDS, so that every output row is written
+// as one 1 KB run (the staging is described below).  HBM-bound.
 //
 // The shift decodes two codes to fp32 (exact), multiplies by 2^-k (exact) and
 // converts back with round-to-nearest-even; for E - k >= 1 that is the plain
@@ -54,9 +51,174 @@ __device__ __forceinline__ uint32_t shift_word(uint32_t w, float f)
     }
 }
 
-// FMT: element format of the codes (the shift is the same exponent move).
+// Transposed 16x16 byte sub-tile: w[j][x] holds row j, bytes 4x..4x+3 of the
+// lane's sub-tile; o[c][i] receives column c, rows 4i..4i+3.
+__device__ __forceinline__ void transpose16x16(const uint32_t (&w)[16][4], uint32_t (&o)[16][4])
+{
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int x = 0; x < 4; x++)
+            tr4x4(w[4 * i + 0][x], w[4 * i + 1][x], w[4 * i + 2][x], w[4 * i + 3][x], o[4 * x + 0][i],
+                  o[4 * x + 1][i], o[4 * x + 2][i], o[4 * x + 3][i]);
+}
+
+// ---- LDS staging of TB transposed blocks ----------------------------------------
+// A workgroup of TB waves takes TB consecutive 128-row blocks (rows of the
+// source, columns of the transposed copy) of one 128-column block.  Each wave
+// transposes its block in registers and writes it into an LDS tile of 128
+// output rows x TB*128 bytes; the workgroup then stores every output row as
+// one run of TB*128 contiguous bytes (1 KB at TB = 8).  Measured on the
+// MI355X against one wave per block with 512-byte runs per output row
+// (four waves): +5% on [32768, 7168] and [32768, 2048] with the Infinity
+// Cache flushed, +10% on [8192, 7168].
+// Tile row r keeps its 16-byte chunk ch at position ch ^ (((r >> 4) & 1) << 3):
+// the 16 lanes of a quarter-wave write rows r and r + 16 at the same chunk
+// index, which the swizzle moves to the other half of the 64 banks, and the
+// store phase reads 16 consecutive chunks of one row, a permutation within
+// an aligned group of 16 -- both free of bank conflicts.
+template <int TB> struct Stage {
+    static constexpr int RS = TB * 128; // bytes per tile row
+    static constexpr int CPR = TB * 8;  // 16-byte chunks per tile row
+    static constexpr int TILE = 128 * RS;
+    static constexpr int LDS = TILE + 64; // + the per-wave scale bytes
+    static_assert(TB >= 2, "the swizzle needs at least 16 chunks per row");
+    __device__ static int at(int r, int ch) { return r * RS + 16 * (ch ^ (((r >> 4) & 1) << 3)); }
+};
+
+// The lane's 16 columns x 16 bytes of wave `w`'s block into the tile.
+template <int TB>
+__device__ __forceinline__ void stage_put(uint8_t *lds, int w, int tsub, int csub, const uint32_t (&o)[16][4])
+{
+#pragma unroll
+    for (int c = 0; c < 16; c++)
+        *reinterpret_cast<uint4 *>(lds + Stage<TB>::at(csub * 16 + c, w * 8 + tsub)) =
+            make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]);
+}
+
+// Store the tile: output row r goes to out + r * ld_out, chunks of blocks
+// [0, nvalid) only (a last group may hold fewer than TB blocks).
+template <int TB>
+__device__ __forceinline__ void stage_store(const uint8_t *lds, uint8_t *out, int64_t ld_out, int nvalid)
+{
+    constexpr int NTH = TB * 64, NCH = 128 * Stage<TB>::CPR;
+#pragma unroll
+    for (int k = 0; k < NCH / NTH; k++) {
+        const int idx = (int)threadIdx.x + k * NTH;
+        const int r = idx / Stage<TB>::CPR, ch = idx % Stage<TB>::CPR;
+        if (ch / 8 < nvalid)
+            st_stream16(out + r * ld_out + ch * 16, *reinterpret_cast<const uint4 *>(lds + Stage<TB>::at(r, ch)));
+    }
+}
+
+// The TB scale bytes of output row r (blocks [0, nvalid)) at dst: one 8-, 4-
+// or 2-byte store when the group is whole and dst aligned, else bytes.
+template <int TB>
+__device__ __forceinline__ void store_scale_run(uint8_t *dst, const uint8_t *esc, int nvalid)
+{
+    if (nvalid == TB && ((uintptr_t)dst % TB) == 0) {
+        uint32_t v[2] = {0u, 0u};
+#pragma unroll
+        for (int b = 0; b < TB; b++)
+            v[b / 4] |= (uint32_t)esc[b] << (8 * (b % 4));
+        if constexpr (TB == 8)
+            *reinterpret_cast<uint2 *>(dst) = make_uint2(v[0], v[1]);
+        else if constexpr (TB == 4)
+            *reinterpret_cast<uint32_t *>(dst) = v[0];
+        else
+            *reinterpret_cast<uint16_t *>(dst) = (uint16_t)v[0];
+    } else {
+        for (int b = 0; b < nvalid; b++)
+            dst[b] = esc[b];
+    }
+}
+
+// Direct transpose of dense [T, C] codes.  Workgroup (tg, cb): row blocks
+// tg*TB .. tg*TB + TB-1 (those below T/128) of column block cb; consecutive
+// workgroups take consecutive row groups of one column block.
+// ROWSCALE: 1x128 scales and the exponent shift; else 128x128 block scales,
+// k = 0 (an exact byte transpose).  FMT: element format of the codes (the
+// shift is the same exponent move).  blockIdx.y: matrix of a dense batch.
+template <int TB, bool ROWSCALE, int FMT = FMT_E4M3>
+__global__ __launch_bounds__(TB * 64) void direct_transpose_kernel(const uint8_t *__restrict__ q,
+                                                                   const uint8_t *__restrict__ s, int64_t T,
+                                                                   int64_t C, uint8_t *__restrict__ qt,
+                                                                   uint8_t *__restrict__ st)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    uint8_t *esc = lds + Stage<TB>::TILE;
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int64_t ncb = C / 128, ntb = T / 128;
+    const int64_t ngt = (ntb + TB - 1) / TB;
+    const int64_t tg = blockIdx.x % ngt, cb = blockIdx.x / ngt;
+    const int nvalid = (int)min((int64_t)TB, ntb - tg * TB);
+    {
+        const int64_t e = blockIdx.y;
+        q += e * T * C;
+        qt += e * T * C;
+        s += e * (ROWSCALE ? T * ncb : ntb * ncb);
+        st += e * (ROWSCALE ? C * ntb : ntb * ncb);
+    }
+    const int tsub = lane & 7, csub = lane >> 3;
+    if (wave < nvalid) { // uniform per wave
+        const int64_t tb = tg * TB + wave;
+        const int64_t t0 = tb * 128 + tsub * 16;
+        const int64_t c0 = cb * 128 + csub * 16;
+        uint32_t w[16][4];
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            const uint4 v = ld_stream16(q + (t0 + j) * C + c0);
+            w[j][0] = v.x;
+            w[j][1] = v.y;
+            w[j][2] = v.z;
+            w[j][3] = v.w;
+        }
+        int emax;
+        if constexpr (ROWSCALE) {
+            int e[16];
+            uint32_t m = 0;
+#pragma unroll
+            for (int j = 0; j < 16; j++) {
+                e[j] = s[(t0 + j) * ncb + cb];
+                m = max(m, (uint32_t)e[j]);
+            }
+            emax = (int)group_max_u32<8>(m); // lanes with equal csub hold all 128 rows
+#pragma unroll
+            for (int j = 0; j < 16; j++) {
+                const int k = min(emax - e[j], 64); // E5M2 codes survive shifts up to 32, E4M3 up to 17
+                const float f = pow2f(-k);
+#pragma unroll
+                for (int x = 0; x < 4; x++)
+                    w[j][x] = shift_word<FMT>(w[j][x], f);
+            }
+        } else {
+            emax = s[tb * ncb + cb];
+        }
+        uint32_t o[16][4];
+        transpose16x16(w, o);
+        stage_put<TB>(lds, wave, tsub, csub, o);
+        if (lane == 0)
+            esc[wave] = (uint8_t)emax;
+    }
+    __syncthreads();
+    stage_store<TB>(lds, qt + (cb * 128) * T + tg * TB * 128, T, nvalid);
+    if constexpr (ROWSCALE) {
+        if (threadIdx.x < 128)
+            store_scale_run<TB>(st + (cb * 128 + threadIdx.x) * ntb + tg * TB, esc, nvalid);
+    } else {
+        if (threadIdx.x == 0)
+            store_scale_run<TB>(st + cb * ntb + tg * TB, esc, nvalid);
+    }
+}
+
+// The register-only form for small transposes (too few row-block groups to
+// keep every CU busy with the staged form): one wave per 128x128 block, the
+// four waves of a workgroup on consecutive row blocks of one column block (512
+// contiguous bytes per output row), each lane storing its 16 columns directly.
+// No LDS, so up to five workgroups share a CU.  ROWSCALE and FMT as in
+// direct_transpose_kernel.
 template <bool ROWSCALE, int FMT = FMT_E4M3>
-__global__ __launch_bounds__(256) void direct_transpose_kernel(const uint8_t *__restrict__ q,
+__global__ __launch_bounds__(256) void direct_transpose_reg_kernel(const uint8_t *__restrict__ q,
                                                                const uint8_t *__restrict__ s,
                                                                int64_t T, int64_t C,
                                                                uint8_t *__restrict__ qt,
@@ -111,12 +273,7 @@ __global__ __launch_bounds__(256) void direct_transpose_kernel(const uint8_t *__
         }
     }
     uint32_t o[16][4]; // o[c][i]: column c0+c, rows t0+4i .. t0+4i+3
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int x = 0; x < 4; x++)
-            tr4x4(w[4 * i + 0][x], w[4 * i + 1][x], w[4 * i + 2][x], w[4 * i + 3][x], o[4 * x + 0][i],
-                  o[4 * x + 1][i], o[4 * x + 2][i], o[4 * x + 3][i]);
+    transpose16x16(w, o);
 #pragma unroll
     for (int c = 0; c < 16; c++)
         st_stream16(qt + (c0 + c) * T + t0, make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]));
@@ -144,10 +301,14 @@ __global__ void koff_kernel(const int32_t *__restrict__ off, int G, int32_t *__r
 }
 
 // Direct transpose of expert segments: one wave per 128x128 output block
-// (column block kb of the transposed copy, row block cb of C), as in
-// direct_transpose_kernel, except that the block's source rows are the
-// segment's rows present (the last block of a segment may be short: its
-// absent rows count as code 0 and take no part in the block maximum).
+// (column block kb of the transposed copy, row block cb of C), the lane
+// mapping of direct_transpose_kernel without the LDS staging, except that the
+// block's source rows are the segment's rows present (the last block of a
+// segment may be short: its absent rows count as code 0 and take no part in
+// the block maximum).  The four waves of a workgroup take four consecutive
+// column blocks of one output block, i.e. 512 contiguous bytes of each source
+// row: measured faster here than staging eight output blocks through LDS
+// (426 against 467 us on the MoE's [131376, 7168] segments).
 __global__ __launch_bounds__(256) void grouped_direct_transpose_kernel(
     const uint8_t *__restrict__ q, const uint8_t *__restrict__ s, int64_t C, const int32_t *__restrict__ off,
     const int32_t *__restrict__ koff, int G, uint8_t *__restrict__ qt, uint8_t *__restrict__ st, int64_t Kc,
@@ -199,17 +360,74 @@ __global__ __launch_bounds__(256) void grouped_direct_transpose_kernel(
             w[j][x] = shift_word(w[j][x], f);
     }
     uint32_t o[16][4];
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int x = 0; x < 4; x++)
-            tr4x4(w[4 * i + 0][x], w[4 * i + 1][x], w[4 * i + 2][x], w[4 * i + 3][x], o[4 * x + 0][i],
-                  o[4 * x + 1][i], o[4 * x + 2][i], o[4 * x + 3][i]);
+    transpose16x16(w, o);
 #pragma unroll
     for (int c = 0; c < 16; c++)
         st_stream16(qt + (c0 + c) * Kc + kb * 128 + tl, make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]));
     st[(cb * 128 + lane) * nkb + kb] = (uint8_t)emax;
     st[(cb * 128 + 64 + lane) * nkb + kb] = (uint8_t)emax;
+}
+
+// The staged kernels use more than 64 KB of LDS at TB = 8: the limit is raised
+// once per kernel (the template parameter: one flag table per kernel) and device.
+template <auto KERN>
+static int raise_lds_limit(int bytes, const char *name)
+{
+    static bool done[64] = {};
+    const auto kern = KERN;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
+        dev = -1;
+    const bool cached = dev >= 0 && dev < 64;
+    if (!cached || !done[dev]) {
+        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        if (e != hipSuccess)
+            return set_error(FGB_EHIP, "%s: hipFuncSetAttribute failed: %s", name, hipGetErrorString(e));
+        if (cached)
+            done[dev] = true;
+    }
+    return FGB_OK;
+}
+
+template <int TB, bool ROWSCALE, int FMT>
+static int launch_direct(const uint8_t *q, const uint8_t *s, int64_t T, int64_t C, uint8_t *qt, uint8_t *st,
+                         int batch, hipStream_t stm, const char *name)
+{
+    auto kern = direct_transpose_kernel<TB, ROWSCALE, FMT>;
+    int rc = raise_lds_limit<direct_transpose_kernel<TB, ROWSCALE, FMT>>(Stage<TB>::LDS, name);
+    if (rc != FGB_OK)
+        return rc;
+    const int64_t ngt = (T / 128 + TB - 1) / TB;
+    const int64_t grid = ngt * (C / 128);
+    if (grid >= (1ll << 31))
+        return set_error(FGB_EINVAL, "%s: too many blocks", name);
+    kern<<<dim3((unsigned)grid, (unsigned)batch), TB * 64, Stage<TB>::LDS, stm>>>(q, s, T, C, qt, st);
+    FGB_LAUNCHED(name);
+    return FGB_OK;
+}
+
+// Eight row blocks per workgroup, staged through LDS, where that gives at
+// least 384 workgroups (1.5 per CU; the 128 KB tile allows one workgroup per
+// CU); else the register-only form.  Measured on the MI355X, cache flushed:
+// staged 94.3 / 31.2 / 28.7 us against 97.5 / 32.7 / 31.2 us on [32768, 7168],
+// [32768, 2048], [8192, 7168]; on [8192, 2048] (128 staged workgroups) and the
+// [2048, 7168] weight, two- and four-block staging lost 4-19% to the
+// register-only form.
+template <bool ROWSCALE, int FMT = FMT_E4M3>
+static int launch_direct_any(const uint8_t *q, const uint8_t *s, int64_t T, int64_t C, uint8_t *qt, uint8_t *st,
+                             int batch, hipStream_t stm, const char *name)
+{
+    const int64_t ntb = T / 128, work = (C / 128) * batch;
+    if ((ntb + 7) / 8 * work >= 384)
+        return launch_direct<8, ROWSCALE, FMT>(q, s, T, C, qt, st, batch, stm, name);
+    const int64_t nb = ntb * (C / 128);
+    const int64_t grid = (nb + 3) / 4;
+    if (grid >= (1ll << 31))
+        return set_error(FGB_EINVAL, "%s: too many blocks", name);
+    direct_transpose_reg_kernel<ROWSCALE, FMT><<<dim3((unsigned)grid, (unsigned)batch), 256, 0, stm>>>(
+        q, s, T, C, qt, st, nb);
+    FGB_LAUNCHED(name);
+    return FGB_OK;
 }
 
 // ---- three-pass baseline ------------------------------------------------------
@@ -265,18 +483,12 @@ extern "C" int fp8_direct_transpose(const uint8_t *q, const uint8_t *s, int s_gr
                 (long long)rows, (long long)cols);
     FGB_REQUIRE(aligned16(q) && aligned16(qt), FGB_EINVAL,
                 "fp8_direct_transpose: q and qt must be 16-byte aligned");
-    int64_t nb = (rows / 128) * (cols / 128);
-    if (nb == 0)
+    if (rows == 0 || cols == 0)
         return FGB_OK;
-    int64_t grid = (nb + 3) / 4;
-    FGB_REQUIRE(grid < (1ll << 31), FGB_EINVAL, "fp8_direct_transpose: too many blocks");
     hipStream_t stm = (hipStream_t)stream;
     if (s_gran == FGB_ROW1x128)
-        direct_transpose_kernel<true><<<(int)grid, 256, 0, stm>>>(q, s, rows, cols, qt, st, nb);
-    else
-        direct_transpose_kernel<false><<<(int)grid, 256, 0, stm>>>(q, s, rows, cols, qt, st, nb);
-    FGB_LAUNCHED("fp8_direct_transpose");
-    return FGB_OK;
+        return launch_direct_any<true>(q, s, rows, cols, qt, st, 1, stm, "fp8_direct_transpose");
+    return launch_direct_any<false>(q, s, rows, cols, qt, st, 1, stm, "fp8_direct_transpose");
 }
 
 extern "C" int fp8_direct_transpose_fmt(const uint8_t *q, const uint8_t *s, int fmt, int64_t rows, int64_t cols,
@@ -293,14 +505,10 @@ extern "C" int fp8_direct_transpose_fmt(const uint8_t *q, const uint8_t *s, int 
                 (long long)rows, (long long)cols);
     FGB_REQUIRE(aligned16(q) && aligned16(qt), FGB_EINVAL,
                 "fp8_direct_transpose_fmt: q and qt must be 16-byte aligned");
-    int64_t nb = (rows / 128) * (cols / 128);
-    if (nb == 0)
+    if (rows == 0 || cols == 0)
         return FGB_OK;
-    int64_t grid = (nb + 3) / 4;
-    FGB_REQUIRE(grid < (1ll << 31), FGB_EINVAL, "fp8_direct_transpose_fmt: too many blocks");
-    direct_transpose_kernel<true, FMT_E5M2><<<(int)grid, 256, 0, (hipStream_t)stream>>>(q, s, rows, cols, qt, st, nb);
-    FGB_LAUNCHED("fp8_direct_transpose_fmt");
-    return FGB_OK;
+    return launch_direct_any<true, FMT_E5M2>(q, s, rows, cols, qt, st, 1, (hipStream_t)stream,
+                                             "fp8_direct_transpose_fmt");
 }
 
 extern "C" size_t fp8_naive_transpose_workspace_size(int64_t rows, int64_t cols)
@@ -346,13 +554,9 @@ extern "C" int fp8_block_transpose_batched(const uint8_t *q, const uint8_t *s, i
     FGB_REQUIRE(rows >= 0 && cols >= 0 && rows % 128 == 0 && cols % 128 == 0, FGB_EINVAL,
                 "fp8_block_transpose_batched: rows and cols must be multiples of 128");
     FGB_REQUIRE(aligned16(q) && aligned16(qt), FGB_EINVAL, "fp8_block_transpose_batched: q and qt must be 16-byte aligned");
-    const int64_t nb = (rows / 128) * (cols / 128);
-    if (nb == 0)
+    if (rows == 0 || cols == 0)
         return FGB_OK;
-    const dim3 grid((unsigned)((nb + 3) / 4), (unsigned)G);
-    direct_transpose_kernel<false><<<grid, 256, 0, (hipStream_t)stream>>>(q, s, rows, cols, qt, st, nb);
-    FGB_LAUNCHED("fp8_block_transpose_batched");
-    return FGB_OK;
+    return launch_direct_any<false>(q, s, rows, cols, qt, st, G, (hipStream_t)stream, "fp8_block_transpose_batched");
 }
 
 extern "C" int fp8_grouped_direct_transpose(const uint8_t *q, const uint8_t *s, int64_t M_cap, int64_t cols,
@@ -374,6 +578,7 @@ extern "C" int fp8_grouped_direct_transpose(const uint8_t *q, const uint8_t *s, 
     const int64_t nslots = (K_cap / 128) * (cols / 128);
     if (nslots == 0)
         return FGB_OK;
+    FGB_REQUIRE((nslots + 3) / 4 < (1ll << 31), FGB_EINVAL, "fp8_grouped_direct_transpose: too many blocks");
     grouped_direct_transpose_kernel<<<(unsigned)((nslots + 3) / 4), 256, 0, stm>>>(q, s, cols, group_offsets,
                                                                                    k_offsets, G, qt, st, K_cap, nslots);
     FGB_LAUNCHED("fp8_grouped_direct_transpose");

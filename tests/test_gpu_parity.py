@@ -190,7 +190,7 @@ def test_transpose_exhaustive_codes_and_shifts(fgb):
     assert np.array_equal(np_(st), ost)
 
 
-@pytest.mark.parametrize("T,C", [(128, 128), (256, 512), (384, 2048)])
+@pytest.mark.parametrize("T,C", [(128, 128), (256, 512), (384, 2048), (1280, 384), (2176, 256)])
 def test_transpose_random(fgb, T, C):
     say("transpose", T, C)
     q, s = synth.wgrad_codes(T, C, seed=T + C)
@@ -218,16 +218,17 @@ def test_naive_transpose(fgb, T, C):
     assert np.array_equal(np_(qt), oqt)
 
 
-def test_block_transpose_batched(fgb):
-    say("transpose: batched expert weight blocks [8, 512, 256]")
-    q = rand_codes((8, 512, 256), 15)
-    s = rand_scales((8, 4, 2), -30, 10, 16)
+@pytest.mark.parametrize("G,R,C", [(8, 512, 256), (3, 1664, 384)])
+def test_block_transpose_batched(fgb, G, R, C):
+    say(f"transpose: batched expert weight blocks [{G}, {R}, {C}]")
+    q = rand_codes((G, R, C), 15)
+    s = rand_scales((G, R // 128, C // 128), -30, 10, 16)
     qt, st = fgb.fp8_block_transpose_batched(q.to(DEV), s.to(DEV))
     oqt, ost = O.block_transpose_batched(q.numpy(), s.numpy())
     assert np.array_equal(np_(qt), oqt) and np.array_equal(np_(st), ost)
 
 
-@pytest.mark.parametrize("T,C", [(300, 256), (16384, 2048)])
+@pytest.mark.parametrize("T,C", [(300, 256), (2500, 384), (16384, 2048)])
 def test_grouped_direct_transpose(fgb, T, C):
     say("grouped direct transpose of expert segments", T, C)
     topk, G = 8, 32
