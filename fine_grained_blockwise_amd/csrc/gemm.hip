@@ -111,6 +111,72 @@ __device__ __forceinline__ void expert_rows(const GemmArgs &p, int g, int64_t &l
     }
 }
 
+// The m-tiles of the M-grouped layouts, found with one lane per expert: lane l
+// of each pass over 64 experts reads expert g0 + l's row range (one vector
+// load for all experts of the pass instead of one dependent load per expert),
+// counts its 256-row tiles and takes a wave prefix sum of the counts.
+// Measured on the MI355X: the per-expert loop this replaces took 12.6 us per
+// tile of the fc2 expert GEMM (21% of the tile), the dense GEMM's prologue 1.8.
+__device__ __forceinline__ int32_t wave_inclusive_sum(int32_t v)
+{
+    const int lane = (int)(threadIdx.x & 63);
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t u = __shfl_up(v, d);
+        if (lane >= d)
+            v += u;
+    }
+    return v;
+}
+
+// Rows and m-tile count of expert g0 + lane (0 past the last expert).
+__device__ __forceinline__ int32_t expert_tiles_lane(const GemmArgs &p, int g, int64_t &lo, int64_t &hi)
+{
+    lo = hi = 0;
+    if (g >= p.G)
+        return 0;
+    expert_rows(p, g, lo, hi);
+    return hi > lo ? (int32_t)((hi - lo + BM - 1) / BM) : 0;
+}
+
+// Total m-tiles over all experts (uniform over the wave).
+__device__ __forceinline__ int64_t count_mtiles(const GemmArgs &p)
+{
+    const int lane = (int)(threadIdx.x & 63);
+    int64_t total = 0;
+    for (int g0 = 0; g0 < p.G; g0 += 64) {
+        int64_t lo, hi;
+        const int32_t nt = expert_tiles_lane(p, g0 + lane, lo, hi);
+        total += __shfl(wave_inclusive_sum(nt), 63);
+    }
+    return total;
+}
+
+// The expert owning m-tile tm (in expert order, each expert's tiles
+// contiguous), its first row of the tile and its row end; e = -1 if none.
+__device__ __forceinline__ void find_mtile(const GemmArgs &p, int64_t tm, int &e, int64_t &m0, int64_t &m_end)
+{
+    const int lane = (int)(threadIdx.x & 63);
+    int64_t base = 0;
+    e = -1;
+    for (int g0 = 0; g0 < p.G; g0 += 64) {
+        int64_t lo, hi;
+        const int32_t nt = expert_tiles_lane(p, g0 + lane, lo, hi);
+        const int32_t incl = wave_inclusive_sum(nt);
+        const int64_t first = base + incl - nt;
+        const uint64_t hit = __ballot(nt > 0 && tm >= first && tm < first + nt);
+        if (hit) { // uniform
+            const int l = __builtin_ctzll(hit);
+            e = g0 + l;
+            const int64_t lo_e = __shfl(lo, l), hi_e = __shfl(hi, l), first_e = __shfl(first, l);
+            m0 = lo_e + (tm - first_e) * BM;
+            m_end = hi_e;
+            return;
+        }
+        base += __shfl(incl, 63);
+    }
+}
+
 // Contiguous tile ranges per XCD: workgroup b runs on XCD b % 8.
 __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t nb)
 {
@@ -216,12 +282,7 @@ gemm_fp8_kernel(GemmArgs p)
         // The grid is a host-side bound; the m-tiles that exist are counted
         // from the expert row ranges and the surplus workgroups exit, so the
         // XCD mapping spreads only real tiles.
-        int64_t mt = 0;
-        for (int g = 0; g < p.G; g++) {
-            int64_t lo, hi;
-            expert_rows(p, g, lo, hi);
-            mt += hi > lo ? (hi - lo + BM - 1) / BM : 0;
-        }
+        const int64_t mt = count_mtiles(p);
         tiles_here = min(mt, (int64_t)gridDim.x / p.tiles_n) * p.tiles_n;
         if ((int64_t)blockIdx.x >= tiles_here)
             return; // uniform per workgroup
@@ -248,19 +309,8 @@ gemm_fp8_kernel(GemmArgs p)
         m0 = tm * BM;
         m_end = p.M;
     } else {
-        int e = -1;
-        int64_t base = 0;
-        for (int g = 0; g < p.G; g++) {
-            int64_t lo, hi;
-            expert_rows(p, g, lo, hi);
-            const int64_t nt = hi > lo ? (hi - lo + BM - 1) / BM : 0;
-            if (tm >= base && tm < base + nt) {
-                e = g;
-                m0 = lo + (tm - base) * BM;
-                m_end = hi;
-            }
-            base += nt;
-        }
+        int e;
+        find_mtile(p, tm, e, m0, m_end);
         if (e < 0)
             return; // not reached: tm < the counted m-tiles (uniform per workgroup)
         B += (int64_t)e * p.b_stride;
