@@ -66,6 +66,10 @@ constexpr int EPI_CAP = 8 * 64 * (64 * 2 + 16);       // largest staging (8 wave
 constexpr int LDS_BYTES = EPI_OFF + EPI_CAP;          // 140 KB
 static_assert(LDS_BYTES >= RING_OFF + NBUF * BUF_BYTES, "the ring fits");
 
+// Word 3 of a raw buffer descriptor on gfx9-family GPUs: 32-bit data format,
+// no swizzle, no index stride (range checks on the byte offset).
+constexpr int BUF_DWORD3 = 0x00020000;
+
 enum { MODE_EXACT = 0, MODE_FAST = 1 };
 enum { AG_ROW128 = 0, AG_ROW32 = 1 };
 // dense, M-grouped (experts' rows: contiguous segments, or the masked layout), K-grouped (experts' K ranges)
@@ -115,8 +119,8 @@ __device__ __forceinline__ void expert_rows(const GemmArgs &p, int g, int64_t &l
 // of each pass over 64 experts reads expert g0 + l's row range (one vector
 // load for all experts of the pass instead of one dependent load per expert),
 // counts its 256-row tiles and takes a wave prefix sum of the counts.
-// Measured on the MI355X: the per-expert loop this replaces took 12.6 us per
-// tile of the fc2 expert GEMM (21% of the tile), the dense GEMM's prologue 1.8.
+// Measured on the MI355X over 32 experts: 2-5% off each expert GEMM against a
+// loop with one dependent load per expert.
 __device__ __forceinline__ int32_t wave_inclusive_sum(int32_t v)
 {
     const int lane = (int)(threadIdx.x & 63);
@@ -908,14 +912,23 @@ gemm_fp8_kernel(GemmArgs p)
 
     // ---- epilogue --------------------------------------------------------------
     // 32x32 accumulator layout: lane l, register r -> row (r/4)*8 + (l/32)*4 + r%4,
-    // column l%32.  The tile is staged through LDS (free after the barrier
-    // below; from buffer 1 on) so that global stores are 16 bytes per lane along rows: each
-    // wave writes its 128 x WNC block, EPI_ROWS rows at a time, and reads it back
-    // row-contiguous.  FP32 out stages [row][WNC + pad] floats.  BF16 out stages
-    // row pairs: a lane's registers 4q..4q+3 are rows 2p..2p+3 of one column, so
-    // one conversion packs rows (2p, 2p+1) into a dword at [pair][column]; the
-    // read-back takes 32 bytes of one pair (8 columns) and splits them into the
-    // two rows' 16 bytes, with no exchange between lanes.
+    // column l%32.
+    // FP32 out, the wave's 128 x WNC block inside D: every register goes
+    //   straight to memory; one store writes 32 consecutive columns (128 bytes)
+    //   of two rows.
+    // Otherwise the block is staged through LDS (free after the barrier below;
+    //   from buffer 1 on) so that global stores are 16 bytes per lane along
+    //   rows: each wave writes its 128 x WNC block, EPI_ROWS rows at a time, and
+    //   reads it back row-contiguous.  FP32 out stages [row][WNC + pad] floats.
+    //   BF16 out stages row pairs: a lane's registers 4q..4q+3 are rows
+    //   2p..2p+3 of one column, so one conversion packs rows (2p, 2p+1) into a
+    //   dword at [pair][column]; the read-back takes 32 bytes of one pair (8
+    //   columns) and splits them into the two rows' 16 bytes with byte
+    //   permutes, with no exchange between lanes.
+    // The instruction count sets this phase's time (measured: the stores
+    // drain within 0.2-0.4 us), so the common case carries no per-row bound
+    // tests (a wave whose rows and columns all lie inside D, 16-byte aligned)
+    // and no level-1 multiply (no level-1 factors).
     __syncthreads();
     constexpr int ESZ = OUT_BF16 ? 2 : 4;
     constexpr int ROWB = WNC * ESZ + 16; // padded LDS row (bytes)
@@ -924,119 +937,180 @@ gemm_fp8_kernel(GemmArgs p)
     static_assert(NW * EPI_ROWS * ROWB <= EPI_CAP, "the staging fits");
     static_assert(!OUT_BF16 || (EPI_ROWS / 2) * RPB <= EPI_ROWS * ROWB, "the row-pair staging fits the wave's share");
     uint8_t *ep = smem + EPI_OFF + wave * (EPI_ROWS * ROWB);
-    // level-1 factor of each column (MOSS); 1.0 without them, which leaves
-    // every value as it is
+    // level-1 factor of each column (MOSS)
+    const bool has_l1 = p.l1 != nullptr; // uniform
     float l1v[TJ];
 #pragma unroll
     for (int j = 0; j < TJ; j++) {
         const int64_t col = n0 + wn * WNC + j * 32 + l32;
-        l1v[j] = (p.l1 && col < N) ? p.l1[col] : 1.0f;
+        l1v[j] = (has_l1 && col < N) ? p.l1[col] : 1.0f;
     }
     // read-back geometry: one row segment of 16 bytes per lane
     constexpr int LPR = WNC * ESZ / 16; // lanes per row
     constexpr int RPI = 64 / LPR;       // rows per instruction
     const int lr = lane / LPR, lc = lane % LPR;
-    const int64_t col0 = n0 + wn * WNC + lc * (16 / ESZ);
+    const int64_t colw = n0 + wn * WNC; // the wave's first column
+    const int64_t col0 = colw + lc * (16 / ESZ);
     const int64_t row_w = m0 + wm * 128; // the wave's first row
     const int64_t ld_bytes = p.ldd * ESZ;
-    uint8_t *const dwave = (uint8_t *)p.d + (ke * p.d_stride + row_w * p.ldd + col0) * ESZ;
+    uint8_t *const dblock = (uint8_t *)p.d + (ke * p.d_stride + row_w * p.ldd + colw) * ESZ;
+    uint8_t *const dwave = dblock + (col0 - colw) * ESZ;
     // rows of the wave below m_end (0..128) and whether this lane's 16 bytes are a whole aligned segment
     const int rows_ok = (int)min((int64_t)128, max((int64_t)0, m_end - row_w));
     const bool col_ok = col0 < N;
     const bool full = col0 + 16 / ESZ <= N && (((uintptr_t)dwave & 15) == 0) && ((ld_bytes & 15) == 0);
+    // the whole block inside D with aligned rows (uniform over the wave)
+    const bool block_in = rows_ok == 128 && colw + WNC <= N;
+    const bool block_full = block_in && ((((uintptr_t)dblock) | (uintptr_t)ld_bytes) & 15) == 0;
+
+    // level-1 factors applied in place (uniform branch; the stores below read the accumulators)
+    if (has_l1) {
 #pragma unroll
-    for (int part = 0; part < 128 / EPI_ROWS; part++) {
+        for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int ii = 0; ii < EPI_ROWS / 32; ii++) {
-            const int i = part * (EPI_ROWS / 32) + ii;
+            for (int j = 0; j < TJ; j++)
 #pragma unroll
-            for (int j = 0; j < TJ; j++) {
-                if constexpr (OUT_BF16) {
+                for (int r = 0; r < 16; r++)
+                    acc[i][j][r] *= l1v[j];
+    }
+    bool direct = false; // FP32 out stored straight from the registers
+    if constexpr (!OUT_BF16) {
+        if (block_in && 128 * ld_bytes < ((int64_t)1 << 31)) {
+            direct = true;
+            // One batch per row tile: its 16 x TJ values (accumulating, their
+            // loads go first, so that a batch's loads are in flight
+            // together).  Raw buffer accesses on a descriptor of the wave's
+            // block, at byte offset row * ld + the lane's column (4 rows down
+            // for the upper half-wave), every offset below 2^31 (checked
+            // above).
+            const __amdgpu_buffer_rsrc_t rs =
+                __builtin_amdgcn_make_buffer_rsrc((void *)uniform(dblock), 0, 0x7FFFFFFF, BUF_DWORD3);
+            const int lane_off = (int)(hk * 4 * ld_bytes) + l32 * 4;
 #pragma unroll
-                    for (int q = 0; q < 4; q++) {
-                        // Rows ii*32 + q*8 + hk*4 + 0..3 of column j*32 + l32, as
-                        // two row pairs: one dword per pair (low half the even row).
-                        float v[4];
+            for (int i = 0; i < 4; i++) {
+                if (p.accumulate) {
+                    float o[16][TJ];
 #pragma unroll
-                        for (int t = 0; t < 4; t++) {
-                            v[t] = acc[i][j][4 * q + t] * l1v[j];
+                    for (int r = 0; r < 16; r++)
+#pragma unroll
+                        for (int j = 0; j < TJ; j++)
+                            o[r][j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                rs, lane_off + (int)((i * 32 + (r / 4) * 8 + (r % 4)) * ld_bytes) + j * 128, 0, 0));
+#pragma unroll
+                    for (int r = 0; r < 16; r++)
+#pragma unroll
+                        for (int j = 0; j < TJ; j++)
+                            acc[i][j][r] += o[r][j];
+                }
+#pragma unroll
+                for (int r = 0; r < 16; r++)
+#pragma unroll
+                    for (int j = 0; j < TJ; j++)
+                        __builtin_amdgcn_raw_buffer_store_b32(
+                            __float_as_uint(acc[i][j][r]), rs,
+                            lane_off + (int)((i * 32 + (r / 4) * 8 + (r % 4)) * ld_bytes) + j * 128, 0, 0);
+            }
+        }
+    }
+    if (!direct) {
+#pragma unroll
+        for (int part = 0; part < 128 / EPI_ROWS; part++) {
+#pragma unroll
+            for (int ii = 0; ii < EPI_ROWS / 32; ii++) {
+                const int i = part * (EPI_ROWS / 32) + ii;
+#pragma unroll
+                for (int j = 0; j < TJ; j++) {
+                    if constexpr (OUT_BF16) {
+#pragma unroll
+                        for (int q = 0; q < 4; q++) {
+                            // Rows ii*32 + q*8 + hk*4 + 0..3 of column j*32 + l32, as
+                            // two row pairs: one dword per pair (low half the even row).
+                            float v[4];
+#pragma unroll
+                            for (int t = 0; t < 4; t++)
+                                v[t] = acc[i][j][4 * q + t];
+                            const int rp = ii * 16 + q * 4 + hk * 2;
+                            const int col = j * 32 + l32;
+                            *reinterpret_cast<uint32_t *>(ep + rp * RPB + col * 4) = pack_bf16x2(v[0], v[1]);
+                            *reinterpret_cast<uint32_t *>(ep + (rp + 1) * RPB + col * 4) = pack_bf16x2(v[2], v[3]);
                         }
-                        const int rp = ii * 16 + q * 4 + hk * 2;
-                        const int col = j * 32 + l32;
-                        *reinterpret_cast<uint32_t *>(ep + rp * RPB + col * 4) = pack_bf16x2(v[0], v[1]);
-                        *reinterpret_cast<uint32_t *>(ep + (rp + 1) * RPB + col * 4) = pack_bf16x2(v[2], v[3]);
-                    }
-                } else {
-                    // FP32 out: one 4-byte write per value (8-byte pairs measured slower)
+                    } else {
+                        // FP32 out: one 4-byte write per value (8-byte pairs measured slower)
 #pragma unroll
-                    for (int r = 0; r < 16; r++) {
-                        const int row = ii * 32 + (r / 4) * 8 + hk * 4 + (r % 4);
-                        const int col = j * 32 + l32;
-                        const float v = acc[i][j][r] * l1v[j];
-                        *reinterpret_cast<float *>(ep + row * ROWB + col * 4) = v;
+                        for (int r = 0; r < 16; r++) {
+                            const int row = ii * 32 + (r / 4) * 8 + hk * 4 + (r % 4);
+                            const int col = j * 32 + l32;
+                            const float v = acc[i][j][r];
+                            *reinterpret_cast<float *>(ep + row * ROWB + col * 4) = v;
+                        }
                     }
                 }
             }
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0): this wave's LDS writes done
-        __builtin_amdgcn_wave_barrier();
-        if constexpr (OUT_BF16) {
-            // a lane takes 8 columns of one row pair: 32 bytes of pairs -> 16 bytes of each row
+            __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0): this wave's LDS writes done
+            __builtin_amdgcn_wave_barrier();
+            if constexpr (OUT_BF16) {
+                // a lane takes 8 columns of one row pair: 32 bytes of pairs -> 16 bytes of each row
 #pragma unroll
-            for (int rr = 0; rr < EPI_ROWS / 2; rr += RPI) {
-                const int rp = rr + lr;
-                const uint4 x = *reinterpret_cast<const uint4 *>(ep + rp * RPB + lc * 32);
-                const uint4 y = *reinterpret_cast<const uint4 *>(ep + rp * RPB + lc * 32 + 16);
-                const uint32_t w[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
-                uint4 ev, od;
-                uint32_t *e4 = &ev.x, *o4 = &od.x;
+                for (int rr = 0; rr < EPI_ROWS / 2; rr += RPI) {
+                    const int rp = rr + lr;
+                    const uint4 x = *reinterpret_cast<const uint4 *>(ep + rp * RPB + lc * 32);
+                    const uint4 y = *reinterpret_cast<const uint4 *>(ep + rp * RPB + lc * 32 + 16);
+                    const uint32_t w[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+                    uint4 ev, od;
+                    uint32_t *e4 = &ev.x, *o4 = &od.x;
 #pragma unroll
-                for (int k = 0; k < 4; k++) {
-                    e4[k] = (w[2 * k] & 0xFFFFu) | (w[2 * k + 1] << 16);
-                    o4[k] = (w[2 * k] >> 16) | (w[2 * k + 1] & 0xFFFF0000u);
+                    for (int k = 0; k < 4; k++) {
+                        // low halves (the even row) and high halves (the odd row) of two pair words
+                        e4[k] = __builtin_amdgcn_perm(w[2 * k + 1], w[2 * k], 0x05040100u);
+                        o4[k] = __builtin_amdgcn_perm(w[2 * k + 1], w[2 * k], 0x07060302u);
+                    }
+#pragma unroll
+                    for (int s = 0; s < 2; s++) {
+                        const int row_l = part * EPI_ROWS + 2 * rp + s; // row within the wave's 128
+                        const uint4 v = s ? od : ev;
+                        uint8_t *dst = dwave + row_l * ld_bytes;
+                        if (block_full) {
+                            *reinterpret_cast<uint4 *>(dst) = v;
+                            continue;
+                        }
+                        if (row_l >= rows_ok || !col_ok)
+                            continue;
+                        if (full) {
+                            *reinterpret_cast<uint4 *>(dst) = v;
+                        } else {
+                            uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+                            for (int e = 0; e < 8 && col0 + e < N; e++)
+                                reinterpret_cast<uint16_t *>(dst)[e] = (uint16_t)(w4[e / 2] >> (16 * (e & 1)));
+                        }
+                    }
                 }
+            } else {
 #pragma unroll
-                for (int s = 0; s < 2; s++) {
-                    const int row_l = part * EPI_ROWS + 2 * rp + s; // row within the wave's 128
+                for (int rr = 0; rr < EPI_ROWS; rr += RPI) {
+                    const int row_l = part * EPI_ROWS + rr + lr; // row within the wave's 128
+                    uint4 v = *reinterpret_cast<const uint4 *>(ep + (rr + lr) * ROWB + lc * 16);
                     if (row_l >= rows_ok || !col_ok)
                         continue;
-                    const uint4 v = s ? od : ev;
                     uint8_t *dst = dwave + row_l * ld_bytes;
-                    if (full) {
-                        *reinterpret_cast<uint4 *>(dst) = v;
-                    } else {
-                        uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-                        for (int e = 0; e < 8 && col0 + e < N; e++)
-                            reinterpret_cast<uint16_t *>(dst)[e] = (uint16_t)(w4[e / 2] >> (16 * (e & 1)));
-                    }
-                }
-            }
-        } else {
-#pragma unroll
-            for (int rr = 0; rr < EPI_ROWS; rr += RPI) {
-                const int row_l = part * EPI_ROWS + rr + lr; // row within the wave's 128
-                uint4 v = *reinterpret_cast<const uint4 *>(ep + (rr + lr) * ROWB + lc * 16);
-                if (row_l >= rows_ok || !col_ok)
-                    continue;
-                uint8_t *dst = dwave + row_l * ld_bytes;
-                {
-                    float f4[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
-                    float *fd = reinterpret_cast<float *>(dst);
-                    if (full) {
-                        if (p.accumulate) {
-                            float4 o = *reinterpret_cast<const float4 *>(fd);
-                            f4[0] += o.x; f4[1] += o.y; f4[2] += o.z; f4[3] += o.w;
+                    {
+                        float f4[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+                        float *fd = reinterpret_cast<float *>(dst);
+                        if (full) {
+                            if (p.accumulate) {
+                                float4 o = *reinterpret_cast<const float4 *>(fd);
+                                f4[0] += o.x; f4[1] += o.y; f4[2] += o.z; f4[3] += o.w;
+                            }
+                            *reinterpret_cast<float4 *>(fd) = make_float4(f4[0], f4[1], f4[2], f4[3]);
+                        } else {
+                            for (int e = 0; e < 4 && col0 + e < N; e++)
+                                fd[e] = p.accumulate ? fd[e] + f4[e] : f4[e];
                         }
-                        *reinterpret_cast<float4 *>(fd) = make_float4(f4[0], f4[1], f4[2], f4[3]);
-                    } else {
-                        for (int e = 0; e < 4 && col0 + e < N; e++)
-                            fd[e] = p.accumulate ? fd[e] + f4[e] : f4[e];
                     }
                 }
             }
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
         }
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
     }
 }
 
