@@ -441,6 +441,8 @@ def fp8_block_gemm(a, sa, a_gran, b, sb, b_gran, b_l1=None, g1=0, out_dtype=torc
     _need(sb, "fp8_block_gemm: sb", shape=_scale_shape(N, K, b_gran), dtype=torch.uint8)
     if b_l1 is not None:
         _need(b_l1, "fp8_block_gemm: b_l1", shape=(N,), dtype=torch.float32, contiguous=True)
+        if b_gran != ROW1x32:
+            raise ValueError("fp8_block_gemm: b_l1 needs 1x32 B scales (b_gran ROW1x32)")
     d = _gemm_out(d, M, N, out_dtype, "fp8_block_gemm")
     _check_dev(a, sa, b, sb, b_l1, d)
     if d is None:

@@ -46,6 +46,8 @@
 //          supplies chunks 4hs+h and 4hs+2+h.
 //   EXACT: 16-deep sub-step s uses bytes 0-7 (s even) or 8-15 (s odd) of
 //          chunk 2(s/2)+h, converted to 8 bf16 values.
+#include <type_traits>
+
 #include "fgb_internal.h"
 
 namespace fgb {
@@ -835,37 +837,36 @@ gemm_fp8_kernel(GemmArgs p)
                     sfB[t] = scale_f32(B32 ? (cb[t] >> (8 * q)) & 0xFFu
                                            : (BG == BG_BLOCK ? cb[0] : (cb[0] >> (8 * t)) & 0xFFu));
         };
-        auto convert = [&](int sub, const uint4(&xa)[4], const uint4(&xb)[TJ]) {
+        // Masked layout (decode: experts with few valid rows): the wave's
+        // 32-row tiles past the expert's valid rows take neither conversions
+        // nor MFMAs, and a wave with no valid row (NV = 0) only makes its
+        // copies and meets every barrier.  The main loop is specialised on the
+        // wave's count NV of valid row tiles (uniform over the wave, read into
+        // a scalar register): tested inside the loop, the conditional MFMAs
+        // made the compiler copy and spill the accumulators.
+        auto main_loop = [&](auto nv_tag) {
+            constexpr int NV = decltype(nv_tag)::value;
+            auto convert = [&](int sub, const uint4(&xa)[4], const uint4(&xb)[TJ]) {
 #pragma unroll
-            for (int t = 0; t < 4; t++)
-                if constexpr (AF == FMT_E5M2)
-                    cA[t] = sub == 0 ? cvt8_bf16_e5m2(xa[t].x, xa[t].y, sfA[t]) : cvt8_bf16_e5m2(xa[t].z, xa[t].w, sfA[t]);
-                else
-                    cA[t] = sub == 0 ? cvt8_bf16(xa[t].x, xa[t].y, sfA[t]) : cvt8_bf16(xa[t].z, xa[t].w, sfA[t]);
+                for (int t = 0; t < NV; t++)
+                    if constexpr (AF == FMT_E5M2)
+                        cA[t] = sub == 0 ? cvt8_bf16_e5m2(xa[t].x, xa[t].y, sfA[t]) : cvt8_bf16_e5m2(xa[t].z, xa[t].w, sfA[t]);
+                    else
+                        cA[t] = sub == 0 ? cvt8_bf16(xa[t].x, xa[t].y, sfA[t]) : cvt8_bf16(xa[t].z, xa[t].w, sfA[t]);
 #pragma unroll
-            for (int t = 0; t < TJ; t++)
-                cB[t] = sub == 0 ? cvt8_bf16(xb[t].x, xb[t].y, sfB[t]) : cvt8_bf16(xb[t].z, xb[t].w, sfB[t]);
-        };
-        // Masked layout (decode: experts with few valid rows): the wave's 32-row
-        // tiles past the expert's valid rows take no MFMAs, and a wave with no
-        // valid row skips its conversions too (rows_here below); it still makes
-        // its copies and meets every barrier.  Both conditions are uniform over
-        // the wave.  Only this form takes the branches: where full tiles
-        // dominate they cost ~5%.
-        const int nv = GK != GK_MM ? 4
-                                   : (int)min((int64_t)4, max((int64_t)0, (m_end - m0 - (int64_t)(wave_u / (NW / 2)) * 128 + 31) / 32));
-        auto mfmas = [&]() {
+                for (int t = 0; t < TJ; t++)
+                    cB[t] = sub == 0 ? cvt8_bf16(xb[t].x, xb[t].y, sfB[t]) : cvt8_bf16(xb[t].z, xb[t].w, sfB[t]);
+            };
+            auto mfmas = [&]() {
 #pragma unroll
-            for (int i = 0; i < 4; i++)
-                if (GK != GK_MM || i == 0 || i < nv)
+                for (int i = 0; i < NV; i++)
 #pragma unroll
-                for (int j = 0; j < TJ; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cA[i], cB[j], acc[i][j], 0, 0, 0);
-        };
-        const bool rows_here = GK != GK_MM || m0 + (int64_t)(wave_u / (NW / 2)) * 128 < m_end;
+                    for (int j = 0; j < TJ; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cA[i], cB[j], acc[i][j], 0, 0, 0);
+            };
 #define FGB_SLOT(SUB, RX, DMA)                                                                                         \
     do {                                                                                                               \
-        if (rows_here) {                                                                                               \
+        if constexpr (NV > 0) {                                                                                        \
             convert(SUB, rA[RX], rB[RX]);                                                                              \
             mfmas();                                                                                                   \
         }                                                                                                              \
@@ -874,35 +875,49 @@ gemm_fp8_kernel(GemmArgs p)
         __builtin_amdgcn_sched_barrier(0);                                                                             \
     } while (0)
 
-        read_pair(0, 0, rA[0], rB[0]);
-        factors(0);
-        for (int ks = 0; ks < nk32; ks++) {
-            // slots 0-1: read pair 1; sub-steps 0, 1 (pair 0)
-            read_pair(ks, 1, rA[1], rB[1]);
-            FGB_SLOT(0, 0, (dma_tile(ks + 1, 3), dma_tile(ks + 1, 4)));
-            FGB_SLOT(1, 0, (dma_tile(ks + 1, 5), dma_tile(ks + 1, 6)));
-            // slots 2-3: read pair 2; sub-steps 2, 3 (pair 1)
-            read_pair(ks, 2, rA[0], rB[0]);
-            factors(1);
-            FGB_SLOT(0, 1, dma_tile(ks + 1, 7));
-            FGB_SLOT(1, 1, (void)0);
-            // slots 4-5: read pair 3; sub-steps 4, 5 (pair 2)
-            read_pair(ks, 3, rA[1], rB[1]);
-            factors(2);
-            FGB_SLOT(0, 0, (void)0);
-            FGB_SLOT(1, 0, (void)0);
-            // slots 6-7: step ks+1 has landed (nothing issued after it) and
-            // buffer ks % 2 is free; the next step's scales and pair 0; sub-steps
-            // 6, 7 (pair 3).  After the last step these reads touch only LDS
-            // and are discarded.
-            FGB_WAIT_SYNC(0);
-            read_scales(ks + 1, sva, svb);
-            read_pair(ks + 1, 0, rA[0], rB[0]);
-            factors(3);
-            FGB_SLOT(0, 1, (dma_step(ks + 2, 0, 0)));
-            FGB_SLOT(1, 1, (dma_tile(ks + 2, 1), dma_tile(ks + 2, 2)));
-            pack_scales(sva, svb, ca, cb);
+            read_pair(0, 0, rA[0], rB[0]);
             factors(0);
+            for (int ks = 0; ks < nk32; ks++) {
+                // slots 0-1: read pair 1; sub-steps 0, 1 (pair 0)
+                read_pair(ks, 1, rA[1], rB[1]);
+                FGB_SLOT(0, 0, (dma_tile(ks + 1, 3), dma_tile(ks + 1, 4)));
+                FGB_SLOT(1, 0, (dma_tile(ks + 1, 5), dma_tile(ks + 1, 6)));
+                // slots 2-3: read pair 2; sub-steps 2, 3 (pair 1)
+                read_pair(ks, 2, rA[0], rB[0]);
+                factors(1);
+                FGB_SLOT(0, 1, dma_tile(ks + 1, 7));
+                FGB_SLOT(1, 1, (void)0);
+                // slots 4-5: read pair 3; sub-steps 4, 5 (pair 2)
+                read_pair(ks, 3, rA[1], rB[1]);
+                factors(2);
+                FGB_SLOT(0, 0, (void)0);
+                FGB_SLOT(1, 0, (void)0);
+                // slots 6-7: step ks+1 has landed (nothing issued after it) and
+                // buffer ks % 2 is free; the next step's scales and pair 0; sub-steps
+                // 6, 7 (pair 3).  After the last step these reads touch only LDS
+                // and are discarded.
+                FGB_WAIT_SYNC(0);
+                read_scales(ks + 1, sva, svb);
+                read_pair(ks + 1, 0, rA[0], rB[0]);
+                factors(3);
+                FGB_SLOT(0, 1, (dma_step(ks + 2, 0, 0)));
+                FGB_SLOT(1, 1, (dma_tile(ks + 2, 1), dma_tile(ks + 2, 2)));
+                pack_scales(sva, svb, ca, cb);
+                factors(0);
+            }
+        };
+        if constexpr (GK != GK_MM) {
+            main_loop(std::integral_constant<int, 4>{});
+        } else {
+            const int nv = __builtin_amdgcn_readfirstlane(
+                (int)min((int64_t)4, max((int64_t)0, (m_end - m0 - (int64_t)(wave_u / (NW / 2)) * 128 + 31) / 32)));
+            switch (nv) {
+            case 0: main_loop(std::integral_constant<int, 0>{}); break;
+            case 1: main_loop(std::integral_constant<int, 1>{}); break;
+            case 2: main_loop(std::integral_constant<int, 2>{}); break;
+            case 3: main_loop(std::integral_constant<int, 3>{}); break;
+            default: main_loop(std::integral_constant<int, 4>{}); break;
+            }
         }
 #undef FGB_SLOT
     }
@@ -963,21 +978,15 @@ gemm_fp8_kernel(GemmArgs p)
     const bool block_in = rows_ok == 128 && colw + WNC <= N;
     const bool block_full = block_in && ((((uintptr_t)dblock) | (uintptr_t)ld_bytes) & 15) == 0;
 
-    // level-1 factors applied in place (uniform branch; the stores below read the accumulators)
-    if (has_l1) {
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-            for (int j = 0; j < TJ; j++)
-#pragma unroll
-                for (int r = 0; r < 16; r++)
-                    acc[i][j][r] *= l1v[j];
-    }
+    // Level-1 factors come only with 1x32 B scales (MOSS); other kernels
+    // store the accumulators as they are.  Without factors l1v is 1.0, which
+    // leaves every value unchanged.
+    constexpr bool L1 = BG == BG_ROW32;
     bool direct = false; // FP32 out stored straight from the registers
     if constexpr (!OUT_BF16) {
         if (block_in && 128 * ld_bytes < ((int64_t)1 << 31)) {
             direct = true;
-            // One batch per row tile: its 16 x TJ values (accumulating, their
+            // One batch per 32 x 32 tile: its 16 values (accumulating, their
             // loads go first, so that a batch's loads are in flight
             // together).  Raw buffer accesses on a descriptor of the wave's
             // block, at byte offset row * ld + the lane's column (4 rows down
@@ -987,29 +996,29 @@ gemm_fp8_kernel(GemmArgs p)
                 __builtin_amdgcn_make_buffer_rsrc((void *)uniform(dblock), 0, 0x7FFFFFFF, BUF_DWORD3);
             const int lane_off = (int)(hk * 4 * ld_bytes) + l32 * 4;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                if (p.accumulate) {
-                    float o[16][TJ];
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < TJ; j++) {
+                    float v[16];
 #pragma unroll
                     for (int r = 0; r < 16; r++)
+                        v[r] = L1 ? acc[i][j][r] * l1v[j] : acc[i][j][r];
+                    if (p.accumulate) {
+                        float o[16];
 #pragma unroll
-                        for (int j = 0; j < TJ; j++)
-                            o[r][j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                        for (int r = 0; r < 16; r++)
+                            o[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
                                 rs, lane_off + (int)((i * 32 + (r / 4) * 8 + (r % 4)) * ld_bytes) + j * 128, 0, 0));
 #pragma unroll
+                        for (int r = 0; r < 16; r++)
+                            v[r] += o[r];
+                    }
+#pragma unroll
                     for (int r = 0; r < 16; r++)
-#pragma unroll
-                        for (int j = 0; j < TJ; j++)
-                            acc[i][j][r] += o[r][j];
-                }
-#pragma unroll
-                for (int r = 0; r < 16; r++)
-#pragma unroll
-                    for (int j = 0; j < TJ; j++)
                         __builtin_amdgcn_raw_buffer_store_b32(
-                            __float_as_uint(acc[i][j][r]), rs,
-                            lane_off + (int)((i * 32 + (r / 4) * 8 + (r % 4)) * ld_bytes) + j * 128, 0, 0);
-            }
+                            __float_as_uint(v[r]), rs, lane_off + (int)((i * 32 + (r / 4) * 8 + (r % 4)) * ld_bytes) + j * 128,
+                            0, 0);
+                }
         }
     }
     if (!direct) {
@@ -1028,7 +1037,7 @@ gemm_fp8_kernel(GemmArgs p)
                             float v[4];
 #pragma unroll
                             for (int t = 0; t < 4; t++)
-                                v[t] = acc[i][j][4 * q + t];
+                                v[t] = L1 ? acc[i][j][4 * q + t] * l1v[j] : acc[i][j][4 * q + t];
                             const int rp = ii * 16 + q * 4 + hk * 2;
                             const int col = j * 32 + l32;
                             *reinterpret_cast<uint32_t *>(ep + rp * RPB + col * 4) = pack_bf16x2(v[0], v[1]);
@@ -1040,7 +1049,7 @@ gemm_fp8_kernel(GemmArgs p)
                         for (int r = 0; r < 16; r++) {
                             const int row = ii * 32 + (r / 4) * 8 + hk * 4 + (r % 4);
                             const int col = j * 32 + l32;
-                            const float v = acc[i][j][r];
+                            const float v = L1 ? acc[i][j][r] * l1v[j] : acc[i][j][r];
                             *reinterpret_cast<float *>(ep + row * ROWB + col * 4) = v;
                         }
                     }
@@ -1229,6 +1238,8 @@ extern "C" int fp8_block_gemm_fmt(const uint8_t *a, const uint8_t *sa, int a_gra
         return set_error(FGB_EUNSUPPORTED, "fp8_block_gemm: unknown b_gran");
     FGB_REQUIRE((ag == AG_ROW32) == (bg == BG_ROW32), FGB_EUNSUPPORTED,
                 "fp8_block_gemm: FGB_ROW1x32 scales must be used on both operands");
+    FGB_REQUIRE(!b_l1 || b_gran == FGB_ROW1x32, FGB_EUNSUPPORTED,
+                "fp8_block_gemm: b_l1 needs 1x32 B scales (the level-2 scales of the two-level format)");
     FGB_REQUIRE(!b_l1 || (g1 > 0 && K <= g1), FGB_EUNSUPPORTED,
                 "fp8_block_gemm: b_l1 needs K <= g1 (one level-1 group along K)");
     if (ag == AG_ROW32)

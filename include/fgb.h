@@ -253,7 +253,8 @@ size_t fp8_naive_transpose_workspace_size(int64_t rows, int64_t cols);
  *                   paired with ROW1x32; 1x32 scale tensors 4-byte aligned.
  *   b_l1, g1      : optional [MOSS] §3 level-1 FP32 factor per column of D,
  *                   b_l1 [N] (dense), applied to the FP32 result; requires
- *                   K <= g1 (one level-1 group along K); NULL = none.
+ *                   b_gran = FGB_ROW1x32 (the level-2 scales it goes with)
+ *                   and K <= g1 (one level-1 group along K); NULL = none.
  *   d, d_dtype    : D [M, N], ld ldd, FGB_F32 or FGB_BF16 (round to nearest
  *                   even).  accumulate != 0 (FP32 only): D += A * B^T.
  *   mode          : FGB_GEMM_EXACT -- each code times its scale 2^(byte-127)

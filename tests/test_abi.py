@@ -73,7 +73,8 @@ def test_gemm_validation():
     assert call(ag=2) == 2          # BLOCK128 A scales are not a mode
     assert call(ag=1, bg=2) == 2    # 1x32 must pair with 1x32
     assert call(acc=1, dt=1) == 2   # accumulate needs FP32 output
-    assert call(l1=f, g1=256) == 2  # level-1 factor needs K <= g1
+    assert call(l1=f, g1=256, ag=1, bg=1) == 2  # level-1 factor needs K <= g1
+    assert call(l1=f, g1=1024) == 2  # level-1 factor needs 1x32 B scales
     assert call(a=None) == 1
     assert call(mode=2) == 2
     assert call(ag=1, bg=1, sa=_fake(0x1001)) == 1  # 1x32 scales need 4-byte alignment

@@ -38,6 +38,8 @@ def test_block_gemm_scale_shapes_and_output():
            "output dtype")
     raises(lambda: fgb.fp8_block_gemm(a, sa, fgb.ROW1x128, b, sb, fgb.BLOCK128, b_l1=z(N - 1, dtype=torch.float32)),
            "b_l1 must have shape")
+    raises(lambda: fgb.fp8_block_gemm(a, sa, fgb.ROW1x128, b, sb, fgb.BLOCK128, b_l1=z(N, dtype=torch.float32)),
+           "1x32 B scales")
     # well-formed CPU tensors get as far as the device check
     raises(lambda: fgb.fp8_block_gemm(a, sa, fgb.ROW1x128, b, sb, fgb.BLOCK128), "on the GPU")
 
