@@ -254,7 +254,8 @@ __device__ __forceinline__ v16f mfma_scaled(v8i a, v8i b, v16f c, uint32_t sa, u
 }
 
 // AF: element format of A's codes (FMT_E4M3, or FMT_E5M2 for gradients).
-template <int MODE, int AG, int BG, bool OUT_BF16, int GK, int AF = FMT_E4M3>
+// ACC: FP32 out, D += the product (dense and K-grouped forms only).
+template <int MODE, int AG, int BG, bool OUT_BF16, int GK, int AF = FMT_E4M3, bool ACC = false>
 __global__ __launch_bounds__((Waves<MODE, GK>::NW * 64)) __attribute__((amdgpu_waves_per_eu(Waves<MODE, GK>::NW / 4, Waves<MODE, GK>::NW / 4))) void
 gemm_fp8_kernel(GemmArgs p)
 {
@@ -928,22 +929,20 @@ gemm_fp8_kernel(GemmArgs p)
     // ---- epilogue --------------------------------------------------------------
     // 32x32 accumulator layout: lane l, register r -> row (r/4)*8 + (l/32)*4 + r%4,
     // column l%32.
-    // FP32 out, the wave's 128 x WNC block inside D: every register goes
-    //   straight to memory; one store writes 32 consecutive columns (128 bytes)
-    //   of two rows.
-    // Otherwise the block is staged through LDS (free after the barrier below;
+    // FP32 out: every register goes straight to memory; one store writes 32
+    //   consecutive columns (128 bytes) of two rows.
+    // BF16 out: the block is staged through LDS (free after the barrier below;
     //   from buffer 1 on) so that global stores are 16 bytes per lane along
     //   rows: each wave writes its 128 x WNC block, EPI_ROWS rows at a time, and
-    //   reads it back row-contiguous.  FP32 out stages [row][WNC + pad] floats.
-    //   BF16 out stages row pairs: a lane's registers 4q..4q+3 are rows
-    //   2p..2p+3 of one column, so one conversion packs rows (2p, 2p+1) into a
-    //   dword at [pair][column]; the read-back takes 32 bytes of one pair (8
-    //   columns) and splits them into the two rows' 16 bytes with byte
-    //   permutes, with no exchange between lanes.
+    //   reads it back row-contiguous, as row pairs: a lane's registers
+    //   4q..4q+3 are rows 2p..2p+3 of one column, so one conversion packs rows
+    //   (2p, 2p+1) into a dword at [pair][column]; the read-back takes 32
+    //   bytes of one pair (8 columns) and splits them into the two rows' 16
+    //   bytes with byte permutes, with no exchange between lanes.
     // The instruction count sets this phase's time (measured: the stores
-    // drain within 0.2-0.4 us), so the common case carries no per-row bound
-    // tests (a wave whose rows and columns all lie inside D, 16-byte aligned)
-    // and no level-1 multiply (no level-1 factors).
+    // drain within 0.2-0.4 us), so a block inside D (16-byte aligned rows)
+    // carries no per-row bound tests, and only the kernels with 1x32 B scales
+    // (the only ones given level-1 factors) multiply by them.
     __syncthreads();
     constexpr int ESZ = OUT_BF16 ? 2 : 4;
     constexpr int ROWB = WNC * ESZ + 16; // padded LDS row (bytes)
@@ -975,53 +974,59 @@ gemm_fp8_kernel(GemmArgs p)
     const bool col_ok = col0 < N;
     const bool full = col0 + 16 / ESZ <= N && (((uintptr_t)dwave & 15) == 0) && ((ld_bytes & 15) == 0);
     // the whole block inside D with aligned rows (uniform over the wave)
-    const bool block_in = rows_ok == 128 && colw + WNC <= N;
-    const bool block_full = block_in && ((((uintptr_t)dblock) | (uintptr_t)ld_bytes) & 15) == 0;
+    const bool block_full = rows_ok == 128 && colw + WNC <= N && ((((uintptr_t)dblock) | (uintptr_t)ld_bytes) & 15) == 0;
 
     // Level-1 factors come only with 1x32 B scales (MOSS); other kernels
     // store the accumulators as they are.  Without factors l1v is 1.0, which
     // leaves every value unchanged.
     constexpr bool L1 = BG == BG_ROW32;
-    bool direct = false; // FP32 out stored straight from the registers
     if constexpr (!OUT_BF16) {
-        if (block_in && 128 * ld_bytes < ((int64_t)1 << 31)) {
-            direct = true;
-            // One batch per 32 x 32 tile: its 16 values (accumulating, their
-            // loads go first, so that a batch's loads are in flight
-            // together).  Raw buffer accesses on a descriptor of the wave's
-            // block, at byte offset row * ld + the lane's column (4 rows down
-            // for the upper half-wave), every offset below 2^31 (checked
-            // above).
-            const __amdgpu_buffer_rsrc_t rs =
-                __builtin_amdgcn_make_buffer_rsrc((void *)uniform(dblock), 0, 0x7FFFFFFF, BUF_DWORD3);
-            const int lane_off = (int)(hk * 4 * ld_bytes) + l32 * 4;
+        // FP32 out, every block: raw buffer accesses, one descriptor per 32-row
+        // tile whose record count covers only the tile's rows below m_end, at
+        // byte offset row * ld + the lane's column (4 rows down for the upper
+        // half-wave).  A lane whose column lies past N gets an offset of at
+        // least 2^30, above every record count (the launcher keeps 32 * ld
+        // below 2^30), so the range check drops its stores and zeroes its
+        // loads, as it does for rows past m_end.  One batch per 32 x 32 tile:
+        // its 16 values (accumulating, their loads go first, so that a
+        // batch's loads are in flight together).  Accumulation is a template
+        // parameter: tested at run time, the two store sequences made the
+        // compiler move every accumulator into vector registers first and
+        // spill 40-57 of them.
+        constexpr int OOB = 1 << 30;
+        int lane_off[TJ];
 #pragma unroll
-            for (int i = 0; i < 4; i++)
+        for (int j = 0; j < TJ; j++)
+            lane_off[j] = (colw + j * 32 + l32 < N ? 0 : OOB) + (int)(hk * 4 * ld_bytes) + l32 * 4 + j * 128;
 #pragma unroll
-                for (int j = 0; j < TJ; j++) {
-                    float v[16];
+        for (int i = 0; i < 4; i++) {
+            const int rows_i = min(32, max(0, rows_ok - i * 32));
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)uniform(dblock + (int64_t)i * 32 * ld_bytes), 0,
+                __builtin_amdgcn_readfirstlane(rows_i * (int)ld_bytes), BUF_DWORD3);
+#pragma unroll
+            for (int j = 0; j < TJ; j++) {
+                float v[16];
+#pragma unroll
+                for (int r = 0; r < 16; r++)
+                    v[r] = L1 ? acc[i][j][r] * l1v[j] : acc[i][j][r];
+                if constexpr (ACC) {
+                    float o[16];
 #pragma unroll
                     for (int r = 0; r < 16; r++)
-                        v[r] = L1 ? acc[i][j][r] * l1v[j] : acc[i][j][r];
-                    if (p.accumulate) {
-                        float o[16];
-#pragma unroll
-                        for (int r = 0; r < 16; r++)
-                            o[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                                rs, lane_off + (int)((i * 32 + (r / 4) * 8 + (r % 4)) * ld_bytes) + j * 128, 0, 0));
-#pragma unroll
-                        for (int r = 0; r < 16; r++)
-                            v[r] += o[r];
-                    }
+                        o[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                            rs, lane_off[j] + ((r / 4) * 8 + (r % 4)) * (int)ld_bytes, 0, 0));
 #pragma unroll
                     for (int r = 0; r < 16; r++)
-                        __builtin_amdgcn_raw_buffer_store_b32(
-                            __float_as_uint(v[r]), rs, lane_off + (int)((i * 32 + (r / 4) * 8 + (r % 4)) * ld_bytes) + j * 128,
-                            0, 0);
+                        v[r] += o[r];
                 }
+#pragma unroll
+                for (int r = 0; r < 16; r++)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[r]), rs,
+                                                          lane_off[j] + ((r / 4) * 8 + (r % 4)) * (int)ld_bytes, 0, 0);
+            }
         }
-    }
-    if (!direct) {
+    } else {
 #pragma unroll
         for (int part = 0; part < 128 / EPI_ROWS; part++) {
 #pragma unroll
@@ -1029,91 +1034,55 @@ gemm_fp8_kernel(GemmArgs p)
                 const int i = part * (EPI_ROWS / 32) + ii;
 #pragma unroll
                 for (int j = 0; j < TJ; j++) {
-                    if constexpr (OUT_BF16) {
 #pragma unroll
-                        for (int q = 0; q < 4; q++) {
-                            // Rows ii*32 + q*8 + hk*4 + 0..3 of column j*32 + l32, as
-                            // two row pairs: one dword per pair (low half the even row).
-                            float v[4];
+                    for (int q = 0; q < 4; q++) {
+                        // Rows ii*32 + q*8 + hk*4 + 0..3 of column j*32 + l32, as
+                        // two row pairs: one dword per pair (low half the even row).
+                        float v[4];
 #pragma unroll
-                            for (int t = 0; t < 4; t++)
-                                v[t] = L1 ? acc[i][j][4 * q + t] * l1v[j] : acc[i][j][4 * q + t];
-                            const int rp = ii * 16 + q * 4 + hk * 2;
-                            const int col = j * 32 + l32;
-                            *reinterpret_cast<uint32_t *>(ep + rp * RPB + col * 4) = pack_bf16x2(v[0], v[1]);
-                            *reinterpret_cast<uint32_t *>(ep + (rp + 1) * RPB + col * 4) = pack_bf16x2(v[2], v[3]);
-                        }
-                    } else {
-                        // FP32 out: one 4-byte write per value (8-byte pairs measured slower)
-#pragma unroll
-                        for (int r = 0; r < 16; r++) {
-                            const int row = ii * 32 + (r / 4) * 8 + hk * 4 + (r % 4);
-                            const int col = j * 32 + l32;
-                            const float v = L1 ? acc[i][j][r] * l1v[j] : acc[i][j][r];
-                            *reinterpret_cast<float *>(ep + row * ROWB + col * 4) = v;
-                        }
+                        for (int t = 0; t < 4; t++)
+                            v[t] = L1 ? acc[i][j][4 * q + t] * l1v[j] : acc[i][j][4 * q + t];
+                        const int rp = ii * 16 + q * 4 + hk * 2;
+                        const int col = j * 32 + l32;
+                        *reinterpret_cast<uint32_t *>(ep + rp * RPB + col * 4) = pack_bf16x2(v[0], v[1]);
+                        *reinterpret_cast<uint32_t *>(ep + (rp + 1) * RPB + col * 4) = pack_bf16x2(v[2], v[3]);
                     }
                 }
             }
             __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0): this wave's LDS writes done
             __builtin_amdgcn_wave_barrier();
-            if constexpr (OUT_BF16) {
-                // a lane takes 8 columns of one row pair: 32 bytes of pairs -> 16 bytes of each row
+            // a lane takes 8 columns of one row pair: 32 bytes of pairs -> 16 bytes of each row
 #pragma unroll
-                for (int rr = 0; rr < EPI_ROWS / 2; rr += RPI) {
-                    const int rp = rr + lr;
-                    const uint4 x = *reinterpret_cast<const uint4 *>(ep + rp * RPB + lc * 32);
-                    const uint4 y = *reinterpret_cast<const uint4 *>(ep + rp * RPB + lc * 32 + 16);
-                    const uint32_t w[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
-                    uint4 ev, od;
-                    uint32_t *e4 = &ev.x, *o4 = &od.x;
+            for (int rr = 0; rr < EPI_ROWS / 2; rr += RPI) {
+                const int rp = rr + lr;
+                const uint4 x = *reinterpret_cast<const uint4 *>(ep + rp * RPB + lc * 32);
+                const uint4 y = *reinterpret_cast<const uint4 *>(ep + rp * RPB + lc * 32 + 16);
+                const uint32_t w[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+                uint4 ev, od;
+                uint32_t *e4 = &ev.x, *o4 = &od.x;
 #pragma unroll
-                    for (int k = 0; k < 4; k++) {
-                        // low halves (the even row) and high halves (the odd row) of two pair words
-                        e4[k] = __builtin_amdgcn_perm(w[2 * k + 1], w[2 * k], 0x05040100u);
-                        o4[k] = __builtin_amdgcn_perm(w[2 * k + 1], w[2 * k], 0x07060302u);
-                    }
-#pragma unroll
-                    for (int s = 0; s < 2; s++) {
-                        const int row_l = part * EPI_ROWS + 2 * rp + s; // row within the wave's 128
-                        const uint4 v = s ? od : ev;
-                        uint8_t *dst = dwave + row_l * ld_bytes;
-                        if (block_full) {
-                            *reinterpret_cast<uint4 *>(dst) = v;
-                            continue;
-                        }
-                        if (row_l >= rows_ok || !col_ok)
-                            continue;
-                        if (full) {
-                            *reinterpret_cast<uint4 *>(dst) = v;
-                        } else {
-                            uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-                            for (int e = 0; e < 8 && col0 + e < N; e++)
-                                reinterpret_cast<uint16_t *>(dst)[e] = (uint16_t)(w4[e / 2] >> (16 * (e & 1)));
-                        }
-                    }
+                for (int k = 0; k < 4; k++) {
+                    // low halves (the even row) and high halves (the odd row) of two pair words
+                    e4[k] = __builtin_amdgcn_perm(w[2 * k + 1], w[2 * k], 0x05040100u);
+                    o4[k] = __builtin_amdgcn_perm(w[2 * k + 1], w[2 * k], 0x07060302u);
                 }
-            } else {
 #pragma unroll
-                for (int rr = 0; rr < EPI_ROWS; rr += RPI) {
-                    const int row_l = part * EPI_ROWS + rr + lr; // row within the wave's 128
-                    uint4 v = *reinterpret_cast<const uint4 *>(ep + (rr + lr) * ROWB + lc * 16);
+                for (int s = 0; s < 2; s++) {
+                    const int row_l = part * EPI_ROWS + 2 * rp + s; // row within the wave's 128
+                    const uint4 v = s ? od : ev;
+                    uint8_t *dst = dwave + row_l * ld_bytes;
+                    if (block_full) {
+                        *reinterpret_cast<uint4 *>(dst) = v;
+                        continue;
+                    }
                     if (row_l >= rows_ok || !col_ok)
                         continue;
-                    uint8_t *dst = dwave + row_l * ld_bytes;
-                    {
-                        float f4[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
-                        float *fd = reinterpret_cast<float *>(dst);
-                        if (full) {
-                            if (p.accumulate) {
-                                float4 o = *reinterpret_cast<const float4 *>(fd);
-                                f4[0] += o.x; f4[1] += o.y; f4[2] += o.z; f4[3] += o.w;
-                            }
-                            *reinterpret_cast<float4 *>(fd) = make_float4(f4[0], f4[1], f4[2], f4[3]);
-                        } else {
-                            for (int e = 0; e < 4 && col0 + e < N; e++)
-                                fd[e] = p.accumulate ? fd[e] + f4[e] : f4[e];
-                        }
+                    if (full) {
+                        *reinterpret_cast<uint4 *>(dst) = v;
+                    } else {
+                        uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+                        for (int e = 0; e < 8 && col0 + e < N; e++)
+                            reinterpret_cast<uint16_t *>(dst)[e] = (uint16_t)(w4[e / 2] >> (16 * (e & 1)));
                     }
                 }
             }
@@ -1123,10 +1092,13 @@ gemm_fp8_kernel(GemmArgs p)
     }
 }
 
-template <int MODE, int AG, int BG, bool OUT_BF16, int GK, int AF = FMT_E4M3>
+template <int MODE, int AG, int BG, bool OUT_BF16, int GK, int AF = FMT_E4M3, bool ACC = false>
 static int launch_one(const GemmArgs &p, int64_t grid, hipStream_t st)
 {
-    auto kern = gemm_fp8_kernel<MODE, AG, BG, OUT_BF16, GK, AF>;
+    auto kern = gemm_fp8_kernel<MODE, AG, BG, OUT_BF16, GK, AF, ACC>;
+    // FP32 output: the epilogue's buffer offsets stay below 2^31 for rows up to 2^23 elements
+    if (!OUT_BF16 && p.ldd >= ((int64_t)1 << 23))
+        return set_error(FGB_EUNSUPPORTED, "gemm: FP32 output rows (ldd) must be shorter than 2^23 elements");
     // The LDS limit is raised once per instantiation and device (a process may
     // use several devices); devices beyond the table set it on every call.
     static bool attr_set[64] = {};
@@ -1146,27 +1118,36 @@ static int launch_one(const GemmArgs &p, int64_t grid, hipStream_t st)
     return FGB_OK;
 }
 
+// The instantiation for the output type and, with FP32 output in the dense
+// and K-grouped forms, accumulation into D.
+template <int MODE, int AG, int BG, int GK, int AF = FMT_E4M3>
+static int launch_out(bool bf16, const GemmArgs &p, int64_t grid, hipStream_t st)
+{
+    if (bf16)
+        return launch_one<MODE, AG, BG, true, GK, AF>(p, grid, st);
+    if constexpr (GK == GK_NONE || GK == GK_K) {
+        if (p.accumulate)
+            return launch_one<MODE, AG, BG, false, GK, AF, true>(p, grid, st);
+    }
+    return launch_one<MODE, AG, BG, false, GK, AF>(p, grid, st);
+}
+
 template <int MODE, int GK>
 static int dispatch_mode(int ag, int bg, bool bf16, const GemmArgs &p, int64_t grid, hipStream_t st)
 {
     if constexpr (GK == GK_M || GK == GK_MM) {
         if (ag == AG_ROW128 && bg == BG_BLOCK)
-            return bf16 ? launch_one<MODE, AG_ROW128, BG_BLOCK, true, GK>(p, grid, st)
-                        : launch_one<MODE, AG_ROW128, BG_BLOCK, false, GK>(p, grid, st);
+            return launch_out<MODE, AG_ROW128, BG_BLOCK, GK>(bf16, p, grid, st);
     } else if constexpr (GK == GK_K) {
         if (ag == AG_ROW128 && bg == BG_ROW128)
-            return bf16 ? launch_one<MODE, AG_ROW128, BG_ROW128, true, GK_K>(p, grid, st)
-                        : launch_one<MODE, AG_ROW128, BG_ROW128, false, GK_K>(p, grid, st);
+            return launch_out<MODE, AG_ROW128, BG_ROW128, GK_K>(bf16, p, grid, st);
     } else {
         if (ag == AG_ROW128 && bg == BG_BLOCK)
-            return bf16 ? launch_one<MODE, AG_ROW128, BG_BLOCK, true, GK_NONE>(p, grid, st)
-                        : launch_one<MODE, AG_ROW128, BG_BLOCK, false, GK_NONE>(p, grid, st);
+            return launch_out<MODE, AG_ROW128, BG_BLOCK, GK_NONE>(bf16, p, grid, st);
         if (ag == AG_ROW128 && bg == BG_ROW128)
-            return bf16 ? launch_one<MODE, AG_ROW128, BG_ROW128, true, GK_NONE>(p, grid, st)
-                        : launch_one<MODE, AG_ROW128, BG_ROW128, false, GK_NONE>(p, grid, st);
+            return launch_out<MODE, AG_ROW128, BG_ROW128, GK_NONE>(bf16, p, grid, st);
         if (ag == AG_ROW32 && bg == BG_ROW32)
-            return bf16 ? launch_one<MODE, AG_ROW32, BG_ROW32, true, GK_NONE>(p, grid, st)
-                        : launch_one<MODE, AG_ROW32, BG_ROW32, false, GK_NONE>(p, grid, st);
+            return launch_out<MODE, AG_ROW32, BG_ROW32, GK_NONE>(bf16, p, grid, st);
     }
     return set_error(FGB_EUNSUPPORTED, "gemm: unsupported scale granularity pair (%d, %d)", ag, bg);
 }
@@ -1184,10 +1165,8 @@ template <int MODE>
 static int dispatch_e5m2_mode(int bg, bool bf16, const GemmArgs &p, int64_t grid, hipStream_t st)
 {
     if (bg == BG_BLOCK)
-        return bf16 ? launch_one<MODE, AG_ROW128, BG_BLOCK, true, GK_NONE, FMT_E5M2>(p, grid, st)
-                    : launch_one<MODE, AG_ROW128, BG_BLOCK, false, GK_NONE, FMT_E5M2>(p, grid, st);
-    return bf16 ? launch_one<MODE, AG_ROW128, BG_ROW128, true, GK_NONE, FMT_E5M2>(p, grid, st)
-                : launch_one<MODE, AG_ROW128, BG_ROW128, false, GK_NONE, FMT_E5M2>(p, grid, st);
+        return launch_out<MODE, AG_ROW128, BG_BLOCK, GK_NONE, FMT_E5M2>(bf16, p, grid, st);
+    return launch_out<MODE, AG_ROW128, BG_ROW128, GK_NONE, FMT_E5M2>(bf16, p, grid, st);
 }
 
 } // namespace fgb

@@ -256,7 +256,9 @@ size_t fp8_naive_transpose_workspace_size(int64_t rows, int64_t cols);
  *                   b_gran = FGB_ROW1x32 (the level-2 scales it goes with)
  *                   and K <= g1 (one level-1 group along K); NULL = none.
  *   d, d_dtype    : D [M, N], ld ldd, FGB_F32 or FGB_BF16 (round to nearest
- *                   even).  accumulate != 0 (FP32 only): D += A * B^T.
+ *                   even); FP32 output needs ldd < 2^23 (else
+ *                   FGB_EUNSUPPORTED).  accumulate != 0 (FP32 only):
+ *                   D += A * B^T.
  *   mode          : FGB_GEMM_EXACT -- each code times its scale 2^(byte-127)
  *                   (byte 0 included, meaning 2^-127) becomes a bf16, products
  *                   are exact and summed in FP32 (round to nearest even),
@@ -302,8 +304,8 @@ int fp8_block_gemm_fmt(const uint8_t *a, const uint8_t *sa, int a_gran, int a_fm
  *   a  [G, M_max, K] codes, sa [G, M_max, K/128] (1x128 scales), dense
  *   b  [G, N, K] codes, sb [G, ceil(N/128), K/128] (128x128 scales), dense
  *   masked_m : device int32 [G]; values are clamped to [0, M_max]
- *   d  [G, M_max, N] dense, FGB_BF16 or FGB_F32; for each expert e only rows
- *      [0, masked_m[e]) are computed and written.
+ *   d  [G, M_max, N] dense, FGB_BF16 or FGB_F32 (FP32: N < 2^23); for each
+ *      expert e only rows [0, masked_m[e]) are computed and written.
  *   mode as for fp8_block_gemm.  K % 128 == 0.
  */
 int fp8_grouped_gemm_masked(const uint8_t *a, const uint8_t *sa, const uint8_t *b, const uint8_t *sb,
@@ -320,8 +322,8 @@ int fp8_grouped_gemm_masked(const uint8_t *a, const uint8_t *sa, const uint8_t *
  *                   off[G] <= M_cap (as written by permute_pad).  Rows
  *                   [off[g], off[g+1]) use expert g.  Read on the device:
  *                   no host synchronisation.
- *   d  [M_cap, N], dense, FGB_BF16 or FGB_F32.  Rows >= off[G] are neither
- *      read nor written.
+ *   d  [M_cap, N], dense, FGB_BF16 or FGB_F32 (FP32: N < 2^23).  Rows >=
+ *      off[G] are neither read nor written.
  *   mode: FGB_GEMM_EXACT or FGB_GEMM_FAST as for fp8_block_gemm.
  * K % 128 == 0.
  */
@@ -342,7 +344,7 @@ int fp8_grouped_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t *b, cons
  *               k_offsets[0] >= 0, k_offsets[G] <= K_cap (as written by
  *               fp8_grouped_direct_transpose).  Read on the device: no host
  *               synchronisation and no check of these conditions.
- *   d  [G, M, N] dense, FGB_F32 or FGB_BF16; an expert with an empty range
+ *   d  [G, M, N] dense, FGB_F32 (N < 2^23) or FGB_BF16; an expert with an empty range
  *      gets D_e = 0 (or keeps D_e when accumulating).  accumulate != 0
  *      (FP32 only): D_e += A_e * B_e^T.
  *   mode: FGB_GEMM_EXACT or FGB_GEMM_FAST as for fp8_block_gemm.

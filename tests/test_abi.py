@@ -77,6 +77,7 @@ def test_gemm_validation():
     assert call(l1=f, g1=1024) == 2  # level-1 factor needs 1x32 B scales
     assert call(a=None) == 1
     assert call(mode=2) == 2
+    assert call(dt=0, ldd=1 << 23) == 2  # FP32 rows of 2^23 elements or more
     assert call(ag=1, bg=1, sa=_fake(0x1001)) == 1  # 1x32 scales need 4-byte alignment
     assert L.fp8_grouped_gemm(f, f, f, f, f, 0, 100, 256, 512, f, 1, 0, None) == 1
     assert L.fp8_grouped_gemm(f, f, f, f, f, 4, 100, 256, 512, f, 1, 5, None) == 2
