@@ -145,41 +145,51 @@ __device__ __forceinline__ int32_t expert_tiles_lane(const GemmArgs &p, int g, i
     return hi > lo ? (int32_t)((hi - lo + BM - 1) / BM) : 0;
 }
 
-// Total m-tiles over all experts (uniform over the wave).
-__device__ __forceinline__ int64_t count_mtiles(const GemmArgs &p)
+// One pass over 64 experts (lane l: expert g0 + l): row range, tile count
+// and the inclusive prefix sum of the counts.  The first pass is loaded once
+// and serves both the tile count and the lookup below (one dependent round
+// of loads fewer per workgroup for the usual G <= 64).
+struct ExpertPass {
+    int64_t lo, hi;
+    int32_t nt, incl;
+};
+__device__ __forceinline__ ExpertPass expert_pass(const GemmArgs &p, int g0)
 {
-    const int lane = (int)(threadIdx.x & 63);
-    int64_t total = 0;
-    for (int g0 = 0; g0 < p.G; g0 += 64) {
-        int64_t lo, hi;
-        const int32_t nt = expert_tiles_lane(p, g0 + lane, lo, hi);
-        total += __shfl(wave_inclusive_sum(nt), 63);
-    }
+    ExpertPass x;
+    x.nt = expert_tiles_lane(p, g0 + (int)(threadIdx.x & 63), x.lo, x.hi);
+    x.incl = wave_inclusive_sum(x.nt);
+    return x;
+}
+
+// Total m-tiles over all experts (uniform over the wave); ep0 = expert_pass(p, 0).
+__device__ __forceinline__ int64_t count_mtiles(const GemmArgs &p, const ExpertPass &ep0)
+{
+    int64_t total = __shfl(ep0.incl, 63);
+    for (int g0 = 64; g0 < p.G; g0 += 64)
+        total += __shfl(expert_pass(p, g0).incl, 63);
     return total;
 }
 
 // The expert owning m-tile tm (in expert order, each expert's tiles
 // contiguous), its first row of the tile and its row end; e = -1 if none.
-__device__ __forceinline__ void find_mtile(const GemmArgs &p, int64_t tm, int &e, int64_t &m0, int64_t &m_end)
+__device__ __forceinline__ void find_mtile(const GemmArgs &p, const ExpertPass &ep0, int64_t tm, int &e,
+                                           int64_t &m0, int64_t &m_end)
 {
-    const int lane = (int)(threadIdx.x & 63);
     int64_t base = 0;
     e = -1;
     for (int g0 = 0; g0 < p.G; g0 += 64) {
-        int64_t lo, hi;
-        const int32_t nt = expert_tiles_lane(p, g0 + lane, lo, hi);
-        const int32_t incl = wave_inclusive_sum(nt);
-        const int64_t first = base + incl - nt;
-        const uint64_t hit = __ballot(nt > 0 && tm >= first && tm < first + nt);
+        const ExpertPass x = g0 == 0 ? ep0 : expert_pass(p, g0);
+        const int64_t first = base + x.incl - x.nt;
+        const uint64_t hit = __ballot(x.nt > 0 && tm >= first && tm < first + x.nt);
         if (hit) { // uniform
             const int l = __builtin_ctzll(hit);
             e = g0 + l;
-            const int64_t lo_e = __shfl(lo, l), hi_e = __shfl(hi, l), first_e = __shfl(first, l);
+            const int64_t lo_e = __shfl(x.lo, l), hi_e = __shfl(x.hi, l), first_e = __shfl(first, l);
             m0 = lo_e + (tm - first_e) * BM;
             m_end = hi_e;
             return;
         }
-        base += __shfl(incl, 63);
+        base += __shfl(x.incl, 63);
     }
 }
 
@@ -281,6 +291,7 @@ gemm_fp8_kernel(GemmArgs p)
     // each expert's range, so every expert's tiles spread over all XCDs
     // (expert K ranges differ widely; whole experts per XCD would unbalance them).
     int64_t tiles_here = gridDim.x;
+    ExpertPass ep0 = {}; // M-grouped: the first 64 experts (see expert_pass)
     int ke = 0; // K-grouped: this workgroup's expert, whose K range is [koffs[ke], koffs[ke+1])
     if constexpr (GK == GK_K)
         tiles_here = gridDim.x / p.G;
@@ -289,7 +300,8 @@ gemm_fp8_kernel(GemmArgs p)
         // The grid is a host-side bound; the m-tiles that exist are counted
         // from the expert row ranges and the surplus workgroups exit, so the
         // XCD mapping spreads only real tiles.
-        const int64_t mt = count_mtiles(p);
+        ep0 = expert_pass(p, 0);
+        const int64_t mt = count_mtiles(p, ep0);
         tiles_here = min(mt, (int64_t)gridDim.x / p.tiles_n) * p.tiles_n;
         if ((int64_t)blockIdx.x >= tiles_here)
             return; // uniform per workgroup
@@ -317,7 +329,7 @@ gemm_fp8_kernel(GemmArgs p)
         m_end = p.M;
     } else {
         int e;
-        find_mtile(p, tm, e, m0, m_end);
+        find_mtile(p, ep0, tm, e, m0, m_end);
         if (e < 0)
             return; // not reached: tm < the counted m-tiles (uniform per workgroup)
         B += (int64_t)e * p.b_stride;
