@@ -50,7 +50,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--gemm-mode", choices=["exact", "fast"], default="exact")
     ap.add_argument("--parts", default="linear,moe,moe_bwd,wgrad,moss")
     ap.add_argument("--no-cpu-baseline", action="store_true")
