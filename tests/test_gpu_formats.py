@@ -220,6 +220,36 @@ def test_grouped_gemm_masked_small(fgb, mode):
 
 
 @pytest.mark.parametrize("mode", MODES)
+def test_grouped_gemm_masked_every_valid_tile_count(fgb, mode):
+    """Valid row counts that give each wave of a 256-row tile every count of
+    valid 32-row tiles (0 to 4, the upper and lower 128 rows), with partial
+    32-row tiles; every valid output checked, the rows past each mask untouched."""
+    say("masked grouped gemm: 0-4 valid 32-row tiles per wave", mode)
+    masked = np.array([32, 61, 96, 128, 129, 190, 224, 256], np.int32)
+    G, M_max, N, K = masked.size, 256, 192, 384
+    a = rand_codes((G, M_max, K), 111)
+    sa = rand_scales((G, M_max, K // 128), -6, 6, 112)
+    b = rand_codes((G, N, K), 113)
+    sb = rand_scales((G, (N + 127) // 128, K // 128), -6, 6, 114)
+    for bf16 in (False, True):
+        fill = 7.0
+        d = torch.full((G, M_max, N), fill, dtype=torch.bfloat16 if bf16 else torch.float32, device=DEV)
+        fgb.fp8_grouped_gemm_masked(a.to(DEV), sa.to(DEV), b.to(DEV), sb.to(DEV), torch.from_numpy(masked).to(DEV),
+                                    d=d, mode=_mode(fgb, mode))
+        got = np_(d)  # fp32 values, or bf16 bit patterns
+        untouched = np.uint16(0x40E0) if bf16 else np.float32(fill)  # 7.0
+        for g in range(G):
+            assert np.all(got[g, masked[g]:] == untouched), g
+        gi = np.concatenate([np.full(masked[g] * N, g) for g in range(G)])
+        mi = np.concatenate([np.repeat(np.arange(masked[g]), N) for g in range(G)])
+        ni = np.concatenate([np.tile(np.arange(N), masked[g]) for g in range(G)])
+        an, san, bn, sbn = a.numpy(), sa.numpy(), b.numpy(), sb.numpy()
+        ref = _masked_ref(an, san, bn, sbn, masked, gi, mi, ni)
+        bounds = _masked_bounds(an, san, bn, sbn, gi, mi, ni) if mode == "fast" else None
+        check_gemm(got[gi, mi, ni], ref, mode, bf16, bounds, K)
+
+
+@pytest.mark.parametrize("mode", MODES)
 def test_grouped_gemm_masked_decode_sampled(fgb, mode):
     """Decode-shaped: 32 experts of fc1 (N=4096, K=7168), M_max = 512 rows each
     (a token reaches an expert at most once), valid counts from top-8 routing
