@@ -320,10 +320,18 @@ __global__ __launch_bounds__(256) void grouped_direct_transpose_kernel(
         return;
     const int64_t ncb = C / 128, nkb = Kc / 128;
     const int64_t kb = slot / ncb, cb = slot % ncb; // (K-block-major measured faster here)
+    // The segment holding K block kb: lane l of each pass reads expert g0 + l's
+    // K range (one vector load instead of a dependent walk), a ballot names it.
     int ex = -1;
-    for (int g = 0; g < G; g++)
-        if (kb * 128 >= koff[g] && kb * 128 < koff[g + 1])
-            ex = g;
+    for (int g0 = 0; g0 < G; g0 += 64) {
+        const int g = g0 + lane;
+        const int64_t k = kb * 128;
+        const uint64_t hit = __ballot(g < G && k >= koff[g] && k < koff[g + 1]);
+        if (hit) { // uniform
+            ex = g0 + __builtin_ctzll(hit);
+            break;
+        }
+    }
     if (ex < 0)
         return; // past the last segment (uniform per wave)
     const int64_t r0 = off[ex] + (kb * 128 - koff[ex]);
