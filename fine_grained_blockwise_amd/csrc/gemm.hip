@@ -1196,16 +1196,21 @@ extern "C" int fp8_block_gemm_fmt(const uint8_t *a, const uint8_t *sa, int a_gra
     FGB_REQUIRE(b_fmt == FGB_E4M3, FGB_EUNSUPPORTED, "fp8_block_gemm: b_fmt must be FGB_E4M3");
     FGB_REQUIRE(a_fmt == FGB_E4M3 || (a_gran == FGB_ROW1x128 && b_gran != FGB_ROW1x32 && !b_l1), FGB_EUNSUPPORTED,
                 "fp8_block_gemm: an E5M2 A needs 1x128 A scales, 128x128 or 1x128 B scales and no b_l1");
-    FGB_REQUIRE(a && sa && b && sb && d, FGB_EINVAL, "fp8_block_gemm: null pointer");
-    FGB_REQUIRE(M > 0 && N > 0 && K > 0 && K % 128 == 0, FGB_EINVAL,
-                "fp8_block_gemm: need M, N > 0 and K a positive multiple of 128 (M=%lld N=%lld K=%lld)",
+    FGB_REQUIRE(M >= 0 && N >= 0 && K >= 0 && K % 128 == 0, FGB_EINVAL,
+                "fp8_block_gemm: need M, N >= 0 and K a multiple of 128 (M=%lld N=%lld K=%lld)",
                 (long long)M, (long long)N, (long long)K);
-    FGB_REQUIRE(lda >= K && ldb >= K && lda % 16 == 0 && ldb % 16 == 0, FGB_EINVAL,
+    // Empty D: nothing to write (the operands may be empty tensors without storage).
+    if (M == 0 || N == 0)
+        return FGB_OK;
+    FGB_REQUIRE(d && (K == 0 || (a && sa && b && sb)), FGB_EINVAL, "fp8_block_gemm: null pointer");
+    // (with K = 0 no operand is read: their layouts are not checked)
+    FGB_REQUIRE(K == 0 || (lda >= K && ldb >= K && lda % 16 == 0 && ldb % 16 == 0), FGB_EINVAL,
                 "fp8_block_gemm: lda/ldb must be >= K and multiples of 16");
-    FGB_REQUIRE(256 * lda < (1ll << 32) && 256 * ldb < (1ll << 32), FGB_EINVAL,
+    FGB_REQUIRE(K == 0 || (256 * lda < (1ll << 32) && 256 * ldb < (1ll << 32)), FGB_EINVAL,
                 "fp8_block_gemm: lda/ldb too large");
     FGB_REQUIRE(ldd >= N, FGB_EINVAL, "fp8_block_gemm: ldd must be >= N");
-    FGB_REQUIRE(aligned16(a) && aligned16(b), FGB_EINVAL, "fp8_block_gemm: a and b must be 16-byte aligned");
+    FGB_REQUIRE(K == 0 || (aligned16(a) && aligned16(b)), FGB_EINVAL,
+                "fp8_block_gemm: a and b must be 16-byte aligned");
     FGB_REQUIRE(d_dtype == FGB_F32 || d_dtype == FGB_BF16, FGB_EUNSUPPORTED,
                 "fp8_block_gemm: d_dtype must be FGB_F32 or FGB_BF16");
     FGB_REQUIRE(mode == FGB_GEMM_EXACT || mode == FGB_GEMM_FAST, FGB_EUNSUPPORTED,
@@ -1233,7 +1238,7 @@ extern "C" int fp8_block_gemm_fmt(const uint8_t *a, const uint8_t *sa, int a_gra
                 "fp8_block_gemm: b_l1 needs 1x32 B scales (the level-2 scales of the two-level format)");
     FGB_REQUIRE(!b_l1 || (g1 > 0 && K <= g1), FGB_EUNSUPPORTED,
                 "fp8_block_gemm: b_l1 needs K <= g1 (one level-1 group along K)");
-    if (ag == AG_ROW32)
+    if (ag == AG_ROW32 && K > 0)
         FGB_REQUIRE(((uintptr_t)sa & 3) == 0 && ((uintptr_t)sb & 3) == 0, FGB_EINVAL,
                     "fp8_block_gemm: 1x32 scale tensors must be 4-byte aligned");
     GemmArgs p{};

@@ -244,7 +244,9 @@ size_t fp8_naive_transpose_workspace_size(int64_t rows, int64_t cols);
  * ([DSV3] §1): Fprop A = X, B = W; Dgrad A = dY, B = W^T (block transpose);
  * Wgrad A = dY^T, B = X^T (both from fp8_direct_transpose, 1x128 scales).
  * Every K group's product sum is scaled by 2^(ea + eb) and accumulated in
- * FP32 ([DSV3] §4, §5.3).
+ * FP32 ([DSV3] §4, §5.3).  M, N >= 0 and K >= 0 a multiple of 128: M = 0 or
+ * N = 0 writes nothing (operand pointers may be NULL); K = 0 gives the empty
+ * sum, D = 0 (D unchanged when accumulating).
  *   a, sa, a_gran : A codes [M, K] (ld lda) and scales, FGB_ROW1x128 -> sa
  *                   [M, K/128], FGB_ROW1x32 -> sa [M, K/32] (dense)
  *   b, sb, b_gran : B codes [N, K] (ld ldb) and scales, FGB_BLOCK128 -> sb

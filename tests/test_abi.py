@@ -68,7 +68,10 @@ def test_gemm_validation():
                                 a["M"], a["N"], a["K"], a["lda"], a["ldb"], a["d"], a["dt"],
                                 a["ldd"], a["acc"], a.get("mode", 0), None, 0, None)
     assert call(K=500) == 1
-    assert call(M=0) == 1
+    assert call(M=-1) == 1
+    assert call(M=0) == 0 and call(N=0) == 0  # empty D: nothing to do, nothing launched
+    assert call(M=0, a=None, sa=None, b=None, sb=None, d=None) == 0
+    assert call(d=None, K=0) == 1  # a non-empty D must exist
     assert call(lda=500, K=256) == 1
     assert call(ag=2) == 2          # BLOCK128 A scales are not a mode
     assert call(ag=1, bg=2) == 2    # 1x32 must pair with 1x32

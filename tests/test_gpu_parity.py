@@ -366,6 +366,29 @@ def test_gemm_ragged(fgb, M, N, K, bg, mode):
         check_gemm(np_(d), ref, mode, bf16, bounds, K)
 
 
+def test_gemm_empty_and_k0(fgb):
+    """M = 0 writes nothing; K = 0 is the empty sum: D = 0, or D unchanged when accumulating."""
+    say("gemm: M = 0 and K = 0")
+    M, N, K = 300, 260, 256
+    b = rand_codes((N, K), 5).to(DEV)
+    sb = rand_scales(((N + 127) // 128, K // 128), -4, 4, 6).to(DEV)
+    a0 = torch.empty((0, K), dtype=torch.uint8, device=DEV)
+    sa0 = torch.empty((0, K // 128), dtype=torch.uint8, device=DEV)
+    for dt in (torch.float32, torch.bfloat16):
+        assert fgb.fp8_block_gemm(a0, sa0, fgb.ROW1x128, b, sb, fgb.BLOCK128, out_dtype=dt).shape == (0, N)
+    e = lambda r: torch.empty((r, 0), dtype=torch.uint8, device=DEV)
+    ak, sak, bk, sbk = e(M), e(M), e(N), e((N + 127) // 128)
+    for mode in MODES:
+        for dt in (torch.float32, torch.bfloat16):
+            d = torch.full((M, N), 3.0, dtype=dt, device=DEV)
+            fgb.fp8_block_gemm(ak, sak, fgb.ROW1x128, bk, sbk, fgb.BLOCK128, d=d, mode=_mode(fgb, mode))
+            assert torch.count_nonzero(d).item() == 0, (mode, dt)
+        base = torch.randn(M, N, device=DEV) + 0.5  # no -0.0 (the empty sum adds +0.0)
+        d = base.clone()
+        fgb.fp8_block_gemm(ak, sak, fgb.ROW1x128, bk, sbk, fgb.BLOCK128, d=d, accumulate=True, mode=_mode(fgb, mode))
+        assert torch.equal(d, base), mode
+
+
 def test_gemm_accumulate_and_ldd(fgb):
     say("gemm accumulate into strided fp32 D")
     M, N, K = 256, 384, 256
