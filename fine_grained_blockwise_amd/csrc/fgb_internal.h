@@ -190,7 +190,7 @@ __device__ __forceinline__ void st_stream4(void *p, uint32_t v)
     __builtin_nontemporal_store(v, reinterpret_cast<uint32_t *>(p));
 }
 
-// Ordinary (write-back) 16- and 8-byte stores, for kernels whose traffic is
+// Ordinary (write-back) 16-byte stores, for kernels whose traffic is
 // mostly writes: on the MI355X a stream of ordinary 16-byte stores sustained
 // ~8% more than nontemporal ones (5.85 against 5.40 TB/s writing 1 GB).
 __device__ __forceinline__ void st_plain16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
