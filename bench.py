@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--parts", default="linear,moe,moe_bwd,wgrad,moss")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-study", action="store_true", help="skip the untimed transpose comparison")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph leg (the step captured once and replayed --steps times)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB read + 1 GiB write elementwise kernel 3 times (the reference "
@@ -256,6 +258,45 @@ def step(fgb, torch, W, rec, mode):
         out["moss"] = (xh, y, wh)
         out.setdefault("obs", {})["moss"] = dict(s2=s2, ws2=ws2, aq=aq, as_=as_, q=q, s1=s1)
     return out
+
+
+def _tensors(x):
+    if isinstance(x, dict):
+        for k in sorted(x):
+            if k != "obs":
+                yield from _tensors(x[k])
+    elif isinstance(x, (tuple, list)):
+        for v in x:
+            yield from _tensors(v)
+    elif x is not None:
+        yield x
+
+
+def graph_leg(fgb, torch, W, args, eager_out):
+    """The same step captured once in a HIP graph and replayed: the step time
+    without per-launch host overhead, and whether every output of the replays
+    equals the eager step's bit for bit (the inputs do not change)."""
+    rec = Recorder(torch)  # off: plain calls
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gout = step(fgb, torch, W, rec, args.gemm_mode)
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    a, b = list(_tensors(eager_out)), list(_tensors(gout))
+    match = len(a) == len(b) and all(x.shape == y.shape and x.dtype == y.dtype and torch.equal(x, y)
+                                     for x, y in zip(a, b))
+    del g, gout
+    torch.cuda.synchronize()
+    log(f"graph leg: {ms:.3f} ms/step over {args.steps} replays; outputs match eager: {match}")
+    return {"ms_per_step": round(ms, 3), "replays": args.steps, "outputs_compared": len(a),
+            "outputs_match_eager": match}
 
 
 def source_sha(paths):
@@ -797,6 +838,7 @@ def main():
     rec.on = False
     ms_step = (t1 - t0) * 1e3 / args.steps
     res = rec.results()
+    graph = None if args.no_graph else graph_leg(fgb, torch, W, args, out)
 
     kernels = {}
     floor_s = 0.0  # GEMMs at the dense FP8 peak (the value)
@@ -928,6 +970,7 @@ def main():
                    "gemm_contraction": "bf16 MFMA on exact scaled fp8->bf16 operands" if args.gemm_mode == "exact"
                    else "fp8 scaled MFMA"},
         "roofline": roofline,
+        "graph": graph,
         "cpu_baseline": cpu,
         "inputs_sha256_every_64th_row": input_digest(torch, W),
         "kernels": kernels,
