@@ -1056,37 +1056,60 @@ gemm_fp8_kernel(GemmArgs p)
                             v[t] = L1 ? acc[i][j][4 * q + t] * l1v[j] : acc[i][j][4 * q + t];
                         const int rp = ii * 16 + q * 4 + hk * 2;
                         const int col = j * 32 + l32;
-                        *reinterpret_cast<uint32_t *>(ep + rp * RPB + col * 4) = pack_bf16x2(v[0], v[1]);
-                        *reinterpret_cast<uint32_t *>(ep + (rp + 1) * RPB + col * 4) = pack_bf16x2(v[2], v[3]);
+                        // 16-byte chunk c of a row pair sits at chunk c ^ ((c >> 3) & 1)
+                        const int cs = col ^ (((col >> 5) & 1) << 2);
+                        *reinterpret_cast<uint32_t *>(ep + rp * RPB + cs * 4) = pack_bf16x2(v[0], v[1]);
+                        *reinterpret_cast<uint32_t *>(ep + (rp + 1) * RPB + cs * 4) = pack_bf16x2(v[2], v[3]);
                     }
                 }
             }
             __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0): this wave's LDS writes done
             __builtin_amdgcn_wave_barrier();
             // a lane takes 8 columns of one row pair: 32 bytes of pairs -> 16 bytes of each row
-#pragma unroll
-            for (int rr = 0; rr < EPI_ROWS / 2; rr += RPI) {
-                const int rp = rr + lr;
-                const uint4 x = *reinterpret_cast<const uint4 *>(ep + rp * RPB + lc * 32);
-                const uint4 y = *reinterpret_cast<const uint4 *>(ep + rp * RPB + lc * 32 + 16);
+            constexpr int NRD = EPI_ROWS / 2 / RPI; // read-backs per lane
+            const int flip = (lc >> 2) & 1;         // chunks 2 lc and 2 lc + 1, swizzled as written
+            // low halves (the even row) and high halves (the odd row) of two pair words
+            auto unpair = [](const uint4 &x, const uint4 &y, uint4 &ev, uint4 &od) {
                 const uint32_t w[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
-                uint4 ev, od;
                 uint32_t *e4 = &ev.x, *o4 = &od.x;
 #pragma unroll
                 for (int k = 0; k < 4; k++) {
-                    // low halves (the even row) and high halves (the odd row) of two pair words
                     e4[k] = __builtin_amdgcn_perm(w[2 * k + 1], w[2 * k], 0x05040100u);
                     o4[k] = __builtin_amdgcn_perm(w[2 * k + 1], w[2 * k], 0x07060302u);
                 }
+            };
+            if (block_full) {
+                // The whole block inside D: every LDS read first, then the
+                // stores, in one straight-line sequence with no per-row tests.
+                uint4 xs[NRD], ys[NRD];
+#pragma unroll
+                for (int t = 0; t < NRD; t++) {
+                    const uint8_t *src = ep + (t * RPI + lr) * RPB;
+                    xs[t] = *reinterpret_cast<const uint4 *>(src + ((2 * lc) ^ flip) * 16);
+                    ys[t] = *reinterpret_cast<const uint4 *>(src + ((2 * lc + 1) ^ flip) * 16);
+                }
+                uint8_t *dst = dwave + (int64_t)(part * EPI_ROWS + 2 * lr) * ld_bytes;
+#pragma unroll
+                for (int t = 0; t < NRD; t++) {
+                    uint4 ev, od;
+                    unpair(xs[t], ys[t], ev, od);
+                    *reinterpret_cast<uint4 *>(dst) = ev;
+                    *reinterpret_cast<uint4 *>(dst + ld_bytes) = od;
+                    dst += 2 * RPI * ld_bytes;
+                }
+            } else {
+#pragma unroll
+            for (int rr = 0; rr < EPI_ROWS / 2; rr += RPI) {
+                const int rp = rr + lr;
+                const uint4 x = *reinterpret_cast<const uint4 *>(ep + rp * RPB + ((2 * lc) ^ flip) * 16);
+                const uint4 y = *reinterpret_cast<const uint4 *>(ep + rp * RPB + ((2 * lc + 1) ^ flip) * 16);
+                uint4 ev, od;
+                unpair(x, y, ev, od);
 #pragma unroll
                 for (int s = 0; s < 2; s++) {
                     const int row_l = part * EPI_ROWS + 2 * rp + s; // row within the wave's 128
                     const uint4 v = s ? od : ev;
                     uint8_t *dst = dwave + row_l * ld_bytes;
-                    if (block_full) {
-                        *reinterpret_cast<uint4 *>(dst) = v;
-                        continue;
-                    }
                     if (row_l >= rows_ok || !col_ok)
                         continue;
                     if (full) {
@@ -1097,6 +1120,7 @@ gemm_fp8_kernel(GemmArgs p)
                             reinterpret_cast<uint16_t *>(dst)[e] = (uint16_t)(w4[e / 2] >> (16 * (e & 1)));
                     }
                 }
+            }
             }
             __builtin_amdgcn_s_waitcnt(0xc07f);
             __builtin_amdgcn_wave_barrier();
