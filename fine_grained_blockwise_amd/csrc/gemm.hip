@@ -1000,42 +1000,83 @@ gemm_fp8_kernel(GemmArgs p)
         // least 2^30, above every record count (the launcher keeps 32 * ld
         // below 2^30), so the range check drops its stores and zeroes its
         // loads, as it does for rows past m_end.  One batch per 32 x 32 tile:
-        // its 16 values (accumulating, their loads go first, so that a
-        // batch's loads are in flight together).  Accumulation is a template
-        // parameter: tested at run time, the two store sequences made the
-        // compiler move every accumulator into vector registers first and
-        // spill 40-57 of them.
+        // its 16 values.  Accumulation is a template parameter: tested at run
+        // time, the two store sequences made the compiler move every
+        // accumulator into vector registers first and spill 40-57 of them.
+        // Accumulating, the old values of D are read AHEAD batches before
+        // their use, one register set per batch in flight: read batch by
+        // batch, every batch waited out the full HBM latency of its loads
+        // (34 us of epilogue per tile against 7 us without accumulation).
         constexpr int OOB = 1 << 30;
         int lane_off[TJ];
 #pragma unroll
         for (int j = 0; j < TJ; j++)
             lane_off[j] = (colw + j * 32 + l32 < N ? 0 : OOB) + (int)(hk * 4 * ld_bytes) + l32 * 4 + j * 128;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
+        auto tile_rsrc = [&](int i) {
             const int rows_i = min(32, max(0, rows_ok - i * 32));
-            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)uniform(dblock + (int64_t)i * 32 * ld_bytes), 0,
-                __builtin_amdgcn_readfirstlane(rows_i * (int)ld_bytes), BUF_DWORD3);
+            return __builtin_amdgcn_make_buffer_rsrc((void *)uniform(dblock + (int64_t)i * 32 * ld_bytes), 0,
+                                                     __builtin_amdgcn_readfirstlane(rows_i * (int)ld_bytes),
+                                                     BUF_DWORD3);
+        };
+        auto batch = [&](int b, float (&v)[16]) { // the 16 output values of batch b = (i, j)
+            const int i = b / TJ, j = b % TJ;
 #pragma unroll
-            for (int j = 0; j < TJ; j++) {
+            for (int r = 0; r < 16; r++)
+                v[r] = L1 ? acc[i][j][r] * l1v[j] : acc[i][j][r];
+        };
+        auto store = [&](int b, const float (&v)[16]) {
+            const __amdgpu_buffer_rsrc_t rs = tile_rsrc(b / TJ);
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[r]), rs,
+                                                      lane_off[b % TJ] + ((r / 4) * 8 + (r % 4)) * (int)ld_bytes, 0,
+                                                      0);
+        };
+        constexpr int NB = 4 * TJ; // batches per wave
+        if constexpr (ACC) {
+            constexpr int AHEAD = 3;
+            float o[AHEAD][16];
+            auto load = [&](int b, float (&dst)[16]) {
+                const __amdgpu_buffer_rsrc_t rs = tile_rsrc(b / TJ);
+#pragma unroll
+                for (int r = 0; r < 16; r++)
+                    dst[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                        rs, lane_off[b % TJ] + ((r / 4) * 8 + (r % 4)) * (int)ld_bytes, 0, 0));
+            };
+#pragma unroll
+            for (int b = 0; b < AHEAD; b++)
+                load(b, o[b]);
+#pragma unroll
+            for (int b = 0; b < NB; b++) {
                 float v[16];
+                batch(b, v);
 #pragma unroll
                 for (int r = 0; r < 16; r++)
-                    v[r] = L1 ? acc[i][j][r] * l1v[j] : acc[i][j][r];
-                if constexpr (ACC) {
-                    float o[16];
+                    v[r] += o[b % AHEAD][r];
+                store(b, v);
+                if (b + AHEAD < NB)
+                    load(b + AHEAD, o[b % AHEAD]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int rows_i = min(32, max(0, rows_ok - i * 32));
+                const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)uniform(dblock + (int64_t)i * 32 * ld_bytes), 0,
+                    __builtin_amdgcn_readfirstlane(rows_i * (int)ld_bytes), BUF_DWORD3);
+#pragma unroll
+                for (int j = 0; j < TJ; j++) {
+                    float v[16];
 #pragma unroll
                     for (int r = 0; r < 16; r++)
-                        o[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                            rs, lane_off[j] + ((r / 4) * 8 + (r % 4)) * (int)ld_bytes, 0, 0));
+                        v[r] = L1 ? acc[i][j][r] * l1v[j] : acc[i][j][r];
 #pragma unroll
                     for (int r = 0; r < 16; r++)
-                        v[r] += o[r];
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[r]), rs,
+                                                              lane_off[j] + ((r / 4) * 8 + (r % 4)) * (int)ld_bytes,
+                                                              0, 0);
                 }
-#pragma unroll
-                for (int r = 0; r < 16; r++)
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[r]), rs,
-                                                          lane_off[j] + ((r / 4) * 8 + (r % 4)) * (int)ld_bytes, 0, 0);
             }
         }
     } else {
