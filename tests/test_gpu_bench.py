@@ -25,6 +25,8 @@ def test_bench_line_contract():
     assert 0 < line["value"] < 100 and line["ms_per_step"] > 0 and line["higher_is_better"] is True
     assert line["vs_baseline"] is None and line["cpu_baseline"] is None
     assert "workload" in line["config"]
+    g = line["graph"]  # the step replayed as one HIP graph equals the eager step bit for bit
+    assert g["outputs_match_eager"] is True and g["ms_per_step"] > 0 and g["outputs_compared"] == 3
     rf = line["roofline"]
     for k in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
         assert k in rf, k
