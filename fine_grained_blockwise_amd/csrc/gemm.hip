@@ -46,6 +46,7 @@
 //          supplies chunks 4hs+h and 4hs+2+h.
 //   EXACT: 16-deep sub-step s uses bytes 0-7 (s even) or 8-15 (s odd) of
 //          chunk 2(s/2)+h, converted to 8 bf16 values.
+#include <atomic>
 #include <type_traits>
 
 #include "fgb_internal.h"
@@ -1178,17 +1179,18 @@ static int launch_one(const GemmArgs &p, int64_t grid, hipStream_t st)
         return set_error(FGB_EUNSUPPORTED, "gemm: FP32 output rows (ldd) must be shorter than 2^23 elements");
     // The LDS limit is raised once per instantiation and device (a process may
     // use several devices); devices beyond the table set it on every call.
-    static bool attr_set[64] = {};
+    // Threads that launch at once may both set it, which is harmless.
+    static std::atomic<bool> attr_set[64] = {};
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess)
         dev = -1;
     const bool cached = dev >= 0 && dev < 64;
-    if (!cached || !attr_set[dev]) {
+    if (!cached || !attr_set[dev].load(std::memory_order_acquire)) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
         if (e != hipSuccess)
             return set_error(FGB_EHIP, "gemm: hipFuncSetAttribute failed: %s", hipGetErrorString(e));
         if (cached)
-            attr_set[dev] = true;
+            attr_set[dev].store(true, std::memory_order_release);
     }
     kern<<<(unsigned)grid, Waves<MODE, GK>::NW * 64, LDS_BYTES, st>>>(p);
     FGB_LAUNCHED("gemm_fp8_kernel");

@@ -21,6 +21,8 @@
 // The shift decodes two codes to fp32 (exact), multiplies by 2^-k (exact) and
 // converts back with round-to-nearest-even; for E - k >= 1 that is the plain
 // exponent decrement, below it the subnormal re-rounding.
+#include <atomic>
+
 #include "fgb_internal.h"
 
 namespace fgb {
@@ -382,18 +384,18 @@ __global__ __launch_bounds__(256) void grouped_direct_transpose_kernel(
 template <auto KERN>
 static int raise_lds_limit(int bytes, const char *name)
 {
-    static bool done[64] = {};
+    static std::atomic<bool> done[64] = {}; // threads that launch at once may both set it: harmless
     const auto kern = KERN;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess)
         dev = -1;
     const bool cached = dev >= 0 && dev < 64;
-    if (!cached || !done[dev]) {
+    if (!cached || !done[dev].load(std::memory_order_acquire)) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
         if (e != hipSuccess)
             return set_error(FGB_EHIP, "%s: hipFuncSetAttribute failed: %s", name, hipGetErrorString(e));
         if (cached)
-            done[dev] = true;
+            done[dev].store(true, std::memory_order_release);
     }
     return FGB_OK;
 }
