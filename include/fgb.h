@@ -275,7 +275,7 @@ size_t fp8_naive_transpose_workspace_size(int64_t rows, int64_t cols);
  *                   largest, so |error| <= 2^-10 * sum over runs of the
  *                   run's largest |scaled product| plus FP32 rounding.
  *   workspace     : unused, may be NULL (ws_bytes ignored).
- * K % 128 == 0; M, N >= 1; 256 * lda and 256 * ldb below 2^32.
+ * 256 * lda and 256 * ldb below 2^32 (when K > 0).
  */
 int fp8_block_gemm(const uint8_t *a, const uint8_t *sa, int a_gran, const uint8_t *b,
                    const uint8_t *sb, int b_gran, const float *b_l1, int64_t g1, int64_t M,
