@@ -3,9 +3,8 @@ MOSS against the oracle, bit for bit: random shapes (ragged row counts,
 partial 128-row weight blocks, one group up to many per row), bf16 and fp32
 inputs whose rows span 2^-30..2^30 in magnitude, with all-zero rows and
 32-element groups 2^-60 below the rest of their row; both element formats
-and both scale rules
-of the row-wise quantizer; row-wise and 128x128-block scales in the
-transposes; random level-1 group sizes in MOSS."""
+and both scale rules of the row-wise quantizer; row-wise and 128x128-block
+scales in the transposes; random level-1 group sizes in MOSS."""
 import numpy as np
 import pytest
 import torch
