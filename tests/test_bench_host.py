@@ -32,3 +32,17 @@ def test_every_step_operation_has_an_oracle_rate():
     assert bench.oracle_family("moe_bwd.unpermute_backward_quant dO") == "unpermute_bwd"
     assert bench.oracle_family("moe_bwd.dswiglu_quant") == "dswiglu"
     assert bench.oracle_family("lin.transpose W (block)") == "transpose"
+
+
+def test_graph_leg_compares_every_step_output():
+    """The graph leg compares the replayed step's outputs with the eager step's:
+    every tensor the step returns, in a fixed order, and none of the
+    observability tensors (kept under "obs")."""
+    import bench
+
+    out = {"lin": ("y", "dx", "dw"), "moe": ("o", "offs"), "moe_bwd": ("dx", "dw1", "dw2"), "wg": "dw",
+           "moss": ("xh", "y", "wh"), "obs": {"lin": {"xq": "not compared"}}}
+    got = list(bench._tensors(out))
+    assert got == ["y", "dx", "dw", "o", "offs", "dx", "dw1", "dw2", "xh", "y", "wh", "dw"]
+    assert "not compared" not in got
+    assert list(bench._tensors({"lin": ("a", None, "b")})) == ["a", "b"]
