@@ -631,6 +631,57 @@ def _time_us(torch, fn, reps=10):
     return e0.elapsed_time(e1) / reps * 1e3
 
 
+def median_flushed_us(torch, scratch, fn):
+    """Median duration of fn in us over the last 20 of 21 repetitions, each
+    preceded by a write of the 512 MB scratch buffer (twice the 256 MB
+    Infinity Cache), so fn's operands come from HBM."""
+    ts = []
+    for r in range(21):
+        scratch.fill_(float(r))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    ts = sorted(ts[1:])
+    return (ts[9] + ts[10]) / 2
+
+
+def hbm_reference(fgb, torch, dev):
+    """What plain byte movement sustains in each access pattern of the
+    data-movement kernels (fgb_hbm_probe: the same 16-byte nontemporal loads
+    and stores, nothing else), on a [32768, 7168] byte matrix, cache flushed
+    as in isolated_flushed; beside them the library's k = 0 block transpose of
+    the same matrix (a pure byte transpose with its LDS staging)."""
+    scratch = torch.empty(512 * 2 ** 20 // 4, dtype=torch.float32, device=dev)
+    rows, cols = 32768, 7168
+    n = rows * cols
+    g = torch.Generator(device="cpu").manual_seed(5)
+    src = torch.randint(0, 256, (rows, cols), dtype=torch.uint8, generator=g).to(dev)
+    dst = torch.empty_like(src)
+    red = torch.empty(n // 256, dtype=torch.uint8, device=dev)
+    sb = torch.full((rows // 128, cols // 128), 127, dtype=torch.uint8, device=dev)
+    out = {}
+
+    def rec(name, nbytes, fn):
+        us = median_flushed_us(torch, scratch, fn)
+        out[name] = {"us": round(us, 1), "GB/s": round(nbytes / us / 1e3, 1),
+                     "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+    rec("copy", 2 * n, lambda: fgb.fgb_hbm_probe(src, dst, fgb.PROBE_COPY))
+    rec("read", n + n // 256, lambda: fgb.fgb_hbm_probe(src, red, fgb.PROBE_READ))
+    rec("fill (write only)", n, lambda: fgb.fgb_hbm_probe(None, dst, fgb.PROBE_FILL))
+    rec("strided read (128-byte row pieces), contiguous write", 2 * n,
+        lambda: fgb.fgb_hbm_probe(src, dst, fgb.PROBE_STRIDED_READ))
+    rec("contiguous read, strided write (128-byte row pieces)", 2 * n,
+        lambda: fgb.fgb_hbm_probe(src, dst, fgb.PROBE_STRIDED_WRITE))
+    rec("block transpose k = 0 [32768, 7168]", 2 * (n + n // 16384),
+        lambda: fgb.fp8_direct_transpose(src, sb, fgb.BLOCK128))
+    del scratch, src, dst, red
+    return {"matrix": [rows, cols], "patterns": out}
+
+
 def isolated_flushed(fgb, torch, W, dev):
     """The bandwidth kernels of the step, each timed alone: before every one of
     21 repetitions a 512 MB scratch buffer is written (twice the 256 MB
@@ -639,17 +690,7 @@ def isolated_flushed(fgb, torch, W, dev):
     scratch = torch.empty(512 * 2 ** 20 // 4, dtype=torch.float32, device=dev)
 
     def med_us(fn):
-        ts = []
-        for r in range(21):
-            scratch.fill_(float(r))
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1) * 1e3)
-        ts = sorted(ts[1:])
-        return (ts[9] + ts[10]) / 2
+        return median_flushed_us(torch, scratch, fn)
 
     out = {}
 
@@ -939,6 +980,8 @@ def main():
     if "moe" in W and "lin" in W and "wg" in W and not args.no_study:
         extra["isolated_flushed"] = isolated_flushed(fgb, torch, W, dev)
         log(f"isolated, Infinity Cache flushed: {extra['isolated_flushed']}")
+        extra["hbm_reference"] = hbm_reference(fgb, torch, dev)
+        log(f"HBM reference patterns: {extra['hbm_reference']}")
     if "moe" in W and "dO" in W["moe"] and "lin" in W and not args.no_study:
         extra["format_variants"] = format_variants(fgb, torch, W, dev, args)
         log(f"format variants: {extra['format_variants']}")

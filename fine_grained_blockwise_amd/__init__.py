@@ -22,7 +22,8 @@ __all__ = [
     "fp8_block_transpose_batched", "fp8_grouped_direct_transpose", "fp8_kgrouped_gemm", "swiglu_quant_cache",
     "unpermute_backward_quant", "fp8_quant_rowwise_fmt", "fp8_dequant_fmt", "fgb_fp8_encode",
     "fp8_direct_transpose_fmt", "mx2_quant_rule", "fp8_block_gemm_fmt", "fp8_grouped_gemm_masked",
-    "permute_pad_noalloc", "PERMUTE_PAD_NOALLOC_SCRATCH_BYTES",
+    "permute_pad_noalloc", "PERMUTE_PAD_NOALLOC_SCRATCH_BYTES", "fgb_hbm_probe",
+    "PROBE_COPY", "PROBE_READ", "PROBE_FILL", "PROBE_STRIDED_READ", "PROBE_STRIDED_WRITE",
     "E4M3", "E5M2", "SCALE_CEIL", "SCALE_OCP_FLOOR", "F32", "BF16", "ROW1x128", "ROW1x32", "BLOCK128", "GEMM_EXACT", "GEMM_FAST",
 ]
 
@@ -34,6 +35,7 @@ ROW1x128, ROW1x32, BLOCK128 = 0, 1, 2
 GEMM_EXACT, GEMM_FAST = 0, 1
 E4M3, E5M2 = 0, 1
 SCALE_CEIL, SCALE_OCP_FLOOR = 0, 1
+PROBE_COPY, PROBE_READ, PROBE_FILL, PROBE_STRIDED_READ, PROBE_STRIDED_WRITE = 0, 1, 2, 3, 4
 
 SYMBOLS = [
     "fgb_last_error", "fgb_version", "fp8_quant_rowwise", "fp8_quant_blockwise", "fp8_dequant",
@@ -44,7 +46,7 @@ SYMBOLS = [
     "fp8_grouped_direct_transpose", "fp8_kgrouped_gemm", "swiglu_quant_cache", "unpermute_backward_quant",
     "fp8_quant_rowwise_fmt", "fp8_dequant_fmt", "fgb_fp8_encode", "fp8_direct_transpose_fmt", "mx2_quant_rule",
     "fp8_block_gemm_fmt", "fp8_grouped_gemm_masked", "fp8_quant_blockwise_t", "swiglu_f32", "dswiglu_f32",
-    "permute_pad_noalloc",
+    "permute_pad_noalloc", "fgb_hbm_probe",
 ]
 
 
@@ -67,6 +69,7 @@ _SIG = {
     "fp8_quant_blockwise": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p]),
     "fp8_dequant": (_i32, [_p, _p, _i32, _i64, _i64, _p, _i32, _p]),
     "fgb_e4m3_encode": (_i32, [_p, _i64, _p, _p]),
+    "fgb_hbm_probe": (_i32, [_p, _p, _i64, _i64, _i32, _p]),
     "fp8_direct_transpose": (_i32, [_p, _p, _i32, _i64, _i64, _p, _p, _p]),
     "fp8_naive_transpose": (_i32, [_p, _p, _i64, _i64, _p, _p, _p, _sz, _p]),
     "fp8_block_transpose_batched": (_i32, [_p, _p, _i32, _i64, _i64, _p, _p, _p]),
@@ -333,6 +336,32 @@ def fgb_e4m3_encode(x):
     q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     _call("fgb_e4m3_encode", _ptr(x), x.numel(), _ptr(q), _stream(x))
     return q
+
+
+def fgb_hbm_probe(src, dst, pattern):
+    """Diagnostic byte movement in one access pattern (PROBE_*); src and dst are
+    contiguous uint8 [rows, cols] tensors (rows, cols multiples of 128), except
+    that PROBE_READ's dst holds rows*cols/256 bytes and PROBE_FILL takes no src.
+    Returns dst."""
+    if pattern not in (PROBE_COPY, PROBE_READ, PROBE_FILL, PROBE_STRIDED_READ, PROBE_STRIDED_WRITE):
+        raise ValueError(f"fgb_hbm_probe: unknown pattern {pattern}")
+    ref = dst if src is None else src
+    _check_2d_codes(ref, "fgb_hbm_probe: src")
+    rows, cols = ref.shape
+    if rows % 128 or cols % 128:
+        raise ValueError("fgb_hbm_probe: rows and cols must be multiples of 128")
+    if pattern == PROBE_FILL:
+        if src is not None:
+            _need(src, "fgb_hbm_probe: src", shape=(rows, cols), dtype=torch.uint8, contiguous=True)
+    else:
+        _need(src, "fgb_hbm_probe: src", shape=(rows, cols), dtype=torch.uint8, contiguous=True)
+    _need(dst, "fgb_hbm_probe: dst", dtype=torch.uint8, contiguous=True)
+    need = rows * cols // 256 if pattern == PROBE_READ else rows * cols
+    if dst.numel() != need:
+        raise ValueError(f"fgb_hbm_probe: dst must hold {need} bytes, got {dst.numel()}")
+    _check_dev(src, dst)
+    _call("fgb_hbm_probe", _ptr(src), _ptr(dst), rows, cols, pattern, _stream(dst))
+    return dst
 
 
 def fp8_direct_transpose(q, s, s_gran=ROW1x128):

@@ -541,6 +541,37 @@ int mx2_quant_rule(const void *x, int64_t R, int64_t C, int64_t g1, int rule, ui
 int mx2_dequant(const uint8_t *q, const uint8_t *s2, const float *s1, int64_t R, int64_t C,
                 int64_t g1, float *out, void *stream);
 
+/* access patterns of fgb_hbm_probe */
+#define FGB_PROBE_COPY 0
+#define FGB_PROBE_READ 1
+#define FGB_PROBE_FILL 2
+#define FGB_PROBE_STRIDED_READ 3
+#define FGB_PROBE_STRIDED_WRITE 4
+
+/*
+ * fgb_hbm_probe -- diagnostic, not part of the method: plain byte movement in
+ * the access patterns of the data-movement kernels, with their 16-byte
+ * nontemporal loads and stores, so that each kernel's bandwidth can be set
+ * beside what its pattern sustains on the same device.  src and dst are
+ * device buffers of rows * cols bytes (rows % 128 == 0, cols % 128 == 0),
+ * 16-byte aligned, not overlapping:
+ *   FGB_PROBE_COPY          dst = src;
+ *   FGB_PROBE_READ          dst[16*b .. 16*b+15] = XOR of the 16-byte words of
+ *                           src[4096*b .. 4096*b+4095] (dst needs rows*cols/256
+ *                           bytes);
+ *   FGB_PROBE_FILL          dst = 0 (src unused, may be null);
+ *   FGB_PROBE_STRIDED_READ  src read as [rows, cols] by 128x128 blocks, the
+ *                           way the direct transpose reads its codes (16
+ *                           rows of 16 bytes per lane, 8 lanes per 128-byte
+ *                           row piece); block b = tb + (rows/128)*cb written
+ *                           to dst[16384*b ..] as 16 rows of 1 KB, row j of
+ *                           the lane's 16 at dst[16384*b + 1024*j + 16*lane];
+ *   FGB_PROBE_STRIDED_WRITE the inverse map: dst as [rows, cols] written by
+ *                           128-byte row pieces from contiguous src blocks.
+ * One kernel on `stream`; FGB_EINVAL / FGB_EUNSUPPORTED on bad arguments.
+ */
+int fgb_hbm_probe(const void *src, void *dst, int64_t rows, int64_t cols, int pattern, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -191,3 +191,15 @@ def test_permute_pad_noalloc_rejects_sizes_beyond_its_scratch():
     assert L.permute_pad_workspace_size(T + 256, topk, 32) > fgb.PERMUTE_PAD_NOALLOC_SCRATCH_BYTES
     # argument errors come first, as for permute_pad
     assert L.permute_pad_noalloc(None, f, f, 16, topk, 32, 7168, 16, f, f, f, f, 16 * topk + 15 * 32, None) == 1
+
+
+def test_hbm_probe_validation():
+    import fine_grained_blockwise_amd as fgb
+    L = fgb.lib()
+    f = _fake()
+    assert L.fgb_hbm_probe(f, f, 256, 256, 9, None) == 2             # unknown pattern
+    assert L.fgb_hbm_probe(None, f, 256, 256, fgb.PROBE_COPY, None) == 1
+    assert b"null" in L.fgb_last_error()
+    assert L.fgb_hbm_probe(f, f, 200, 256, fgb.PROBE_STRIDED_READ, None) == 1  # rows % 128
+    assert L.fgb_hbm_probe(f, _fake(0x1008), 256, 256, fgb.PROBE_COPY, None) == 1  # alignment
+    assert L.fgb_hbm_probe(f, f, 0, 256, fgb.PROBE_COPY, None) == 0  # empty: touches nothing
