@@ -560,12 +560,16 @@ __global__ __launch_bounds__(256) void dswiglu_quant_kernel(const uint8_t *__res
                 const uint32_t gw[2] = {gq[u].x, gq[u].y}, uw[2] = {uq[u].x, uq[u].y};
                 const uint32_t aw[4] = {av[u].x, av[u].y, av[u].z, av[u].w};
                 float g[8], uu[8], a[8], dg[8], du[8];
+                // decode x scale in one conversion per two codes (the scale
+                // operand's exponent field is the power of two; exact)
 #pragma unroll
                 for (int k = 0; k < 2; k++) {
-                    const float2 g0 = dec2_lo(gw[k]), g1 = dec2_hi(gw[k]);
-                    const float2 u0 = dec2_lo(uw[k]), u1 = dec2_hi(uw[k]);
-                    g[4 * k + 0] = g0.x * fg; g[4 * k + 1] = g0.y * fg; g[4 * k + 2] = g1.x * fg; g[4 * k + 3] = g1.y * fg;
-                    uu[4 * k + 0] = u0.x * fu; uu[4 * k + 1] = u0.y * fu; uu[4 * k + 2] = u1.x * fu; uu[4 * k + 3] = u1.y * fu;
+                    const fgb_f32x2 g0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)gw[k], fg, false);
+                    const fgb_f32x2 g1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)gw[k], fg, true);
+                    const fgb_f32x2 u0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)uw[k], fu, false);
+                    const fgb_f32x2 u1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)uw[k], fu, true);
+                    g[4 * k + 0] = g0.x; g[4 * k + 1] = g0.y; g[4 * k + 2] = g1.x; g[4 * k + 3] = g1.y;
+                    uu[4 * k + 0] = u0.x; uu[4 * k + 1] = u0.y; uu[4 * k + 2] = u1.x; uu[4 * k + 3] = u1.y;
                 }
 #pragma unroll
                 for (int k = 0; k < 4; k++) {
