@@ -656,6 +656,25 @@ def test_dswiglu_quant(fgb, M, F, use_off):
     assert np.array_equal(np_(dq)[:rows], oq[:rows])
 
 
+def test_dswiglu_quant_smallest_scale_bytes(fgb):
+    """Cache scale bytes 0..3 (2^-127..2^-124: decoded inputs in the fp32
+    subnormal range) and the largest bytes the rule allows beside ordinary
+    ones: the scale byte is read as 2^(byte - 127) for every byte, as the
+    oracle reads it."""
+    say("dswiglu_quant smallest scale bytes")
+    M, F = 64, 256
+    g = torch.Generator().manual_seed(7)
+    hq = torch.randint(0, 256, (M, 2 * F), dtype=torch.uint8, generator=g)
+    hq[(hq & 0x7F) == 0x7F] = 0x11  # no NaN codes
+    choices = torch.tensor([0, 1, 2, 3, 100, 120, 127, 130], dtype=torch.uint8)
+    hs = choices[torch.randint(0, len(choices), (M, 2 * F // 128), generator=g)]
+    da = (torch.randn((M, F), generator=g) * 0.1).to(torch.bfloat16)
+    dq, ds = fgb.dswiglu_quant(hq.to(DEV), hs.to(DEV), da.to(DEV), None)
+    oq, os_ = O.dswiglu_quant(hq.numpy(), hs.numpy(), bits(da), None)
+    assert np.array_equal(np_(ds), os_)
+    assert np.array_equal(np_(dq), oq)
+
+
 def _every_swiglu_input():
     """Every g the SwiGLU kernels can see: all finite bf16 values (the forward's
     input) and every finite E4M3 code times every 1x128 scale 2^-22..2^127
