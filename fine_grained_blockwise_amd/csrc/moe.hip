@@ -731,16 +731,21 @@ __global__ __launch_bounds__(256) void ub_token_quant_kernel(const uint16_t *__r
         const uint16_t *src = dout + t * H;
         for (int64_t c0 = 0; c0 < H8; c0 += 64 * UBT_U) {
             float x[UBT_U][8];
+            uint32_t ax[UBT_U]; // |x| maximum of each 128-group (bits), over the group's 16 lanes
 #pragma unroll
             for (int u = 0; u < UBT_U; u++) {
                 const int64_t c = c0 + u * 64 + lane;
                 const uint4 v = c < H8 ? ld_stream16(src + c * 8) : make_uint4(0, 0, 0, 0);
                 const uint32_t x4[4] = {v.x, v.y, v.z, v.w};
+                uint32_t m = 0;
 #pragma unroll
                 for (int k = 0; k < 4; k++) {
                     x[u][2 * k] = bf16lo(x4[k]);
                     x[u][2 * k + 1] = bf16hi(x4[k]);
+                    m = max(m, max(__float_as_uint(x[u][2 * k]) & 0x7FFFFFFFu,
+                                   __float_as_uint(x[u][2 * k + 1]) & 0x7FFFFFFFu));
                 }
+                ax[u] = group_max_u32<16>(m);
             }
             for (int k = 0; k < topk; k++) {
                 const int32_t r = __builtin_amdgcn_readlane(rv, k);
@@ -760,8 +765,14 @@ __global__ __launch_bounds__(256) void ub_token_quant_kernel(const uint16_t *__r
                         y[2 * j] = bf16lo(b);
                         y[2 * j + 1] = bf16hi(b);
                     }
-                    int e;
-                    const uint2 o = quant8_group16(y, e);
+                    // The group's amax of y = bf16(w * x) is bf16(|w| * amax|x|): the fp32
+                    // product and the bf16 rounding are monotonic in |x|, so the
+                    // per-slot group reduction is not needed.
+                    const float am = bf16lo(pack_bf16x2(fabsf(w) * __uint_as_float(ax[u]), 0.0f));
+                    const int e = scale_exp_from_bits(__float_as_uint(am), -22);
+                    const float sc = pow2f(-e);
+                    const uint2 o = make_uint2(cvt4_e4m3(y[0] * sc, y[1] * sc, y[2] * sc, y[3] * sc),
+                                               cvt4_e4m3(y[4] * sc, y[5] * sc, y[6] * sc, y[7] * sc));
                     if (c < H8) {
                         st_stream8(dq + c * 8, o);
                         if ((lane & 15) == 0)
