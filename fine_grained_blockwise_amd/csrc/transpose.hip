@@ -321,16 +321,26 @@ __global__ __launch_bounds__(256) void direct_transpose_reg_kernel(const uint8_t
 }
 
 // ---- expert segments, for the expert backward's Wgrad --------------------------
-// koff[e+1] = koff[e] + ceil(len_e / 128) * 128 (one thread; G <= 1024).
-__global__ void koff_kernel(const int32_t *__restrict__ off, int G, int32_t *__restrict__ koff)
+// koff[e+1] = koff[e] + ceil(len_e / 128) * 128 (G <= 1024): one wave, lane
+// l taking expert g0 + l of each pass of 64, an inclusive wave prefix sum of
+// the padded lengths plus the carry of the passes before.
+__global__ __launch_bounds__(64) void koff_kernel(const int32_t *__restrict__ off, int G, int32_t *__restrict__ koff)
 {
-    if (threadIdx.x == 0 && blockIdx.x == 0) {
-        int32_t k = 0;
+    const int lane = lane_id();
+    int32_t carry = 0;
+    if (lane == 0)
         koff[0] = 0;
-        for (int e = 0; e < G; e++) {
-            k += ((off[e + 1] - off[e] + 127) / 128) * 128;
-            koff[e + 1] = k;
+    for (int g0 = 0; g0 < G; g0 += 64) {
+        const int g = g0 + lane;
+        int32_t v = g < G ? ((off[g + 1] - off[g] + 127) / 128) * 128 : 0;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int32_t u = __shfl_up(v, d);
+            v += lane >= d ? u : 0;
         }
+        if (g < G)
+            koff[g + 1] = carry + v;
+        carry += __shfl(v, 63);
     }
 }
 
