@@ -910,6 +910,8 @@ def main():
     roofline = {"bound": dkind, "achieved": round(dach, 1), "peak": dpeak,
                 "unit": "GB/s" if dkind == "hbm" else "TFLOP/s", "frac": round(dach / dpeak, 4),
                 "traffic": traffic_for(dname, args.gemm_mode), "kernel": dname}
+    if dkind == "mfma":  # the FP8 GEMM's rate against the dense FP8 peak, beside its contraction's own
+        roofline["frac_of_fp8_peak"] = round(dach / FP8_PEAK_TFLOPS, 4)
 
     extra = {}
     if "moss" in out:

@@ -32,6 +32,8 @@ def test_bench_line_contract():
         assert k in rf, k
     assert rf["bound"] in ("hbm", "mfma", "alu")
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
+    if rf["bound"] == "mfma":
+        assert abs(rf["frac_of_fp8_peak"] - rf["achieved"] / 5000.0) < 1e-3
     assert len(line["kernels"]) == 9  # the Linear forward and backward: 3 quant, 2 transposes, W^T, 3 GEMMs
     # every GEMM is priced at the dense FP8 peak in `value`; the mode's own instruction peak beside it
     assert line["value_at_contraction_peak"] >= line["value"] > 0
